@@ -1,0 +1,380 @@
+// Host side of the C ABI declared in include/mk.h: handle lifetime, device
+// memory, weight packing, and the per-step launches.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/mk.h"
+#include "mk_internal.h"
+#include "mk_plan.h"
+
+namespace mk {
+hipError_t launch_step(const Params* dev_params, int ncu, size_t lds_bytes, const int32_t* tokens,
+                       const int32_t* positions, void* kv, float* logits, int stage, uint32_t flags,
+                       hipStream_t stream);
+hipError_t set_step_kernel_lds(size_t lds_bytes);
+hipError_t launch_pack(const void* rows, uint32_t n, const uint16_t* const* mats, uint8_t* dst, hipStream_t stream);
+}  // namespace mk
+
+using namespace mk;
+
+struct mk_handle {
+    mk_config cfg{};
+    Plan plan;
+    Params hp{};
+    Params* dparams = nullptr;
+    std::vector<void*> allocs;  // everything hipMalloc'ed, freed in mk_destroy
+    size_t lds_bytes = 0;
+    bool loaded = false;
+    std::string last_error;
+};
+
+static thread_local std::string g_create_error;
+
+namespace {
+
+struct HipError {
+    hipError_t e;
+    const char* what;
+};
+
+#define HIPCHK(call)                                     \
+    do {                                                 \
+        hipError_t _e = (call);                          \
+        if (_e != hipSuccess) throw HipError{_e, #call}; \
+    } while (0)
+
+template <class T>
+T* dalloc(mk_handle* h, size_t count) {
+    void* p = nullptr;
+    if (count == 0) count = 1;
+    hipError_t e = hipMalloc(&p, count * sizeof(T));
+    if (e != hipSuccess) throw HipError{e, "hipMalloc"};
+    h->allocs.push_back(p);
+    return (T*)p;
+}
+
+template <class T>
+T* dupload(mk_handle* h, const std::vector<T>& v) {
+    T* d = dalloc<T>(h, v.size());
+    if (!v.empty()) HIPCHK(hipMemcpy(d, v.data(), v.size() * sizeof(T), hipMemcpyHostToDevice));
+    return d;
+}
+
+int fail(mk_handle* h, int code, const std::string& msg) {
+    if (h) h->last_error = msg;
+    else g_create_error = msg;
+    return code;
+}
+
+int hip_fail(mk_handle* h, const HipError& e) {
+    std::string msg = std::string(e.what) + ": " + hipGetErrorString(e.e);
+    return fail(h, e.e == hipErrorOutOfMemory ? MK_ERR_OOM : MK_ERR_HIP, msg);
+}
+
+void free_all(mk_handle* h) {
+    for (void* p : h->allocs) (void)hipFree(p);
+    h->allocs.clear();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mk_status_string(int s) {
+    switch (s) {
+    case MK_OK: return "ok";
+    case MK_ERR_INVALID_ARG: return "invalid argument";
+    case MK_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case MK_ERR_HIP: return "HIP runtime error";
+    case MK_ERR_OOM: return "out of memory";
+    case MK_ERR_STATE: return "invalid call order";
+    case MK_ERR_DEVICE: return "device error record";
+    default: return "unknown status";
+    }
+}
+
+const char* mk_last_error(const mk_handle* h) { return h ? h->last_error.c_str() : g_create_error.c_str(); }
+
+size_t mk_kv_cache_bytes(const mk_config* c) {
+    if (!c) return 0;
+    std::string err;
+    if (validate_config(*c, err) != MK_OK) return 0;
+    return (size_t)c->n_layers * 2 * c->batch * c->n_kv_heads * (size_t)c->max_seq * c->head_dim * 2;
+}
+
+int mk_schedule_inspect(const mk_config* cfg, int32_t n_cus, mk_schedule_info* out) {
+    if (!cfg || !out || n_cus < 1) return fail(nullptr, MK_ERR_INVALID_ARG, "null argument or n_cus < 1");
+    Plan p;
+    std::string err;
+    int rc;
+    try {
+        rc = build_plan(*cfg, n_cus, p, err);
+    } catch (const std::bad_alloc&) {
+        return fail(nullptr, MK_ERR_OOM, "host allocation failed");
+    }
+    if (rc != MK_OK) return fail(nullptr, rc, err);
+    std::memset(out, 0, sizeof *out);
+    out->n_cus = p.ncu;
+    out->n_splits = p.n_split;
+    out->n_chunks = p.n_chunk;
+    out->total_insts = (int64_t)p.insts.size();
+    for (int cu = 0; cu < p.ncu; ++cu)
+        out->max_insts_per_cu = std::max(out->max_insts_per_cu, (int32_t)(p.queue_begin[cu + 1] - p.queue_begin[cu]));
+    out->packed_weight_bytes = (int64_t)p.total_units * UNIT_BYTES;
+    int64_t mx = 0, mn = INT64_MAX;
+    for (uint64_t len : p.stream_len) {
+        mx = std::max(mx, (int64_t)len * UNIT_BYTES);
+        mn = std::min(mn, (int64_t)len * UNIT_BYTES);
+    }
+    out->max_stream_bytes_per_wave = mx;
+    out->min_stream_bytes_per_wave = mn;
+    out->launches_multikernel = p.n_stages;
+    out->valid = check_plan(p, err) ? 1 : 0;
+    if (!out->valid) g_create_error = err;
+    return MK_OK;
+}
+
+int mk_create(const mk_config* cfg, mk_handle** out) {
+    if (!out) return fail(nullptr, MK_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (!cfg) return fail(nullptr, MK_ERR_INVALID_ARG, "cfg is NULL");
+    std::string err;
+    int rc = validate_config(*cfg, err);
+    if (rc != MK_OK) return fail(nullptr, rc, err);
+    mk_handle* h = new (std::nothrow) mk_handle();
+    if (!h) return fail(nullptr, MK_ERR_OOM, "host allocation failed");
+    h->cfg = *cfg;
+    try {
+        int ndev = 0;
+        HIPCHK(hipGetDeviceCount(&ndev));
+        if (cfg->device < 0 || cfg->device >= ndev) {
+            delete h;
+            return fail(nullptr, MK_ERR_INVALID_ARG, "device ordinal out of range");
+        }
+        HIPCHK(hipSetDevice(cfg->device));
+        int ncu_dev = 0;
+        HIPCHK(hipDeviceGetAttribute(&ncu_dev, hipDeviceAttributeMultiprocessorCount, cfg->device));
+        int ncu = cfg->n_cus ? cfg->n_cus : ncu_dev;
+        if (ncu > ncu_dev) {
+            delete h;
+            return fail(nullptr, MK_ERR_INVALID_ARG, "n_cus exceeds the device's CU count");
+        }
+        Plan& p = h->plan;
+        rc = build_plan(*cfg, ncu, p, err);
+        if (rc == MK_OK && !check_plan(p, err)) rc = MK_ERR_UNSUPPORTED_SHAPE;
+        if (rc != MK_OK) {
+            delete h;
+            return fail(nullptr, rc, err);
+        }
+        // LDS: two x buffers (also scratch of attention/reduce), sync words, rest = rings
+        const int xstride = std::max(std::max(p.ku_h, p.ku_q), p.ku_f) * UNIT_ELEMS;
+        size_t xb = (size_t)p.B * xstride * 4;
+        const size_t attn_scratch = (size_t)(p.G * p.D + 2 * p.D + NW * (p.D + 2) + NW * 64) * 4;
+        const size_t red_scratch = (size_t)p.n_split * (p.D + 2) * 4;
+        xb = std::max(xb, std::max(attn_scratch, red_scratch));
+        xb = (xb + 15) / 16 * 16;
+        const size_t sync_bytes = 512;
+        long ring_budget = (long)LDS_BYTES - 2 * (long)xb - (long)sync_bytes;
+        int ring_units = (int)std::min<long>(32, ring_budget / (NW * UNIT_BYTES));
+        if (ring_units < 2) {
+            delete h;
+            return fail(nullptr, MK_ERR_UNSUPPORTED_SHAPE, "batch x hidden too large for the LDS budget");
+        }
+        h->lds_bytes = (size_t)NW * ring_units * UNIT_BYTES + 2 * xb + sync_bytes;
+
+        Params& hp = h->hp;
+        hp.L = p.L; hp.H = p.H; hp.Hq = p.Hq; hp.Hkv = p.Hkv; hp.D = p.D; hp.F = p.F; hp.V = p.V; hp.B = p.B;
+        hp.max_seq = p.max_seq; hp.G = p.G; hp.n_split = p.n_split; hp.n_chunk = p.n_chunk;
+        hp.ku_h = p.ku_h; hp.ku_q = p.ku_q; hp.ku_f = p.ku_f; hp.xstride = xstride;
+        hp.ring_units = ring_units; hp.xbuf_bytes = (int)xb; hp.ncu = ncu;
+        hp.eps = p.eps; hp.inv_sqrt_d = (float)(1.0 / std::sqrt((double)p.D));
+        hp.spin_limit = 1u << 25;
+        for (int i = 0; i <= p.n_chunk; ++i) hp.chunk_begin[i] = p.chunk_begin[i];
+        hp.n_stages = p.n_stages;
+
+        hp.wstream = dalloc<uint8_t>(h, (size_t)p.total_units * UNIT_BYTES);
+        hp.stream_base = dupload(h, p.stream_base);
+        hp.insts = dupload(h, p.insts);
+        hp.queue_begin = dupload(h, p.queue_begin);
+        hp.unit_off = dupload(h, p.unit_off);
+        hp.stage_pc = dupload(h, p.stage_pc);
+        hp.embed = dalloc<uint16_t>(h, (size_t)p.V * p.H);
+        hp.gain_attn = dalloc<uint16_t>(h, (size_t)p.L * p.H);
+        hp.gain_mlp = dalloc<uint16_t>(h, (size_t)p.L * p.H);
+        hp.gain_final = dalloc<uint16_t>(h, (size_t)p.H);
+        // RoPE table: angle p * theta^(-2i/D) in double, cos/sin rounded to fp32
+        {
+            const int half = p.D / 2;
+            std::vector<float> rope((size_t)p.max_seq * half * 2);
+            for (int i = 0; i < half; ++i) {
+                const double f = std::pow((double)p.theta, -2.0 * i / p.D);
+                for (int pos = 0; pos < p.max_seq; ++pos) {
+                    const double a = (double)pos * f;
+                    rope[((size_t)pos * half + i) * 2 + 0] = (float)std::cos(a);
+                    rope[((size_t)pos * half + i) * 2 + 1] = (float)std::sin(a);
+                }
+            }
+            hp.rope = dupload(h, rope);
+        }
+        // tagged activations (zeroed: tag 0 never matches a step epoch)
+        const size_t B = p.B, L = p.L, H = p.H, QD = (size_t)p.Hq * p.D, KD = (size_t)p.Hkv * p.D;
+        const size_t n_q = L * B * QD, n_kv = L * B * KD, n_part = L * B * p.Hq * p.n_split * (p.D + 2);
+        const size_t n_attn = L * B * QD, n_h = L * B * H, n_act = L * B * p.F;
+        const size_t words = n_q + 2 * n_kv + n_part + n_attn + 2 * n_h + n_act;
+        uint64_t* arena = dalloc<uint64_t>(h, words);
+        HIPCHK(hipMemset(arena, 0, words * 8));
+        uint64_t* cur = arena;
+        hp.q = cur; cur += n_q;
+        hp.knew = cur; cur += n_kv;
+        hp.vnew = cur; cur += n_kv;
+        hp.part = cur; cur += n_part;
+        hp.attn = cur; cur += n_attn;
+        hp.hmid = cur; cur += n_h;
+        hp.act = cur; cur += n_act;
+        hp.hout = cur; cur += n_h;
+        hp.dacc = dalloc<float>(h, B * H);
+        hp.mats = nullptr;
+        hp.epoch = dalloc<uint32_t>(h, (size_t)ncu);
+        HIPCHK(hipMemset(hp.epoch, 0, (size_t)ncu * 4));
+        hp.error = dalloc<uint32_t>(h, 8);
+        HIPCHK(hipMemset(hp.error, 0, 32));
+        h->dparams = dalloc<Params>(h, 1);
+        HIPCHK(hipMemcpy(h->dparams, &hp, sizeof hp, hipMemcpyHostToDevice));
+        HIPCHK(set_step_kernel_lds(h->lds_bytes));
+        HIPCHK(hipDeviceSynchronize());
+    } catch (const HipError& e) {
+        int code = hip_fail(nullptr, e);
+        free_all(h);
+        delete h;
+        return code;
+    } catch (const std::bad_alloc&) {
+        free_all(h);
+        delete h;
+        return fail(nullptr, MK_ERR_OOM, "host allocation failed");
+    }
+    *out = h;
+    return MK_OK;
+}
+
+int mk_load_weights(mk_handle* h, const mk_weights* w, void* stream) {
+    if (!h) return fail(nullptr, MK_ERR_INVALID_ARG, "handle is NULL");
+    if (!w || !w->embed || !w->final_norm || !w->attn_norm || !w->wq || !w->wk || !w->wv || !w->wo ||
+        !w->mlp_norm || !w->w_gate || !w->w_up || !w->w_down)
+        return fail(h, MK_ERR_INVALID_ARG, "a weight pointer is NULL");
+    const Plan& p = h->plan;
+    if (!p.tied && !w->lm_head) return fail(h, MK_ERR_INVALID_ARG, "lm_head is NULL for an untied model");
+    for (int l = 0; l < p.L; ++l)
+        if (!w->attn_norm[l] || !w->wq[l] || !w->wk[l] || !w->wv[l] || !w->wo[l] || !w->mlp_norm[l] ||
+            !w->w_gate[l] || !w->w_up[l] || !w->w_down[l])
+            return fail(h, MK_ERR_INVALID_ARG, "a per-layer weight pointer is NULL");
+    hipStream_t s = (hipStream_t)stream;
+    void* d_rows = nullptr;
+    void* d_mats = nullptr;
+    try {
+        HIPCHK(hipSetDevice(h->cfg.device));
+        std::vector<const uint16_t*> mats((size_t)p.n_mats(), nullptr);
+        for (int l = 0; l < p.L; ++l) {
+            const size_t b = (size_t)l * MATS_PER_LAYER;
+            mats[b + MAT_WQ] = (const uint16_t*)w->wq[l];
+            mats[b + MAT_WK] = (const uint16_t*)w->wk[l];
+            mats[b + MAT_WV] = (const uint16_t*)w->wv[l];
+            mats[b + MAT_WO] = (const uint16_t*)w->wo[l];
+            mats[b + MAT_GATE] = (const uint16_t*)w->w_gate[l];
+            mats[b + MAT_UP] = (const uint16_t*)w->w_up[l];
+            mats[b + MAT_DOWN] = (const uint16_t*)w->w_down[l];
+        }
+        mats[p.lm_mat()] = (const uint16_t*)(p.tied ? w->embed : w->lm_head);
+        HIPCHK(hipMalloc(&d_rows, p.pack.size() * sizeof(PackRow)));
+        HIPCHK(hipMalloc(&d_mats, mats.size() * sizeof(void*)));
+        HIPCHK(hipMemcpyAsync(d_rows, p.pack.data(), p.pack.size() * sizeof(PackRow), hipMemcpyHostToDevice, s));
+        HIPCHK(hipMemcpyAsync(d_mats, mats.data(), mats.size() * sizeof(void*), hipMemcpyHostToDevice, s));
+        HIPCHK(launch_pack(d_rows, (uint32_t)p.pack.size(), (const uint16_t* const*)d_mats, (uint8_t*)h->hp.wstream, s));
+        const size_t HB = (size_t)p.H * 2;
+        HIPCHK(hipMemcpyAsync((void*)h->hp.embed, w->embed, (size_t)p.V * HB, hipMemcpyDeviceToDevice, s));
+        for (int l = 0; l < p.L; ++l) {
+            HIPCHK(hipMemcpyAsync((uint8_t*)h->hp.gain_attn + l * HB, w->attn_norm[l], HB, hipMemcpyDeviceToDevice, s));
+            HIPCHK(hipMemcpyAsync((uint8_t*)h->hp.gain_mlp + l * HB, w->mlp_norm[l], HB, hipMemcpyDeviceToDevice, s));
+        }
+        HIPCHK(hipMemcpyAsync((void*)h->hp.gain_final, w->final_norm, HB, hipMemcpyDeviceToDevice, s));
+        HIPCHK(hipStreamSynchronize(s));
+        HIPCHK(hipFree(d_rows));
+        d_rows = nullptr;
+        HIPCHK(hipFree(d_mats));
+        d_mats = nullptr;
+    } catch (const HipError& e) {
+        if (d_rows) (void)hipFree(d_rows);
+        if (d_mats) (void)hipFree(d_mats);
+        return hip_fail(h, e);
+    }
+    static_assert(sizeof(PackRow) == 32, "PackRow matches the device pack record");
+    h->loaded = true;
+    h->last_error.clear();
+    return MK_OK;
+}
+
+static int step_args_ok(mk_handle* h, const int32_t* tokens, const int32_t* positions, void* kv, float* logits) {
+    if (!h) return fail(nullptr, MK_ERR_INVALID_ARG, "handle is NULL");
+    if (!tokens || !positions || !kv || !logits) return fail(h, MK_ERR_INVALID_ARG, "a step pointer is NULL");
+    if (!h->loaded) return fail(h, MK_ERR_STATE, "mk_load_weights has not been called");
+    return MK_OK;
+}
+
+int mk_decode_step(mk_handle* h, const int32_t* tokens, const int32_t* positions, void* kv_cache, float* logits,
+                   void* stream) {
+    int rc = step_args_ok(h, tokens, positions, kv_cache, logits);
+    if (rc != MK_OK) return rc;
+    hipError_t e = launch_step(h->dparams, h->hp.ncu, h->lds_bytes, tokens, positions, kv_cache, logits, -1,
+                               KF_BUMP_EPOCH, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(h, HipError{e, "mk_step_kernel launch"});
+    return MK_OK;
+}
+
+int mk_decode_step_multikernel(mk_handle* h, const int32_t* tokens, const int32_t* positions, void* kv_cache,
+                               float* logits, void* stream) {
+    int rc = step_args_ok(h, tokens, positions, kv_cache, logits);
+    if (rc != MK_OK) return rc;
+    const int ns = h->hp.n_stages;
+    for (int st = 0; st < ns; ++st) {
+        hipError_t e = launch_step(h->dparams, h->hp.ncu, h->lds_bytes, tokens, positions, kv_cache, logits, st,
+                                   st == ns - 1 ? KF_BUMP_EPOCH : 0u, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(h, HipError{e, "mk_step_kernel stage launch"});
+    }
+    return MK_OK;
+}
+
+int mk_get_device_error(mk_handle* h, mk_device_error* out) {
+    if (!h || !out) return fail(h, MK_ERR_INVALID_ARG, "null argument");
+    uint32_t rec[8] = {0};
+    try {
+        HIPCHK(hipSetDevice(h->cfg.device));
+        HIPCHK(hipDeviceSynchronize());
+        HIPCHK(hipMemcpy(rec, h->hp.error, sizeof rec, hipMemcpyDeviceToHost));
+        if (rec[0] || rec[7]) HIPCHK(hipMemset(h->hp.error, 0, sizeof rec));
+    } catch (const HipError& e) {
+        return hip_fail(h, e);
+    }
+    out->code = rec[0];
+    out->workgroup = rec[1];
+    out->pc = rec[2];
+    out->opcode = rec[3];
+    out->wave = rec[4];
+    out->detail = rec[5];
+    return rec[0] ? MK_ERR_DEVICE : MK_OK;
+}
+
+int mk_destroy(mk_handle* h) {
+    if (!h) return MK_OK;
+    (void)hipSetDevice(h->cfg.device);
+    (void)hipDeviceSynchronize();
+    free_all(h);
+    delete h;
+    return MK_OK;
+}
+
+}  // extern "C"

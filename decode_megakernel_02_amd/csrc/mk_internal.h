@@ -1,0 +1,102 @@
+// Internal definitions shared by the host plan builder (mk_plan.cpp), the host
+// API (mk_api.cpp) and the device code (mk_kernels.hip).  Not part of the ABI.
+#pragma once
+#include <stdint.h>
+
+namespace mk {
+
+// Workgroup shape: one workgroup per CU, NW compute waves, each paired with one
+// loader wave that streams that compute wave's packed weights into its LDS ring.
+constexpr int NW = 8;                 // compute waves
+constexpr int NLOAD = NW;             // loader waves (1:1 with compute waves)
+constexpr int WG_THREADS = 64 * (NW + NLOAD);
+constexpr int UNIT_BYTES = 1024;      // one DMA: 64 lanes x 16 B
+constexpr int UNIT_ELEMS = 512;       // bf16 per unit
+constexpr int MAX_BATCH = 8;
+constexpr int LDS_BYTES = 160 * 1024; // gfx950 LDS per CU
+
+// Fused ops, in the order they appear inside one layer.  The page
+// "Megakernels: Deleting the Kernel Boundary to Win Back Microseconds"
+// (section "One launch, one interpreter") lists the same seven opcodes.
+enum Op : uint16_t {
+    OP_NONE = 0,
+    OP_RMS_QKV_ROPE = 1,  // RMSNorm + fused QKV rows + RoPE + K/V append
+    OP_ATTENTION = 2,     // split-KV partial attention for (row, KV group, split)
+    OP_ATTN_REDUCE = 3,   // log-sum-exp merge of the splits of one (row, head)
+    OP_O_PROJ_RES = 4,    // O projection + residual
+    OP_RMS_UP_GATE = 5,   // RMSNorm + gate/up rows + SiLU product
+    OP_DOWN_RES = 6,      // one K-chunk of down-proj for a CU's rows; the last chunk adds the residual
+    OP_RMS_LM_HEAD = 7,   // final RMSNorm + LM head rows
+};
+
+constexpr int STAGES_PER_LAYER = 6;  // QKV, ATTN, REDUCE, O, UPGATE, DOWN; LM head last
+
+// One queue entry (16 bytes).  GEMV ops: row-groups [rg0, rg0 + nrg) of the
+// op's row-group space, distributed round-robin over the NW compute waves
+// (row-group i goes to wave i % NW).  DOWN_RES: a = chunk.
+// ATTENTION: a = batch row, b = KV group, rg0 = split.
+// ATTN_REDUCE: a = batch row, b = query head.
+struct Inst {
+    uint16_t op;
+    uint16_t layer;
+    uint32_t rg0;
+    uint32_t nrg;
+    uint16_t a, b;
+};
+static_assert(sizeof(Inst) == 16, "Inst is 16 bytes");
+
+// Everything the kernel reads, in one device-resident block.
+struct Params {
+    // model / run shape
+    int32_t L, H, Hq, Hkv, D, F, V, B, max_seq;
+    int32_t G;              // Hq / Hkv
+    int32_t n_split, n_chunk;
+    int32_t ku_h;           // units per row for K = H (padded to 512)
+    int32_t ku_q;           // units per row for K = Hq*D
+    int32_t ku_f;           // units per row for one down chunk (padded)
+    int32_t xstride;        // floats per batch row in the LDS x buffer (max padded K)
+    int32_t ring_units;     // ring slots (1 KB units) per compute wave
+    int32_t xbuf_bytes;     // bytes of one of the two LDS x buffers
+    int32_t ncu;            // workgroups in the grid
+    float eps;
+    float inv_sqrt_d;
+    uint32_t spin_limit;    // bounded waits (watchdog)
+    int32_t chunk_begin[17];// down-proj chunk boundaries in [0, F], n_chunk + 1 entries
+
+    // packed weights: per (cu, wave) stream of units
+    const uint8_t* wstream;
+    const uint64_t* stream_base;   // [ncu * NW] unit offset of each stream
+    const Inst* insts;             // all queues back to back
+    const uint32_t* queue_begin;   // [ncu + 1] index into insts
+    const uint32_t* unit_off;      // [(queue_begin[cu] + pc + cu) * NW + w]: units before pc (pc in 0..len)
+    const uint32_t* stage_pc;      // [ncu * (n_stages + 1)] first pc of each stage in each queue
+    int32_t n_stages;
+
+    // weights read in place
+    const uint16_t* embed;         // [V][H] bf16 (token gather)
+    const uint16_t* gain_attn;     // [L][H]
+    const uint16_t* gain_mlp;      // [L][H]
+    const uint16_t* gain_final;    // [H]
+    const float* rope;             // [max_seq][D/2][2] (cos, sin)
+
+    // tagged activations: 64-bit words {low: fp32 bits, high: step epoch}
+    uint64_t* q;      // [L][B][Hq*D]
+    uint64_t* knew;   // [L][B][Hkv*D]  (bf16-rounded value of the new K row)
+    uint64_t* vnew;   // [L][B][Hkv*D]
+    uint64_t* part;   // [L][B][Hq][n_split][D+2]  (m, l, o[D])
+    uint64_t* attn;   // [L][B][Hq*D]
+    uint64_t* hmid;   // [L][B][H]   residual stream after the attention block
+    uint64_t* act;    // [L][B][F]   SwiGLU output
+    uint64_t* hout;   // [L][B][H]   residual stream after the MLP block (input of layer l+1)
+    float* dacc;      // [B][H]      down-proj chunk accumulator, private to the row's owner wave
+    const void* const* mats;  // unused by the step kernels (pack only)
+
+    uint32_t* epoch;  // [ncu] per-workgroup step counter
+    uint32_t* error;  // [8] device error record (code, wg, pc, op, wave, detail), abort flag at [7]
+};
+
+// Kernel launch flags.
+constexpr uint32_t KF_BUMP_EPOCH = 1u;  // last launch of a step: advance the per-workgroup epoch
+
+
+}  // namespace mk

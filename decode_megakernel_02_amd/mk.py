@@ -1,0 +1,177 @@
+"""ctypes binding of the decode library's C ABI (include/mk.h).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels of libmk.so.  Functions keep the C names; torch tensors (device
+memory) are passed as raw pointers.  If libmk.so has not been built, loading
+fails with an error instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, List, Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmk.so")
+
+MK_OK = 0
+MK_ERR_INVALID_ARG = -1
+MK_ERR_UNSUPPORTED_SHAPE = -2
+MK_ERR_HIP = -3
+MK_ERR_OOM = -4
+MK_ERR_STATE = -5
+MK_ERR_DEVICE = -6
+
+_P = ctypes.c_void_p
+
+
+class MkConfig(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("hidden", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
+                ("tied_embeddings", ctypes.c_int32), ("batch", ctypes.c_int32), ("max_seq", ctypes.c_int32),
+                ("device", ctypes.c_int32), ("n_cus", ctypes.c_int32), ("n_splits", ctypes.c_int32),
+                ("n_chunks", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class MkWeights(ctypes.Structure):
+    _fields_ = [("embed", _P), ("final_norm", _P), ("lm_head", _P)] + [
+        (n, ctypes.POINTER(_P)) for n in
+        ["attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down"]]
+
+
+class MkDeviceError(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint32) for n in ["code", "workgroup", "pc", "opcode", "wave", "detail"]]
+
+
+class MkScheduleInfo(ctypes.Structure):
+    _fields_ = [("n_cus", ctypes.c_int32), ("n_splits", ctypes.c_int32), ("n_chunks", ctypes.c_int32),
+                ("max_insts_per_cu", ctypes.c_int32), ("total_insts", ctypes.c_int64),
+                ("packed_weight_bytes", ctypes.c_int64), ("max_stream_bytes_per_wave", ctypes.c_int64),
+                ("min_stream_bytes_per_wave", ctypes.c_int64), ("launches_multikernel", ctypes.c_int32),
+                ("valid", ctypes.c_int32)]
+
+
+EXPORTS = ["mk_create", "mk_load_weights", "mk_kv_cache_bytes", "mk_decode_step", "mk_decode_step_multikernel",
+           "mk_destroy", "mk_status_string", "mk_last_error", "mk_get_device_error", "mk_schedule_inspect"]
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with decode_megakernel_02_amd/build.py "
+                               "(there is no fallback implementation)")
+        L = ctypes.CDLL(LIB_PATH)
+        H = ctypes.c_void_p  # mk_handle*
+        L.mk_create.argtypes = [ctypes.POINTER(MkConfig), ctypes.POINTER(H)]
+        L.mk_load_weights.argtypes = [H, ctypes.POINTER(MkWeights), _P]
+        L.mk_kv_cache_bytes.argtypes = [ctypes.POINTER(MkConfig)]
+        L.mk_kv_cache_bytes.restype = ctypes.c_size_t
+        L.mk_decode_step.argtypes = [H, _P, _P, _P, _P, _P]
+        L.mk_decode_step_multikernel.argtypes = [H, _P, _P, _P, _P, _P]
+        L.mk_destroy.argtypes = [H]
+        L.mk_status_string.argtypes = [ctypes.c_int]
+        L.mk_status_string.restype = ctypes.c_char_p
+        L.mk_last_error.argtypes = [H]
+        L.mk_last_error.restype = ctypes.c_char_p
+        L.mk_get_device_error.argtypes = [H, ctypes.POINTER(MkDeviceError)]
+        L.mk_schedule_inspect.argtypes = [ctypes.POINTER(MkConfig), ctypes.c_int32, ctypes.POINTER(MkScheduleInfo)]
+        for name in ["mk_create", "mk_load_weights", "mk_decode_step", "mk_decode_step_multikernel", "mk_destroy",
+                     "mk_get_device_error", "mk_schedule_inspect"]:
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+class MkError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{mk_status_string(code)} ({code}): {msg}")
+        self.code = code
+
+
+def mk_status_string(code: int) -> str:
+    return lib().mk_status_string(code).decode()
+
+
+def mk_last_error(handle=None) -> str:
+    return lib().mk_last_error(handle).decode()
+
+
+def _check(code: int, handle=None):
+    if code != MK_OK:
+        raise MkError(code, mk_last_error(handle))
+
+
+def make_config(shape, batch: int, max_seq: int, device: int = 0, n_cus: int = 0, n_splits: int = 0,
+                n_chunks: int = 0, flags: int = 0) -> MkConfig:
+    """MkConfig from a model shape object (attributes as in synth.ModelShape)."""
+    return MkConfig(shape.n_layers, shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.ffn,
+                    shape.vocab, shape.rms_eps, shape.rope_theta, 1 if shape.tied else 0, batch, max_seq, device,
+                    n_cus, n_splits, n_chunks, flags)
+
+
+def mk_create(cfg: MkConfig):
+    h = ctypes.c_void_p()
+    _check(lib().mk_create(ctypes.byref(cfg), ctypes.byref(h)))
+    return h
+
+
+def mk_kv_cache_bytes(cfg: MkConfig) -> int:
+    return int(lib().mk_kv_cache_bytes(ctypes.byref(cfg)))
+
+
+def mk_schedule_inspect(cfg: MkConfig, n_cus: int) -> MkScheduleInfo:
+    info = MkScheduleInfo()
+    _check(lib().mk_schedule_inspect(ctypes.byref(cfg), n_cus, ctypes.byref(info)))
+    return info
+
+
+def _ptr(t) -> int:
+    return t.data_ptr() if hasattr(t, "data_ptr") else int(t)
+
+
+def mk_load_weights(handle, weights: Dict[str, object], stream: Optional[int] = None):
+    """`weights`: {'embed', 'final_norm', 'lm_head' (or None), 'layers': [dict]} of device tensors (bf16)."""
+    layers: List[Dict[str, object]] = weights["layers"]
+    L = len(layers)
+    arrays = {}
+    w = MkWeights()
+    w.embed = _ptr(weights["embed"])
+    w.final_norm = _ptr(weights["final_norm"])
+    w.lm_head = _ptr(weights["lm_head"]) if weights.get("lm_head") is not None else None
+    for kind in ["attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down"]:
+        arr = (_P * L)(*[_ptr(layers[l][kind]) for l in range(L)])
+        arrays[kind] = arr
+        setattr(w, kind, ctypes.cast(arr, ctypes.POINTER(_P)))
+    _check(lib().mk_load_weights(handle, ctypes.byref(w), stream), handle)
+
+
+def mk_decode_step(handle, tokens, positions, kv_cache, logits, stream: Optional[int] = None):
+    _check(lib().mk_decode_step(handle, _ptr(tokens), _ptr(positions), _ptr(kv_cache), _ptr(logits), stream), handle)
+
+
+def mk_decode_step_multikernel(handle, tokens, positions, kv_cache, logits, stream: Optional[int] = None):
+    _check(lib().mk_decode_step_multikernel(handle, _ptr(tokens), _ptr(positions), _ptr(kv_cache), _ptr(logits),
+                                            stream), handle)
+
+
+def mk_get_device_error(handle) -> Optional[MkDeviceError]:
+    e = MkDeviceError()
+    rc = lib().mk_get_device_error(handle, ctypes.byref(e))
+    if rc == MK_ERR_DEVICE:
+        return e
+    _check(rc, handle)
+    return None
+
+
+def mk_destroy(handle):
+    _check(lib().mk_destroy(handle))
+
+
+def current_stream() -> int:
+    """hipStream_t of torch's current stream on the current device."""
+    import torch
+    return torch.cuda.current_stream().cuda_stream

@@ -1,0 +1,175 @@
+/*
+ * mk.h — C ABI of the MI355X (gfx950) decode library.
+ *
+ * One greedy decode step of a Llama-style decoder runs as ONE persistent
+ * kernel launch (mk_decode_step), or, for A/B comparison, as one launch per
+ * fused op and layer (mk_decode_step_multikernel).  The step is the fused op
+ * sequence that the page "Megakernels: Deleting the Kernel Boundary to Win
+ * Back Microseconds" lists in its section "One launch, one interpreter"
+ * (RMSNorm+QKV+RoPE, attention, attention reduce, O-proj+residual,
+ * RMSNorm+up/gate+SiLU, down-proj+residual, RMSNorm+LM head), executed by an
+ * on-device interpreter over per-CU instruction queues built on the host ahead
+ * of time (same section), with the data dependencies that the kernel boundary
+ * used to give rebuilt on device (section "Correctness without the free
+ * barrier").
+ *
+ * Conventions for every entry point:
+ *   - Return 0 (MK_OK) or a negative mk_status; no C++ exception crosses the ABI.
+ *   - "device pointer" arguments are HIP device allocations on the handle's
+ *     device; "host pointer" arguments are ordinary CPU memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   - The caller owns every buffer it passes; the library owns the handle and
+ *     everything it allocates.
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MK_OK = 0,
+    MK_ERR_INVALID_ARG = -1,       /* null pointer, out-of-range value */
+    MK_ERR_UNSUPPORTED_SHAPE = -2, /* config the kernels do not handle */
+    MK_ERR_HIP = -3,               /* a HIP runtime call failed; see mk_last_error */
+    MK_ERR_OOM = -4,               /* device or host allocation failed */
+    MK_ERR_STATE = -5,             /* call order violated (e.g. decode before load) */
+    MK_ERR_DEVICE = -6             /* the kernel reported an error record */
+} mk_status;
+
+/* Model and run shape.  Llama-style decoder: per layer RMSNorm, Q/K/V, RoPE
+ * (rotate-half pairs (i, i + D/2), frequency theta^(-2i/D)), causal GQA
+ * attention (query head h reads KV group h * n_kv_heads / n_q_heads), O-proj
+ * + residual, RMSNorm, SwiGLU MLP, down-proj + residual; then RMSNorm and
+ * LM head (the embedding matrix when tied_embeddings).                    */
+typedef struct {
+    int32_t n_layers;
+    int32_t hidden;          /* H; must equal n_q_heads * head_dim */
+    int32_t n_q_heads;
+    int32_t n_kv_heads;      /* divides n_q_heads */
+    int32_t head_dim;        /* D: 64 or 128 */
+    int32_t ffn;             /* F */
+    int32_t vocab;           /* V */
+    float rms_eps;
+    float rope_theta;
+    int32_t tied_embeddings; /* 1: LM head reads the embedding matrix */
+    int32_t batch;           /* B rows per step, 1..8, fixed per handle */
+    int32_t max_seq;         /* KV slots per (layer, K/V, row, group) */
+    int32_t device;          /* HIP device ordinal */
+    int32_t n_cus;           /* 0 = every CU of the device; else a smaller grid */
+    int32_t n_splits;        /* split-KV partitions per (row, KV group); 0 = auto */
+    int32_t n_chunks;        /* K-chunks of the down projection; 0 = auto (4) */
+    uint32_t flags;          /* MK_FLAG_* */
+} mk_config;
+
+#define MK_FLAG_NONE 0u
+
+/* Per-layer weight pointers: arrays of n_layers DEVICE pointers held in HOST
+ * memory.  Every tensor is bf16, row-major in the nn.Linear layout [out][in]:
+ *   attn_norm[l], mlp_norm[l]: [H]
+ *   wq[l]: [Hq*D][H]   wk[l], wv[l]: [Hkv*D][H]   wo[l]: [H][Hq*D]
+ *   w_gate[l], w_up[l]: [F][H]   w_down[l]: [H][F]
+ * embed: [V][H], final_norm: [H], lm_head: [V][H] (ignored when tied).      */
+typedef struct {
+    const void* embed;
+    const void* final_norm;
+    const void* lm_head;
+    const void* const* attn_norm;
+    const void* const* wq;
+    const void* const* wk;
+    const void* const* wv;
+    const void* const* wo;
+    const void* const* mlp_norm;
+    const void* const* w_gate;
+    const void* const* w_up;
+    const void* const* w_down;
+} mk_weights;
+
+typedef struct mk_handle mk_handle;
+
+/* Validates `cfg`, queries the device, builds the per-CU instruction queues
+ * and the packed-weight layout, and allocates all library-owned device
+ * memory (packed weights, queues, activation scratch, RoPE table).  On error
+ * *out is set to NULL.  Shape limits: H = Hq*D, Hq % Hkv == 0, D in {64,128},
+ * (Hq/Hkv) divides 8, H and F multiples of 8, 1 <= batch <= 8.            */
+int mk_create(const mk_config* cfg, mk_handle** out);
+
+/* Copies the caller's weights (device pointers, see mk_weights) into the
+ * library's packed layout on `stream`, then synchronises `stream`; the caller
+ * may free its tensors afterwards.  May be called again to replace weights. */
+int mk_load_weights(mk_handle* h, const mk_weights* w, void* stream);
+
+/* Bytes of the caller-owned KV cache: bf16 [L][2 (K,V)][B][Hkv][max_seq][D],
+ * K stored after RoPE.  Returns 0 for an invalid config.                  */
+size_t mk_kv_cache_bytes(const mk_config* cfg);
+
+/* One greedy-decode step for every batch row, as ONE kernel launch on
+ * `stream` (asynchronous; no allocation, no host synchronisation).
+ *   tokens    device int32[B], ids in [0, V)
+ *   positions device int32[B], 0 <= p < max_seq; cache slots [0, p) of row b
+ *             must hold that row's earlier K/V; the step writes slot p
+ *   kv_cache  device buffer of mk_kv_cache_bytes(cfg)
+ *   logits    device float32[B][V] (written)
+ * Steps on one handle must be ordered on one stream: the handle's scratch is
+ * reused by every step.  Out-of-range ids/positions are detected on device,
+ * recorded (mk_get_device_error) and the affected outputs are left unwritten. */
+int mk_decode_step(mk_handle* h, const int32_t* tokens, const int32_t* positions,
+                   void* kv_cache, float* logits, void* stream);
+
+/* Same arguments, results and ordering rules; the same op bodies launched
+ * once per op and layer (6 * n_layers + 1 launches), ordered only by the
+ * kernel boundaries.  For A/B comparison with mk_decode_step.             */
+int mk_decode_step_multikernel(mk_handle* h, const int32_t* tokens, const int32_t* positions,
+                               void* kv_cache, float* logits, void* stream);
+
+/* Frees everything the handle owns.  NULL is accepted. */
+int mk_destroy(mk_handle* h);
+
+/* Static description of a status code. */
+const char* mk_status_string(int status);
+
+/* Text of the last error on this handle ("" if none); valid until the next
+ * call on the handle.  With h == NULL: the last mk_create failure.        */
+const char* mk_last_error(const mk_handle* h);
+
+/* Device-side error record, written by the first workgroup that detects a
+ * range violation or whose bounded wait expires.                          */
+typedef struct {
+    uint32_t code;       /* 0 none, 1 wait timeout, 2 token out of range, 3 position out of range */
+    uint32_t workgroup;
+    uint32_t pc;         /* instruction index in that workgroup's queue */
+    uint32_t opcode;
+    uint32_t wave;
+    uint32_t detail;     /* op-specific (e.g. the awaited tag or the bad value) */
+} mk_device_error;
+
+/* Synchronises the handle's device, copies the error record to *out and
+ * clears it.  Returns MK_OK, or MK_ERR_DEVICE when a record was present.  */
+int mk_get_device_error(mk_handle* h, mk_device_error* out);
+
+/* Host-only inspection of the schedule for `cfg` on `n_cus` CUs: builds it,
+ * checks that every output row / unit is produced exactly once and that the
+ * per-CU queues can complete (simulated in stage order).  Needs no GPU.   */
+typedef struct {
+    int32_t n_cus;
+    int32_t n_splits;
+    int32_t n_chunks;
+    int32_t max_insts_per_cu;
+    int64_t total_insts;
+    int64_t packed_weight_bytes;   /* bytes streamed per step (weights, incl. padding) */
+    int64_t max_stream_bytes_per_wave;
+    int64_t min_stream_bytes_per_wave;
+    int32_t launches_multikernel;
+    int32_t valid;                 /* 1 if all checks passed */
+} mk_schedule_info;
+
+int mk_schedule_inspect(const mk_config* cfg, int32_t n_cus, mk_schedule_info* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_H */

@@ -1,0 +1,116 @@
+"""GPU parity of the decode step (megakernel and per-op launches) against the
+CPU oracle, through the C ABI.
+
+Bar (per step, over all B x V logits): max|diff| <= 3e-2 and
+max|diff| / max|ref| <= 2e-2; greedy tokens identical wherever the oracle's
+top-2 logit gap exceeds 0.05.  The oracle is teacher-forced on the tokens the
+GPU produced, so every step compares identical inputs.
+"""
+import numpy as np
+import pytest
+
+import synth
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+def tiny_prefill_run(multikernel: bool, n_cus: int = 0, n_splits: int = 0, batch: int = 1, seed: int = 1234):
+    w_shape = synth.TINY
+    weights = synth.make_weights(w_shape, seed=seed)
+    wl = synth.WORKLOADS["tiny_b1_p32"]
+    prompt = synth.make_prompts(w_shape.vocab, batch, wl.prompt)
+    max_seq = wl.prompt + wl.decode
+    dec = H.GpuDecoder(w_shape, weights, batch, max_seq, n_cus=n_cus, n_splits=n_splits)
+    try:
+        # prefill by decode steps over the prompt, then greedy decode
+        run = H.Run([], [], [])
+        for i in range(wl.prompt):
+            toks, pos = prompt[:, i], np.full(batch, i, dtype=np.int32)
+            run.tokens.append(toks.copy())
+            run.positions.append(pos.copy())
+            run.logits.append(dec.step(toks, pos, multikernel))
+        g = dec.greedy(np.argmax(run.logits[-1], axis=1), np.full(batch, wl.prompt), wl.decode, multikernel)
+        run.tokens += g.tokens
+        run.positions += g.positions
+        run.logits += g.logits
+        kv = dec.kv_host()
+    finally:
+        dec.close()
+    return weights, run, kv, max_seq
+
+
+@pytest.mark.parametrize("multikernel", [False, True], ids=["megakernel", "multikernel"])
+def test_tiny_prefill_and_greedy_decode_matches_oracle(multikernel):
+    weights, run, kv, max_seq = tiny_prefill_run(multikernel)
+    ref = H.oracle_replay(synth.TINY, weights, 1, max_seq, run)
+    stats = H.compare(run, ref, "tiny")
+    print("tiny", "multikernel" if multikernel else "megakernel", stats)
+    assert stats["tokens_checked"] > 0
+
+
+def test_tiny_kv_cache_matches_oracle_cache():
+    weights, run, kv, max_seq = tiny_prefill_run(False)
+    import oracle
+    orc = oracle.Oracle(synth.TINY, weights, 1, max_seq)
+    cache = np.zeros_like(kv)
+    for t, p in zip(run.tokens, run.positions):
+        orc.decode_step(cache, t, p)
+    a = H.bits_to_f32(kv) if hasattr(H, "bits_to_f32") else (kv.astype(np.uint32) << 16).view(np.float32)
+    b = (cache.astype(np.uint32) << 16).view(np.float32)
+    # bf16 K/V rows: equal up to one bf16 rounding step of the row's own values
+    assert np.max(np.abs(a - b)) <= 2e-2 * max(1.0, np.max(np.abs(b)))
+    assert np.mean(a == b) > 0.9
+
+
+def test_megakernel_equals_multikernel_bitwise():
+    _, run_a, kv_a, _ = tiny_prefill_run(False)
+    _, run_b, kv_b, _ = tiny_prefill_run(True)
+    for a, b in zip(run_a.logits, run_b.logits):
+        np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(kv_a, kv_b)
+
+
+def test_runs_are_deterministic():
+    _, run_a, _, _ = tiny_prefill_run(False)
+    _, run_b, _, _ = tiny_prefill_run(False)
+    for a, b in zip(run_a.logits, run_b.logits):
+        np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("n_cus,n_splits", [(7, 1), (64, 3), (256, 5)])
+def test_tiny_ragged_tiles_and_splits(n_cus, n_splits):
+    weights, run, _, max_seq = tiny_prefill_run(False, n_cus=n_cus, n_splits=n_splits)
+    ref = H.oracle_replay(synth.TINY, weights, 1, max_seq, run)
+    H.compare(run, ref, f"tiny ncu={n_cus} splits={n_splits}")
+
+
+def test_tiny_batch4_rows_independent():
+    weights, run, _, max_seq = tiny_prefill_run(False, batch=4)
+    ref = H.oracle_replay(synth.TINY, weights, 4, max_seq, run)
+    H.compare(run, ref, "tiny b4")
+
+
+def test_invalid_token_reports_device_error_and_writes_nothing():
+    import torch
+    from decode_megakernel_02_amd import mk
+    weights = synth.make_weights(synth.TINY)
+    dec = H.GpuDecoder(synth.TINY, weights, 1, 8)
+    try:
+        dec.logits.fill_(7.0)
+        dec.tokens.copy_(torch.tensor([synth.TINY.vocab], dtype=torch.int32))
+        dec.positions.zero_()
+        mk.mk_decode_step(dec.h, dec.tokens, dec.positions, dec.kv, dec.logits, mk.current_stream())
+        err = mk.mk_get_device_error(dec.h)
+        assert err is not None and err.code == 2
+        assert torch.all(dec.logits == 7.0) and torch.all(dec.kv == 0)
+        # a bad position is reported too, and the handle keeps working afterwards
+        dec.tokens.zero_()
+        dec.positions.fill_(8)
+        mk.mk_decode_step(dec.h, dec.tokens, dec.positions, dec.kv, dec.logits, mk.current_stream())
+        err = mk.mk_get_device_error(dec.h)
+        assert err is not None and err.code == 3
+        lg = dec.step([5], [0])
+        assert np.all(np.isfinite(lg))
+    finally:
+        dec.close()
