@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Decode throughput of the single-launch megakernel on one MI355X.
+
+Workload (default): Llama-3.2-1B-shaped decoder with random bf16 weights
+N(0, 0.02), batch 1, a 1024-token context pre-filled in the KV cache with
+seeded N(0,1) bf16 rows, greedy decode.  One timed step = one mk_decode_step
+launch (the whole forward pass) + argmax + position advance, all on one
+stream with no host synchronisation inside the timed region.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode tokens/s at batch 1 + achieved % of HBM roofline (Llama-1B-shaped)"
+KERNEL_NAME = "mk_step_kernel"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ["mk_kernels.hip", "mk_internal.h", "mk_plan.cpp", "mk_api.cpp"]:
+        with open(os.path.join(ROOT, "decode_megakernel_02_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, only if
+    it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{KERNEL_NAME}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(shape, weights, kv_host, first_tok, prompt, n_steps: int):
+    import numpy as np
+
+    import oracle
+    threads = max(1, min(64, os.cpu_count() or 1))
+    orc = oracle.Oracle(shape, weights, 1, kv_host.shape[4])
+    cache = kv_host.copy()
+    tok = np.array([first_tok], dtype=np.int32)
+    orc.decode_step(cache, tok, np.array([prompt], dtype=np.int32), threads)  # warm-up
+    t0 = time.perf_counter()
+    for i in range(n_steps):
+        lg = orc.decode_step(cache, tok, np.array([prompt + 1 + i], dtype=np.int32), threads)
+        tok = np.array([int(np.argmax(lg[0]))], dtype=np.int32)
+    dt = (time.perf_counter() - t0) / n_steps
+    return {"value": 1.0 / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_steps} greedy decode steps of the same workload after 1 warm-up step "
+                      f"(fp64 C oracle, {threads} threads, rows split across threads); "
+                      f"{dt * 1e3:.1f} ms/step"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama1b_b1_p1024")
+    ap.add_argument("--mk-steps", type=int, default=64, help="timed steps of the per-op-launch path")
+    ap.add_argument("--cpu-steps", type=int, default=5, help="timed oracle steps (0: skip the CPU baseline)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the decode path has no "
+              "multi-GPU variant; see DESIGN.md for how it would shard.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from decode_megakernel_02_amd import mk
+    from decode_megakernel_02_amd import roofline as R
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(3)
+    wl = synth.WORKLOADS[args.workload]
+    shape, B, P = wl.model, wl.batch, wl.prompt
+    K, W = args.steps, args.warmup
+    max_seq = P + W + max(K, args.mk_steps) + 8
+
+    t0 = time.perf_counter()
+    weights = synth.make_weights(shape)
+    log(f"weights generated in {time.perf_counter() - t0:.1f}s ({shape.weight_bytes() / 1e9:.2f} GB)")
+    kv_host = synth.make_kv_cache(shape, B, max_seq, P)
+    first = synth.make_first_tokens(shape.vocab, B)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+    dw = {"embed": up(weights["embed"]), "final_norm": up(weights["final_norm"]),
+          "lm_head": up(weights["lm_head"]) if weights["lm_head"] is not None else None,
+          "layers": [{k: up(v) for k, v in L.items()} for L in weights["layers"]]}
+    cfg = mk.make_config(shape, B, max_seq)
+    h = mk.mk_create(cfg)
+    stream = mk.current_stream()
+    mk.mk_load_weights(h, dw, stream)
+    del dw
+    torch.cuda.empty_cache()
+    kv = up(kv_host.reshape(-1))
+    tokens = torch.tensor(first, dtype=torch.int32, device="cuda")
+    positions = torch.full((B,), P, dtype=torch.int32, device="cuda")
+    logits = torch.empty(B, shape.vocab, dtype=torch.float32, device="cuda")
+    log(f"handle ready; schedule: {mk.mk_schedule_inspect(cfg, torch.cuda.get_device_properties(0).multi_processor_count).total_insts} instructions")
+
+    def greedy(n, fn):
+        for _ in range(n):
+            fn(h, tokens, positions, kv, logits, stream)
+            tokens.copy_(torch.argmax(logits, dim=1))
+            positions.add_(1)
+
+    def check_device():
+        err = mk.mk_get_device_error(h)
+        if err is not None:
+            raise RuntimeError(f"device error record: code {err.code} wg {err.workgroup} pc {err.pc} "
+                               f"op {err.opcode} detail {err.detail:#x}")
+
+    # ---- megakernel: warm-up, then K timed greedy steps
+    greedy(W, mk.mk_decode_step)
+    torch.cuda.synchronize()
+    check_device()
+    t0 = time.perf_counter()
+    greedy(K, mk.mk_decode_step)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    check_device()
+    log(f"megakernel: {K} steps in {wall * 1e3:.1f} ms")
+
+    # ---- per-launch kernel time (events on the launch stream), same positions
+    positions.fill_(P + W)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record()
+        mk.mk_decode_step(h, tokens, positions, kv, logits, stream)
+        ev[i][1].record()
+        tokens.copy_(torch.argmax(logits, dim=1))
+        positions.add_(1)
+    torch.cuda.synchronize()
+    check_device()
+    kern_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    kern_mean = statistics.mean(kern_us)
+
+    # ---- per-op launches (same op bodies, 6L+1 launches per step)
+    KM = args.mk_steps
+    positions.fill_(P)
+    greedy(3, mk.mk_decode_step_multikernel)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    greedy(KM, mk.mk_decode_step_multikernel)
+    torch.cuda.synchronize()
+    wall_mk = time.perf_counter() - t0
+    positions.fill_(P + 3)
+    evm = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(KM)]
+    for i in range(KM):
+        evm[i][0].record()
+        mk.mk_decode_step_multikernel(h, tokens, positions, kv, logits, stream)
+        evm[i][1].record()
+        tokens.copy_(torch.argmax(logits, dim=1))
+        positions.add_(1)
+    torch.cuda.synchronize()
+    check_device()
+    kern_mk = statistics.mean(a.elapsed_time(b) * 1e3 for a, b in evm)
+    log(f"multikernel: {KM} steps in {wall_mk * 1e3:.1f} ms")
+
+    # ---- roofline of the dominant (only) kernel
+    keys = R.mean_keys(P, W, K)  # the event-timed pass covers steps W .. W+K-1
+    bytes_step = R.step_bytes(shape, B, keys)
+    achieved = bytes_step / (kern_mean * 1e-6) / 1e9
+    peak = R.MI355X_HBM_PEAK_GBPS
+    traffic = measured_traffic(args.workload)
+    ms_per_step = wall / K * 1e3
+
+    out = {
+        "metric": METRIC,
+        "value": B * K / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{shape.name}, batch {B}, {P}-token synthetic KV prefill, greedy decode",
+                   "batch": B, "prompt_tokens": P, "decode_steps": K, "kv_prefill": "seeded N(0,1) bf16 rows",
+                   "weights": "seeded N(0,0.02) bf16, norm gains 1.0", "accumulate": "fp32",
+                   "kernel_launches_per_step": 1},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": peak, "unit": "GB/s", "frac": achieved / peak,
+                     "traffic": traffic},
+        "kernel_us_per_step": kern_mean,
+        "kernel_us_median": statistics.median(kern_us),
+        "bytes_per_step": bytes_step,
+        "floor_us_per_step": R.floor_us(bytes_step),
+        "multikernel": {"ms_per_step": wall_mk / KM * 1e3, "tokens_per_s": B * KM / wall_mk,
+                        "kernel_us_per_step": kern_mk, "launches_per_step": shape.n_layers * 6 + 1,
+                        "megakernel_speedup": kern_mk / kern_mean},
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if args.cpu_steps > 0:
+        log("timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline(shape, weights, kv_host, int(first[0]), P, args.cpu_steps)
+    mk.mk_destroy(h)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -14,7 +14,7 @@
 #include "mk_plan.h"
 
 namespace mk {
-hipError_t launch_step(const Params* dev_params, int ncu, size_t lds_bytes, const int32_t* tokens,
+hipError_t launch_step(const Params* dev_params, int head_dim, int ncu, size_t lds_bytes, const int32_t* tokens,
                        const int32_t* positions, void* kv, float* logits, int stage, uint32_t flags,
                        hipStream_t stream);
 hipError_t set_step_kernel_lds(size_t lds_bytes);
@@ -182,7 +182,7 @@ int mk_create(const mk_config* cfg, mk_handle** out) {
         const size_t sync_bytes = 512;
         long ring_budget = (long)LDS_BYTES - 2 * (long)xb - (long)sync_bytes;
         int ring_units = (int)std::min<long>(32, ring_budget / (NW * UNIT_BYTES));
-        if (ring_units < 2) {
+        if (ring_units < std::max(2, std::max(std::max(p.ku_h, p.ku_q), p.ku_f))) {
             delete h;
             return fail(nullptr, MK_ERR_UNSUPPORTED_SHAPE, "batch x hidden too large for the LDS budget");
         }
@@ -240,6 +240,12 @@ int mk_create(const mk_config* cfg, mk_handle** out) {
         hp.hout = cur; cur += n_h;
         hp.dacc = dalloc<float>(h, B * H);
         hp.mats = nullptr;
+        hp.prof = nullptr;
+        if (cfg->flags & MK_FLAG_PROFILE) {
+            const size_t n = (size_t)ncu * (NW + NLOAD) * PROF_SLOTS;
+            hp.prof = dalloc<uint64_t>(h, n);
+            HIPCHK(hipMemset(hp.prof, 0, n * 8));
+        }
         hp.epoch = dalloc<uint32_t>(h, (size_t)ncu);
         HIPCHK(hipMemset(hp.epoch, 0, (size_t)ncu * 4));
         hp.error = dalloc<uint32_t>(h, 8);
@@ -329,7 +335,7 @@ int mk_decode_step(mk_handle* h, const int32_t* tokens, const int32_t* positions
                    void* stream) {
     int rc = step_args_ok(h, tokens, positions, kv_cache, logits);
     if (rc != MK_OK) return rc;
-    hipError_t e = launch_step(h->dparams, h->hp.ncu, h->lds_bytes, tokens, positions, kv_cache, logits, -1,
+    hipError_t e = launch_step(h->dparams, h->hp.D, h->hp.ncu, h->lds_bytes, tokens, positions, kv_cache, logits, -1,
                                KF_BUMP_EPOCH, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(h, HipError{e, "mk_step_kernel launch"});
     return MK_OK;
@@ -341,7 +347,7 @@ int mk_decode_step_multikernel(mk_handle* h, const int32_t* tokens, const int32_
     if (rc != MK_OK) return rc;
     const int ns = h->hp.n_stages;
     for (int st = 0; st < ns; ++st) {
-        hipError_t e = launch_step(h->dparams, h->hp.ncu, h->lds_bytes, tokens, positions, kv_cache, logits, st,
+        hipError_t e = launch_step(h->dparams, h->hp.D, h->hp.ncu, h->lds_bytes, tokens, positions, kv_cache, logits, st,
                                    st == ns - 1 ? KF_BUMP_EPOCH : 0u, (hipStream_t)stream);
         if (e != hipSuccess) return hip_fail(h, HipError{e, "mk_step_kernel stage launch"});
     }
@@ -366,6 +372,21 @@ int mk_get_device_error(mk_handle* h, mk_device_error* out) {
     out->wave = rec[4];
     out->detail = rec[5];
     return rec[0] ? MK_ERR_DEVICE : MK_OK;
+}
+
+int mk_get_profile(mk_handle* h, uint64_t* counters, size_t n) {
+    if (!h || !counters) return fail(h, MK_ERR_INVALID_ARG, "null argument");
+    if (!h->hp.prof) return fail(h, MK_ERR_STATE, "handle was created without MK_FLAG_PROFILE");
+    const size_t need = (size_t)h->hp.ncu * (NW + NLOAD) * PROF_SLOTS;
+    if (n < need) return fail(h, MK_ERR_INVALID_ARG, "counter buffer too small");
+    try {
+        HIPCHK(hipSetDevice(h->cfg.device));
+        HIPCHK(hipDeviceSynchronize());
+        HIPCHK(hipMemcpy(counters, h->hp.prof, need * 8, hipMemcpyDeviceToHost));
+    } catch (const HipError& e) {
+        return hip_fail(h, e);
+    }
+    return MK_OK;
 }
 
 int mk_destroy(mk_handle* h) {

@@ -5,10 +5,11 @@
 
 namespace mk {
 
-// Workgroup shape: one workgroup per CU, NW compute waves, each paired with one
-// loader wave that streams that compute wave's packed weights into its LDS ring.
+// Workgroup shape: one workgroup per CU, NW compute waves and NLOAD loader
+// waves; each loader streams the packed weights of NW / NLOAD compute waves
+// into their LDS rings.
 constexpr int NW = 8;                 // compute waves
-constexpr int NLOAD = NW;             // loader waves (1:1 with compute waves)
+constexpr int NLOAD = 4;              // loader waves, each serving two compute waves
 constexpr int WG_THREADS = 64 * (NW + NLOAD);
 constexpr int UNIT_BYTES = 1024;      // one DMA: 64 lanes x 16 B
 constexpr int UNIT_ELEMS = 512;       // bf16 per unit
@@ -65,7 +66,7 @@ struct Params {
 
     // packed weights: per (cu, wave) stream of units
     const uint8_t* wstream;
-    const uint64_t* stream_base;   // [ncu * NW] unit offset of each stream
+    const uint64_t* stream_base;   // [ncu * NW] unit 0 of each stream; unit k at base + k * NW
     const Inst* insts;             // all queues back to back
     const uint32_t* queue_begin;   // [ncu + 1] index into insts
     const uint32_t* unit_off;      // [(queue_begin[cu] + pc + cu) * NW + w]: units before pc (pc in 0..len)
@@ -91,12 +92,14 @@ struct Params {
     float* dacc;      // [B][H]      down-proj chunk accumulator, private to the row's owner wave
     const void* const* mats;  // unused by the step kernels (pack only)
 
+    uint64_t* prof;   // [ncu][NW + NLOAD][8] cycle counters, or null
     uint32_t* epoch;  // [ncu] per-workgroup step counter
     uint32_t* error;  // [8] device error record (code, wg, pc, op, wave, detail), abort flag at [7]
 };
 
 // Kernel launch flags.
 constexpr uint32_t KF_BUMP_EPOCH = 1u;  // last launch of a step: advance the per-workgroup epoch
+constexpr int PROF_SLOTS = 8;          // counters per wave
 
 
 }  // namespace mk

@@ -31,7 +31,9 @@ typedef __attribute__((address_space(1))) void glb_void;
 
 #define CBAR() asm volatile("" ::: "memory")
 
-constexpr int MAXOUT = 8;  // DMA units in flight per loader wave
+constexpr int MAXOUT = 16;  // DMA units in flight per loader wave
+constexpr int NSERVE = NW / NLOAD;
+static_assert(NSERVE == 2, "each loader wave serves two compute waves");
 
 // ------------------------------------------------------------- primitives --
 
@@ -115,10 +117,18 @@ __device__ __forceinline__ void wait_vm_le(uint32_t n) {
     case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
     case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
     case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+    case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+    case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+    case 11: asm volatile("s_waitcnt vmcnt(11)" ::: "memory"); break;
+    case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+    case 13: asm volatile("s_waitcnt vmcnt(13)" ::: "memory"); break;
+    case 14: asm volatile("s_waitcnt vmcnt(14)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
     }
 }
-static_assert(MAXOUT == 8, "wait_vm_le covers 0..7");
+static_assert(MAXOUT == 16, "wait_vm_le covers 0..15");
 
 // ------------------------------------------------------------ wave context --
 
@@ -129,7 +139,11 @@ struct Ctx {
     uint32_t pc;       // instruction index in this CU's queue (for error records)
     uint32_t op;
     bool aborted;
+    bool prof;         // accumulate cycle counters
+    uint64_t cnt[5];   // see mk_get_profile
 };
+
+__device__ __forceinline__ uint64_t cycles() { return __builtin_readcyclecounter(); }
 
 __device__ __forceinline__ bool abort_flag(const Params* p) {
     return __hip_atomic_load(&p->error[7], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
@@ -191,6 +205,7 @@ __device__ __forceinline__ Lds lds_map(uint8_t* smem, const Params& p) {
 
 // barrier among the NW compute waves (loader waves never join it)
 __device__ __forceinline__ void cbar(Ctx& cx, const Lds& s, uint32_t& seq) {
+    const uint64_t t0 = cx.prof ? cycles() : 0;
     seq += NW;
     CBAR();
     if (cx.lane == 0) __hip_atomic_fetch_add(s.bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -198,36 +213,114 @@ __device__ __forceinline__ void cbar(Ctx& cx, const Lds& s, uint32_t& seq) {
     while (lds_ld(s.bar) < seq)
         if (!keep_waiting(cx, spins, 0xBA000000u | seq)) break;
     CBAR();
+    if (cx.prof) cx.cnt[3] += cycles() - t0;
 }
 
 // ------------------------------------------------------------- loader wave --
 
-// Streams units [ub, ue) of compute wave w's stream into its ring.  Never
-// blocks while DMA is in flight: when the ring is full it retires the oldest
-// outstanding unit instead, so it cannot wait on the compute wave in a cycle.
-__device__ __forceinline__ void loader(Ctx& cx, const Lds& s, int w, uint32_t ub, uint32_t ue) {
+// One compute wave's stream as seen by its loader.  Every field is wave
+// uniform (scalar registers).
+struct LoadStream {
+    const uint8_t* src;   // this lane's 16 bytes of unit 0
+    uint32_t ring_lds;    // LDS byte address of the ring
+    uint32_t n, issued, done, slot, consumed;
+    uint32_t a_landed, a_consumed;
+};
+
+__device__ __forceinline__ void load_stream_init(const Ctx& cx, const Lds& s, LoadStream& ls, int w, uint32_t ub,
+                                                 uint32_t ue) {
     const Params& p = *cx.p;
-    const uint32_t n = ue - ub, ru = (uint32_t)p.ring_units;
-    const uint8_t* src = p.wstream + (p.stream_base[cx.cu * NW + w] + ub) * (uint64_t)UNIT_BYTES + cx.lane * 16;
-    uint8_t* ring = s.ring + (size_t)w * ru * UNIT_BYTES;
-    const uint32_t a_landed = lds_addr(&s.landed[w]), a_consumed = lds_addr(&s.consumed[w]);
-    uint32_t issued = 0, done = 0, slot = 0, spins = 0;
-    while (done < n) {
-        const uint32_t cons = asm_lds_ld(a_consumed);
-        while (issued < n && issued - done < (uint32_t)MAXOUT && issued < cons + ru) {
-            __builtin_amdgcn_global_load_lds((const glb_void*)(src + (uint64_t)issued * UNIT_BYTES),
-                                             (lds_void*)(ring + (size_t)slot * UNIT_BYTES), 16, 0, 0);
-            ++issued;
-            slot = slot + 1 == ru ? 0 : slot + 1;
+    // the loaded values are the same in every lane: make that visible to the
+    // compiler so the loader's loop state lives in scalar registers
+    ub = __builtin_amdgcn_readfirstlane(ub);
+    ue = __builtin_amdgcn_readfirstlane(ue);
+    const uint64_t base = p.stream_base[cx.cu * NW + w];
+    const uint64_t base_u = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32)) << 32) |
+                            __builtin_amdgcn_readfirstlane((uint32_t)base);
+    ls.src = p.wstream + (base_u + (uint64_t)ub * NW) * UNIT_BYTES + cx.lane * 16;
+    ls.ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(s.ring + (size_t)w * p.ring_units * UNIT_BYTES));
+    ls.n = ue - ub;
+    ls.issued = ls.done = ls.slot = ls.consumed = 0;
+    ls.a_landed = lds_addr(&s.landed[w]);
+    ls.a_consumed = lds_addr(&s.consumed[w]);
+}
+
+// issue the stream's next unit if its ring has a free slot (re-reading the
+// consumer's count only when the ring looks full)
+__device__ __forceinline__ bool load_stream_issue(LoadStream& ls, uint32_t ru) {
+    if (ls.issued >= ls.n) return false;
+    if (ls.issued >= ls.consumed + ru) {
+        ls.consumed = __builtin_amdgcn_readfirstlane(asm_lds_ld(ls.a_consumed));
+        if (ls.issued >= ls.consumed + ru) return false;
+    }
+    __builtin_amdgcn_global_load_lds((const glb_void*)(ls.src + (uint64_t)ls.issued * (NW * UNIT_BYTES)),
+                                     (lds_void*)(uintptr_t)(ls.ring_lds + ls.slot * UNIT_BYTES), 16, 0, 0);
+    ++ls.issued;
+    ls.slot = ls.slot + 1 == ru ? 0 : ls.slot + 1;
+    return true;
+}
+
+constexpr uint32_t KEEP_IN_FLIGHT = 8;  // units left outstanding when retiring a batch
+
+// Streams the units [ub, ue) of compute waves w0 and w1 into their rings.
+// DMA completes in issue order, so a bit FIFO (bit i = stream of the i-th
+// oldest outstanding unit) says whose units a vmcnt step retires.  Units are
+// retired in batches, keeping KEEP_IN_FLIGHT outstanding while the rings have
+// room.  The loader never blocks while DMA is in flight: when both rings are
+// full it retires what is outstanding instead, so it cannot wait on a compute
+// wave in a cycle.  It runs at raised instruction priority so the compute
+// waves' polling cannot starve it of issue slots.
+__device__ __forceinline__ void loader(Ctx& cx, const Lds& s, int w0, const uint32_t* uoff, uint32_t pc0,
+                                       uint32_t pc1) {
+    __builtin_amdgcn_s_setprio(2);
+    const uint32_t ru = __builtin_amdgcn_readfirstlane((uint32_t)cx.p->ring_units);
+    const int w1 = w0 + 1;
+    LoadStream a, b;
+    load_stream_init(cx, s, a, w0, uoff[(size_t)pc0 * NW + w0], uoff[(size_t)pc1 * NW + w0]);
+    load_stream_init(cx, s, b, w1, uoff[(size_t)pc0 * NW + w1], uoff[(size_t)pc1 * NW + w1]);
+    uint32_t fifo = 0, out = 0, spins = 0;
+    bool turn_b = false;
+    while (a.done < a.n || b.done < b.n) {
+        while (out < (uint32_t)MAXOUT) {
+            uint32_t sid;
+            bool issued;
+            if (turn_b) {
+                issued = load_stream_issue(b, ru);
+                sid = 1;
+                if (!issued) { issued = load_stream_issue(a, ru); sid = 0; }
+            } else {
+                issued = load_stream_issue(a, ru);
+                sid = 0;
+                if (!issued) { issued = load_stream_issue(b, ru); sid = 1; }
+            }
+            if (!issued) break;
+            fifo |= sid << out;
+            ++out;
+            turn_b = !turn_b;
         }
-        if (issued > done) {
-            wait_vm_le(issued - done - 1);  // the oldest outstanding unit has landed
-            ++done;
-            asm_lds_st(a_landed, done);
+        if (out > 0) {
+            // retire all but KEEP_IN_FLIGHT units (all of them when nothing more could be issued)
+            const bool blocked = out < (uint32_t)MAXOUT;
+            const uint32_t keep = blocked ? 0u : KEEP_IN_FLIGHT;
+            const uint64_t t0 = cx.prof ? cycles() : 0;
+            wait_vm_le(keep);
+            if (cx.prof) cx.cnt[1] += cycles() - t0;
+            const uint32_t k = out - keep;
+            const uint32_t mask = k >= 32 ? 0xffffffffu : (1u << k) - 1u;
+            const uint32_t nb = (uint32_t)__builtin_popcount(fifo & mask);
+            fifo = k >= 32 ? 0u : fifo >> k;
+            out = keep;
+            if (k - nb) asm_lds_st(a.a_landed, a.done += k - nb);
+            if (nb) asm_lds_st(b.a_landed, b.done += nb);
+            if (cx.prof) cx.cnt[3] += k;
             spins = 0;
-        } else if (!keep_waiting(cx, spins, 0x10000000u | done)) {
-            break;
+        } else {
+            const uint64_t t0 = cx.prof ? cycles() : 0;
+            const bool go_on = keep_waiting(cx, spins, 0x10000000u | (a.done << 12) | b.done);
+            if (cx.prof) cx.cnt[2] += cycles() - t0;
+            if (!go_on) break;
         }
+        if (cx.prof) cx.cnt[4] += 1;
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -235,23 +328,37 @@ __device__ __forceinline__ void loader(Ctx& cx, const Lds& s, int w, uint32_t ub
 // ------------------------------------------------------------ compute side --
 
 struct Stream {  // compute wave's read cursor in its ring
-    uint32_t unit;  // units consumed in this launch
+    uint32_t unit;      // units read in this launch
     uint32_t slot;
+    uint32_t landed;    // landed count last read from LDS (only ever grows)
+    uint32_t released;  // units handed back to the loader
 };
 
-__device__ __forceinline__ uint4 ring_take(Ctx& cx, const Lds& s, Stream& st) {
-    uint32_t spins = 0;
-    while (lds_ld(&s.landed[cx.wave]) <= st.unit)
-        if (!keep_waiting(cx, spins, 0x20000000u | st.unit)) break;
-    CBAR();
-    const uint4 v = *(const uint4*)(s.ring + ((size_t)cx.wave * cx.p->ring_units + st.slot) * UNIT_BYTES + cx.lane * 16);
-    return v;
-}
+// hand the slots read so far back to the loader
 __device__ __forceinline__ void ring_release(Ctx& cx, const Lds& s, Stream& st) {
-    ++st.unit;
-    st.slot = st.slot + 1 == (uint32_t)cx.p->ring_units ? 0 : st.slot + 1;
+    if (st.released == st.unit) return;
     CBAR();
     lds_st(&s.consumed[cx.wave], st.unit);
+    st.released = st.unit;
+}
+// Next unit of this wave's stream.  Everything already read is released before
+// waiting, so the loader always has room to make progress.
+__device__ __forceinline__ uint4 ring_take(Ctx& cx, const Lds& s, Stream& st) {
+    if (st.unit >= st.landed) {
+        ring_release(cx, s, st);
+        const uint64_t t0 = cx.prof ? cycles() : 0;
+        uint32_t spins = 0;
+        while ((st.landed = lds_ld(&s.landed[cx.wave])) <= st.unit)
+            if (!keep_waiting(cx, spins, 0x20000000u | st.unit)) break;
+        CBAR();
+        if (cx.prof) cx.cnt[1] += cycles() - t0;
+    }
+    if (cx.prof) cx.cnt[4] += 1;
+    return *(const uint4*)(s.ring + ((size_t)cx.wave * cx.p->ring_units + st.slot) * UNIT_BYTES + cx.lane * 16);
+}
+__device__ __forceinline__ void ring_advance(const Ctx& cx, Stream& st) {
+    ++st.unit;
+    st.slot = st.slot + 1 == (uint32_t)cx.p->ring_units ? 0 : st.slot + 1;
 }
 
 // x buffer layout per batch row: [half][chunk][4] with element k in half
@@ -275,15 +382,16 @@ __device__ __forceinline__ float dot8(const uint4 w, const float4 a, const float
 
 // Reads n tagged words *addr(i) (thread t of the 512 compute threads takes
 // i = t, t+512, ...), waiting until each carries this step's epoch, and hands
-// (i, value) to put.  Loads are issued eight at a time so latencies overlap.
+// (i, value) to put.  Loads are issued four at a time so latencies overlap.
 template <class Addr, class Put>
 __device__ __forceinline__ void acquire(Ctx& cx, int n, Addr&& addr, Put&& put) {
+    const uint64_t t_begin = cx.prof ? cycles() : 0;
     const int t = cx.wave * 64 + cx.lane;
     constexpr int NT = NW * 64;
-    for (int i0 = t; i0 < n; i0 += 8 * NT) {
-        uint64_t w[8];
+    for (int i0 = t; i0 < n; i0 += 4 * NT) {
+        uint64_t w[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 4; ++j) {
             const int i = i0 + j * NT;
             w[j] = i < n ? ld_tag(addr(i)) : ((uint64_t)cx.epoch << 32);
         }
@@ -291,19 +399,20 @@ __device__ __forceinline__ void acquire(Ctx& cx, int n, Addr&& addr, Put&& put) 
         while (true) {
             bool ok = true;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) ok &= tag_of(w[j]) == cx.epoch;
+            for (int j = 0; j < 4; ++j) ok &= tag_of(w[j]) == cx.epoch;
             if (ok) break;
             if (!keep_waiting(cx, spins, 0x30000000u | (uint32_t)i0)) break;
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < 4; ++j)
                 if (tag_of(w[j]) != cx.epoch) w[j] = ld_tag(addr(i0 + j * NT));
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 4; ++j) {
             const int i = i0 + j * NT;
             if (i < n) put(i, val_of(w[j]));
         }
     }
+    if (cx.prof) cx.cnt[2] += cycles() - t_begin;
 }
 
 // Poll a single tagged word (epilogue inputs that were produced long before).
@@ -321,8 +430,67 @@ struct RowOut {
     float mine[2];  // row r's dot product for batch row `lane` (lanes < B)
 };
 
+// wait until at least `need` units of this wave's stream have landed;
+// everything already read is released first so the loader can progress
+__device__ __forceinline__ void ring_wait(Ctx& cx, const Lds& s, Stream& st, uint32_t need) {
+    if (st.landed >= need) return;
+    ring_release(cx, s, st);
+    const uint64_t t0 = cx.prof ? cycles() : 0;
+    uint32_t spins = 0;
+    while ((st.landed = lds_ld(&s.landed[cx.wave])) < need)
+        if (!keep_waiting(cx, spins, 0x20000000u | st.unit)) break;
+    CBAR();
+    if (cx.prof) cx.cnt[1] += cycles() - t0;
+}
+
+// Batch-1 row dot products with this wave's x slice in registers: the KU
+// units of a row are read from the ring together and accumulated in KU
+// independent chains.
+template <int KU>
+struct XSlice {
+    float4 lo[KU], hi[KU];
+};
+
+template <int KU>
+__device__ __forceinline__ void load_xslice(const Ctx& cx, const float* xb, int xstride, XSlice<KU>& x) {
+    const float4* xr = (const float4*)xb;
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+        x.lo[u] = xr[u * 64 + cx.lane];
+        x.hi[u] = xr[(xstride >> 3) + u * 64 + cx.lane];
+    }
+}
+
+template <int KU, int NROWS>
+__device__ __forceinline__ void rowgroup_dot_b1(Ctx& cx, const Lds& s, Stream& st, const XSlice<KU>& x, uint32_t ru,
+                                                RowOut& out) {
+#pragma unroll
+    for (int r = 0; r < NROWS; ++r) {
+        ring_wait(cx, s, st, st.unit + KU);
+        uint4 w[KU];
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+            uint32_t sl = st.slot + u;
+            sl = sl >= ru ? sl - ru : sl;
+            w[u] = *(const uint4*)(s.ring + ((size_t)cx.wave * ru + sl) * UNIT_BYTES + cx.lane * 16);
+        }
+        float acc[KU];
+#pragma unroll
+        for (int u = 0; u < KU; ++u) acc[u] = dot8(w[u], x.lo[u], x.hi[u]);
+        float sum = acc[0];
+#pragma unroll
+        for (int u = 1; u < KU; ++u) sum += acc[u];
+        st.unit += KU;
+        st.slot += KU;
+        st.slot = st.slot >= ru ? st.slot - ru : st.slot;
+        ring_release(cx, s, st);
+        if (cx.prof) cx.cnt[4] += KU;
+        out.mine[r] = wave_sum(sum);
+    }
+}
+
 // Dot products of one row-group (NROWS = 1 or 2 rows of ku units each) with x
-// for every batch row; weights come from the ring.
+// for every batch row (x read from LDS); general path for any batch size.
 template <int NROWS>
 __device__ __forceinline__ void rowgroup_dot(Ctx& cx, const Lds& s, Stream& st, const float* xb, int ku, RowOut& out) {
     const Params& p = *cx.p;
@@ -343,7 +511,8 @@ __device__ __forceinline__ void rowgroup_dot(Ctx& cx, const Lds& s, Stream& st, 
                     acc[b] += dot8(w, lo, hi);
                 }
             }
-            ring_release(cx, s, st);
+            ring_advance(cx, st);
+            if ((u & 3) == 3 || u == ku - 1) ring_release(cx, s, st);
         }
         float mine = 0.f;
 #pragma unroll
@@ -405,6 +574,9 @@ struct Step {  // per-launch batch inputs, lane b holds row b
 
 // ------------------------------------------------------------ GEMV ops ------
 
+// KU > 0: batch-1 path with KU units per row (x slice in registers);
+// KU == 0: general path.
+template <int KU>
 __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint32_t& seq, const Inst& in, float* xb,
                                         const Step& sp) {
     const Params& p = *cx.p;
@@ -477,6 +649,18 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
     }
     if (cx.aborted) return;
 
+    XSlice<KU == 0 ? 1 : KU> xs;
+    const uint32_t ru = __builtin_amdgcn_readfirstlane((uint32_t)p.ring_units);
+    if constexpr (KU > 0) load_xslice<KU>(cx, xb, __builtin_amdgcn_readfirstlane(p.xstride), xs);
+    auto dot1 = [&](RowOut& o) {
+        if constexpr (KU > 0) rowgroup_dot_b1<KU, 1>(cx, s, st, xs, ru, o);
+        else rowgroup_dot<1>(cx, s, st, xb, ku, o);
+    };
+    auto dot2 = [&](RowOut& o) {
+        if constexpr (KU > 0) rowgroup_dot_b1<KU, 2>(cx, s, st, xs, ru, o);
+        else rowgroup_dot<2>(cx, s, st, xb, ku, o);
+    };
+
     // ---- this wave's row-groups; lane b < B finishes batch row b
     const int D = p.D, half = D / 2;
     const bool lane_row = cx.lane < B;
@@ -486,7 +670,7 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
         RowOut o;
         switch (in.op) {
         case OP_RMS_QKV_ROPE: {
-            rowgroup_dot<2>(cx, s, st, xb, ku, o);
+            dot2(o);
             if (lane_row) {
                 const int pos = sp.pos;
                 const float y1 = o.mine[0] * scale, y2 = o.mine[1] * scale;
@@ -530,12 +714,12 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
                 if (l == 0) hin = bf2f(p.embed[(size_t)sp.tok * H + rg]);
                 else hin = wait_word(cx, p.hout + ((size_t)(l - 1) * B + b) * H + rg);
             }
-            rowgroup_dot<1>(cx, s, st, xb, ku, o);
+            dot1(o);
             if (lane_row) st_tag(p.hmid + ((size_t)l * B + b) * H + rg, hin + o.mine[0], cx.epoch);
             break;
         }
         case OP_RMS_UP_GATE: {
-            rowgroup_dot<2>(cx, s, st, xb, ku, o);
+            dot2(o);
             if (lane_row) {
                 const float gt = o.mine[0] * scale, up = o.mine[1] * scale;
                 const float a = gt / (1.0f + __expf(-gt)) * up;  // silu(gate) * up
@@ -547,7 +731,7 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
             const bool first = in.a == 0, last = in.a == p.n_chunk - 1;
             float hm = 0.f;
             if (last && lane_row) hm = wait_word(cx, p.hmid + ((size_t)l * B + b) * H + rg);
-            rowgroup_dot<1>(cx, s, st, xb, ku, o);
+            dot1(o);
             if (lane_row) {
                 float* acc = p.dacc + (size_t)b * H + rg;  // written and read only by this wave's lane b
                 const float v = o.mine[0] + (first ? 0.f : *acc);
@@ -557,7 +741,7 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
             break;
         }
         default: {  // OP_RMS_LM_HEAD
-            rowgroup_dot<1>(cx, s, st, xb, ku, o);
+            dot1(o);
             if (lane_row) sp.logits[(size_t)b * p.V + rg] = o.mine[0] * scale;
             break;
         }
@@ -568,21 +752,91 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
 
 // ------------------------------------------------------- attention ops ------
 
+// element i (0..63) of a 64-dim row held as eight packed-bf16 uint4s
+__device__ __forceinline__ float bf_elem(const uint4 (&r)[8], int i) {
+    const uint4 c = r[i >> 3];
+    const uint32_t w = ((i >> 1) & 3) == 0 ? c.x : ((i >> 1) & 3) == 1 ? c.y : ((i >> 1) & 3) == 2 ? c.z : c.w;
+    return (i & 1) ? bf_hi(w) : bf_lo(w);
+}
+
+// Wave64 reduce-scatter of e * row[d] (d < 64) by recursive halving: afterwards
+// lane d holds the sum over lanes of e * row[d].  The first halving step is
+// fused with the products so at most 32 values are live; 63 lane exchanges.
+__device__ __forceinline__ float pv_reduce_scatter64(const uint4 (&row)[8], float e, int lane) {
+    float v[32];
+    {
+        const bool upper = (lane & 32) != 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int i = h * 16; i < h * 16 + 16; ++i) {
+                const float a = e * bf_elem(row, i), b = e * bf_elem(row, i + 32);
+                v[i] = (upper ? b : a) + __shfl_xor(upper ? a : b, 32);
+            }
+            CBAR();
+        }
+    }
+#pragma unroll
+    for (int d = 16, m = 32; d >= 1; d >>= 1, m >>= 1) {
+        const bool upper = (lane & d) != 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (i < m / 2) {
+                const float a = v[i], b = v[i + m / 2];
+                v[i] = (upper ? b : a) + __shfl_xor(upper ? a : b, d);
+            }
+        }
+    }
+    return v[0];
+}
+
 // Split-KV partial attention of query heads g*G .. g*G+G-1 of batch row b over
 // keys [j0, j1) of split s: writes (m, l, o[D]) with m the max score, l the
 // sum of exp(score - m) and o the exp-weighted sum of V rows (unnormalised).
-__device__ __forceinline__ void op_attention(Ctx& cx, const Lds& s, uint32_t& seq, const Inst& in, float* xb, const Step& sp) {
+// Waves split the group's heads and 64-key blocks; in a block lane j owns key
+// j (its K and V rows, loaded with independent 16-byte loads), and the PV
+// product is reduce-scattered so lane d ends with dims d (and d + 64).
+template <int D>
+__device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& seq, const Inst& in, float* xb,
+                                               const Step& sp) {
+    constexpr int NH = D / 64;       // 64-dim halves
     const Params& p = *cx.p;
-    const int B = p.B, D = p.D, G = p.G, l = in.layer, b = in.a, g = in.b, split = (int)in.rg0;
+    const int B = p.B, G = p.G, l = in.layer, b = in.a, g = in.b, split = (int)in.rg0;
     const int pos = sp.positions[b];
     const int S = pos + 1;
     const int j0 = (int)((long long)split * S / p.n_split), j1 = (int)((long long)(split + 1) * S / p.n_split);
-    // LDS scratch inside this instruction's x buffer
     float* qs = xb;                  // [G][D], pre-scaled by 1/sqrt(D)
     float* kn = qs + G * D;          // [D] new K row (bf16 values)
     float* vn = kn + D;              // [D] new V row
     float* stt = vn + D;             // [NW][D + 2] per-wave (m, l, o)
-    float* ev = stt + NW * (D + 2);  // [NW][64] exp weights of the current key block
+    const int gi = cx.wave % G, wph = NW / G, sub = cx.wave / G;
+    const uint16_t* Kc = sp.kv + ((((size_t)l * 2 + 0) * B + b) * p.Hkv + g) * (size_t)p.max_seq * D;
+    const uint16_t* Vc = sp.kv + ((((size_t)l * 2 + 1) * B + b) * p.Hkv + g) * (size_t)p.max_seq * D;
+    const int nkeys = j1 - j0;
+
+    // K rows written by earlier steps do not depend on this step: load the
+    // first block's first 64 dims before waiting for q.  Rows are handled in
+    // 64-dim halves (eight 16-byte chunks) to bound register use.
+    uint4 kr[8], vr[8];
+    auto load_half = [&](uint4 (&r)[8], const uint16_t* base, int kb, int h) {
+        const int j = j0 + kb * 64 + cx.lane;
+        const bool old = j < j1 && j < pos;
+        const uint4* src = (const uint4*)(base + (size_t)(old ? j : 0) * D + h * 64);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) r[c] = old ? src[c] : make_uint4(0, 0, 0, 0);
+    };
+    auto pack_lds = [&](uint4 (&r)[8], const float* row) {  // exact: the values are bf16
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const float* v = row + c * 8;
+            r[c] = make_uint4((uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16),
+                              (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16),
+                              (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16),
+                              (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16));
+        }
+    };
+    if (sub * 64 < nkeys) load_half(kr, Kc, sub, 0);
+
     // q of the group's heads, then the new K and V rows, in one polled read
     const uint64_t* qsrc = p.q + ((size_t)l * B + b) * p.Hq * D + (size_t)g * G * D;
     const uint64_t* ksrc = p.knew + ((size_t)l * B + b) * p.Hkv * D + (size_t)g * D;
@@ -594,84 +848,63 @@ __device__ __forceinline__ void op_attention(Ctx& cx, const Lds& s, uint32_t& se
     cbar(cx, s, seq);
     if (cx.aborted) return;
 
-    const int gi = cx.wave % G, wph = NW / G, sub = cx.wave / G;
     const float* qh = qs + gi * D;
-    const uint16_t* Kc = sp.kv + ((((size_t)l * 2 + 0) * B + b) * p.Hkv + g) * (size_t)p.max_seq * D;
-    const uint16_t* Vc = sp.kv + ((((size_t)l * 2 + 1) * B + b) * p.Hkv + g) * (size_t)p.max_seq * D;
-    const int dpl = D / 64;  // dims per lane in the PV product: lane owns [lane*dpl, lane*dpl + dpl)
     const float ninf = -__builtin_inff();
-    float m = ninf, lsum = 0.f, o0 = 0.f, o1 = 0.f;
-    const int nkeys = j1 - j0;
+    float m = ninf, lsum = 0.f, o[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) o[h] = 0.f;
     for (int kb = sub; kb * 64 < nkeys; kb += wph) {
         const int j = j0 + kb * 64 + cx.lane;
         const bool valid = j < j1;
-        float sc = ninf;
-        if (valid) {
-            float acc = 0.f;
-            if (j < pos) {
-                const uint4* kr = (const uint4*)(Kc + (size_t)j * D);
-                for (int c = 0; c < D / 8; ++c) {
-                    const uint4 w = kr[c];
-                    const float4 a = *(const float4*)(qh + c * 8), bq = *(const float4*)(qh + c * 8 + 4);
-                    acc += dot8(w, a, bq);
-                }
-            } else {  // j == pos: the row written by this step
-                for (int d = 0; d < D; ++d) acc = fmaf(qh[d], kn[d], acc);
+        const bool is_new = valid && j == pos;  // the row this step appended: from LDS
+        float acc = 0.f;
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            CBAR();  // keeps the two halves' loads apart (register budget)
+            if (kb != sub || h != 0) load_half(kr, Kc, kb, h);
+            if (is_new) pack_lds(kr, kn + h * 64);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const float4 a = *(const float4*)(qh + h * 64 + c * 8), bq = *(const float4*)(qh + h * 64 + c * 8 + 4);
+                acc += dot8(kr[c], a, bq);
             }
-            sc = acc;
         }
-        const float mb = wave_max(sc);
-        const float mn = fmaxf(m, mb);
+        const float sc = valid ? acc : ninf;
+        const float mn = fmaxf(m, wave_max(sc));
         const float e = valid ? __expf(sc - mn) : 0.f;
         const float corr = m == ninf ? 0.f : __expf(m - mn);
         lsum = lsum * corr + wave_sum(e);
-        o0 *= corr;
-        o1 *= corr;
         m = mn;
-        ev[cx.wave * 64 + cx.lane] = e;
-        CBAR();
-        const int nb = min(64, j1 - (j0 + kb * 64));
-        for (int jj = 0; jj < nb; ++jj) {
-            const int jk = j0 + kb * 64 + jj;
-            const float ej = ev[cx.wave * 64 + jj];
-            float v0, v1 = 0.f;
-            if (jk < pos) {
-                if (dpl == 1) {
-                    v0 = bf2f(Vc[(size_t)jk * D + cx.lane]);
-                } else {
-                    const uint32_t two = *(const uint32_t*)(Vc + (size_t)jk * D + 2 * cx.lane);
-                    v0 = bf_lo(two);
-                    v1 = bf_hi(two);
-                }
-            } else {
-                v0 = vn[cx.lane * dpl];
-                if (dpl == 2) v1 = vn[cx.lane * 2 + 1];
-            }
-            o0 = fmaf(ej, v0, o0);
-            o1 = fmaf(ej, v1, o1);
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            CBAR();
+            load_half(vr, Vc, kb, h);
+            if (is_new) pack_lds(vr, vn + h * 64);
+            o[h] = o[h] * corr + pv_reduce_scatter64(vr, e, cx.lane);
         }
-        CBAR();
     }
-    // per-wave state -> LDS, merge per head
+    // per-wave state -> LDS, merge the waves of each head
     float* my = stt + cx.wave * (D + 2);
     if (cx.lane == 0) {
         my[0] = m;
         my[1] = lsum;
     }
-    my[2 + cx.lane * dpl] = o0;
-    if (dpl == 2) my[2 + cx.lane * 2 + 1] = o1;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) my[2 + h * 64 + cx.lane] = o[h];
     cbar(cx, s, seq);
     if (sub != 0 || cx.aborted) return;
     float M = ninf;
     for (int w = gi; w < NW; w += G) M = fmaxf(M, stt[w * (D + 2)]);
-    float Ls = 0.f, O0 = 0.f, O1 = 0.f;
+    float Ls = 0.f, O[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) O[h] = 0.f;
     if (M != ninf) {
         for (int w = gi; w < NW; w += G) {
             const float* sw = stt + w * (D + 2);
             const float f = sw[0] == ninf ? 0.f : __expf(sw[0] - M);
             Ls = fmaf(sw[1], f, Ls);
-            O0 = fmaf(sw[2 + cx.lane * dpl], f, O0);
-            if (dpl == 2) O1 = fmaf(sw[2 + cx.lane * 2 + 1], f, O1);
+#pragma unroll
+            for (int h = 0; h < NH; ++h) O[h] = fmaf(sw[2 + h * 64 + cx.lane], f, O[h]);
         }
     }
     const int head = g * G + gi;
@@ -680,9 +913,11 @@ __device__ __forceinline__ void op_attention(Ctx& cx, const Lds& s, uint32_t& se
         st_tag(out + 0, M, cx.epoch);
         st_tag(out + 1, Ls, cx.epoch);
     }
-    st_tag(out + 2 + cx.lane * dpl, O0, cx.epoch);
-    if (dpl == 2) st_tag(out + 2 + cx.lane * 2 + 1, O1, cx.epoch);
+#pragma unroll
+    for (int h = 0; h < NH; ++h) st_tag(out + 2 + h * 64 + cx.lane, O[h], cx.epoch);
 }
+
+
 
 // Log-sum-exp merge of the n_split partials of (row b, head):
 // out = sum_s o_s e^(m_s - M) / sum_s l_s e^(m_s - M), M = max_s m_s.
@@ -696,26 +931,28 @@ __device__ __forceinline__ void op_reduce(Ctx& cx, const Lds& s, uint32_t& seq, 
     const float ninf = -__builtin_inff();
     float M = ninf;
     for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, xb[sp * W]);
-    const int dpl = D / 64;
+    const int nh = D / 64;  // lane owns dims lane (and lane + 64)
     float Ls = 0.f, O0 = 0.f, O1 = 0.f;
     for (int sp = 0; sp < ns; ++sp) {
         const float ms = xb[sp * W];
         if (ms == ninf) continue;
         const float f = __expf(ms - M);
         Ls = fmaf(xb[sp * W + 1], f, Ls);
-        O0 = fmaf(xb[sp * W + 2 + cx.lane * dpl], f, O0);
-        if (dpl == 2) O1 = fmaf(xb[sp * W + 2 + cx.lane * 2 + 1], f, O1);
+        O0 = fmaf(xb[sp * W + 2 + cx.lane], f, O0);
+        if (nh == 2) O1 = fmaf(xb[sp * W + 2 + 64 + cx.lane], f, O1);
     }
     const float inv = 1.0f / Ls;
     uint64_t* out = p.attn + ((size_t)l * B + b) * p.Hq * D + (size_t)head * D;
-    st_tag(out + cx.lane * dpl, O0 * inv, cx.epoch);
-    if (dpl == 2) st_tag(out + cx.lane * 2 + 1, O1 * inv, cx.epoch);
+    st_tag(out + cx.lane, O0 * inv, cx.epoch);
+    if (nh == 2) st_tag(out + 64 + cx.lane, O1 * inv, cx.epoch);
 }
 
 // --------------------------------------------------------------- the kernel --
 
 // stage < 0: run the whole queue (one launch per step); stage >= 0: only that
-// stage's instructions (one launch per op and layer).
+// stage's instructions (one launch per op and layer).  One instantiation per
+// head size.
+template <int HEAD_DIM>
 __global__ void __launch_bounds__(WG_THREADS, 1)
 mk_step_kernel(const Params* __restrict__ pp, const int32_t* tokens, const int32_t* positions, uint16_t* kv,
                float* logits, int stage, uint32_t flags) {
@@ -729,6 +966,16 @@ mk_step_kernel(const Params* __restrict__ pp, const int32_t* tokens, const int32
     cx.aborted = false;
     cx.pc = 0;
     cx.op = 0;
+    cx.prof = p.prof != nullptr;
+    for (int k = 0; k < 5; ++k) cx.cnt[k] = 0;
+    const uint64_t t_kernel = cx.prof ? cycles() : 0;
+    auto flush_prof = [&](int wave_slot) {
+        if (cx.prof && cx.lane == 0) {
+            uint64_t* o = p.prof + ((size_t)cx.cu * (NW + NLOAD) + wave_slot) * PROF_SLOTS;
+            o[0] = cycles() - t_kernel;
+            for (int k = 1; k < 5; ++k) o[k] = cx.cnt[k];
+        }
+    };
     cx.epoch = p.epoch[cx.cu] + 1;
     const Lds s = lds_map(smem, p);
 
@@ -771,14 +1018,15 @@ mk_step_kernel(const Params* __restrict__ pp, const int32_t* tokens, const int32
     __syncthreads();
 
     const uint32_t* uoff = p.unit_off + ((size_t)qb + cx.cu) * NW;
-    if (wave >= NW) {  // loader
-        const int w = wave - NW;
-        cx.wave = w;
-        loader(cx, s, w, uoff[(size_t)pc0 * NW + w], uoff[(size_t)pc1 * NW + w]);
+    if (wave >= NW) {  // loader of compute waves 2i and 2i+1
+        const int w0 = (wave - NW) * NSERVE;
+        cx.wave = wave;
+        loader(cx, s, w0, uoff, pc0, pc1);
+        flush_prof(wave);
         return;
     }
     cx.wave = wave;
-    Stream st{0, 0};
+    Stream st{0, 0, 0, 0};
     uint32_t seq = 0;
     for (uint32_t pc = pc0; pc < pc1 && !cx.aborted; ++pc) {
         const Inst in = p.insts[qb + pc];
@@ -786,11 +1034,19 @@ mk_step_kernel(const Params* __restrict__ pp, const int32_t* tokens, const int32
         cx.op = in.op;
         float* xb = (pc - pc0) & 1 ? s.xbuf[1] : s.xbuf[0];
         switch (in.op) {
-        case OP_ATTENTION: op_attention(cx, s, seq, in, xb, sp); break;
+        case OP_ATTENTION: op_attention_t<HEAD_DIM>(cx, s, seq, in, xb, sp); break;
         case OP_ATTN_REDUCE: op_reduce(cx, s, seq, in, xb); break;
-        default: op_gemv(cx, s, st, seq, in, xb, sp); break;
+        default: {
+            const int ku = in.op == OP_O_PROJ_RES ? p.ku_q : in.op == OP_DOWN_RES ? p.ku_f : p.ku_h;
+            if (p.B != 1) op_gemv<0>(cx, s, st, seq, in, xb, sp);
+            else if (ku == 4) op_gemv<4>(cx, s, st, seq, in, xb, sp);
+            else if (ku == 2) op_gemv<2>(cx, s, st, seq, in, xb, sp);
+            else op_gemv<0>(cx, s, st, seq, in, xb, sp);
+            break;
+        }
         }
     }
+    flush_prof(wave);
     if ((flags & KF_BUMP_EPOCH) && wave == 0 && cx.lane == 0) p.epoch[cx.cu] = cx.epoch;
 }
 
@@ -807,9 +1063,13 @@ __global__ void __launch_bounds__(256) mk_pack_kernel(const PackRowDev* rows, ui
     for (uint32_t r = blockIdx.x; r < n; r += gridDim.x) {
         const PackRowDev pr = rows[r];
         const uint16_t* src = mats[pr.mat] + (size_t)pr.row * pr.src_cols + pr.k0;
-        uint16_t* out = (uint16_t*)(dst + pr.dst_unit * (uint64_t)UNIT_BYTES);
         const uint32_t n_el = pr.kunits * UNIT_ELEMS;
-        for (uint32_t e = threadIdx.x; e < n_el; e += blockDim.x) out[e] = e < pr.klen ? src[e] : (uint16_t)0;
+        for (uint32_t e = threadIdx.x; e < n_el; e += blockDim.x) {
+            // element e lies in the row's unit e / 512, and consecutive units of a
+            // stream are NW units apart in the packed buffer
+            uint16_t* out = (uint16_t*)(dst + (pr.dst_unit + (uint64_t)(e / UNIT_ELEMS) * NW) * UNIT_BYTES);
+            out[e % UNIT_ELEMS] = e < pr.klen ? src[e] : (uint16_t)0;
+        }
     }
 }
 
@@ -818,23 +1078,24 @@ __global__ void __launch_bounds__(256) mk_pack_kernel(const PackRowDev* rows, ui
 // The whole-step launch waits across workgroups, so it needs every workgroup
 // resident at once: a cooperative launch guarantees that (or fails).  Per-op
 // launches only read results of earlier launches and use an ordinary launch.
-hipError_t launch_step(const Params* dev_params, int ncu, size_t lds_bytes, const int32_t* tokens,
+hipError_t launch_step(const Params* dev_params, int head_dim, int ncu, size_t lds_bytes, const int32_t* tokens,
                        const int32_t* positions, void* kv, float* logits, int stage, uint32_t flags,
                        hipStream_t stream) {
     uint16_t* kv16 = (uint16_t*)kv;
-    if (stage < 0) {
-        void* args[] = {(void*)&dev_params, (void*)&tokens, (void*)&positions, (void*)&kv16, (void*)&logits,
-                        (void*)&stage, (void*)&flags};
-        return hipLaunchCooperativeKernel((const void*)mk_step_kernel, dim3(ncu), dim3(WG_THREADS), args,
-                                          (unsigned)lds_bytes, stream);
-    }
-    hipLaunchKernelGGL(mk_step_kernel, dim3(ncu), dim3(WG_THREADS), lds_bytes, stream, dev_params, tokens, positions,
-                       kv16, logits, stage, flags);
-    return hipGetLastError();
+    const void* fn = head_dim == 64 ? (const void*)mk_step_kernel<64> : (const void*)mk_step_kernel<128>;
+    void* args[] = {(void*)&dev_params, (void*)&tokens, (void*)&positions, (void*)&kv16, (void*)&logits,
+                    (void*)&stage, (void*)&flags};
+    if (stage < 0)
+        return hipLaunchCooperativeKernel(fn, dim3(ncu), dim3(WG_THREADS), args, (unsigned)lds_bytes, stream);
+    return hipLaunchKernel(fn, dim3(ncu), dim3(WG_THREADS), args, lds_bytes, stream);
 }
 
 hipError_t set_step_kernel_lds(size_t lds_bytes) {
-    return hipFuncSetAttribute((const void*)mk_step_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+    hipError_t e = hipFuncSetAttribute((const void*)mk_step_kernel<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds_bytes);
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute((const void*)mk_step_kernel<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)lds_bytes);
 }
 
 hipError_t launch_pack(const void* rows, uint32_t n, const uint16_t* const* mats, uint8_t* dst, hipStream_t stream) {

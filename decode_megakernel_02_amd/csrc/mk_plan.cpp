@@ -239,16 +239,21 @@ int build_plan(const mk_config& c, int ncu, Plan& p, std::string& err) {
         }
         for (int w = 0; w < NW; ++w) p.stream_len[(size_t)cu * NW + w] = len[w];
     }
+    // A CU's NW streams are interleaved unit by unit: unit k of wave w sits at
+    // cu_base + k * NW + w, so the CU's concurrent reads stay inside one
+    // advancing window of NW units (HBM row locality).
     p.stream_base.assign((size_t)ncu * NW, 0);
     uint64_t acc = 0;
-    for (size_t i = 0; i < p.stream_base.size(); ++i) {
-        p.stream_base[i] = acc;
-        acc += p.stream_len[i];
+    for (int cu = 0; cu < ncu; ++cu) {
+        uint64_t mx = 0;
+        for (int w = 0; w < NW; ++w) mx = std::max(mx, p.stream_len[(size_t)cu * NW + w]);
+        for (int w = 0; w < NW; ++w) p.stream_base[(size_t)cu * NW + w] = acc + w;
+        acc += mx * NW;
     }
     p.total_units = acc;
 
     // pack table: one entry per stream row, in stream order
-    std::vector<uint64_t> cursor(p.stream_base.begin(), p.stream_base.end());
+    std::vector<uint64_t> cursor((size_t)ncu * NW, 0);
     for (int cu = 0; cu < ncu; ++cu) {
         for (const Inst& in : b.q[cu]) {
             if (in.op == OP_ATTENTION || in.op == OP_ATTN_REDUCE) continue;
@@ -256,9 +261,10 @@ int build_plan(const mk_config& c, int ncu, Plan& p, std::string& err) {
             RowRef rr[2];
             for (uint32_t i = 0; i < in.nrg; ++i) {
                 int nrows = b.rows_of(in, in.rg0 + i, rr);
-                uint64_t& cur = cursor[(size_t)cu * NW + i % NW];
+                uint64_t& cur = cursor[(size_t)cu * NW + i % NW];  // unit index within the wave's stream
                 for (int k = 0; k < nrows; ++k) {
-                    p.pack.push_back(PackRow{rr[k].mat, rr[k].row, rr[k].k0, rr[k].klen, rr[k].cols, ku, cur});
+                    p.pack.push_back(PackRow{rr[k].mat, rr[k].row, rr[k].k0, rr[k].klen, rr[k].cols, ku,
+                                             p.stream_base[(size_t)cu * NW + i % NW] + cur * NW});
                     cur += ku;
                 }
             }
@@ -409,11 +415,12 @@ bool check_plan(const Plan& p, std::string& err) {
         }
     }
     // --- stream layout: pack rows tile every stream exactly
-    uint64_t units = 0;
+    uint64_t units = 0, stream_units = 0;
     for (const PackRow& r : p.pack) units += r.kunits;
-    if (units != p.total_units) {
+    for (uint64_t len : p.stream_len) stream_units += len;
+    if (units != stream_units) {
         snprintf(buf, sizeof buf, "pack rows cover %llu units, streams hold %llu", (unsigned long long)units,
-                 (unsigned long long)p.total_units);
+                 (unsigned long long)stream_units);
         err = buf;
         return false;
     }

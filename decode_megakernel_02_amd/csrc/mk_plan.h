@@ -22,7 +22,7 @@ struct PackRow {
     uint32_t klen;
     uint32_t src_cols;   // row length of the source matrix
     uint32_t kunits;
-    uint64_t dst_unit;   // absolute unit index in the packed buffer
+    uint64_t dst_unit;   // absolute unit index in the packed buffer (first unit; later units every NW)
 };
 
 struct Plan {
@@ -41,7 +41,7 @@ struct Plan {
     std::vector<uint32_t> stage_pc;      // [ncu * (n_stages + 1)]
     std::vector<uint32_t> unit_off;      // [(queue_begin[cu] + cu + pc) * NW + w]
     // streams
-    std::vector<uint64_t> stream_base;   // [ncu * NW]
+    std::vector<uint64_t> stream_base;   // [ncu * NW] unit 0 of each stream; unit k at base + k * NW
     std::vector<uint64_t> stream_len;    // [ncu * NW]
     uint64_t total_units = 0;
     std::vector<PackRow> pack;

@@ -53,7 +53,11 @@ class MkScheduleInfo(ctypes.Structure):
 
 
 EXPORTS = ["mk_create", "mk_load_weights", "mk_kv_cache_bytes", "mk_decode_step", "mk_decode_step_multikernel",
-           "mk_destroy", "mk_status_string", "mk_last_error", "mk_get_device_error", "mk_schedule_inspect"]
+           "mk_destroy", "mk_status_string", "mk_last_error", "mk_get_device_error", "mk_get_profile",
+           "mk_schedule_inspect"]
+MK_FLAG_PROFILE = 1
+PROF_WAVES = 12  # 8 compute + 4 loader waves per workgroup
+PROF_SLOTS = 8
 
 _lib = None
 
@@ -79,8 +83,9 @@ def lib():
         L.mk_last_error.restype = ctypes.c_char_p
         L.mk_get_device_error.argtypes = [H, ctypes.POINTER(MkDeviceError)]
         L.mk_schedule_inspect.argtypes = [ctypes.POINTER(MkConfig), ctypes.c_int32, ctypes.POINTER(MkScheduleInfo)]
+        L.mk_get_profile.argtypes = [H, _P, ctypes.c_size_t]
         for name in ["mk_create", "mk_load_weights", "mk_decode_step", "mk_decode_step_multikernel", "mk_destroy",
-                     "mk_get_device_error", "mk_schedule_inspect"]:
+                     "mk_get_device_error", "mk_schedule_inspect", "mk_get_profile"]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -165,6 +170,14 @@ def mk_get_device_error(handle) -> Optional[MkDeviceError]:
         return e
     _check(rc, handle)
     return None
+
+
+def mk_get_profile(handle, n_cus: int):
+    """Cycle counters of the last step as a numpy array [n_cus][12][8] (uint64)."""
+    import numpy as np
+    out = np.zeros((n_cus, PROF_WAVES, PROF_SLOTS), dtype=np.uint64)
+    _check(lib().mk_get_profile(handle, out.ctypes.data, out.size), handle)
+    return out
 
 
 def mk_destroy(handle):

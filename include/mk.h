@@ -67,6 +67,7 @@ typedef struct {
 } mk_config;
 
 #define MK_FLAG_NONE 0u
+#define MK_FLAG_PROFILE 1u  /* per-wave cycle counters, read with mk_get_profile */
 
 /* Per-layer weight pointers: arrays of n_layers DEVICE pointers held in HOST
  * memory.  Every tensor is bf16, row-major in the nn.Linear layout [out][in]:
@@ -150,6 +151,16 @@ typedef struct {
 /* Synchronises the handle's device, copies the error record to *out and
  * clears it.  Returns MK_OK, or MK_ERR_DEVICE when a record was present.  */
 int mk_get_device_error(mk_handle* h, mk_device_error* out);
+
+/* Per-wave cycle counters of the last step (handle created with
+ * MK_FLAG_PROFILE): counters[(cu * 12 + wave) * 8 + k], 8 x uint64 per wave,
+ * waves 0..7 compute, 8..11 loaders.  Compute k: 0 cycles in the kernel,
+ * 1 waiting for weight units, 2 waiting for tagged inputs, 3 in workgroup
+ * barriers, 4 units read.  Loader k: 0 cycles in the kernel, 1 waiting for
+ * DMA completion, 2 idle with full rings, 3 units loaded, 4 loop iterations.
+ * `n` is the capacity of `counters` in elements; synchronises the device.
+ * Returns MK_ERR_STATE when profiling is off.                             */
+int mk_get_profile(mk_handle* h, uint64_t* counters, size_t n);
 
 /* Host-only inspection of the schedule for `cfg` on `n_cus` CUs: builds it,
  * checks that every output row / unit is produced exactly once and that the

@@ -114,3 +114,29 @@ def test_invalid_token_reports_device_error_and_writes_nothing():
         assert np.all(np.isfinite(lg))
     finally:
         dec.close()
+
+
+# ------------------------------------------------ full-size 1B-shaped model --
+
+@pytest.fixture(scope="module")
+def llama1b():
+    shape = synth.LLAMA_1B
+    return shape, synth.make_weights(shape)
+
+
+@pytest.mark.parametrize("multikernel", [False, True], ids=["megakernel", "multikernel"])
+def test_llama1b_synthetic_kv_matches_oracle(llama1b, multikernel):
+    import os
+    shape, weights = llama1b
+    P, steps = 1024, 3
+    max_seq = P + steps + 1
+    kv = synth.make_kv_cache(shape, 1, max_seq, P)
+    first = synth.make_first_tokens(shape.vocab, 1)
+    dec = H.GpuDecoder(shape, weights, 1, max_seq, kv_init=kv)
+    try:
+        run = dec.greedy(first, np.array([P]), steps, multikernel)
+    finally:
+        dec.close()
+    ref = H.oracle_replay(shape, weights, 1, max_seq, run, kv_init=kv, nthreads=min(32, os.cpu_count() or 1))
+    stats = H.compare(run, ref, "llama1b")
+    print("llama1b", "multikernel" if multikernel else "megakernel", stats)
