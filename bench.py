@@ -84,11 +84,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama1b_b1_p1024")
     ap.add_argument("--mk-steps", type=int, default=64, help="timed steps of the per-op-launch path")
-    ap.add_argument("--cpu-steps", type=int, default=5, help="timed oracle steps (0: skip the CPU baseline)")
+    ap.add_argument("--cpu-steps", type=int, default=32, help="timed oracle steps (0: skip the CPU baseline)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first run a plain device copy of this many MiB (3 launches), the reference "
+                         "kernel for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the decode path has no "
-              "multi-GPU variant; see DESIGN.md for how it would shard.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the decode path runs on a "
+              "single GPU and has no multi-GPU variant.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -101,6 +104,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(3)
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)  # reads n bytes, writes n bytes
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 launches, {n} bytes read + {n} bytes written each")
+        del src, dst
     wl = synth.WORKLOADS[args.workload]
     shape, B, P = wl.model, wl.batch, wl.prompt
     K, W = args.steps, args.warmup
@@ -156,10 +168,11 @@ def main():
     # ---- per-launch kernel time (events on the launch stream), same positions
     positions.fill_(P + W)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    cur = torch.cuda.current_stream()  # the stream mk_decode_step launches on
     for i in range(K):
-        ev[i][0].record()
+        ev[i][0].record(cur)
         mk.mk_decode_step(h, tokens, positions, kv, logits, stream)
-        ev[i][1].record()
+        ev[i][1].record(cur)
         tokens.copy_(torch.argmax(logits, dim=1))
         positions.add_(1)
     torch.cuda.synchronize()
@@ -179,9 +192,9 @@ def main():
     positions.fill_(P + 3)
     evm = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(KM)]
     for i in range(KM):
-        evm[i][0].record()
+        evm[i][0].record(cur)
         mk.mk_decode_step_multikernel(h, tokens, positions, kv, logits, stream)
-        evm[i][1].record()
+        evm[i][1].record(cur)
         tokens.copy_(torch.argmax(logits, dim=1))
         positions.add_(1)
     torch.cuda.synchronize()

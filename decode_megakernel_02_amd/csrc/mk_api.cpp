@@ -126,9 +126,9 @@ int mk_schedule_inspect(const mk_config* cfg, int32_t n_cus, mk_schedule_info* o
     out->total_insts = (int64_t)p.insts.size();
     for (int cu = 0; cu < p.ncu; ++cu)
         out->max_insts_per_cu = std::max(out->max_insts_per_cu, (int32_t)(p.queue_begin[cu + 1] - p.queue_begin[cu]));
-    out->packed_weight_bytes = (int64_t)p.total_units * UNIT_BYTES;
     int64_t mx = 0, mn = INT64_MAX;
     for (uint64_t len : p.stream_len) {
+        out->packed_weight_bytes += (int64_t)len * UNIT_BYTES;
         mx = std::max(mx, (int64_t)len * UNIT_BYTES);
         mn = std::min(mn, (int64_t)len * UNIT_BYTES);
     }
@@ -224,15 +224,13 @@ int mk_create(const mk_config* cfg, mk_handle** out) {
         }
         // tagged activations (zeroed: tag 0 never matches a step epoch)
         const size_t B = p.B, L = p.L, H = p.H, QD = (size_t)p.Hq * p.D, KD = (size_t)p.Hkv * p.D;
-        const size_t n_q = L * B * QD, n_kv = L * B * KD, n_part = L * B * p.Hq * p.n_split * (p.D + 2);
+        const size_t n_qkv = L * B * (QD + 2 * KD), n_part = L * B * p.Hq * p.n_split * (p.D + 2);
         const size_t n_attn = L * B * QD, n_h = L * B * H, n_act = L * B * p.F;
-        const size_t words = n_q + 2 * n_kv + n_part + n_attn + 2 * n_h + n_act;
+        const size_t words = n_qkv + n_part + n_attn + 2 * n_h + n_act;
         uint64_t* arena = dalloc<uint64_t>(h, words);
         HIPCHK(hipMemset(arena, 0, words * 8));
         uint64_t* cur = arena;
-        hp.q = cur; cur += n_q;
-        hp.knew = cur; cur += n_kv;
-        hp.vnew = cur; cur += n_kv;
+        hp.qkv = cur; cur += n_qkv;
         hp.part = cur; cur += n_part;
         hp.attn = cur; cur += n_attn;
         hp.hmid = cur; cur += n_h;
@@ -240,6 +238,12 @@ int mk_create(const mk_config* cfg, mk_handle** out) {
         hp.hout = cur; cur += n_h;
         hp.dacc = dalloc<float>(h, B * H);
         hp.mats = nullptr;
+        hp.trace = nullptr;
+        if (cfg->flags & MK_FLAG_TRACE) {
+            const size_t n = p.insts.size() * TRACE_SLOTS;
+            hp.trace = dalloc<uint64_t>(h, n);
+            HIPCHK(hipMemset(hp.trace, 0, n * 8));
+        }
         hp.prof = nullptr;
         if (cfg->flags & MK_FLAG_PROFILE) {
             const size_t n = (size_t)ncu * (NW + NLOAD) * PROF_SLOTS;
@@ -383,6 +387,21 @@ int mk_get_profile(mk_handle* h, uint64_t* counters, size_t n) {
         HIPCHK(hipSetDevice(h->cfg.device));
         HIPCHK(hipDeviceSynchronize());
         HIPCHK(hipMemcpy(counters, h->hp.prof, need * 8, hipMemcpyDeviceToHost));
+    } catch (const HipError& e) {
+        return hip_fail(h, e);
+    }
+    return MK_OK;
+}
+
+int mk_get_trace(mk_handle* h, uint64_t* records, size_t n) {
+    if (!h || !records) return fail(h, MK_ERR_INVALID_ARG, "null argument");
+    if (!h->hp.trace) return fail(h, MK_ERR_STATE, "handle was created without MK_FLAG_TRACE");
+    const size_t need = h->plan.insts.size() * TRACE_SLOTS;
+    if (n < need) return fail(h, MK_ERR_INVALID_ARG, "record buffer too small");
+    try {
+        HIPCHK(hipSetDevice(h->cfg.device));
+        HIPCHK(hipDeviceSynchronize());
+        HIPCHK(hipMemcpy(records, h->hp.trace, need * 8, hipMemcpyDeviceToHost));
     } catch (const HipError& e) {
         return hip_fail(h, e);
     }

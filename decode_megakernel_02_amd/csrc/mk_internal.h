@@ -81,9 +81,8 @@ struct Params {
     const float* rope;             // [max_seq][D/2][2] (cos, sin)
 
     // tagged activations: 64-bit words {low: fp32 bits, high: step epoch}
-    uint64_t* q;      // [L][B][Hq*D]
-    uint64_t* knew;   // [L][B][Hkv*D]  (bf16-rounded value of the new K row)
-    uint64_t* vnew;   // [L][B][Hkv*D]
+    uint64_t* qkv;    // [L][B][Hkv][(G+2)*D]: the group's G query heads (after RoPE), then the
+                      // new K row (after RoPE) and V row, both rounded to bf16 values
     uint64_t* part;   // [L][B][Hq][n_split][D+2]  (m, l, o[D])
     uint64_t* attn;   // [L][B][Hq*D]
     uint64_t* hmid;   // [L][B][H]   residual stream after the attention block
@@ -93,6 +92,7 @@ struct Params {
     const void* const* mats;  // unused by the step kernels (pack only)
 
     uint64_t* prof;   // [ncu][NW + NLOAD][8] cycle counters, or null
+    uint64_t* trace;  // [total instructions][TRACE_SLOTS] timeline records, or null
     uint32_t* epoch;  // [ncu] per-workgroup step counter
     uint32_t* error;  // [8] device error record (code, wg, pc, op, wave, detail), abort flag at [7]
 };
@@ -100,6 +100,12 @@ struct Params {
 // Kernel launch flags.
 constexpr uint32_t KF_BUMP_EPOCH = 1u;  // last launch of a step: advance the per-workgroup epoch
 constexpr int PROF_SLOTS = 8;          // counters per wave
+// Timeline record per instruction (100 MHz real-time clock): [0] op | layer << 8 |
+// a << 16 | b << 32 | cu << 48, then per compute wave w at [1 + 5w]: start,
+// cross-CU inputs loaded, inputs ready (after the workgroup barrier), main
+// loop done (before the epilogue / merge), end; then the gather wave's start,
+// all polled inputs current, inputs staged.
+constexpr int TRACE_SLOTS = 1 + 5 * NW + 3;
 
 
 }  // namespace mk

@@ -26,14 +26,59 @@
 
 namespace mk {
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glb_void;
+// Explicit address spaces: the compiler otherwise emits flat instructions for
+// pointers it cannot trace, and a flat access to LDS is routed through the
+// vector-memory path, where it queues behind the loader's DMA.
+#define LDS __attribute__((address_space(3)))
+#define GLB __attribute__((address_space(1)))
+typedef LDS void lds_void;
+typedef GLB void glb_void;
+// Kernel parameters are read through the constant address space: they never
+// change during a launch, and no LDS or global store can alias them, so the
+// compiler keeps loaded fields instead of re-reading them after every store.
+typedef const __attribute__((address_space(4))) Params CParams;
+
+template <class T>
+__device__ __forceinline__ T gld(const T* p) {
+    return *(const GLB T*)p;
+}
+// vector loads through native clang vector types (HIP's vector structs copy
+// through generic references, which turns them back into flat accesses)
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 gld_u4(const void* p) {
+    const u32x4 v = *(const GLB u32x4*)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 lds_u4(const LDS void* p) {
+    const u32x4 v = *(const LDS u32x4*)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 lds_f4(const LDS float* p) {
+    const f32x4 v = *(const LDS f32x4*)p;
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float2 gld_f2(const float* p) {
+    const u32x2 v = *(const GLB u32x2*)p;
+    return make_float2(__uint_as_float(v.x), __uint_as_float(v.y));
+}
+template <class T>
+__device__ __forceinline__ void gst(T* p, T v) {
+    *(GLB T*)p = v;
+}
 
 #define CBAR() asm volatile("" ::: "memory")
 
-constexpr int MAXOUT = 16;  // DMA units in flight per loader wave
-constexpr int NSERVE = NW / NLOAD;
-static_assert(NSERVE == 2, "each loader wave serves two compute waves");
+#ifndef MK_MAXOUT
+#define MK_MAXOUT 16
+#endif
+#ifndef MK_KEEP
+#define MK_KEEP 8
+#endif
+constexpr int MAXOUT = MK_MAXOUT;  // DMA units in flight per loader wave
+constexpr int NWL = NLOAD - 1;  // weight loader waves; the last loader wave gathers inputs
+static_assert(NW <= 3 * NWL, "a weight loader serves at most three compute waves");
 
 // ------------------------------------------------------------- primitives --
 
@@ -41,11 +86,12 @@ __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u <<
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 // float -> bf16 bits, round to nearest even
+// (branch free: it runs in single active lanes of a wave)
 __device__ __forceinline__ uint16_t f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t q = (u >> 16) | 0x40u;  // NaN: keep it a quiet NaN
+    return (uint16_t)((u & 0x7fffffffu) > 0x7f800000u ? q : r);
 }
 
 template <int ctrl, int row_mask>
@@ -78,10 +124,11 @@ __device__ __forceinline__ float wave_max(float x) {
 // (agent-coherent) 8-byte stores and loads; an aligned 8-byte store is seen
 // whole or not at all, so value and tag always travel together.
 __device__ __forceinline__ void st_tag(uint64_t* p, float v, uint32_t tag) {
-    __hip_atomic_store(p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store((GLB uint64_t*)p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t ld_tag(const uint64_t* p) {
-    return __hip_atomic_load((uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_load((GLB uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t tag_of(uint64_t w) { return (uint32_t)(w >> 32); }
 __device__ __forceinline__ float val_of(uint64_t w) { return __uint_as_float((uint32_t)w); }
@@ -89,16 +136,16 @@ __device__ __forceinline__ float val_of(uint64_t w) { return __uint_as_float((ui
 // LDS sync words between waves of one workgroup.  LDS requests of one wave
 // complete in order, so a data write followed by a flag write is observed in
 // that order by any wave that reads the flag and then the data.
-__device__ __forceinline__ uint32_t lds_ld(const uint32_t* p) {
-    return __hip_atomic_load((uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+__device__ __forceinline__ uint32_t lds_ld(const LDS uint32_t* p) {
+    return __hip_atomic_load((LDS uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-__device__ __forceinline__ void lds_st(uint32_t* p, uint32_t v) {
+__device__ __forceinline__ void lds_st(LDS uint32_t* p, uint32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 // The loader wave issues LDS DMA; the compiler would guard its own LDS
 // accesses with vmcnt(0) waits (the DMA may alias them), so the loader touches
 // its sync words through inline asm instead.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(const lds_void*)p; }
+__device__ __forceinline__ uint32_t lds_addr(const lds_void* p) { return (uint32_t)(uintptr_t)p; }
 __device__ __forceinline__ uint32_t asm_lds_ld(uint32_t a) {
     uint32_t v;
     asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
@@ -128,44 +175,69 @@ __device__ __forceinline__ void wait_vm_le(uint32_t n) {
     default: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
     }
 }
-static_assert(MAXOUT == 16, "wait_vm_le covers 0..15");
+static_assert(MAXOUT <= 16, "wait_vm_le covers 0..15");
 
 // ------------------------------------------------------------ wave context --
 
 struct Ctx {
-    const Params* p;
+    CParams* p;
     int cu, wave, lane;
     uint32_t epoch;
     uint32_t pc;       // instruction index in this CU's queue (for error records)
     uint32_t op;
     bool aborted;
     bool prof;         // accumulate cycle counters
-    uint64_t cnt[5];   // see mk_get_profile
+    bool trace;        // write timeline records
+    uint64_t t_acq;    // real time at which the current instruction's cross-CU inputs were loaded
+    uint64_t t_in;     // real time at which the current instruction's inputs were ready
+    uint64_t t_mid;    // real time at which the main loop ended
+    uint64_t cnt[8];   // see mk_get_profile
 };
 
 __device__ __forceinline__ uint64_t cycles() { return __builtin_readcyclecounter(); }
+// constant-rate (100 MHz) clock shared by all CUs
+__device__ __forceinline__ uint64_t rtime() { return __builtin_amdgcn_s_memrealtime(); }
+__device__ __forceinline__ void mark_inputs(Ctx& cx) {
+    if (cx.trace) cx.t_in = rtime();
+}
+__device__ __forceinline__ void mark_acquired(Ctx& cx) {
+    if (cx.trace) cx.t_acq = rtime();
+}
+__device__ __forceinline__ void mark_mid(Ctx& cx) {
+    if (cx.trace) cx.t_mid = rtime();
+}
 
-__device__ __forceinline__ bool abort_flag(const Params* p) {
-    return __hip_atomic_load(&p->error[7], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+__device__ __forceinline__ bool abort_flag(CParams* p) {
+    return __hip_atomic_load((GLB uint32_t*)&p->error[7], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
 }
 __device__ __forceinline__ void record_error_rec(uint32_t* e, uint32_t code, uint32_t cu, uint32_t pc, uint32_t op,
                                              uint32_t wave, uint32_t detail) {
-    if (atomicCAS(&e[0], 0u, code) == 0u) {
-        e[1] = cu;
-        e[2] = pc;
-        e[3] = op;
-        e[4] = wave;
-        e[5] = detail;
+    GLB uint32_t* g = (GLB uint32_t*)e;
+    uint32_t expected = 0u;
+    if (__hip_atomic_compare_exchange_strong(g, &expected, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT)) {
+        g[1] = cu;
+        g[2] = pc;
+        g[3] = op;
+        g[4] = wave;
+        g[5] = detail;
     }
-    __hip_atomic_store(&e[7], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store((GLB uint32_t*)&e[7], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void record_error(Ctx& cx, uint32_t code, uint32_t detail) {
     record_error_rec(cx.p->error, code, (uint32_t)cx.cu, cx.pc, cx.op, (uint32_t)cx.wave, detail);
     cx.aborted = true;
 }
 // one iteration of a bounded wait; returns false once the wait must give up
+// Every wait loop polls on wave-uniform values (scalar branches) and sleeps
+// between polls: spinning waves would otherwise take most of the CU's scalar
+// issue slots away from the waves doing the work.
+__device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ bool any_lane(bool c) { return __builtin_amdgcn_ballot_w64(c) != 0; }
+
+template <int SLEEP = 1>
 __device__ __forceinline__ bool keep_waiting(Ctx& cx, uint32_t& spins, uint32_t detail) {
-    if (cx.aborted) return false;
+    if (uni(cx.aborted)) return false;
     ++spins;
     if ((spins & 63u) == 0u && abort_flag(cx.p)) {
         cx.aborted = true;
@@ -175,31 +247,40 @@ __device__ __forceinline__ bool keep_waiting(Ctx& cx, uint32_t& spins, uint32_t 
         record_error(cx, 1u, detail);
         return false;
     }
-    __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_s_sleep(SLEEP);
     return true;
 }
 
 // ---------------------------------------------------------------- LDS map --
 
+constexpr int SYNC_WORDS = 2 * NW + 4 + 2 * MAX_BATCH;  // counters + ss, zeroed at launch
+static_assert(SYNC_WORDS <= 64, "sync words precede the prefetch dump");  // dump: words 64..127 of 512 B
+
 struct Lds {
-    uint8_t* ring;      // [NW][ring_units][1024]
-    float* xbuf[2];     // two x buffers of xbuf_bytes each
-    uint32_t* landed;   // [NW] units landed in each compute wave's ring
-    uint32_t* consumed; // [NW] units consumed
-    uint32_t* bar;      // compute-wave barrier counter
-    float* red;         // [MAX_BATCH][NW] partial sums of squares
+    LDS uint8_t* ring;      // [NW][ring_units][1024]
+    LDS float* xbuf[2];     // two x buffers of xbuf_bytes each
+    LDS uint32_t* landed;   // [NW] units landed in each compute wave's ring
+    LDS uint32_t* consumed; // [NW] units consumed
+    LDS uint32_t* bar;      // compute-wave barrier counter
+    LDS uint32_t* gathered; // instructions of this launch whose inputs are staged
+    LDS uint32_t* done;     // instruction completions of the compute waves (NW per instruction)
+    LDS float* ss;          // [2][MAX_BATCH] sum of squares of each x buffer's raw input rows
+    LDS uint32_t* pf_dump;  // [64] landing words of the cache-prefetch touches (never read)
 };
-__device__ __forceinline__ Lds lds_map(uint8_t* smem, const Params& p) {
+__device__ __forceinline__ Lds lds_map(LDS uint8_t* smem, CParams& p) {
     Lds m;
     m.ring = smem;
     size_t off = (size_t)NW * p.ring_units * UNIT_BYTES;
-    m.xbuf[0] = (float*)(smem + off);
-    m.xbuf[1] = (float*)(smem + off + p.xbuf_bytes);
-    uint32_t* sync = (uint32_t*)(smem + off + 2 * (size_t)p.xbuf_bytes);
+    m.xbuf[0] = (LDS float*)(smem + off);
+    m.xbuf[1] = (LDS float*)(smem + off + p.xbuf_bytes);
+    LDS uint32_t* sync = (LDS uint32_t*)(smem + off + 2 * (size_t)p.xbuf_bytes);
     m.landed = sync;
     m.consumed = sync + NW;
     m.bar = sync + 2 * NW;
-    m.red = (float*)(sync + 2 * NW + 4);
+    m.gathered = sync + 2 * NW + 1;
+    m.done = sync + 2 * NW + 2;
+    m.ss = (LDS float*)(sync + 2 * NW + 4);
+    m.pf_dump = sync + 64;
     return m;
 }
 
@@ -208,10 +289,19 @@ __device__ __forceinline__ void cbar(Ctx& cx, const Lds& s, uint32_t& seq) {
     const uint64_t t0 = cx.prof ? cycles() : 0;
     seq += NW;
     CBAR();
-    if (cx.lane == 0) __hip_atomic_fetch_add(s.bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    uint32_t spins = 0;
-    while (lds_ld(s.bar) < seq)
-        if (!keep_waiting(cx, spins, 0xBA000000u | seq)) break;
+    uint32_t old = 0;
+    if (cx.lane == 0) old = __hip_atomic_fetch_add(s.bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (uni(old) + 1u == seq) {
+        // last to arrive: wake the waves sleeping in this barrier
+        asm volatile("s_wakeup" ::: "memory");
+        if (cx.prof) cx.cnt[7] += 1;
+    } else {
+        uint32_t spins = 0;
+        while (uni(lds_ld(s.bar)) < seq)
+            if (!keep_waiting<4>(cx, spins, 0xBA000000u | seq)) break;
+        if (cx.prof) cx.cnt[6] += spins;
+    }
+    if (cx.prof) cx.cnt[5] += 1;
     CBAR();
     if (cx.prof) cx.cnt[3] += cycles() - t0;
 }
@@ -221,7 +311,7 @@ __device__ __forceinline__ void cbar(Ctx& cx, const Lds& s, uint32_t& seq) {
 // One compute wave's stream as seen by its loader.  Every field is wave
 // uniform (scalar registers).
 struct LoadStream {
-    const uint8_t* src;   // this lane's 16 bytes of unit 0
+    const uint8_t* src;   // this lane's 16 bytes of the next unit to issue
     uint32_t ring_lds;    // LDS byte address of the ring
     uint32_t n, issued, done, slot, consumed;
     uint32_t a_landed, a_consumed;
@@ -229,7 +319,7 @@ struct LoadStream {
 
 __device__ __forceinline__ void load_stream_init(const Ctx& cx, const Lds& s, LoadStream& ls, int w, uint32_t ub,
                                                  uint32_t ue) {
-    const Params& p = *cx.p;
+    CParams& p = *cx.p;
     // the loaded values are the same in every lane: make that visible to the
     // compiler so the loader's loop state lives in scalar registers
     ub = __builtin_amdgcn_readfirstlane(ub);
@@ -245,58 +335,111 @@ __device__ __forceinline__ void load_stream_init(const Ctx& cx, const Lds& s, Lo
     ls.a_consumed = lds_addr(&s.consumed[w]);
 }
 
-// issue the stream's next unit if its ring has a free slot (re-reading the
-// consumer's count only when the ring looks full)
-__device__ __forceinline__ bool load_stream_issue(LoadStream& ls, uint32_t ru) {
-    if (ls.issued >= ls.n) return false;
-    if (ls.issued >= ls.consumed + ru) {
-        ls.consumed = __builtin_amdgcn_readfirstlane(asm_lds_ld(ls.a_consumed));
-        if (ls.issued >= ls.consumed + ru) return false;
+constexpr uint32_t ISSUE_BATCH = 4;  // units issued per stream per turn
+#ifndef MK_PF_DIST
+#define MK_PF_DIST 0
+#endif
+constexpr uint32_t PF_DIST = MK_PF_DIST;  // cache prefetch distance in steps of NW units (0: off)
+
+// Issues up to `max` (<= ISSUE_BATCH) consecutive units of the stream, as many
+// as its ring has room for (re-reading the consumer's count only when the
+// ring looks too full); returns how many.
+__device__ __forceinline__ uint32_t load_stream_issue(LoadStream& ls, uint32_t ru, uint32_t max) {
+    if (ls.issued >= ls.n) return 0;
+    if (ls.issued + max > ls.consumed + ru) ls.consumed = uni(asm_lds_ld(ls.a_consumed));
+    uint32_t k = ls.consumed + ru - ls.issued;
+    k = k < max ? k : max;
+    k = k < ls.n - ls.issued ? k : ls.n - ls.issued;
+#pragma unroll
+    for (uint32_t i = 0; i < ISSUE_BATCH; ++i) {
+        if (i < k) {
+            __builtin_amdgcn_global_load_lds((const glb_void*)ls.src,
+                                             (lds_void*)(uintptr_t)(ls.ring_lds + ls.slot * UNIT_BYTES), 16, 0, 0);
+            ls.src += NW * UNIT_BYTES;
+            ls.slot = ls.slot + 1 == ru ? 0 : ls.slot + 1;
+        }
     }
-    __builtin_amdgcn_global_load_lds((const glb_void*)(ls.src + (uint64_t)ls.issued * (NW * UNIT_BYTES)),
-                                     (lds_void*)(uintptr_t)(ls.ring_lds + ls.slot * UNIT_BYTES), 16, 0, 0);
-    ++ls.issued;
-    ls.slot = ls.slot + 1 == ru ? 0 : ls.slot + 1;
-    return true;
+    ls.issued += k;
+    return k;
 }
 
-constexpr uint32_t KEEP_IN_FLIGHT = 8;  // units left outstanding when retiring a batch
+constexpr uint32_t KEEP_IN_FLIGHT = MK_KEEP;  // units left outstanding when retiring a batch
+static_assert(MK_KEEP < MK_MAXOUT, "a retire step must free at least one unit");
+#ifndef MK_LOADER_PRIO
+#define MK_LOADER_PRIO 2
+#endif
+#ifndef MK_LOADER_SLEEP
+#define MK_LOADER_SLEEP 2
+#endif
 
-// Streams the units [ub, ue) of compute waves w0 and w1 into their rings.
-// DMA completes in issue order, so a bit FIFO (bit i = stream of the i-th
-// oldest outstanding unit) says whose units a vmcnt step retires.  Units are
-// retired in batches, keeping KEEP_IN_FLIGHT outstanding while the rings have
-// room.  The loader never blocks while DMA is in flight: when both rings are
-// full it retires what is outstanding instead, so it cannot wait on a compute
-// wave in a cycle.  It runs at raised instruction priority so the compute
-// waves' polling cannot starve it of issue slots.
+// Streams the units of up to three compute waves (w, w + 3, w + 6) into their
+// rings.  DMA completes in issue order, so a FIFO of 2-bit stream ids (entry
+// i = stream of the i-th oldest outstanding unit) says whose units a vmcnt
+// step retires.  Units are retired in batches, keeping KEEP_IN_FLIGHT
+// outstanding while the rings have room.  The loader never blocks while DMA
+// is in flight: when every ring is full it retires what is outstanding
+// instead, so it cannot wait on a compute wave in a cycle.  It runs at raised
+// instruction priority so the compute waves' polling cannot starve it of
+// issue slots.
 __device__ __forceinline__ void loader(Ctx& cx, const Lds& s, int w0, const uint32_t* uoff, uint32_t pc0,
                                        uint32_t pc1) {
-    __builtin_amdgcn_s_setprio(2);
-    const uint32_t ru = __builtin_amdgcn_readfirstlane((uint32_t)cx.p->ring_units);
-    const int w1 = w0 + 1;
-    LoadStream a, b;
+    __builtin_amdgcn_s_setprio(MK_LOADER_PRIO);
+    const uint32_t ru = uni((uint32_t)cx.p->ring_units);
+    LoadStream a, b, c;
+    const int w1 = w0 + NWL, w2 = w0 + 2 * NWL;
     load_stream_init(cx, s, a, w0, uoff[(size_t)pc0 * NW + w0], uoff[(size_t)pc1 * NW + w0]);
     load_stream_init(cx, s, b, w1, uoff[(size_t)pc0 * NW + w1], uoff[(size_t)pc1 * NW + w1]);
-    uint32_t fifo = 0, out = 0, spins = 0;
-    bool turn_b = false;
-    while (a.done < a.n || b.done < b.n) {
+    if (w2 < NW) load_stream_init(cx, s, c, w2, uoff[(size_t)pc0 * NW + w2], uoff[(size_t)pc1 * NW + w2]);
+    else load_stream_init(cx, s, c, w0, 0, 0);  // no third stream
+    // The last weight loader also prefetches the CU's packed weights (one
+    // contiguous region: its NW streams interleave unit by unit) up to
+    // PF_DIST steps of NW units ahead of its first stream, one 4-byte touch
+    // per 128-byte line, into a dump word of LDS: while the rings are full the
+    // HBM stream keeps filling the caches instead of idling.
+    const bool pf_on = PF_DIST > 0 && w0 == NWL - 1;
+    const GLB uint8_t* pf_src = nullptr;
+    uint32_t pf_k = 0, pf_end = 0, pf_ref = 0;
+    const uint32_t pf_dump = lds_addr(s.pf_dump);
+    if (pf_on) {
+        CParams& p = *cx.p;
+        uint32_t k0 = 0xffffffffu, k1 = 0;
+        for (int w = 0; w < NW; ++w) {
+            k0 = min(k0, uni(uoff[(size_t)pc0 * NW + w]));
+            k1 = max(k1, uni(uoff[(size_t)pc1 * NW + w]));
+        }
+        const uint64_t base = p.stream_base[cx.cu * NW];
+        const uint64_t base_u = ((uint64_t)uni((uint32_t)(base >> 32)) << 32) | uni((uint32_t)base);
+        pf_src = (const GLB uint8_t*)(p.wstream + base_u * UNIT_BYTES) + cx.lane * 128;
+        pf_k = k0;
+        pf_end = k1;
+        pf_ref = uni(uoff[(size_t)pc0 * NW + w0]);  // first unit of stream a
+    }
+    auto issue = [&](uint32_t sid, uint32_t max) -> uint32_t {
+        return sid == 0 ? load_stream_issue(a, ru, max)
+                        : sid == 1 ? load_stream_issue(b, ru, max) : load_stream_issue(c, ru, max);
+    };
+    uint32_t fifo = 0, out = 0, spins = 0, turn = 0;
+    while (a.done < a.n || b.done < b.n || c.done < c.n) {
         while (out < (uint32_t)MAXOUT) {
-            uint32_t sid;
-            bool issued;
-            if (turn_b) {
-                issued = load_stream_issue(b, ru);
-                sid = 1;
-                if (!issued) { issued = load_stream_issue(a, ru); sid = 0; }
-            } else {
-                issued = load_stream_issue(a, ru);
-                sid = 0;
-                if (!issued) { issued = load_stream_issue(b, ru); sid = 1; }
+            const uint32_t max = MAXOUT - out < ISSUE_BATCH ? MAXOUT - out : ISSUE_BATCH;
+            uint32_t sid = turn;
+            uint32_t k = issue(sid, max);
+            if (!k) { sid = sid == 2 ? 0 : sid + 1; k = issue(sid, max); }
+            if (!k) { sid = sid == 2 ? 0 : sid + 1; k = issue(sid, max); }
+            if (!k) {
+                if (pf_on && pf_k < pf_end && pf_k < pf_ref + a.issued + PF_DIST) {
+                    __builtin_amdgcn_global_load_lds((const glb_void*)(pf_src + (size_t)pf_k * (NW * UNIT_BYTES)),
+                                                     (lds_void*)(uintptr_t)pf_dump, 4, 0, 0);
+                    ++pf_k;
+                    fifo |= 3u << (2 * out);
+                    ++out;
+                    continue;
+                }
+                break;
             }
-            if (!issued) break;
-            fifo |= sid << out;
-            ++out;
-            turn_b = !turn_b;
+            fifo |= (sid * (0x55u & ((1u << (2 * k)) - 1u))) << (2 * out);  // k entries of sid
+            out += k;
+            turn = sid == 2 ? 0 : sid + 1;
         }
         if (out > 0) {
             // retire all but KEEP_IN_FLIGHT units (all of them when nothing more could be issued)
@@ -306,17 +449,21 @@ __device__ __forceinline__ void loader(Ctx& cx, const Lds& s, int w0, const uint
             wait_vm_le(keep);
             if (cx.prof) cx.cnt[1] += cycles() - t0;
             const uint32_t k = out - keep;
-            const uint32_t mask = k >= 32 ? 0xffffffffu : (1u << k) - 1u;
-            const uint32_t nb = (uint32_t)__builtin_popcount(fifo & mask);
-            fifo = k >= 32 ? 0u : fifo >> k;
+            const uint32_t f = k >= 16 ? fifo : fifo & ((1u << (2 * k)) - 1u);
+            const uint32_t lo = f & 0x55555555u, hi = (f >> 1) & 0x55555555u;
+            const uint32_t n1 = (uint32_t)__builtin_popcount(lo & ~hi), n2 = (uint32_t)__builtin_popcount(hi & ~lo);
+            const uint32_t n3 = (uint32_t)__builtin_popcount(lo & hi);  // prefetch touches
+            const uint32_t n0 = k - n1 - n2 - n3;
+            fifo = k >= 16 ? 0u : fifo >> (2 * k);
             out = keep;
-            if (k - nb) asm_lds_st(a.a_landed, a.done += k - nb);
-            if (nb) asm_lds_st(b.a_landed, b.done += nb);
+            if (n0) asm_lds_st(a.a_landed, a.done += n0);
+            if (n1) asm_lds_st(b.a_landed, b.done += n1);
+            if (n2) asm_lds_st(c.a_landed, c.done += n2);
             if (cx.prof) cx.cnt[3] += k;
             spins = 0;
         } else {
             const uint64_t t0 = cx.prof ? cycles() : 0;
-            const bool go_on = keep_waiting(cx, spins, 0x10000000u | (a.done << 12) | b.done);
+            const bool go_on = keep_waiting<MK_LOADER_SLEEP>(cx, spins, 0x10000000u | (a.done << 12) | b.done);
             if (cx.prof) cx.cnt[2] += cycles() - t0;
             if (!go_on) break;
         }
@@ -348,13 +495,13 @@ __device__ __forceinline__ uint4 ring_take(Ctx& cx, const Lds& s, Stream& st) {
         ring_release(cx, s, st);
         const uint64_t t0 = cx.prof ? cycles() : 0;
         uint32_t spins = 0;
-        while ((st.landed = lds_ld(&s.landed[cx.wave])) <= st.unit)
+        while ((st.landed = uni(lds_ld(&s.landed[cx.wave]))) <= st.unit)
             if (!keep_waiting(cx, spins, 0x20000000u | st.unit)) break;
         CBAR();
         if (cx.prof) cx.cnt[1] += cycles() - t0;
     }
     if (cx.prof) cx.cnt[4] += 1;
-    return *(const uint4*)(s.ring + ((size_t)cx.wave * cx.p->ring_units + st.slot) * UNIT_BYTES + cx.lane * 16);
+    return lds_u4(s.ring + ((size_t)cx.wave * cx.p->ring_units + st.slot) * UNIT_BYTES + cx.lane * 16);
 }
 __device__ __forceinline__ void ring_advance(const Ctx& cx, Stream& st) {
     ++st.unit;
@@ -364,8 +511,9 @@ __device__ __forceinline__ void ring_advance(const Ctx& cx, Stream& st) {
 // x buffer layout per batch row: [half][chunk][4] with element k in half
 // (k % 8) / 4, chunk k / 8, position k % 4, so a lane's 8 elements of one unit
 // are two 16-byte reads at consecutive addresses across lanes.
-__device__ __forceinline__ int xidx(const Params& p, int b, int k) {
-    return b * p.xstride + ((k & 4) ? (p.xstride >> 1) : 0) + (k >> 3) * 4 + (k & 3);
+// xs = floats per batch row.  For k0 a multiple of 8, xidx(k0 + k) = xidx(k) + k0 / 2.
+__device__ __forceinline__ int xidx(int xs, int b, int k) {
+    return b * xs + ((k & 4) ? (xs >> 1) : 0) + (k >> 3) * 4 + (k & 3);
 }
 
 __device__ __forceinline__ float dot8(const uint4 w, const float4 a, const float4 b) {
@@ -380,48 +528,13 @@ __device__ __forceinline__ float dot8(const uint4 w, const float4 a, const float
     return s;
 }
 
-// Reads n tagged words *addr(i) (thread t of the 512 compute threads takes
-// i = t, t+512, ...), waiting until each carries this step's epoch, and hands
-// (i, value) to put.  Loads are issued four at a time so latencies overlap.
-template <class Addr, class Put>
-__device__ __forceinline__ void acquire(Ctx& cx, int n, Addr&& addr, Put&& put) {
-    const uint64_t t_begin = cx.prof ? cycles() : 0;
-    const int t = cx.wave * 64 + cx.lane;
-    constexpr int NT = NW * 64;
-    for (int i0 = t; i0 < n; i0 += 4 * NT) {
-        uint64_t w[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int i = i0 + j * NT;
-            w[j] = i < n ? ld_tag(addr(i)) : ((uint64_t)cx.epoch << 32);
-        }
-        uint32_t spins = 0;
-        while (true) {
-            bool ok = true;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) ok &= tag_of(w[j]) == cx.epoch;
-            if (ok) break;
-            if (!keep_waiting(cx, spins, 0x30000000u | (uint32_t)i0)) break;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (tag_of(w[j]) != cx.epoch) w[j] = ld_tag(addr(i0 + j * NT));
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int i = i0 + j * NT;
-            if (i < n) put(i, val_of(w[j]));
-        }
-    }
-    if (cx.prof) cx.cnt[2] += cycles() - t_begin;
-}
-
 // Poll a single tagged word (epilogue inputs that were produced long before).
 __device__ __forceinline__ float wait_word(Ctx& cx, const uint64_t* p) {
     uint64_t w = ld_tag(p);
     uint32_t spins = 0;
-    while (tag_of(w) != cx.epoch) {
+    while (any_lane(tag_of(w) != cx.epoch)) {
         if (!keep_waiting(cx, spins, 0x40000000u)) break;
-        w = ld_tag(p);
+        if (tag_of(w) != cx.epoch) w = ld_tag(p);
     }
     return val_of(w);
 }
@@ -437,7 +550,7 @@ __device__ __forceinline__ void ring_wait(Ctx& cx, const Lds& s, Stream& st, uin
     ring_release(cx, s, st);
     const uint64_t t0 = cx.prof ? cycles() : 0;
     uint32_t spins = 0;
-    while ((st.landed = lds_ld(&s.landed[cx.wave])) < need)
+    while ((st.landed = uni(lds_ld(&s.landed[cx.wave]))) < need)
         if (!keep_waiting(cx, spins, 0x20000000u | st.unit)) break;
     CBAR();
     if (cx.prof) cx.cnt[1] += cycles() - t0;
@@ -452,12 +565,11 @@ struct XSlice {
 };
 
 template <int KU>
-__device__ __forceinline__ void load_xslice(const Ctx& cx, const float* xb, int xstride, XSlice<KU>& x) {
-    const float4* xr = (const float4*)xb;
+__device__ __forceinline__ void load_xslice(const Ctx& cx, const LDS float* xb, int xstride, XSlice<KU>& x) {
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
-        x.lo[u] = xr[u * 64 + cx.lane];
-        x.hi[u] = xr[(xstride >> 3) + u * 64 + cx.lane];
+        x.lo[u] = lds_f4(xb + 4 * (u * 64 + cx.lane));
+        x.hi[u] = lds_f4(xb + 4 * ((xstride >> 3) + u * 64 + cx.lane));
     }
 }
 
@@ -472,7 +584,7 @@ __device__ __forceinline__ void rowgroup_dot_b1(Ctx& cx, const Lds& s, Stream& s
         for (int u = 0; u < KU; ++u) {
             uint32_t sl = st.slot + u;
             sl = sl >= ru ? sl - ru : sl;
-            w[u] = *(const uint4*)(s.ring + ((size_t)cx.wave * ru + sl) * UNIT_BYTES + cx.lane * 16);
+            w[u] = lds_u4(s.ring + ((size_t)cx.wave * ru + sl) * UNIT_BYTES + cx.lane * 16);
         }
         float acc[KU];
 #pragma unroll
@@ -492,9 +604,10 @@ __device__ __forceinline__ void rowgroup_dot_b1(Ctx& cx, const Lds& s, Stream& s
 // Dot products of one row-group (NROWS = 1 or 2 rows of ku units each) with x
 // for every batch row (x read from LDS); general path for any batch size.
 template <int NROWS>
-__device__ __forceinline__ void rowgroup_dot(Ctx& cx, const Lds& s, Stream& st, const float* xb, int ku, RowOut& out) {
-    const Params& p = *cx.p;
-    const int B = p.B;
+__device__ __forceinline__ void rowgroup_dot(Ctx& cx, const Lds& s, Stream& st, const LDS float* xb, int ku,
+                                             RowOut& out) {
+    CParams& p = *cx.p;
+    const int B = p.B, xs = (int)uni((uint32_t)p.xstride);
 #pragma unroll
     for (int r = 0; r < NROWS; ++r) {
         float acc[MAX_BATCH];
@@ -506,8 +619,8 @@ __device__ __forceinline__ void rowgroup_dot(Ctx& cx, const Lds& s, Stream& st, 
 #pragma unroll
             for (int b = 0; b < MAX_BATCH; ++b) {
                 if (b < B) {
-                    const float4* xr = (const float4*)(xb + b * p.xstride);
-                    const float4 lo = xr[c], hi = xr[(p.xstride >> 3) + c];
+                    const LDS float* xr = xb + b * xs;
+                    const float4 lo = lds_f4(xr + 4 * c), hi = lds_f4(xr + 4 * ((xs >> 3) + c));
                     acc[b] += dot8(w, lo, hi);
                 }
             }
@@ -526,44 +639,6 @@ __device__ __forceinline__ void rowgroup_dot(Ctx& cx, const Lds& s, Stream& st, 
     }
 }
 
-// Zero x[b][k] for k in [kvalid, kpad) (padding multiplies zero weights; NaN-free).
-__device__ __forceinline__ void x_pad(Ctx& cx, float* xb, int kvalid, int kpad) {
-    const Params& p = *cx.p;
-    const int t = cx.wave * 64 + cx.lane;
-    for (int b = 0; b < p.B; ++b)
-        for (int k = kvalid + t; k < kpad; k += NW * 64) xb[xidx(p, b, k)] = 0.f;
-}
-
-// Finish an RMSNorm input held raw in LDS: after a barrier, each thread sums
-// the squares of its elements of every batch row and multiplies them by the
-// gain in place; per-wave partials go through LDS (fixed summation order) and
-// lane b returns 1/sqrt(mean(h_b^2) + eps).  Two compute-wave barriers.
-__device__ __forceinline__ float rms_finish(Ctx& cx, const Lds& s, uint32_t& seq, float* xb, const uint16_t* gain,
-                                            int K) {
-    const Params& p = *cx.p;
-    const int t = cx.wave * 64 + cx.lane;
-    cbar(cx, s, seq);
-    for (int b = 0; b < p.B; ++b) {
-        float ss = 0.f;
-        for (int k = t; k < K; k += NW * 64) {
-            float* x = xb + xidx(p, b, k);
-            const float v = *x;
-            ss = fmaf(v, v, ss);
-            *x = v * bf2f(gain[k]);
-        }
-        ss = wave_sum(ss);
-        if (cx.lane == 0) s.red[b * NW + cx.wave] = ss;
-    }
-    cbar(cx, s, seq);
-    float my = 0.f;
-    if (cx.lane < p.B) {
-        float tot = 0.f;
-        for (int w = 0; w < NW; ++w) tot += s.red[cx.lane * NW + w];
-        my = 1.0f / sqrtf(tot / (float)K + p.eps);
-    }
-    return my;
-}
-
 struct Step {  // per-launch batch inputs, lane b holds row b
     int tok, pos;
     const int32_t* tokens;
@@ -572,82 +647,264 @@ struct Step {  // per-launch batch inputs, lane b holds row b
     float* logits;
 };
 
+// ------------------------------------------------------------ gather wave --
+//
+// The last loader wave stages every instruction's cross-CU inputs in an LDS
+// x buffer one instruction ahead of the compute waves (the two buffers
+// alternate by instruction), so the compute waves start each instruction
+// with a single LDS counter check instead of polling remote memory and
+// meeting at a barrier.  For RMSNorm inputs it also sums the squares of the
+// raw rows and stores x * gain.
+
+// Reads the n (even) tagged words at base, two adjacent words per lane per
+// 16-byte load and 128 * NB words per round, polling until every tag carries
+// this step's epoch; put(k, v_k, v_k+1, gain pair) stores them.  With GAIN,
+// the bf16 gain pair at gain + k is loaded alongside.  Buffer loads keep the
+// addresses in scalar registers; their range check returns zeros past n.
+constexpr uint32_t RSRC_WORD3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9)
+constexpr int CPOL_SC1 = 16;                 // device-coherent load: bypasses the non-coherent L2 copy
+
+template <int NB, bool GAIN, class Put>
+__device__ __forceinline__ void gather_region(Ctx& cx, const uint64_t* base, int n, const uint16_t* gain, Put&& put) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, n * 8, RSRC_WORD3);
+    __amdgpu_buffer_rsrc_t rg = rs;
+    if (GAIN) rg = __builtin_amdgcn_make_buffer_rsrc((void*)gain, (short)0, n * 2, RSRC_WORD3);
+    const uint32_t ep = cx.epoch;
+    for (int k0 = 0; k0 < n; k0 += 128 * NB) {
+        u32x4 w[NB];
+        uint32_t g[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const int k = k0 + j * 128 + 2 * cx.lane;
+            w[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, k * 8, 0, CPOL_SC1);
+            if (GAIN) g[j] = __builtin_amdgcn_raw_buffer_load_b32(rg, k * 2, 0, 0);
+        }
+        uint32_t spins = 0;
+        while (true) {
+            bool stale = false;
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const int k = k0 + j * 128 + 2 * cx.lane;
+                stale |= k < n && (w[j].y != ep || w[j].w != ep);
+            }
+            if (!any_lane(stale)) break;
+            if (!keep_waiting(cx, spins, 0x50000000u | (uint32_t)k0)) return;
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const int k = k0 + j * 128 + 2 * cx.lane;
+                if (k < n && (w[j].y != ep || w[j].w != ep))
+                    w[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, k * 8, 0, CPOL_SC1);
+            }
+        }
+        if (cx.trace) cx.t_acq = rtime();  // every tag current
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const int k = k0 + j * 128 + 2 * cx.lane;
+            if (k < n) put(k, __uint_as_float(w[j].x), __uint_as_float(w[j].z), GAIN ? g[j] : 0x3f803f80u);
+        }
+    }
+}
+
+constexpr int GATHER_NB = 16;      // 16-byte loads per lane per polling round (2048 words)
+constexpr int GATHER_NB_ATTN = 6;  // (G + 2) * D <= 768 words
+
+// x[b][k] = raw[b][k] * gain[k] in the x-buffer layout, plus zero padding up
+// to kpad; ss[b] = sum_k raw[b][k]^2 when ss_out is given.
+template <bool GAIN, class Row>
+__device__ __forceinline__ void gather_x(Ctx& cx, int B, int K, int kpad, Row&& row, const uint16_t* gain,
+                                         LDS float* xb, LDS float* ss_out) {
+    const int xs = (int)uni((uint32_t)cx.p->xstride);
+    for (int b = 0; b < B; ++b) {
+        float ss = 0.f;
+        // lane l stores pairs k = k0 + 2l (k0 a multiple of 128): one base address per lane
+        LDS float* xl = xb + xidx(xs, b, 2 * cx.lane);
+        gather_region<GATHER_NB, GAIN>(cx, row(b), K, gain,
+                                      [&](int k, float v0, float v1, uint32_t gp) {
+                                          ss = fmaf(v0, v0, ss);
+                                          ss = fmaf(v1, v1, ss);
+                                          LDS float* x = xl + (k - 2 * cx.lane) / 2;  // k, k+1 adjacent
+                                          x[0] = v0 * bf_lo(gp);
+                                          x[1] = v1 * bf_hi(gp);
+                                      });
+        for (int k = K + cx.lane; k < kpad; k += 64) xb[xidx(xs, b, k)] = 0.f;
+        if (ss_out) {
+            ss = wave_sum(ss);
+            if (cx.lane == 0) ss_out[b] = ss;
+        }
+    }
+}
+
+// Embedding rows (bf16, written before the launch: no tags) as the input of
+// the first layer's RMSNorm.
+__device__ __forceinline__ void gather_embed(Ctx& cx, const Step& sp, int kpad, const uint16_t* gain, LDS float* xb,
+                                             LDS float* ss_out) {
+    CParams& p = *cx.p;
+    const int H = p.H, xs = (int)uni((uint32_t)p.xstride);
+    for (int b = 0; b < p.B; ++b) {
+        const int tok = gld(sp.tokens + b);
+        const uint32_t* row = (const uint32_t*)(p.embed + (size_t)tok * H);  // H even: bf16 pairs
+        float ss = 0.f;
+        for (int k0 = 0; k0 < H; k0 += 128 * GATHER_NB) {
+            uint32_t e[GATHER_NB], g[GATHER_NB];
+#pragma unroll
+            for (int j = 0; j < GATHER_NB; ++j) {
+                const int k = k0 + j * 128 + 2 * cx.lane;
+                e[j] = k < H ? gld(row + k / 2) : 0u;
+                g[j] = k < H ? gld((const uint32_t*)(gain + k)) : 0u;
+            }
+#pragma unroll
+            for (int j = 0; j < GATHER_NB; ++j) {
+                const int k = k0 + j * 128 + 2 * cx.lane;
+                if (k < H) {
+                    const float v0 = bf_lo(e[j]), v1 = bf_hi(e[j]);
+                    ss = fmaf(v0, v0, ss);
+                    ss = fmaf(v1, v1, ss);
+                    LDS float* x = xb + xidx(xs, b, k);
+                    x[0] = v0 * bf_lo(g[j]);
+                    x[1] = v1 * bf_hi(g[j]);
+                }
+            }
+        }
+        for (int k = H + cx.lane; k < kpad; k += 64) xb[xidx(xs, b, k)] = 0.f;
+        ss = wave_sum(ss);
+        if (cx.lane == 0) ss_out[b] = ss;
+    }
+}
+
+// Stages the inputs of one instruction in xb (see the op bodies for layouts).
+__device__ __forceinline__ void gather_inst(Ctx& cx, const Step& sp, const Inst& in, LDS float* xb, LDS float* ss) {
+    CParams& p = *cx.p;
+    const int B = p.B, H = p.H, l = in.layer;
+    switch (in.op) {
+    case OP_RMS_QKV_ROPE:
+    case OP_RMS_LM_HEAD: {
+        const int src_layer = in.op == OP_RMS_LM_HEAD ? p.L : l;  // residual stream entering this layer
+        const uint16_t* gain = in.op == OP_RMS_LM_HEAD ? p.gain_final : p.gain_attn + (size_t)l * H;
+        const int kpad = p.ku_h * UNIT_ELEMS;
+        if (src_layer == 0) {
+            gather_embed(cx, sp, kpad, gain, xb, ss);
+        } else {
+            const uint64_t* src = p.hout + (size_t)(src_layer - 1) * B * H;
+            gather_x<true>(cx, B, H, kpad, [&](int b) { return src + (size_t)b * H; }, gain, xb, ss);
+        }
+        break;
+    }
+    case OP_RMS_UP_GATE: {
+        const uint64_t* src = p.hmid + (size_t)l * B * H;
+        gather_x<true>(cx, B, H, p.ku_h * UNIT_ELEMS, [&](int b) { return src + (size_t)b * H; },
+                       p.gain_mlp + (size_t)l * H, xb, ss);
+        break;
+    }
+    case OP_O_PROJ_RES: {
+        const int K = p.Hq * p.D;
+        const uint64_t* src = p.attn + (size_t)l * B * K;
+        gather_x<false>(cx, B, K, p.ku_q * UNIT_ELEMS, [&](int b) { return src + (size_t)b * K; }, nullptr, xb,
+                        nullptr);
+        break;
+    }
+    case OP_DOWN_RES: {
+        const int c0 = p.chunk_begin[in.a], K = p.chunk_begin[in.a + 1] - c0;
+        const uint64_t* src = p.act + (size_t)l * B * p.F + c0;
+        gather_x<false>(cx, B, K, p.ku_f * UNIT_ELEMS, [&](int b) { return src + (size_t)b * p.F; }, nullptr, xb,
+                        nullptr);
+        break;
+    }
+    case OP_ATTENTION: {
+        // qs [G][D] (pre-scaled by 1/sqrt(D)), kn [D], vn [D]: one contiguous block
+        const int b = in.a, g = in.b, D = p.D, nq = p.G * D;
+        const uint64_t* src = p.qkv + (((size_t)l * B + b) * p.Hkv + g) * (size_t)(p.G + 2) * D;
+        const float sc = p.inv_sqrt_d;
+        gather_region<GATHER_NB_ATTN, false>(cx, src, nq + 2 * D, nullptr, [&](int i, float v0, float v1, uint32_t) {
+            const float f = i < nq ? sc : 1.f;  // nq even: a pair never straddles q and k
+            xb[i] = v0 * f;
+            xb[i + 1] = v1 * f;
+        });
+        break;
+    }
+    default: {  // OP_ATTN_REDUCE: the n_split partials (m, l, o[D]) of (row, head)
+        const int b = in.a, head = in.b, W = p.D + 2;
+        const uint64_t* src = p.part + (((size_t)l * B + b) * p.Hq + head) * p.n_split * W;
+        gather_region<GATHER_NB, false>(cx, src, p.n_split * W, nullptr, [&](int i, float v0, float v1, uint32_t) {
+                                           xb[i] = v0;
+                                           xb[i + 1] = v1;
+                                       });
+        break;
+    }
+    }
+}
+
+__device__ __forceinline__ Inst decode_inst(const u32x4 raw) {
+    Inst in;
+    in.op = (uint16_t)(raw.x & 0xffffu);
+    in.layer = (uint16_t)(raw.x >> 16);
+    in.rg0 = raw.y;
+    in.nrg = raw.z;
+    in.a = (uint16_t)(raw.w & 0xffffu);
+    in.b = (uint16_t)(raw.w >> 16);
+    return in;
+}
+
+// The gather wave's loop over instructions [pc0, pc1) of this CU's queue.
+__device__ __forceinline__ void gatherer(Ctx& cx, const Lds& s, const Step& sp, uint32_t qb, uint32_t pc0,
+                                         uint32_t pc1) {
+    CParams& p = *cx.p;
+    __builtin_amdgcn_s_setprio(MK_LOADER_PRIO);
+    const GLB u32x4* iq = (const GLB u32x4*)(p.insts + qb);
+    for (uint32_t pc = pc0; pc < pc1; ++pc) {
+        const uint32_t r = pc - pc0;
+        const u32x4 raw = iq[pc];
+        if (r >= 2) {  // x buffer r & 1 held instruction r - 2: wait until every compute wave is done with it
+            uint32_t spins = 0;
+            while (uni(lds_ld(s.done)) < NW * (r - 1))
+                if (!keep_waiting<2>(cx, spins, 0x60000000u | r)) break;
+        }
+        if (uni(cx.aborted)) break;
+        const Inst in = decode_inst(raw);
+        cx.pc = pc;
+        cx.op = in.op;
+        const uint64_t t0 = cx.trace ? rtime() : 0;
+        cx.t_acq = t0;
+        gather_inst(cx, sp, in, r & 1 ? s.xbuf[1] : s.xbuf[0], s.ss + (r & 1) * MAX_BATCH);
+        if (uni(cx.aborted)) break;
+        CBAR();
+        if (cx.lane == 0) lds_st(s.gathered, r + 1);  // after the staged data (LDS requests of a wave stay ordered)
+        if (cx.trace && cx.lane == 0) {
+            GLB uint64_t* rec = (GLB uint64_t*)p.trace + (size_t)(qb + pc) * TRACE_SLOTS + 1 + 5 * NW;
+            rec[0] = t0;
+            rec[1] = cx.t_acq;
+            rec[2] = rtime();
+        }
+    }
+}
+
+// Compute-wave side: wait until instruction r's inputs are staged.
+__device__ __forceinline__ void wait_inputs(Ctx& cx, const Lds& s, uint32_t r) {
+    const uint64_t t0 = cx.prof ? cycles() : 0;
+    uint32_t spins = 0;
+    while (uni(lds_ld(s.gathered)) <= r)
+        if (!keep_waiting(cx, spins, 0x70000000u | r)) break;
+    CBAR();
+    if (cx.prof) cx.cnt[2] += cycles() - t0;
+    mark_acquired(cx);
+    mark_inputs(cx);
+}
+
 // ------------------------------------------------------------ GEMV ops ------
 
 // KU > 0: batch-1 path with KU units per row (x slice in registers);
 // KU == 0: general path.
 template <int KU>
-__device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint32_t& seq, const Inst& in, float* xb,
+__device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint32_t r, const Inst& in, LDS float* xb,
                                         const Step& sp) {
-    const Params& p = *cx.p;
+    CParams& p = *cx.p;
     const int B = p.B, H = p.H, l = in.layer;
-    int ku, kvalid;
-    // ---- input vector (raw values) into LDS
-    switch (in.op) {
-    case OP_RMS_QKV_ROPE:
-    case OP_RMS_LM_HEAD: {
-        ku = p.ku_h;
-        kvalid = H;
-        const int src_layer = in.op == OP_RMS_LM_HEAD ? p.L : l;  // residual stream entering this layer
-        if (src_layer == 0) {
-            const int t = cx.wave * 64 + cx.lane;
-            for (int b = 0; b < B; ++b) {
-                const int tok = sp.tokens[b];
-                for (int k = t; k < H; k += NW * 64) xb[xidx(p, b, k)] = bf2f(p.embed[(size_t)tok * H + k]);
-            }
-        } else {
-            const uint64_t* src = p.hout + (size_t)(src_layer - 1) * B * H;
-            acquire(cx, B * H, [&](int i) { return src + i; }, [&](int i, float v) {
-                const int b = i / H;
-                xb[xidx(p, b, i - b * H)] = v;
-            });
-        }
-        break;
-    }
-    case OP_RMS_UP_GATE: {
-        ku = p.ku_h;
-        kvalid = H;
-        const uint64_t* src = p.hmid + (size_t)l * B * H;
-        acquire(cx, B * H, [&](int i) { return src + i; }, [&](int i, float v) {
-            const int b = i / H;
-            xb[xidx(p, b, i - b * H)] = v;
-        });
-        break;
-    }
-    case OP_O_PROJ_RES: {
-        ku = p.ku_q;
-        const int K = p.Hq * p.D;
-        kvalid = K;
-        const uint64_t* src = p.attn + (size_t)l * B * K;
-        acquire(cx, B * K, [&](int i) { return src + i; }, [&](int i, float v) {
-            const int b = i / K;
-            xb[xidx(p, b, i - b * K)] = v;
-        });
-        break;
-    }
-    default: {  // OP_DOWN_RES: chunk a of the SwiGLU output
-        ku = p.ku_f;
-        const int c0 = p.chunk_begin[in.a], K = p.chunk_begin[in.a + 1] - c0;
-        kvalid = K;
-        const uint64_t* src = p.act + (size_t)l * B * p.F + c0;
-        acquire(cx, B * K, [&](int i) { const int b = i / K; return src + (size_t)b * p.F + (i - b * K); },
-                [&](int i, float v) {
-                    const int b = i / K;
-                    xb[xidx(p, b, i - b * K)] = v;
-                });
-        break;
-    }
-    }
-    x_pad(cx, xb, kvalid, ku * UNIT_ELEMS);
-    float scale = 1.f;  // lane b: RMSNorm scale of batch row b
-    if (in.op == OP_RMS_QKV_ROPE || in.op == OP_RMS_LM_HEAD) {
-        scale = rms_finish(cx, s, seq, xb, in.op == OP_RMS_LM_HEAD ? p.gain_final : p.gain_attn + (size_t)l * H, H);
-    } else if (in.op == OP_RMS_UP_GATE) {
-        scale = rms_finish(cx, s, seq, xb, p.gain_mlp + (size_t)l * H, H);
-    } else {
-        cbar(cx, s, seq);
-    }
+    const int ku = in.op == OP_O_PROJ_RES ? p.ku_q : in.op == OP_DOWN_RES ? p.ku_f : p.ku_h;
+    // x = raw input * gain, staged by the gather wave; lane b: RMSNorm scale of batch row b
+    wait_inputs(cx, s, r);
     if (cx.aborted) return;
+    float scale = 1.f;
+    if ((in.op == OP_RMS_QKV_ROPE || in.op == OP_RMS_LM_HEAD || in.op == OP_RMS_UP_GATE) && cx.lane < B)
+        scale = 1.0f / sqrtf(s.ss[(r & 1) * MAX_BATCH + cx.lane] / (float)H + p.eps);
 
     XSlice<KU == 0 ? 1 : KU> xs;
     const uint32_t ru = __builtin_amdgcn_readfirstlane((uint32_t)p.ring_units);
@@ -678,19 +935,19 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
                 const int g = rg / PG, t = rg % PG;
                 if (t < (G + 1) * half) {  // q or k: rotate the pair (ii, ii + D/2)
                     const int ii = t < G * half ? t % half : t - G * half;
-                    const float2 cs = *(const float2*)(p.rope + ((size_t)pos * half + ii) * 2);
+                    const float2 cs = gld_f2(p.rope + ((size_t)pos * half + ii) * 2);
                     const float r1 = y1 * cs.x - y2 * cs.y, r2 = y2 * cs.x + y1 * cs.y;
+                    uint64_t* blk = p.qkv + (((size_t)l * B + b) * p.Hkv + g) * (size_t)(G + 2) * D;
                     if (t < G * half) {
-                        const int head = g * G + t / half;
-                        uint64_t* q = p.q + ((size_t)l * B + b) * p.Hq * D + head * D;
+                        uint64_t* q = blk + (t / half) * D;
                         st_tag(q + ii, r1, cx.epoch);
                         st_tag(q + ii + half, r2, cx.epoch);
                     } else {
                         const uint16_t k1 = f2bf(r1), k2 = f2bf(r2);
                         uint16_t* kc = sp.kv + ((((size_t)l * 2 + 0) * B + b) * p.Hkv + g) * (size_t)p.max_seq * D + (size_t)pos * D;
-                        kc[ii] = k1;
-                        kc[ii + half] = k2;
-                        uint64_t* kn = p.knew + ((size_t)l * B + b) * p.Hkv * D + g * D;
+                        gst(kc + ii, k1);
+                        gst(kc + ii + half, k2);
+                        uint64_t* kn = blk + G * D;
                         st_tag(kn + ii, bf2f(k1), cx.epoch);
                         st_tag(kn + ii + half, bf2f(k2), cx.epoch);
                     }
@@ -698,9 +955,9 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
                     const int ii = t - (G + 1) * half;
                     const uint16_t v1 = f2bf(y1), v2 = f2bf(y2);
                     uint16_t* vc = sp.kv + ((((size_t)l * 2 + 1) * B + b) * p.Hkv + g) * (size_t)p.max_seq * D + (size_t)pos * D;
-                    vc[ii] = v1;
-                    vc[ii + half] = v2;
-                    uint64_t* vn = p.vnew + ((size_t)l * B + b) * p.Hkv * D + g * D;
+                    gst(vc + ii, v1);
+                    gst(vc + ii + half, v2);
+                    uint64_t* vn = p.qkv + (((size_t)l * B + b) * p.Hkv + g) * (size_t)(G + 2) * D + (G + 1) * D;
                     st_tag(vn + ii, bf2f(v1), cx.epoch);
                     st_tag(vn + ii + half, bf2f(v2), cx.epoch);
                 }
@@ -711,7 +968,7 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
             // residual stream entering layer l (complete before this layer's QKV began)
             float hin = 0.f;
             if (lane_row) {
-                if (l == 0) hin = bf2f(p.embed[(size_t)sp.tok * H + rg]);
+                if (l == 0) hin = bf2f(gld(p.embed + (size_t)sp.tok * H + rg));
                 else hin = wait_word(cx, p.hout + ((size_t)(l - 1) * B + b) * H + rg);
             }
             dot1(o);
@@ -734,20 +991,21 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
             dot1(o);
             if (lane_row) {
                 float* acc = p.dacc + (size_t)b * H + rg;  // written and read only by this wave's lane b
-                const float v = o.mine[0] + (first ? 0.f : *acc);
+                const float v = o.mine[0] + (first ? 0.f : gld(acc));
                 if (last) st_tag(p.hout + ((size_t)l * B + b) * H + rg, hm + v, cx.epoch);
-                else *acc = v;
+                else gst(acc, v);
             }
             break;
         }
         default: {  // OP_RMS_LM_HEAD
             dot1(o);
-            if (lane_row) sp.logits[(size_t)b * p.V + rg] = o.mine[0] * scale;
+            if (lane_row) gst(sp.logits + (size_t)b * p.V + rg, o.mine[0] * scale);
             break;
         }
         }
         if (cx.aborted) return;
     }
+    mark_mid(cx);
 }
 
 // ------------------------------------------------------- attention ops ------
@@ -797,18 +1055,19 @@ __device__ __forceinline__ float pv_reduce_scatter64(const uint4 (&row)[8], floa
 // j (its K and V rows, loaded with independent 16-byte loads), and the PV
 // product is reduce-scattered so lane d ends with dims d (and d + 64).
 template <int D>
-__device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& seq, const Inst& in, float* xb,
+__device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& seq, uint32_t r, const Inst& in,
+                                               LDS float* xb,
                                                const Step& sp) {
     constexpr int NH = D / 64;       // 64-dim halves
-    const Params& p = *cx.p;
+    CParams& p = *cx.p;
     const int B = p.B, G = p.G, l = in.layer, b = in.a, g = in.b, split = (int)in.rg0;
-    const int pos = sp.positions[b];
+    const int pos = gld(sp.positions + b);
     const int S = pos + 1;
     const int j0 = (int)((long long)split * S / p.n_split), j1 = (int)((long long)(split + 1) * S / p.n_split);
-    float* qs = xb;                  // [G][D], pre-scaled by 1/sqrt(D)
-    float* kn = qs + G * D;          // [D] new K row (bf16 values)
-    float* vn = kn + D;              // [D] new V row
-    float* stt = vn + D;             // [NW][D + 2] per-wave (m, l, o)
+    LDS float* qs = xb;              // [G][D], pre-scaled by 1/sqrt(D)
+    LDS float* kn = qs + G * D;      // [D] new K row (bf16 values)
+    LDS float* vn = kn + D;          // [D] new V row
+    LDS float* stt = vn + D;         // [NW][D + 2] per-wave (m, l, o)
     const int gi = cx.wave % G, wph = NW / G, sub = cx.wave / G;
     const uint16_t* Kc = sp.kv + ((((size_t)l * 2 + 0) * B + b) * p.Hkv + g) * (size_t)p.max_seq * D;
     const uint16_t* Vc = sp.kv + ((((size_t)l * 2 + 1) * B + b) * p.Hkv + g) * (size_t)p.max_seq * D;
@@ -823,32 +1082,27 @@ __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& 
         const bool old = j < j1 && j < pos;
         const uint4* src = (const uint4*)(base + (size_t)(old ? j : 0) * D + h * 64);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) r[c] = old ? src[c] : make_uint4(0, 0, 0, 0);
+        for (int c = 0; c < 8; ++c) r[c] = old ? gld_u4(src + c) : make_uint4(0, 0, 0, 0);
     };
-    auto pack_lds = [&](uint4 (&r)[8], const float* row) {  // exact: the values are bf16
+    // the new row's values are bf16 numbers held as fp32: their upper halves
+    // are the bf16 bits
+    auto pack_lds = [&](uint4 (&r)[8], const LDS float* row) {
+#ifndef MK_NO_PACK
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            const float* v = row + c * 8;
-            r[c] = make_uint4((uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16),
-                              (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16),
-                              (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16),
-                              (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16));
+            const uint4 lo = lds_u4(row + c * 8), hi = lds_u4(row + c * 8 + 4);
+            r[c] = make_uint4((lo.x >> 16) | (lo.y & 0xffff0000u), (lo.z >> 16) | (lo.w & 0xffff0000u),
+                              (hi.x >> 16) | (hi.y & 0xffff0000u), (hi.z >> 16) | (hi.w & 0xffff0000u));
         }
+#endif
     };
     if (sub * 64 < nkeys) load_half(kr, Kc, sub, 0);
 
-    // q of the group's heads, then the new K and V rows, in one polled read
-    const uint64_t* qsrc = p.q + ((size_t)l * B + b) * p.Hq * D + (size_t)g * G * D;
-    const uint64_t* ksrc = p.knew + ((size_t)l * B + b) * p.Hkv * D + (size_t)g * D;
-    const uint64_t* vsrc = p.vnew + ((size_t)l * B + b) * p.Hkv * D + (size_t)g * D;
-    const int nq = G * D;
-    acquire(cx, nq + 2 * D,
-            [&](int i) { return i < nq ? qsrc + i : (i < nq + D ? ksrc + (i - nq) : vsrc + (i - nq - D)); },
-            [&](int i, float v) { qs[i] = i < nq ? v * p.inv_sqrt_d : v; });
-    cbar(cx, s, seq);
+    // q of the group's heads (pre-scaled), then the new K and V rows, staged by the gather wave
+    wait_inputs(cx, s, r);
     if (cx.aborted) return;
 
-    const float* qh = qs + gi * D;
+    const LDS float* qh = qs + gi * D;
     const float ninf = -__builtin_inff();
     float m = ninf, lsum = 0.f, o[NH];
 #pragma unroll
@@ -865,7 +1119,7 @@ __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& 
             if (is_new) pack_lds(kr, kn + h * 64);
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
-                const float4 a = *(const float4*)(qh + h * 64 + c * 8), bq = *(const float4*)(qh + h * 64 + c * 8 + 4);
+                const float4 a = lds_f4(qh + h * 64 + c * 8), bq = lds_f4(qh + h * 64 + c * 8 + 4);
                 acc += dot8(kr[c], a, bq);
             }
         }
@@ -883,8 +1137,9 @@ __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& 
             o[h] = o[h] * corr + pv_reduce_scatter64(vr, e, cx.lane);
         }
     }
+    mark_mid(cx);
     // per-wave state -> LDS, merge the waves of each head
-    float* my = stt + cx.wave * (D + 2);
+    LDS float* my = stt + cx.wave * (D + 2);
     if (cx.lane == 0) {
         my[0] = m;
         my[1] = lsum;
@@ -900,7 +1155,7 @@ __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& 
     for (int h = 0; h < NH; ++h) O[h] = 0.f;
     if (M != ninf) {
         for (int w = gi; w < NW; w += G) {
-            const float* sw = stt + w * (D + 2);
+            const LDS float* sw = stt + w * (D + 2);
             const float f = sw[0] == ninf ? 0.f : __expf(sw[0] - M);
             Ls = fmaf(sw[1], f, Ls);
 #pragma unroll
@@ -921,12 +1176,10 @@ __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& 
 
 // Log-sum-exp merge of the n_split partials of (row b, head):
 // out = sum_s o_s e^(m_s - M) / sum_s l_s e^(m_s - M), M = max_s m_s.
-__device__ __forceinline__ void op_reduce(Ctx& cx, const Lds& s, uint32_t& seq, const Inst& in, float* xb) {
-    const Params& p = *cx.p;
+__device__ __forceinline__ void op_reduce(Ctx& cx, const Lds& s, uint32_t r, const Inst& in, LDS float* xb) {
+    CParams& p = *cx.p;
     const int B = p.B, D = p.D, l = in.layer, b = in.a, head = in.b, ns = p.n_split, W = D + 2;
-    const uint64_t* src = p.part + (((size_t)l * B + b) * p.Hq + head) * ns * W;
-    acquire(cx, ns * W, [&](int i) { return src + i; }, [&](int i, float v) { xb[i] = v; });
-    cbar(cx, s, seq);
+    wait_inputs(cx, s, r);  // xb = the n_split partials, staged by the gather wave
     if (cx.wave != 0 || cx.aborted) return;
     const float ninf = -__builtin_inff();
     float M = ninf;
@@ -953,31 +1206,33 @@ __device__ __forceinline__ void op_reduce(Ctx& cx, const Lds& s, uint32_t& seq, 
 // stage's instructions (one launch per op and layer).  One instantiation per
 // head size.
 template <int HEAD_DIM>
-__global__ void __launch_bounds__(WG_THREADS, 1)
-mk_step_kernel(const Params* __restrict__ pp, const int32_t* tokens, const int32_t* positions, uint16_t* kv,
-               float* logits, int stage, uint32_t flags) {
+__device__ __forceinline__ void step_body(const Params* __restrict__ pp, const int32_t* tokens,
+                                          const int32_t* positions, uint16_t* kv, float* logits, int stage,
+                                          uint32_t flags) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    const Params& p = *pp;
+    CParams& p = *(CParams*)pp;
     Ctx cx;
-    cx.p = pp;
+    cx.p = (CParams*)pp;
     cx.cu = blockIdx.x;
     cx.lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = (int)uni(threadIdx.x >> 6);
     cx.aborted = false;
     cx.pc = 0;
     cx.op = 0;
     cx.prof = p.prof != nullptr;
-    for (int k = 0; k < 5; ++k) cx.cnt[k] = 0;
+    cx.trace = p.trace != nullptr;
+    cx.t_in = cx.t_acq = cx.t_mid = 0;
+    for (int k = 0; k < 8; ++k) cx.cnt[k] = 0;
     const uint64_t t_kernel = cx.prof ? cycles() : 0;
     auto flush_prof = [&](int wave_slot) {
         if (cx.prof && cx.lane == 0) {
-            uint64_t* o = p.prof + ((size_t)cx.cu * (NW + NLOAD) + wave_slot) * PROF_SLOTS;
+            GLB uint64_t* o = (GLB uint64_t*)p.prof + ((size_t)cx.cu * (NW + NLOAD) + wave_slot) * PROF_SLOTS;
             o[0] = cycles() - t_kernel;
-            for (int k = 1; k < 5; ++k) o[k] = cx.cnt[k];
+            for (int k = 1; k < 8; ++k) o[k] = cx.cnt[k];
         }
     };
     cx.epoch = p.epoch[cx.cu] + 1;
-    const Lds s = lds_map(smem, p);
+    const Lds s = lds_map((LDS uint8_t*)smem, p);
 
     // batch inputs: every workgroup validates them; one bad id stops the step
     Step sp;
@@ -1014,40 +1269,106 @@ mk_step_kernel(const Params* __restrict__ pp, const int32_t* tokens, const int32
         pc0 = p.stage_pc[(size_t)cx.cu * (p.n_stages + 1) + stage];
         pc1 = p.stage_pc[(size_t)cx.cu * (p.n_stages + 1) + stage + 1];
     }
-    if (threadIdx.x < 2 * NW + 4) ((uint32_t*)s.landed)[threadIdx.x] = 0;
+    if (threadIdx.x < SYNC_WORDS) s.landed[threadIdx.x] = 0;
     __syncthreads();
 
     const uint32_t* uoff = p.unit_off + ((size_t)qb + cx.cu) * NW;
-    if (wave >= NW) {  // loader of compute waves 2i and 2i+1
-        const int w0 = (wave - NW) * NSERVE;
+    if (wave >= NW + NWL) {  // gather wave
         cx.wave = wave;
-        loader(cx, s, w0, uoff, pc0, pc1);
+        gatherer(cx, s, sp, qb, pc0, pc1);
+        flush_prof(wave);
+        return;
+    }
+    if (wave >= NW) {  // weight loader of compute waves i, i + 3, i + 6
+        cx.wave = wave;
+        loader(cx, s, wave - NW, uoff, pc0, pc1);
         flush_prof(wave);
         return;
     }
     cx.wave = wave;
     Stream st{0, 0, 0, 0};
     uint32_t seq = 0;
+#ifdef MK_CBAR_TEST
+    {
+        const uint64_t t0 = cycles();
+        for (int i = 0; i < 100; ++i) cbar(cx, s, seq);
+        const uint64_t t1 = cycles();
+        for (int i = 0; i < 100; ++i) { seq += NW; }  // (balanced: no-op)
+        seq -= 100 * NW;
+        const uint64_t t2 = cycles();
+        if (cx.lane == 0) {
+            GLB uint64_t* o = (GLB uint64_t*)p.prof + ((size_t)cx.cu * (NW + NLOAD) + wave) * PROF_SLOTS;
+            o[6] = t1 - t0;
+            o[7] = t2 - t1;
+        }
+        cx.prof = false;
+    }
+#endif
+    // instructions are fetched one ahead so the fetch latency overlaps the
+    // current instruction
+    const GLB u32x4* iq = (const GLB u32x4*)(p.insts + qb);
+    u32x4 next = pc0 < pc1 ? iq[pc0] : u32x4{0, 0, 0, 0};
     for (uint32_t pc = pc0; pc < pc1 && !cx.aborted; ++pc) {
-        const Inst in = p.insts[qb + pc];
+        const u32x4 raw = next;
+        if (pc + 1 < pc1) next = iq[pc + 1];
+        Inst in;
+        in.op = (uint16_t)(raw.x & 0xffffu);
+        in.layer = (uint16_t)(raw.x >> 16);
+        in.rg0 = raw.y;
+        in.nrg = raw.z;
+        in.a = (uint16_t)(raw.w & 0xffffu);
+        in.b = (uint16_t)(raw.w >> 16);
         cx.pc = pc;
         cx.op = in.op;
-        float* xb = (pc - pc0) & 1 ? s.xbuf[1] : s.xbuf[0];
+        const uint64_t t_start = cx.trace ? rtime() : 0;
+        cx.t_acq = cx.t_in = cx.t_mid = t_start;
+        const uint32_t r = pc - pc0;
+        LDS float* xb = r & 1 ? s.xbuf[1] : s.xbuf[0];
         switch (in.op) {
-        case OP_ATTENTION: op_attention_t<HEAD_DIM>(cx, s, seq, in, xb, sp); break;
-        case OP_ATTN_REDUCE: op_reduce(cx, s, seq, in, xb); break;
+        case OP_ATTENTION: op_attention_t<HEAD_DIM>(cx, s, seq, r, in, xb, sp); break;
+        case OP_ATTN_REDUCE: op_reduce(cx, s, r, in, xb); break;
         default: {
             const int ku = in.op == OP_O_PROJ_RES ? p.ku_q : in.op == OP_DOWN_RES ? p.ku_f : p.ku_h;
-            if (p.B != 1) op_gemv<0>(cx, s, st, seq, in, xb, sp);
-            else if (ku == 4) op_gemv<4>(cx, s, st, seq, in, xb, sp);
-            else if (ku == 2) op_gemv<2>(cx, s, st, seq, in, xb, sp);
-            else op_gemv<0>(cx, s, st, seq, in, xb, sp);
+            if (p.B != 1) op_gemv<0>(cx, s, st, r, in, xb, sp);
+            else if (ku == 4) op_gemv<4>(cx, s, st, r, in, xb, sp);
+            else if (ku == 2) op_gemv<2>(cx, s, st, r, in, xb, sp);
+            else op_gemv<0>(cx, s, st, r, in, xb, sp);
             break;
         }
+        }
+        // this wave is done with the instruction's staged inputs
+        CBAR();
+        if (cx.lane == 0) __hip_atomic_fetch_add(s.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (cx.trace && cx.lane == 0) {
+            GLB uint64_t* r = (GLB uint64_t*)p.trace + (size_t)(qb + pc) * TRACE_SLOTS;
+            if (wave == 0)
+                r[0] = (uint64_t)in.op | ((uint64_t)in.layer << 8) | ((uint64_t)in.a << 16) | ((uint64_t)in.b << 32) |
+                       ((uint64_t)cx.cu << 48);
+            r[1 + 5 * wave] = t_start;
+            r[2 + 5 * wave] = cx.t_acq;
+            r[3 + 5 * wave] = cx.t_in;
+            r[4 + 5 * wave] = cx.t_mid;
+            r[5 + 5 * wave] = rtime();
         }
     }
     flush_prof(wave);
     if ((flags & KF_BUMP_EPOCH) && wave == 0 && cx.lane == 0) p.epoch[cx.cu] = cx.epoch;
+}
+
+// The whole step in one launch (every workgroup runs its full queue).
+template <int HEAD_DIM>
+__global__ void __launch_bounds__(WG_THREADS, 1)
+mk_decode_kernel(const Params* __restrict__ pp, const int32_t* tokens, const int32_t* positions, uint16_t* kv,
+                 float* logits, int stage, uint32_t flags) {
+    step_body<HEAD_DIM>(pp, tokens, positions, kv, logits, -1, flags);
+}
+
+// One stage of the step (one op of one layer) per launch.
+template <int HEAD_DIM>
+__global__ void __launch_bounds__(WG_THREADS, 1)
+mk_stage_kernel(const Params* __restrict__ pp, const int32_t* tokens, const int32_t* positions, uint16_t* kv,
+                float* logits, int stage, uint32_t flags) {
+    step_body<HEAD_DIM>(pp, tokens, positions, kv, logits, stage, flags);
 }
 
 // ------------------------------------------------------------ pack kernel --
@@ -1082,20 +1403,24 @@ hipError_t launch_step(const Params* dev_params, int head_dim, int ncu, size_t l
                        const int32_t* positions, void* kv, float* logits, int stage, uint32_t flags,
                        hipStream_t stream) {
     uint16_t* kv16 = (uint16_t*)kv;
-    const void* fn = head_dim == 64 ? (const void*)mk_step_kernel<64> : (const void*)mk_step_kernel<128>;
     void* args[] = {(void*)&dev_params, (void*)&tokens, (void*)&positions, (void*)&kv16, (void*)&logits,
                     (void*)&stage, (void*)&flags};
-    if (stage < 0)
+    if (stage < 0) {
+        const void* fn = head_dim == 64 ? (const void*)mk_decode_kernel<64> : (const void*)mk_decode_kernel<128>;
         return hipLaunchCooperativeKernel(fn, dim3(ncu), dim3(WG_THREADS), args, (unsigned)lds_bytes, stream);
+    }
+    const void* fn = head_dim == 64 ? (const void*)mk_stage_kernel<64> : (const void*)mk_stage_kernel<128>;
     return hipLaunchKernel(fn, dim3(ncu), dim3(WG_THREADS), args, lds_bytes, stream);
 }
 
 hipError_t set_step_kernel_lds(size_t lds_bytes) {
-    hipError_t e = hipFuncSetAttribute((const void*)mk_step_kernel<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds_bytes);
-    if (e != hipSuccess) return e;
-    return hipFuncSetAttribute((const void*)mk_step_kernel<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)lds_bytes);
+    const void* fns[] = {(const void*)mk_decode_kernel<64>, (const void*)mk_decode_kernel<128>,
+                         (const void*)mk_stage_kernel<64>, (const void*)mk_stage_kernel<128>};
+    for (const void* fn : fns) {
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_pack(const void* rows, uint32_t n, const uint16_t* const* mats, uint8_t* dst, hipStream_t stream) {

@@ -54,8 +54,10 @@ class MkScheduleInfo(ctypes.Structure):
 
 EXPORTS = ["mk_create", "mk_load_weights", "mk_kv_cache_bytes", "mk_decode_step", "mk_decode_step_multikernel",
            "mk_destroy", "mk_status_string", "mk_last_error", "mk_get_device_error", "mk_get_profile",
-           "mk_schedule_inspect"]
+           "mk_schedule_inspect", "mk_get_trace"]
 MK_FLAG_PROFILE = 1
+MK_FLAG_TRACE = 2
+TRACE_SLOTS = 44
 PROF_WAVES = 12  # 8 compute + 4 loader waves per workgroup
 PROF_SLOTS = 8
 
@@ -84,8 +86,9 @@ def lib():
         L.mk_get_device_error.argtypes = [H, ctypes.POINTER(MkDeviceError)]
         L.mk_schedule_inspect.argtypes = [ctypes.POINTER(MkConfig), ctypes.c_int32, ctypes.POINTER(MkScheduleInfo)]
         L.mk_get_profile.argtypes = [H, _P, ctypes.c_size_t]
+        L.mk_get_trace.argtypes = [H, _P, ctypes.c_size_t]
         for name in ["mk_create", "mk_load_weights", "mk_decode_step", "mk_decode_step_multikernel", "mk_destroy",
-                     "mk_get_device_error", "mk_schedule_inspect", "mk_get_profile"]:
+                     "mk_get_device_error", "mk_schedule_inspect", "mk_get_profile", "mk_get_trace"]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -177,6 +180,14 @@ def mk_get_profile(handle, n_cus: int):
     import numpy as np
     out = np.zeros((n_cus, PROF_WAVES, PROF_SLOTS), dtype=np.uint64)
     _check(lib().mk_get_profile(handle, out.ctypes.data, out.size), handle)
+    return out
+
+
+def mk_get_trace(handle, total_insts: int):
+    """Timeline of the last step as a numpy array [total_insts][44] (uint64)."""
+    import numpy as np
+    out = np.zeros((total_insts, TRACE_SLOTS), dtype=np.uint64)
+    _check(lib().mk_get_trace(handle, out.ctypes.data, out.size), handle)
     return out
 
 

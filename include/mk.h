@@ -68,6 +68,7 @@ typedef struct {
 
 #define MK_FLAG_NONE 0u
 #define MK_FLAG_PROFILE 1u  /* per-wave cycle counters, read with mk_get_profile */
+#define MK_FLAG_TRACE 2u    /* per-instruction timeline, read with mk_get_trace */
 
 /* Per-layer weight pointers: arrays of n_layers DEVICE pointers held in HOST
  * memory.  Every tensor is bf16, row-major in the nn.Linear layout [out][in]:
@@ -116,8 +117,9 @@ size_t mk_kv_cache_bytes(const mk_config* cfg);
  *   kv_cache  device buffer of mk_kv_cache_bytes(cfg)
  *   logits    device float32[B][V] (written)
  * Steps on one handle must be ordered on one stream: the handle's scratch is
- * reused by every step.  Out-of-range ids/positions are detected on device,
- * recorded (mk_get_device_error) and the affected outputs are left unwritten. */
+ * reused by every step.  Out-of-range ids/positions are detected on device
+ * before any work: the error is recorded (mk_get_device_error) and the step
+ * writes neither logits nor KV cache.                                      */
 int mk_decode_step(mk_handle* h, const int32_t* tokens, const int32_t* positions,
                    void* kv_cache, float* logits, void* stream);
 
@@ -156,11 +158,28 @@ int mk_get_device_error(mk_handle* h, mk_device_error* out);
  * MK_FLAG_PROFILE): counters[(cu * 12 + wave) * 8 + k], 8 x uint64 per wave,
  * waves 0..7 compute, 8..11 loaders.  Compute k: 0 cycles in the kernel,
  * 1 waiting for weight units, 2 waiting for tagged inputs, 3 in workgroup
- * barriers, 4 units read.  Loader k: 0 cycles in the kernel, 1 waiting for
+ * barriers, 4 units read, 5 barriers passed, 6 barrier polls, 7 barriers
+ * this wave completed last.  Loader k: 0 cycles in the kernel, 1 waiting for
  * DMA completion, 2 idle with full rings, 3 units loaded, 4 loop iterations.
  * `n` is the capacity of `counters` in elements; synchronises the device.
  * Returns MK_ERR_STATE when profiling is off.                             */
 int mk_get_profile(mk_handle* h, uint64_t* counters, size_t n);
+
+/* Per-instruction timeline of the last step (handle created with
+ * MK_FLAG_TRACE): records[i * 44 + k] for each instruction i of the
+ * concatenated per-CU queues (mk_schedule_info.total_insts records), times
+ * in ticks of the GPU's 100 MHz real-time clock, which all CUs share:
+ *   k = 0: opcode | layer << 8 | a << 16 | b << 32 | cu << 48
+ *          (a, b: batch row and KV group for attention, batch row and head
+ *          for the reduce, chunk for the down projection)
+ *   k = 1 + 5w .. 5 + 5w for compute wave w (0..7): start, inputs from
+ *          other CUs loaded, inputs ready (after the workgroup barrier),
+ *          main loop done (before the epilogue or merge), end.
+ *   k = 41 .. 43: the gather wave's start on the instruction's inputs, all
+ *          polled inputs current, inputs staged in LDS.
+ * `n` is the capacity in elements; synchronises the device.  Returns
+ * MK_ERR_STATE when tracing is off.                                        */
+int mk_get_trace(mk_handle* h, uint64_t* records, size_t n);
 
 /* Host-only inspection of the schedule for `cfg` on `n_cus` CUs: builds it,
  * checks that every output row / unit is produced exactly once and that the
@@ -171,7 +190,7 @@ typedef struct {
     int32_t n_chunks;
     int32_t max_insts_per_cu;
     int64_t total_insts;
-    int64_t packed_weight_bytes;   /* bytes streamed per step (weights, incl. padding) */
+    int64_t packed_weight_bytes;   /* weight bytes streamed per step (incl. row padding to 1 KiB units) */
     int64_t max_stream_bytes_per_wave;
     int64_t min_stream_bytes_per_wave;
     int32_t launches_multikernel;
