@@ -23,7 +23,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "decode tokens/s at batch 1 + achieved % of HBM roofline (Llama-1B-shaped)"
-KERNEL_NAME = "mk_step_kernel"
+KERNEL_NAME = "mk_decode_kernel"  # the single-launch step kernel (the per-op path launches mk_stage_kernel)
 
 
 def log(*a):
@@ -57,6 +57,64 @@ def measured_traffic(workload: str):
         return None
 
 
+def _pmc_per_dispatch(csv_path, name_part):
+    """Counter value per dispatch (summed over the counter's instances) of kernels whose name contains name_part."""
+    import csv
+    import collections
+    agg = collections.OrderedDict()
+    with open(csv_path) as fh:
+        for r in csv.DictReader(fh):
+            if name_part in r["Kernel_Name"]:
+                agg[r["Dispatch_Id"]] = agg.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return list(agg.values())
+
+
+def write_traffic_summary(fetch_csv, write_csv, workload, copy_bytes, command):
+    """HBM bytes per launch of the step kernel from rocprofv3 FETCH_SIZE and WRITE_SIZE passes (KiB per
+    dispatch), each scaled by what the same counter reads for a plain copy kernel of copy_bytes read and
+    copy_bytes written (the elementwise copy that --calib-copy-mib launches in the same process)."""
+    import statistics
+    copy_kernel = "vectorized_elementwise_kernel"
+    f_copy = [v for v in _pmc_per_dispatch(fetch_csv, copy_kernel) if v > copy_bytes / 1024 / 4]
+    w_copy = [v for v in _pmc_per_dispatch(write_csv, copy_kernel) if v > copy_bytes / 1024 / 4]
+    f_scale = (copy_bytes / 1024) / statistics.median(f_copy)
+    w_scale = (copy_bytes / 1024) / statistics.median(w_copy)
+    f_mk = _pmc_per_dispatch(fetch_csv, KERNEL_NAME)
+    w_mk = _pmc_per_dispatch(write_csv, KERNEL_NAME)
+    fetch = statistics.median(f_mk) * 1024 * f_scale
+    write = statistics.median(w_mk) * 1024 * w_scale
+    path = os.path.join(ROOT, "profiles", f"traffic_{KERNEL_NAME}_{workload}.txt")
+    with open(path, "w") as fh:
+        fh.write(f"# HBM traffic of {KERNEL_NAME}, workload {workload}, from rocprofv3 counter passes\n")
+        fh.write(f"# command: {command}\n")
+        fh.write(f"# {len(f_mk)} / {len(w_mk)} dispatches; copy-kernel calibration: {copy_bytes} B read + written, "
+                 f"FETCH_SIZE reads {statistics.median(f_copy):.1f} KiB, WRITE_SIZE reads {statistics.median(w_copy):.1f} KiB\n")
+        fh.write(f"fetch_scale: {f_scale:.4f}\n")
+        fh.write(f"write_scale: {w_scale:.4f}\n")
+        fh.write(f"fetch_bytes_per_launch: {fetch:.0f}\n")
+        fh.write(f"write_bytes_per_launch: {write:.0f}\n")
+        fh.write(f"hbm_bytes_per_launch: {fetch + write:.0f}\n")
+        fh.write(f"kernel_source_hash: {kernel_source_hash()}\n")
+    return path
+
+
+def write_stats_summary(stats_csv, workload, command):
+    """Per-kernel duration table from a rocprofv3 --kernel-trace --stats run."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    path = os.path.join(ROOT, "profiles", f"kernel_trace_{KERNEL_NAME}_{workload}.md")
+    with open(path, "w") as fh:
+        fh.write(f"# Kernel durations, workload {workload} (rocprofv3 --kernel-trace --stats)\n\n")
+        fh.write(f"Command: `{command}`\n\n")
+        fh.write("| kernel | calls | average us | min us | max us | share % |\n|---|---|---|---|---|---|\n")
+        for r in rows:
+            name = r["Name"]
+            short = name.split("(")[0].replace("void ", "")[:80]
+            fh.write(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |\n")
+    return path
+
+
 def cpu_baseline(shape, weights, kv_host, first_tok, prompt, n_steps: int):
     import numpy as np
 
@@ -85,10 +143,21 @@ def main():
     ap.add_argument("--workload", default="llama1b_b1_p1024")
     ap.add_argument("--mk-steps", type=int, default=64, help="timed steps of the per-op-launch path")
     ap.add_argument("--cpu-steps", type=int, default=32, help="timed oracle steps (0: skip the CPU baseline)")
+    ap.add_argument("--stats-summary", nargs=2, metavar=("STATS_CSV", "COMMAND"),
+                    help="write the profiles/ kernel-duration summary from a rocprofv3 --stats run and exit")
+    ap.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
+                    help="write the profiles/ traffic summary from two rocprofv3 counter passes and exit")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (3 launches), the reference "
                          "kernel for scaling HBM byte counters")
     args = ap.parse_args()
+    if args.stats_summary:
+        print(write_stats_summary(args.stats_summary[0], args.workload, args.stats_summary[1]))
+        return
+    if args.traffic_summary:
+        print(write_traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.workload,
+                                    (args.calib_copy_mib or 1024) << 20, args.traffic_summary[2]))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the decode path runs on a "
               "single GPU and has no multi-GPU variant.", file=sys.stderr)

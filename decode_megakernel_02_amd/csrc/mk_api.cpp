@@ -180,19 +180,26 @@ int mk_create(const mk_config* cfg, mk_handle** out) {
         xb = std::max(xb, std::max(attn_scratch, red_scratch));
         xb = (xb + 15) / 16 * 16;
         const size_t sync_bytes = 512;
-        long ring_budget = (long)LDS_BYTES - 2 * (long)xb - (long)sync_bytes;
+        // side buffers: RoPE cos/sin rows of the step's positions (QKV) or the
+        // residual rows of a CU's O / down-projection rows
+        const size_t max_rows = (size_t)((p.H + ncu - 1) / ncu);
+        size_t side = std::max((size_t)p.B * p.D, (size_t)p.B * max_rows);
+        if (side > SIDE_MAX_FLOATS) side = 0;  // too many rows per CU: epilogues read global memory
+        const size_t side_bytes = (side * 4 + 15) / 16 * 16;
+        long ring_budget = (long)LDS_BYTES - 2 * (long)xb - (long)sync_bytes - 2 * (long)side_bytes;
         int ring_units = (int)std::min<long>(32, ring_budget / (NW * UNIT_BYTES));
         if (ring_units < std::max(2, std::max(std::max(p.ku_h, p.ku_q), p.ku_f))) {
             delete h;
             return fail(nullptr, MK_ERR_UNSUPPORTED_SHAPE, "batch x hidden too large for the LDS budget");
         }
-        h->lds_bytes = (size_t)NW * ring_units * UNIT_BYTES + 2 * xb + sync_bytes;
+        h->lds_bytes = (size_t)NW * ring_units * UNIT_BYTES + 2 * xb + sync_bytes + 2 * side_bytes;
 
         Params& hp = h->hp;
         hp.L = p.L; hp.H = p.H; hp.Hq = p.Hq; hp.Hkv = p.Hkv; hp.D = p.D; hp.F = p.F; hp.V = p.V; hp.B = p.B;
         hp.max_seq = p.max_seq; hp.G = p.G; hp.n_split = p.n_split; hp.n_chunk = p.n_chunk;
         hp.ku_h = p.ku_h; hp.ku_q = p.ku_q; hp.ku_f = p.ku_f; hp.xstride = xstride;
         hp.ring_units = ring_units; hp.xbuf_bytes = (int)xb; hp.ncu = ncu;
+        hp.side_floats = (int)(side_bytes / 4);
         hp.eps = p.eps; hp.inv_sqrt_d = (float)(1.0 / std::sqrt((double)p.D));
         hp.spin_limit = 1u << 25;
         for (int i = 0; i <= p.n_chunk; ++i) hp.chunk_begin[i] = p.chunk_begin[i];

@@ -15,6 +15,7 @@ constexpr int UNIT_BYTES = 1024;      // one DMA: 64 lanes x 16 B
 constexpr int UNIT_ELEMS = 512;       // bf16 per unit
 constexpr int MAX_BATCH = 8;
 constexpr int LDS_BYTES = 160 * 1024; // gfx950 LDS per CU
+constexpr int SIDE_MAX_FLOATS = 2048; // cap of one LDS side buffer (epilogue inputs)
 
 // Fused ops, in the order they appear inside one layer.  The page
 // "Megakernels: Deleting the Kernel Boundary to Win Back Microseconds"
@@ -58,6 +59,8 @@ struct Params {
     int32_t xstride;        // floats per batch row in the LDS x buffer (max padded K)
     int32_t ring_units;     // ring slots (1 KB units) per compute wave
     int32_t xbuf_bytes;     // bytes of one of the two LDS x buffers
+    int32_t side_floats;    // floats of each of the two LDS side buffers (epilogue inputs staged by the
+                            // gather wave); 0: epilogue inputs are read from global memory instead
     int32_t ncu;            // workgroups in the grid
     float eps;
     float inv_sqrt_d;
@@ -101,11 +104,12 @@ struct Params {
 constexpr uint32_t KF_BUMP_EPOCH = 1u;  // last launch of a step: advance the per-workgroup epoch
 constexpr int PROF_SLOTS = 8;          // counters per wave
 // Timeline record per instruction (100 MHz real-time clock): [0] op | layer << 8 |
-// a << 16 | b << 32 | cu << 48, then per compute wave w at [1 + 5w]: start,
-// cross-CU inputs loaded, inputs ready (after the workgroup barrier), main
-// loop done (before the epilogue / merge), end; then the gather wave's start,
-// all polled inputs current, inputs staged.
-constexpr int TRACE_SLOTS = 1 + 5 * NW + 3;
+// a << 16 | b << 32 | cu << 48, then per compute wave w at [1 + 6w]: start,
+// cross-CU inputs loaded, inputs ready, main loop done (before the epilogue
+// or merge), end, ticks spent waiting for weight units; then the gather
+// wave's start, all polled inputs current, inputs staged.
+constexpr int TRACE_WAVE_SLOTS = 6;
+constexpr int TRACE_SLOTS = 1 + TRACE_WAVE_SLOTS * NW + 3;
 
 
 }  // namespace mk

@@ -191,6 +191,7 @@ struct Ctx {
     uint64_t t_acq;    // real time at which the current instruction's cross-CU inputs were loaded
     uint64_t t_in;     // real time at which the current instruction's inputs were ready
     uint64_t t_mid;    // real time at which the main loop ended
+    uint64_t t_ring;   // real-time ticks spent waiting for weight units in the current instruction
     uint64_t cnt[8];   // see mk_get_profile
 };
 
@@ -235,7 +236,10 @@ __device__ __forceinline__ void record_error(Ctx& cx, uint32_t code, uint32_t de
 __device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ __forceinline__ bool any_lane(bool c) { return __builtin_amdgcn_ballot_w64(c) != 0; }
 
-template <int SLEEP = 1>
+#ifndef MK_SLEEP
+#define MK_SLEEP 1
+#endif
+template <int SLEEP = MK_SLEEP>
 __device__ __forceinline__ bool keep_waiting(Ctx& cx, uint32_t& spins, uint32_t detail) {
     if (uni(cx.aborted)) return false;
     ++spins;
@@ -266,6 +270,7 @@ struct Lds {
     LDS uint32_t* done;     // instruction completions of the compute waves (NW per instruction)
     LDS float* ss;          // [2][MAX_BATCH] sum of squares of each x buffer's raw input rows
     LDS uint32_t* pf_dump;  // [64] landing words of the cache-prefetch touches (never read)
+    LDS float* side[2];     // epilogue inputs of the instruction staged with xbuf[i] (side_floats each)
 };
 __device__ __forceinline__ Lds lds_map(LDS uint8_t* smem, CParams& p) {
     Lds m;
@@ -281,6 +286,8 @@ __device__ __forceinline__ Lds lds_map(LDS uint8_t* smem, CParams& p) {
     m.done = sync + 2 * NW + 2;
     m.ss = (LDS float*)(sync + 2 * NW + 4);
     m.pf_dump = sync + 64;
+    m.side[0] = (LDS float*)(smem + off + 2 * (size_t)p.xbuf_bytes + 512);
+    m.side[1] = m.side[0] + p.side_floats;
     return m;
 }
 
@@ -494,11 +501,13 @@ __device__ __forceinline__ uint4 ring_take(Ctx& cx, const Lds& s, Stream& st) {
     if (st.unit >= st.landed) {
         ring_release(cx, s, st);
         const uint64_t t0 = cx.prof ? cycles() : 0;
+        const uint64_t r0 = cx.trace ? rtime() : 0;
         uint32_t spins = 0;
         while ((st.landed = uni(lds_ld(&s.landed[cx.wave]))) <= st.unit)
             if (!keep_waiting(cx, spins, 0x20000000u | st.unit)) break;
         CBAR();
         if (cx.prof) cx.cnt[1] += cycles() - t0;
+        if (cx.trace) cx.t_ring += rtime() - r0;
     }
     if (cx.prof) cx.cnt[4] += 1;
     return lds_u4(s.ring + ((size_t)cx.wave * cx.p->ring_units + st.slot) * UNIT_BYTES + cx.lane * 16);
@@ -549,11 +558,13 @@ __device__ __forceinline__ void ring_wait(Ctx& cx, const Lds& s, Stream& st, uin
     if (st.landed >= need) return;
     ring_release(cx, s, st);
     const uint64_t t0 = cx.prof ? cycles() : 0;
+    const uint64_t r0 = cx.trace ? rtime() : 0;
     uint32_t spins = 0;
     while ((st.landed = uni(lds_ld(&s.landed[cx.wave]))) < need)
         if (!keep_waiting(cx, spins, 0x20000000u | st.unit)) break;
     CBAR();
     if (cx.prof) cx.cnt[1] += cycles() - t0;
+    if (cx.trace) cx.t_ring += rtime() - r0;
 }
 
 // Batch-1 row dot products with this wave's x slice in registers: the KU
@@ -771,6 +782,61 @@ __device__ __forceinline__ void gather_embed(Ctx& cx, const Step& sp, int kpad, 
     }
 }
 
+// n tagged words at src (any alignment) into dst[0 .. n), 4 per lane per round.
+__device__ __forceinline__ void gather_words(Ctx& cx, const uint64_t* src, int n, LDS float* dst) {
+    for (int i0 = 0; i0 < n; i0 += 256) {
+        uint64_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = i0 + j * 64 + cx.lane;
+            w[j] = i < n ? ld_tag(src + i) : ((uint64_t)cx.epoch << 32);
+        }
+        uint32_t spins = 0;
+        while (true) {
+            bool stale = false;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) stale |= tag_of(w[j]) != cx.epoch;
+            if (!any_lane(stale)) break;
+            if (!keep_waiting(cx, spins, 0x58000000u | (uint32_t)i0)) return;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (tag_of(w[j]) != cx.epoch) w[j] = ld_tag(src + i0 + j * 64 + cx.lane);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = i0 + j * 64 + cx.lane;
+            if (i < n) dst[i] = val_of(w[j]);
+        }
+    }
+}
+
+// Epilogue inputs staged next to x (when side buffers are enabled):
+//   QKV: side[b * D + 2 i + {0, 1}] = (cos, sin) of pair i at position pos_b
+//   O:   side[b * nrg + j] = residual stream entering the layer, row rg0 + j
+//   last down chunk: side[b * nrg + j] = residual after attention, row rg0 + j
+__device__ __forceinline__ void gather_side(Ctx& cx, const Step& sp, const Inst& in, LDS float* sd) {
+    CParams& p = *cx.p;
+    const int B = p.B, H = p.H, l = in.layer, nrg = (int)in.nrg, rg0 = (int)in.rg0;
+    if (in.op == OP_RMS_QKV_ROPE) {
+        const int D = p.D;
+        for (int b = 0; b < B; ++b) {
+            const float* rope = p.rope + (size_t)gld(sp.positions + b) * D;
+            for (int i = cx.lane; i < D; i += 64) sd[b * D + i] = gld(rope + i);
+        }
+    } else if (in.op == OP_O_PROJ_RES) {
+        for (int b = 0; b < B; ++b) {
+            if (l == 0) {
+                const uint16_t* e = p.embed + (size_t)gld(sp.tokens + b) * H + rg0;
+                for (int j = cx.lane; j < nrg; j += 64) sd[b * nrg + j] = bf2f(gld(e + j));
+            } else {
+                gather_words(cx, p.hout + ((size_t)(l - 1) * B + b) * H + rg0, nrg, sd + b * nrg);
+            }
+        }
+    } else if (in.op == OP_DOWN_RES && in.a == p.n_chunk - 1) {
+        for (int b = 0; b < B; ++b) gather_words(cx, p.hmid + ((size_t)l * B + b) * H + rg0, nrg, sd + b * nrg);
+    }
+}
+
 // Stages the inputs of one instruction in xb (see the op bodies for layouts).
 __device__ __forceinline__ void gather_inst(Ctx& cx, const Step& sp, const Inst& in, LDS float* xb, LDS float* ss) {
     CParams& p = *cx.p;
@@ -865,11 +931,12 @@ __device__ __forceinline__ void gatherer(Ctx& cx, const Lds& s, const Step& sp, 
         const uint64_t t0 = cx.trace ? rtime() : 0;
         cx.t_acq = t0;
         gather_inst(cx, sp, in, r & 1 ? s.xbuf[1] : s.xbuf[0], s.ss + (r & 1) * MAX_BATCH);
+        if (p.side_floats) gather_side(cx, sp, in, r & 1 ? s.side[1] : s.side[0]);
         if (uni(cx.aborted)) break;
         CBAR();
         if (cx.lane == 0) lds_st(s.gathered, r + 1);  // after the staged data (LDS requests of a wave stay ordered)
         if (cx.trace && cx.lane == 0) {
-            GLB uint64_t* rec = (GLB uint64_t*)p.trace + (size_t)(qb + pc) * TRACE_SLOTS + 1 + 5 * NW;
+            GLB uint64_t* rec = (GLB uint64_t*)p.trace + (size_t)(qb + pc) * TRACE_SLOTS + 1 + TRACE_WAVE_SLOTS * NW;
             rec[0] = t0;
             rec[1] = cx.t_acq;
             rec[2] = rtime();
@@ -881,8 +948,11 @@ __device__ __forceinline__ void gatherer(Ctx& cx, const Lds& s, const Step& sp, 
 __device__ __forceinline__ void wait_inputs(Ctx& cx, const Lds& s, uint32_t r) {
     const uint64_t t0 = cx.prof ? cycles() : 0;
     uint32_t spins = 0;
+#ifndef MK_INPUT_SLEEP
+#define MK_INPUT_SLEEP MK_SLEEP
+#endif
     while (uni(lds_ld(s.gathered)) <= r)
-        if (!keep_waiting(cx, spins, 0x70000000u | r)) break;
+        if (!keep_waiting<MK_INPUT_SLEEP>(cx, spins, 0x70000000u | r)) break;
     CBAR();
     if (cx.prof) cx.cnt[2] += cycles() - t0;
     mark_acquired(cx);
@@ -891,11 +961,19 @@ __device__ __forceinline__ void wait_inputs(Ctx& cx, const Lds& s, uint32_t r) {
 
 // ------------------------------------------------------------ GEMV ops ------
 
+// Down-projection partial sums of a wave's first DREG row-groups stay in
+// registers across the chunk instructions of a layer (lane b: batch row b);
+// further row-groups use the global accumulator.
+constexpr int DREG = 4;
+struct DownAcc {
+    float r[DREG];
+};
+
 // KU > 0: batch-1 path with KU units per row (x slice in registers);
 // KU == 0: general path.
 template <int KU>
 __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint32_t r, const Inst& in, LDS float* xb,
-                                        const Step& sp) {
+                                        const Step& sp, DownAcc& da) {
     CParams& p = *cx.p;
     const int B = p.B, H = p.H, l = in.layer;
     const int ku = in.op == OP_O_PROJ_RES ? p.ku_q : in.op == OP_DOWN_RES ? p.ku_f : p.ku_h;
@@ -922,7 +1000,11 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
     const int D = p.D, half = D / 2;
     const bool lane_row = cx.lane < B;
     const int b = lane_row ? cx.lane : 0;
-    for (uint32_t i = cx.wave; i < in.nrg; i += NW) {
+    const int nrg = (int)in.nrg;
+    const LDS float* sd = p.side_floats ? (r & 1 ? s.side[1] : s.side[0]) : nullptr;  // staged epilogue inputs
+    for (uint32_t ri = 0;; ++ri) {
+        const uint32_t i = cx.wave + ri * NW;
+        if (i >= in.nrg) break;
         const uint32_t rg = in.rg0 + i;
         RowOut o;
         switch (in.op) {
@@ -935,7 +1017,8 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
                 const int g = rg / PG, t = rg % PG;
                 if (t < (G + 1) * half) {  // q or k: rotate the pair (ii, ii + D/2)
                     const int ii = t < G * half ? t % half : t - G * half;
-                    const float2 cs = gld_f2(p.rope + ((size_t)pos * half + ii) * 2);
+                    const float2 cs = sd ? make_float2(sd[b * D + 2 * ii], sd[b * D + 2 * ii + 1])
+                                         : gld_f2(p.rope + ((size_t)pos * half + ii) * 2);
                     const float r1 = y1 * cs.x - y2 * cs.y, r2 = y2 * cs.x + y1 * cs.y;
                     uint64_t* blk = p.qkv + (((size_t)l * B + b) * p.Hkv + g) * (size_t)(G + 2) * D;
                     if (t < G * half) {
@@ -967,7 +1050,9 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
         case OP_O_PROJ_RES: {
             // residual stream entering layer l (complete before this layer's QKV began)
             float hin = 0.f;
-            if (lane_row) {
+            if (sd) {
+                if (lane_row) hin = sd[b * nrg + i];
+            } else if (lane_row) {
                 if (l == 0) hin = bf2f(gld(p.embed + (size_t)sp.tok * H + rg));
                 else hin = wait_word(cx, p.hout + ((size_t)(l - 1) * B + b) * H + rg);
             }
@@ -987,13 +1072,26 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
         case OP_DOWN_RES: {
             const bool first = in.a == 0, last = in.a == p.n_chunk - 1;
             float hm = 0.f;
-            if (last && lane_row) hm = wait_word(cx, p.hmid + ((size_t)l * B + b) * H + rg);
+            if (last && lane_row) hm = sd ? sd[b * nrg + i] : wait_word(cx, p.hmid + ((size_t)l * B + b) * H + rg);
+            float* acc = p.dacc + (size_t)b * H + rg;  // global accumulator: this wave's lane b only
+            float prev = 0.f;
+            if (!first) {
+                if (ri < DREG)
+                    prev = ri == 0 ? da.r[0] : ri == 1 ? da.r[1] : ri == 2 ? da.r[2] : da.r[3];
+                else if (lane_row)
+                    prev = gld(acc);
+            }
             dot1(o);
-            if (lane_row) {
-                float* acc = p.dacc + (size_t)b * H + rg;  // written and read only by this wave's lane b
-                const float v = o.mine[0] + (first ? 0.f : gld(acc));
-                if (last) st_tag(p.hout + ((size_t)l * B + b) * H + rg, hm + v, cx.epoch);
-                else gst(acc, v);
+            const float v = o.mine[0] + prev;
+            if (last) {
+                if (lane_row) st_tag(p.hout + ((size_t)l * B + b) * H + rg, hm + v, cx.epoch);
+            } else if (ri < DREG) {
+                if (ri == 0) da.r[0] = v;
+                else if (ri == 1) da.r[1] = v;
+                else if (ri == 2) da.r[2] = v;
+                else da.r[3] = v;
+            } else if (lane_row) {
+                gst(acc, v);
             }
             break;
         }
@@ -1087,14 +1185,12 @@ __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& 
     // the new row's values are bf16 numbers held as fp32: their upper halves
     // are the bf16 bits
     auto pack_lds = [&](uint4 (&r)[8], const LDS float* row) {
-#ifndef MK_NO_PACK
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             const uint4 lo = lds_u4(row + c * 8), hi = lds_u4(row + c * 8 + 4);
             r[c] = make_uint4((lo.x >> 16) | (lo.y & 0xffff0000u), (lo.z >> 16) | (lo.w & 0xffff0000u),
                               (hi.x >> 16) | (hi.y & 0xffff0000u), (hi.z >> 16) | (hi.w & 0xffff0000u));
         }
-#endif
     };
     if (sub * 64 < nkeys) load_half(kr, Kc, sub, 0);
 
@@ -1221,7 +1317,7 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
     cx.op = 0;
     cx.prof = p.prof != nullptr;
     cx.trace = p.trace != nullptr;
-    cx.t_in = cx.t_acq = cx.t_mid = 0;
+    cx.t_in = cx.t_acq = cx.t_mid = cx.t_ring = 0;
     for (int k = 0; k < 8; ++k) cx.cnt[k] = 0;
     const uint64_t t_kernel = cx.prof ? cycles() : 0;
     auto flush_prof = [&](int wave_slot) {
@@ -1288,22 +1384,8 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
     cx.wave = wave;
     Stream st{0, 0, 0, 0};
     uint32_t seq = 0;
-#ifdef MK_CBAR_TEST
-    {
-        const uint64_t t0 = cycles();
-        for (int i = 0; i < 100; ++i) cbar(cx, s, seq);
-        const uint64_t t1 = cycles();
-        for (int i = 0; i < 100; ++i) { seq += NW; }  // (balanced: no-op)
-        seq -= 100 * NW;
-        const uint64_t t2 = cycles();
-        if (cx.lane == 0) {
-            GLB uint64_t* o = (GLB uint64_t*)p.prof + ((size_t)cx.cu * (NW + NLOAD) + wave) * PROF_SLOTS;
-            o[6] = t1 - t0;
-            o[7] = t2 - t1;
-        }
-        cx.prof = false;
-    }
-#endif
+    DownAcc da;
+    for (int k = 0; k < DREG; ++k) da.r[k] = 0.f;
     // instructions are fetched one ahead so the fetch latency overlaps the
     // current instruction
     const GLB u32x4* iq = (const GLB u32x4*)(p.insts + qb);
@@ -1322,6 +1404,7 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
         cx.op = in.op;
         const uint64_t t_start = cx.trace ? rtime() : 0;
         cx.t_acq = cx.t_in = cx.t_mid = t_start;
+        cx.t_ring = 0;
         const uint32_t r = pc - pc0;
         LDS float* xb = r & 1 ? s.xbuf[1] : s.xbuf[0];
         switch (in.op) {
@@ -1329,10 +1412,10 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
         case OP_ATTN_REDUCE: op_reduce(cx, s, r, in, xb); break;
         default: {
             const int ku = in.op == OP_O_PROJ_RES ? p.ku_q : in.op == OP_DOWN_RES ? p.ku_f : p.ku_h;
-            if (p.B != 1) op_gemv<0>(cx, s, st, r, in, xb, sp);
-            else if (ku == 4) op_gemv<4>(cx, s, st, r, in, xb, sp);
-            else if (ku == 2) op_gemv<2>(cx, s, st, r, in, xb, sp);
-            else op_gemv<0>(cx, s, st, r, in, xb, sp);
+            if (p.B != 1) op_gemv<0>(cx, s, st, r, in, xb, sp, da);
+            else if (ku == 4) op_gemv<4>(cx, s, st, r, in, xb, sp, da);
+            else if (ku == 2) op_gemv<2>(cx, s, st, r, in, xb, sp, da);
+            else op_gemv<0>(cx, s, st, r, in, xb, sp, da);
             break;
         }
         }
@@ -1344,11 +1427,13 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
             if (wave == 0)
                 r[0] = (uint64_t)in.op | ((uint64_t)in.layer << 8) | ((uint64_t)in.a << 16) | ((uint64_t)in.b << 32) |
                        ((uint64_t)cx.cu << 48);
-            r[1 + 5 * wave] = t_start;
-            r[2 + 5 * wave] = cx.t_acq;
-            r[3 + 5 * wave] = cx.t_in;
-            r[4 + 5 * wave] = cx.t_mid;
-            r[5 + 5 * wave] = rtime();
+            GLB uint64_t* rw = r + 1 + TRACE_WAVE_SLOTS * wave;
+            rw[0] = t_start;
+            rw[1] = cx.t_acq;
+            rw[2] = cx.t_in;
+            rw[3] = cx.t_mid;
+            rw[4] = rtime();
+            rw[5] = cx.t_ring;
         }
     }
     flush_prof(wave);

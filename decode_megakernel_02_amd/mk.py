@@ -57,7 +57,7 @@ EXPORTS = ["mk_create", "mk_load_weights", "mk_kv_cache_bytes", "mk_decode_step"
            "mk_schedule_inspect", "mk_get_trace"]
 MK_FLAG_PROFILE = 1
 MK_FLAG_TRACE = 2
-TRACE_SLOTS = 44
+TRACE_SLOTS = 52
 PROF_WAVES = 12  # 8 compute + 4 loader waves per workgroup
 PROF_SLOTS = 8
 
@@ -184,7 +184,7 @@ def mk_get_profile(handle, n_cus: int):
 
 
 def mk_get_trace(handle, total_insts: int):
-    """Timeline of the last step as a numpy array [total_insts][44] (uint64)."""
+    """Timeline of the last step as a numpy array [total_insts][52] (uint64)."""
     import numpy as np
     out = np.zeros((total_insts, TRACE_SLOTS), dtype=np.uint64)
     _check(lib().mk_get_trace(handle, out.ctypes.data, out.size), handle)

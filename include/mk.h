@@ -166,16 +166,16 @@ int mk_get_device_error(mk_handle* h, mk_device_error* out);
 int mk_get_profile(mk_handle* h, uint64_t* counters, size_t n);
 
 /* Per-instruction timeline of the last step (handle created with
- * MK_FLAG_TRACE): records[i * 44 + k] for each instruction i of the
+ * MK_FLAG_TRACE): records[i * 52 + k] for each instruction i of the
  * concatenated per-CU queues (mk_schedule_info.total_insts records), times
  * in ticks of the GPU's 100 MHz real-time clock, which all CUs share:
  *   k = 0: opcode | layer << 8 | a << 16 | b << 32 | cu << 48
  *          (a, b: batch row and KV group for attention, batch row and head
  *          for the reduce, chunk for the down projection)
- *   k = 1 + 5w .. 5 + 5w for compute wave w (0..7): start, inputs from
- *          other CUs loaded, inputs ready (after the workgroup barrier),
- *          main loop done (before the epilogue or merge), end.
- *   k = 41 .. 43: the gather wave's start on the instruction's inputs, all
+ *   k = 1 + 6w .. 6 + 6w for compute wave w (0..7): start, inputs loaded,
+ *          inputs ready, main loop done (before the epilogue or merge), end,
+ *          ticks spent waiting for weight units.
+ *   k = 49 .. 51: the gather wave's start on the instruction's inputs, all
  *          polled inputs current, inputs staged in LDS.
  * `n` is the capacity in elements; synchronises the device.  Returns
  * MK_ERR_STATE when tracing is off.                                        */
