@@ -4,8 +4,9 @@
 Workload (default): Llama-3.2-1B-shaped decoder with random bf16 weights
 N(0, 0.02), batch 1, a 1024-token context pre-filled in the KV cache with
 seeded N(0,1) bf16 rows, greedy decode.  One timed step = one mk_decode_step
-launch (the whole forward pass) + argmax + position advance, all on one
-stream with no host synchronisation inside the timed region.
+launch (the whole forward pass) + one mk_greedy_advance launch (argmax into
+the next step's tokens, positions + 1), all on one stream with no host
+synchronisation inside the timed region.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -214,8 +215,7 @@ def main():
     def greedy(n, fn):
         for _ in range(n):
             fn(h, tokens, positions, kv, logits, stream)
-            tokens.copy_(torch.argmax(logits, dim=1))
-            positions.add_(1)
+            mk.mk_greedy_advance(h, logits, tokens, positions, stream)  # argmax -> tokens, positions += 1
 
     def check_device():
         err = mk.mk_get_device_error(h)
@@ -242,8 +242,7 @@ def main():
         ev[i][0].record(cur)
         mk.mk_decode_step(h, tokens, positions, kv, logits, stream)
         ev[i][1].record(cur)
-        tokens.copy_(torch.argmax(logits, dim=1))
-        positions.add_(1)
+        mk.mk_greedy_advance(h, logits, tokens, positions, stream)
     torch.cuda.synchronize()
     check_device()
     kern_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
@@ -264,8 +263,7 @@ def main():
         evm[i][0].record(cur)
         mk.mk_decode_step_multikernel(h, tokens, positions, kv, logits, stream)
         evm[i][1].record(cur)
-        tokens.copy_(torch.argmax(logits, dim=1))
-        positions.add_(1)
+        mk.mk_greedy_advance(h, logits, tokens, positions, stream)
     torch.cuda.synchronize()
     check_device()
     kern_mk = statistics.mean(a.elapsed_time(b) * 1e3 for a, b in evm)

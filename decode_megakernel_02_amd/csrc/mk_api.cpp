@@ -19,6 +19,7 @@ hipError_t launch_step(const Params* dev_params, int head_dim, int ncu, size_t l
                        hipStream_t stream);
 hipError_t set_step_kernel_lds(size_t lds_bytes);
 hipError_t launch_pack(const void* rows, uint32_t n, const uint16_t* const* mats, uint8_t* dst, hipStream_t stream);
+hipError_t launch_greedy(const float* logits, int B, int V, int32_t* tokens, int32_t* positions, hipStream_t stream);
 }  // namespace mk
 
 using namespace mk;
@@ -362,6 +363,13 @@ int mk_decode_step_multikernel(mk_handle* h, const int32_t* tokens, const int32_
                                    st == ns - 1 ? KF_BUMP_EPOCH : 0u, (hipStream_t)stream);
         if (e != hipSuccess) return hip_fail(h, HipError{e, "mk_step_kernel stage launch"});
     }
+    return MK_OK;
+}
+
+int mk_greedy_advance(mk_handle* h, const float* logits, int32_t* tokens, int32_t* positions, void* stream) {
+    if (!h || !logits || !tokens || !positions) return fail(h, MK_ERR_INVALID_ARG, "null argument");
+    hipError_t e = launch_greedy(logits, h->hp.B, h->hp.V, tokens, positions, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(h, HipError{e, "mk_greedy_kernel launch"});
     return MK_OK;
 }
 

@@ -1479,6 +1479,58 @@ __global__ void __launch_bounds__(256) mk_pack_kernel(const PackRowDev* rows, ui
     }
 }
 
+// ------------------------------------------------------------ greedy step --
+
+// One workgroup per batch row: tokens[b] = argmax_v logits[b][v] (lowest index
+// among equal maxima), positions[b] += 1.  Reads the row once with 16-byte
+// loads; the (value, index) pairs are reduced in LDS.
+constexpr int GREEDY_THREADS = 1024;
+__global__ void __launch_bounds__(GREEDY_THREADS) mk_greedy_kernel(const float* logits, int V, int32_t* tokens,
+                                                                    int32_t* positions) {
+    __shared__ float sv[GREEDY_THREADS / 64];
+    __shared__ int si[GREEDY_THREADS / 64];
+    const int b = blockIdx.x, t = threadIdx.x;
+    const float* row = logits + (size_t)b * V;
+    float best = -__builtin_inff();
+    int bi = 0x7fffffff;
+    auto take = [&](float v, int i) {
+        if (v > best || (v == best && i < bi)) {
+            best = v;
+            bi = i;
+        }
+    };
+    const int V4 = ((uintptr_t)row & 15) == 0 ? V / 4 : 0;  // rows of odd V may be unaligned
+    for (int c = t; c < V4; c += GREEDY_THREADS) {
+        const f32x4 v = *(const GLB f32x4*)(row + 4 * c);
+        take(v.x, 4 * c);
+        take(v.y, 4 * c + 1);
+        take(v.z, 4 * c + 2);
+        take(v.w, 4 * c + 3);
+    }
+    for (int i = 4 * V4 + t; i < V; i += GREEDY_THREADS) take(gld(row + i), i);
+    // wave reduction, then across waves
+    for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(best, off);
+        const int oi = __shfl_xor(bi, off);
+        take(ov, oi);
+    }
+    if ((t & 63) == 0) {
+        sv[t >> 6] = best;
+        si[t >> 6] = bi;
+    }
+    __syncthreads();
+    if (t == 0) {
+        for (int w = 1; w < GREEDY_THREADS / 64; ++w) take(sv[w], si[w]);
+        tokens[b] = bi == 0x7fffffff ? 0 : bi;  // all-NaN row: token 0
+        positions[b] += 1;
+    }
+}
+
+hipError_t launch_greedy(const float* logits, int B, int V, int32_t* tokens, int32_t* positions, hipStream_t stream) {
+    hipLaunchKernelGGL(mk_greedy_kernel, dim3(B), dim3(GREEDY_THREADS), 0, stream, logits, V, tokens, positions);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------ host launch --
 
 // The whole-step launch waits across workgroups, so it needs every workgroup

@@ -54,7 +54,7 @@ class MkScheduleInfo(ctypes.Structure):
 
 EXPORTS = ["mk_create", "mk_load_weights", "mk_kv_cache_bytes", "mk_decode_step", "mk_decode_step_multikernel",
            "mk_destroy", "mk_status_string", "mk_last_error", "mk_get_device_error", "mk_get_profile",
-           "mk_schedule_inspect", "mk_get_trace"]
+           "mk_schedule_inspect", "mk_get_trace", "mk_greedy_advance"]
 MK_FLAG_PROFILE = 1
 MK_FLAG_TRACE = 2
 TRACE_SLOTS = 52
@@ -87,8 +87,10 @@ def lib():
         L.mk_schedule_inspect.argtypes = [ctypes.POINTER(MkConfig), ctypes.c_int32, ctypes.POINTER(MkScheduleInfo)]
         L.mk_get_profile.argtypes = [H, _P, ctypes.c_size_t]
         L.mk_get_trace.argtypes = [H, _P, ctypes.c_size_t]
+        L.mk_greedy_advance.argtypes = [H, _P, _P, _P, _P]
         for name in ["mk_create", "mk_load_weights", "mk_decode_step", "mk_decode_step_multikernel", "mk_destroy",
-                     "mk_get_device_error", "mk_schedule_inspect", "mk_get_profile", "mk_get_trace"]:
+                     "mk_get_device_error", "mk_schedule_inspect", "mk_get_profile", "mk_get_trace",
+                     "mk_greedy_advance"]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -164,6 +166,10 @@ def mk_decode_step(handle, tokens, positions, kv_cache, logits, stream: Optional
 def mk_decode_step_multikernel(handle, tokens, positions, kv_cache, logits, stream: Optional[int] = None):
     _check(lib().mk_decode_step_multikernel(handle, _ptr(tokens), _ptr(positions), _ptr(kv_cache), _ptr(logits),
                                             stream), handle)
+
+
+def mk_greedy_advance(handle, logits, tokens, positions, stream: Optional[int] = None):
+    _check(lib().mk_greedy_advance(handle, _ptr(logits), _ptr(tokens), _ptr(positions), stream), handle)
 
 
 def mk_get_device_error(handle) -> Optional[MkDeviceError]:

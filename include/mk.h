@@ -129,6 +129,16 @@ int mk_decode_step(mk_handle* h, const int32_t* tokens, const int32_t* positions
 int mk_decode_step_multikernel(mk_handle* h, const int32_t* tokens, const int32_t* positions,
                                void* kv_cache, float* logits, void* stream);
 
+/* Greedy selection after a step (outside the step kernel): one launch on
+ * `stream` that sets tokens[b] = argmax_v logits[b][v] (the lowest index among
+ * equal maxima) and positions[b] += 1 for every batch row, so that back-to-back
+ * steps need no host work.  logits: device float32[B][V]; tokens, positions:
+ * device int32[B] (the next step's inputs).  Asynchronous; NaN logits never
+ * win a comparison (an all-NaN row yields token 0).  Greedy decoding is the
+ * setting of the speed-of-light figures on the Gemma TPU megakernel page
+ * (withhopper.com); the tie-break is torch.argmax's.                       */
+int mk_greedy_advance(mk_handle* h, const float* logits, int32_t* tokens, int32_t* positions, void* stream);
+
 /* Frees everything the handle owns.  NULL is accepted. */
 int mk_destroy(mk_handle* h);
 
