@@ -189,7 +189,9 @@ int mk_create(const mk_config* cfg, mk_handle** out) {
         const size_t side_bytes = (side * 4 + 15) / 16 * 16;
         long ring_budget = (long)LDS_BYTES - 2 * (long)xb - (long)sync_bytes - 2 * (long)side_bytes;
         int ring_units = (int)std::min<long>(32, ring_budget / (NW * UNIT_BYTES));
-        if (ring_units < std::max(2, std::max(std::max(p.ku_h, p.ku_q), p.ku_f))) {
+        // the batch-1 path reads a whole row of units at once; the general path one unit at a time
+        const int ring_need = p.B == 1 ? std::max(2, std::max(std::max(p.ku_h, p.ku_q), p.ku_f)) : 2;
+        if (ring_units < ring_need) {
             delete h;
             return fail(nullptr, MK_ERR_UNSUPPORTED_SHAPE, "batch x hidden too large for the LDS budget");
         }

@@ -10,7 +10,8 @@
  * published by S. Vigna).  Draw i of stream s under seed k is the (i+1)-th
  * SplitMix64 output from the state base(k, s) = mix(mix(k) ^ (s * C)), so any
  * element can be computed independently of the others (counter-based).
- * Normals use the Box-Muller transform on two consecutive draws.
+ * Normals use the Box-Muller transform on two consecutive draws, whose cosine
+ * and sine branches give two consecutive normals.
  */
 #include <math.h>
 #include <pthread.h>
@@ -39,12 +40,21 @@ uint64_t synth_draw_u64(uint64_t seed, uint64_t stream, uint64_t index) {
     return draw(stream_base(seed, stream), index);
 }
 
-/* Standard normal number `index` of the stream: Box-Muller on draws 2i, 2i+1. */
-static inline double normal_at(uint64_t base, uint64_t index) {
-    uint64_t a = draw(base, 2 * index), b = draw(base, 2 * index + 1);
+/* Box-Muller on draws 2j, 2j+1 gives the pair of standard normals 2j
+ * (cosine branch) and 2j+1 (sine branch) of the stream. */
+static inline void normal_pair(uint64_t base, uint64_t j, double *n0, double *n1) {
+    uint64_t a = draw(base, 2 * j), b = draw(base, 2 * j + 1);
     double u1 = ((double)(a >> 11) + 1.0) * 0x1.0p-53; /* (0, 1] */
     double u2 = (double)(b >> 11) * 0x1.0p-53;         /* [0, 1) */
-    return sqrt(-2.0 * log(u1)) * cos(6.283185307179586476925 * u2);
+    double r = sqrt(-2.0 * log(u1)), t = 6.283185307179586476925 * u2;
+    *n0 = r * cos(t);
+    *n1 = r * sin(t);
+}
+/* Standard normal number `index` of the stream. */
+static inline double normal_at(uint64_t base, uint64_t index) {
+    double n0, n1;
+    normal_pair(base, index >> 1, &n0, &n1);
+    return (index & 1) ? n1 : n0;
 }
 
 double synth_normal_at(uint64_t seed, uint64_t stream, uint64_t index) {
@@ -70,8 +80,20 @@ typedef struct {
 
 static void *normal_worker(void *p) {
     job_t *j = (job_t *)p;
-    for (uint64_t i = j->begin; i < j->end; ++i)
-        j->out_bf16[i] = to_bf16_bits((float)(j->mean + j->std * normal_at(j->base, j->offset + i)));
+    uint64_t i = j->begin;
+    while (i < j->end) {
+        const uint64_t g = j->offset + i;  /* global index */
+        double n0, n1;
+        normal_pair(j->base, g >> 1, &n0, &n1);
+        if ((g & 1) == 0 && i + 1 < j->end) {  /* both members of the pair are ours */
+            j->out_bf16[i] = to_bf16_bits((float)(j->mean + j->std * n0));
+            j->out_bf16[i + 1] = to_bf16_bits((float)(j->mean + j->std * n1));
+            i += 2;
+        } else {
+            j->out_bf16[i] = to_bf16_bits((float)(j->mean + j->std * ((g & 1) ? n1 : n0)));
+            i += 1;
+        }
+    }
     return NULL;
 }
 

@@ -26,3 +26,11 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(scope="session")
+def llama1b():
+    """(shape, host weights) of the Llama-1B-shaped model, generated once per session."""
+    import synth
+    shape = synth.LLAMA_1B
+    return shape, synth.make_weights(shape)

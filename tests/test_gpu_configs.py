@@ -1,0 +1,60 @@
+"""GPU parity at the other benchmark shapes: batch 4 and 8, long contexts
+(8K and 32K tokens in the cache) and the 8B shape (head_dim 128, untied head).
+
+Each case pre-fills the cache with seeded N(0, 1) bf16 rows (identical bytes on
+both sides), runs a few greedy steps through the C ABI and compares every step
+with the teacher-forced CPU oracle to the same bar as the other parity tests.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+THREADS = min(32, os.cpu_count() or 1)
+
+
+def run_and_compare(shape, weights, batch, prompt_lens, steps, label, multikernel=False):
+    P = np.asarray(prompt_lens, dtype=np.int32)
+    max_seq = int(P.max()) + steps + 1
+    kv = synth.make_kv_cache(shape, batch, max_seq, int(P.max()))
+    # rows with shorter prompts: slots [P_b, max) stay unused (the step writes slot P_b and
+    # attends to 0..P_b), so the extra filled slots of those rows are never read
+    first = synth.make_first_tokens(shape.vocab, batch)
+    dec = H.GpuDecoder(shape, weights, batch, max_seq, kv_init=kv)
+    try:
+        run = dec.greedy(first, P, steps, multikernel)
+    finally:
+        dec.close()
+    ref = H.oracle_replay(shape, weights, batch, max_seq, run, kv_init=kv, nthreads=THREADS)
+    stats = H.compare(run, ref, label)
+    print(label, stats, flush=True)
+    return stats
+
+
+@pytest.mark.parametrize("batch", [4, 8])
+def test_llama1b_batch_shared_position(llama1b, batch):
+    shape, weights = llama1b
+    run_and_compare(shape, weights, batch, [1024] * batch, 2, f"llama1b b{batch}")
+
+
+def test_llama1b_batch8_staggered_positions_multikernel(llama1b):
+    shape, weights = llama1b
+    run_and_compare(shape, weights, 8, [1024 - 37 * b for b in range(8)], 2, "llama1b b8 staggered", True)
+
+
+@pytest.mark.parametrize("prompt", [8192, 32768])
+def test_llama1b_long_context(llama1b, prompt):
+    shape, weights = llama1b
+    run_and_compare(shape, weights, 1, [prompt], 2, f"llama1b p{prompt}")
+
+
+@pytest.mark.timeout(600)
+def test_llama8b_head_dim_128():
+    shape = synth.LLAMA_8B
+    weights = synth.make_weights(shape)
+    run_and_compare(shape, weights, 1, [1024], 2, "llama8b")

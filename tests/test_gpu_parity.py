@@ -118,12 +118,6 @@ def test_invalid_token_reports_device_error_and_writes_nothing():
 
 # ------------------------------------------------ full-size 1B-shaped model --
 
-@pytest.fixture(scope="module")
-def llama1b():
-    shape = synth.LLAMA_1B
-    return shape, synth.make_weights(shape)
-
-
 @pytest.mark.parametrize("multikernel", [False, True], ids=["megakernel", "multikernel"])
 def test_llama1b_synthetic_kv_matches_oracle(llama1b, multikernel):
     import os
