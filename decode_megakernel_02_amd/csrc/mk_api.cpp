@@ -173,7 +173,7 @@ int mk_create(const mk_config* cfg, mk_handle** out) {
             delete h;
             return fail(nullptr, rc, err);
         }
-        // LDS: two x buffers (also scratch of attention/reduce), sync words, rest = rings
+        // LDS: rings, nslot x buffers (also scratch of attention/reduce), sync words, nslot side buffers
         const int xstride = std::max(std::max(p.ku_h, p.ku_q), p.ku_f) * UNIT_ELEMS;
         size_t xb = (size_t)p.B * xstride * 4;
         const size_t attn_scratch = (size_t)(p.G * p.D + 2 * p.D + NW * (p.D + 2) + NW * 64) * 4;
@@ -187,15 +187,20 @@ int mk_create(const mk_config* cfg, mk_handle** out) {
         size_t side = std::max((size_t)p.B * p.D, (size_t)p.B * max_rows);
         if (side > SIDE_MAX_FLOATS) side = 0;  // too many rows per CU: epilogues read global memory
         const size_t side_bytes = (side * 4 + 15) / 16 * 16;
-        long ring_budget = (long)LDS_BYTES - 2 * (long)xb - (long)sync_bytes - 2 * (long)side_bytes;
-        int ring_units = (int)std::min<long>(32, ring_budget / (NW * UNIT_BYTES));
         // the batch-1 path reads a whole row of units at once; the general path one unit at a time
         const int ring_need = p.B == 1 ? std::max(2, std::max(std::max(p.ku_h, p.ku_q), p.ku_f)) : 2;
+        auto rings_for = [&](int nslot) {
+            const long budget = (long)LDS_BYTES - nslot * (long)(xb + side_bytes) - (long)sync_bytes;
+            return (int)std::min<long>(32, budget / (NW * UNIT_BYTES));
+        };
+        // three buffer sets when the rings keep at least 12 slots, else two
+        int nslot = rings_for(3) >= std::max(ring_need, 12) ? 3 : 2;
+        const int ring_units = rings_for(nslot);
         if (ring_units < ring_need) {
             delete h;
             return fail(nullptr, MK_ERR_UNSUPPORTED_SHAPE, "batch x hidden too large for the LDS budget");
         }
-        h->lds_bytes = (size_t)NW * ring_units * UNIT_BYTES + 2 * xb + sync_bytes + 2 * side_bytes;
+        h->lds_bytes = (size_t)NW * ring_units * UNIT_BYTES + nslot * (xb + side_bytes) + sync_bytes;
 
         Params& hp = h->hp;
         hp.L = p.L; hp.H = p.H; hp.Hq = p.Hq; hp.Hkv = p.Hkv; hp.D = p.D; hp.F = p.F; hp.V = p.V; hp.B = p.B;
@@ -203,6 +208,7 @@ int mk_create(const mk_config* cfg, mk_handle** out) {
         hp.ku_h = p.ku_h; hp.ku_q = p.ku_q; hp.ku_f = p.ku_f; hp.xstride = xstride;
         hp.ring_units = ring_units; hp.xbuf_bytes = (int)xb; hp.ncu = ncu;
         hp.side_floats = (int)(side_bytes / 4);
+        hp.nslot = nslot;
         hp.eps = p.eps; hp.inv_sqrt_d = (float)(1.0 / std::sqrt((double)p.D));
         hp.spin_limit = 1u << 25;
         for (int i = 0; i <= p.n_chunk; ++i) hp.chunk_begin[i] = p.chunk_begin[i];

@@ -16,6 +16,7 @@ constexpr int UNIT_ELEMS = 512;       // bf16 per unit
 constexpr int MAX_BATCH = 8;
 constexpr int LDS_BYTES = 160 * 1024; // gfx950 LDS per CU
 constexpr int SIDE_MAX_FLOATS = 2048; // cap of one LDS side buffer (epilogue inputs)
+constexpr int MAX_SLOTS = 3;          // staged-input buffer sets
 
 // Fused ops, in the order they appear inside one layer.  The page
 // "Megakernels: Deleting the Kernel Boundary to Win Back Microseconds"
@@ -59,8 +60,9 @@ struct Params {
     int32_t xstride;        // floats per batch row in the LDS x buffer (max padded K)
     int32_t ring_units;     // ring slots (1 KB units) per compute wave
     int32_t xbuf_bytes;     // bytes of one of the two LDS x buffers
-    int32_t side_floats;    // floats of each of the two LDS side buffers (epilogue inputs staged by the
-                            // gather wave); 0: epilogue inputs are read from global memory instead
+    int32_t side_floats;    // floats of each LDS side buffer (epilogue inputs staged by the gather
+                            // wave); 0: epilogue inputs are read from global memory instead
+    int32_t nslot;          // x / side buffer sets (2 or 3): the gather wave runs nslot - 1 instructions ahead
     int32_t ncu;            // workgroups in the grid
     float eps;
     float inv_sqrt_d;

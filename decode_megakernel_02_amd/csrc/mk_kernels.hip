@@ -257,28 +257,27 @@ __device__ __forceinline__ bool keep_waiting(Ctx& cx, uint32_t& spins, uint32_t 
 
 // ---------------------------------------------------------------- LDS map --
 
-constexpr int SYNC_WORDS = 2 * NW + 4 + 2 * MAX_BATCH;  // counters + ss, zeroed at launch
+constexpr int SYNC_WORDS = 2 * NW + 4 + MAX_SLOTS * MAX_BATCH;  // counters + ss, zeroed at launch
 static_assert(SYNC_WORDS <= 64, "sync words precede the prefetch dump");  // dump: words 64..127 of 512 B
 
 struct Lds {
     LDS uint8_t* ring;      // [NW][ring_units][1024]
-    LDS float* xbuf[2];     // two x buffers of xbuf_bytes each
+    LDS float* xbuf0;       // nslot x buffers of xbuf_bytes each, back to back
     LDS uint32_t* landed;   // [NW] units landed in each compute wave's ring
     LDS uint32_t* consumed; // [NW] units consumed
     LDS uint32_t* bar;      // compute-wave barrier counter
     LDS uint32_t* gathered; // instructions of this launch whose inputs are staged
     LDS uint32_t* done;     // instruction completions of the compute waves (NW per instruction)
-    LDS float* ss;          // [2][MAX_BATCH] sum of squares of each x buffer's raw input rows
+    LDS float* ss;          // [MAX_SLOTS][MAX_BATCH] sum of squares of each x buffer's raw input rows
     LDS uint32_t* pf_dump;  // [64] landing words of the cache-prefetch touches (never read)
-    LDS float* side[2];     // epilogue inputs of the instruction staged with xbuf[i] (side_floats each)
+    LDS float* side0;       // nslot side buffers (side_floats each): epilogue inputs staged with x buffer i
 };
 __device__ __forceinline__ Lds lds_map(LDS uint8_t* smem, CParams& p) {
     Lds m;
     m.ring = smem;
     size_t off = (size_t)NW * p.ring_units * UNIT_BYTES;
-    m.xbuf[0] = (LDS float*)(smem + off);
-    m.xbuf[1] = (LDS float*)(smem + off + p.xbuf_bytes);
-    LDS uint32_t* sync = (LDS uint32_t*)(smem + off + 2 * (size_t)p.xbuf_bytes);
+    m.xbuf0 = (LDS float*)(smem + off);
+    LDS uint32_t* sync = (LDS uint32_t*)(smem + off + (size_t)p.nslot * p.xbuf_bytes);
     m.landed = sync;
     m.consumed = sync + NW;
     m.bar = sync + 2 * NW;
@@ -286,9 +285,15 @@ __device__ __forceinline__ Lds lds_map(LDS uint8_t* smem, CParams& p) {
     m.done = sync + 2 * NW + 2;
     m.ss = (LDS float*)(sync + 2 * NW + 4);
     m.pf_dump = sync + 64;
-    m.side[0] = (LDS float*)(smem + off + 2 * (size_t)p.xbuf_bytes + 512);
-    m.side[1] = m.side[0] + p.side_floats;
+    m.side0 = (LDS float*)(smem + off + (size_t)p.nslot * p.xbuf_bytes + 512);
     return m;
+}
+// buffer set `slot` of the staged inputs
+__device__ __forceinline__ LDS float* xslot(const Lds& s, CParams& p, uint32_t slot) {
+    return s.xbuf0 + slot * (uint32_t)(p.xbuf_bytes >> 2);
+}
+__device__ __forceinline__ LDS float* sslot(const Lds& s, CParams& p, uint32_t slot) {
+    return s.side0 + slot * (uint32_t)p.side_floats;
 }
 
 // barrier among the NW compute waves (loader waves never join it)
@@ -916,12 +921,14 @@ __device__ __forceinline__ void gatherer(Ctx& cx, const Lds& s, const Step& sp, 
     CParams& p = *cx.p;
     __builtin_amdgcn_s_setprio(MK_LOADER_PRIO);
     const GLB u32x4* iq = (const GLB u32x4*)(p.insts + qb);
-    for (uint32_t pc = pc0; pc < pc1; ++pc) {
+    const uint32_t nslot = uni((uint32_t)p.nslot);
+    uint32_t slot = 0;
+    for (uint32_t pc = pc0; pc < pc1; ++pc, slot = slot + 1 == nslot ? 0 : slot + 1) {
         const uint32_t r = pc - pc0;
         const u32x4 raw = iq[pc];
-        if (r >= 2) {  // x buffer r & 1 held instruction r - 2: wait until every compute wave is done with it
+        if (r >= nslot) {  // buffer set `slot` held instruction r - nslot: wait until every compute wave is done with it
             uint32_t spins = 0;
-            while (uni(lds_ld(s.done)) < NW * (r - 1))
+            while (uni(lds_ld(s.done)) < NW * (r - nslot + 1))
                 if (!keep_waiting<2>(cx, spins, 0x60000000u | r)) break;
         }
         if (uni(cx.aborted)) break;
@@ -930,8 +937,8 @@ __device__ __forceinline__ void gatherer(Ctx& cx, const Lds& s, const Step& sp, 
         cx.op = in.op;
         const uint64_t t0 = cx.trace ? rtime() : 0;
         cx.t_acq = t0;
-        gather_inst(cx, sp, in, r & 1 ? s.xbuf[1] : s.xbuf[0], s.ss + (r & 1) * MAX_BATCH);
-        if (p.side_floats) gather_side(cx, sp, in, r & 1 ? s.side[1] : s.side[0]);
+        gather_inst(cx, sp, in, xslot(s, p, slot), s.ss + slot * MAX_BATCH);
+        if (p.side_floats) gather_side(cx, sp, in, sslot(s, p, slot));
         if (uni(cx.aborted)) break;
         CBAR();
         if (cx.lane == 0) lds_st(s.gathered, r + 1);  // after the staged data (LDS requests of a wave stay ordered)
@@ -972,8 +979,8 @@ struct DownAcc {
 // KU > 0: batch-1 path with KU units per row (x slice in registers);
 // KU == 0: general path.
 template <int KU>
-__device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint32_t r, const Inst& in, LDS float* xb,
-                                        const Step& sp, DownAcc& da) {
+__device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint32_t r, uint32_t slot, const Inst& in,
+                                        LDS float* xb, const Step& sp, DownAcc& da) {
     CParams& p = *cx.p;
     const int B = p.B, H = p.H, l = in.layer;
     const int ku = in.op == OP_O_PROJ_RES ? p.ku_q : in.op == OP_DOWN_RES ? p.ku_f : p.ku_h;
@@ -982,7 +989,7 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
     if (cx.aborted) return;
     float scale = 1.f;
     if ((in.op == OP_RMS_QKV_ROPE || in.op == OP_RMS_LM_HEAD || in.op == OP_RMS_UP_GATE) && cx.lane < B)
-        scale = 1.0f / sqrtf(s.ss[(r & 1) * MAX_BATCH + cx.lane] / (float)H + p.eps);
+        scale = 1.0f / sqrtf(s.ss[slot * MAX_BATCH + cx.lane] / (float)H + p.eps);
 
     XSlice<KU == 0 ? 1 : KU> xs;
     const uint32_t ru = __builtin_amdgcn_readfirstlane((uint32_t)p.ring_units);
@@ -1001,7 +1008,7 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
     const bool lane_row = cx.lane < B;
     const int b = lane_row ? cx.lane : 0;
     const int nrg = (int)in.nrg;
-    const LDS float* sd = p.side_floats ? (r & 1 ? s.side[1] : s.side[0]) : nullptr;  // staged epilogue inputs
+    const LDS float* sd = p.side_floats ? sslot(s, p, slot) : nullptr;  // staged epilogue inputs
     for (uint32_t ri = 0;; ++ri) {
         const uint32_t i = cx.wave + ri * NW;
         if (i >= in.nrg) break;
@@ -1234,6 +1241,20 @@ __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& 
         }
     }
     mark_mid(cx);
+    const int head = g * G + gi;
+    uint64_t* out = p.part + ((((size_t)l * B + b) * p.Hq + head) * p.n_split + split) * (D + 2);
+    if (nkeys <= 64) {
+        // one key block: the first wave of each head saw every key; it writes
+        // the partial itself (no cross-wave merge)
+        if (sub != 0 || cx.aborted) return;
+        if (cx.lane == 0) {
+            st_tag(out + 0, m, cx.epoch);
+            st_tag(out + 1, lsum, cx.epoch);
+        }
+#pragma unroll
+        for (int h = 0; h < NH; ++h) st_tag(out + 2 + h * 64 + cx.lane, o[h], cx.epoch);
+        return;
+    }
     // per-wave state -> LDS, merge the waves of each head
     LDS float* my = stt + cx.wave * (D + 2);
     if (cx.lane == 0) {
@@ -1258,8 +1279,6 @@ __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& 
             for (int h = 0; h < NH; ++h) O[h] = fmaf(sw[2 + h * 64 + cx.lane], f, O[h]);
         }
     }
-    const int head = g * G + gi;
-    uint64_t* out = p.part + ((((size_t)l * B + b) * p.Hq + head) * p.n_split + split) * (D + 2);
     if (cx.lane == 0) {
         st_tag(out + 0, M, cx.epoch);
         st_tag(out + 1, Ls, cx.epoch);
@@ -1390,7 +1409,9 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
     // current instruction
     const GLB u32x4* iq = (const GLB u32x4*)(p.insts + qb);
     u32x4 next = pc0 < pc1 ? iq[pc0] : u32x4{0, 0, 0, 0};
-    for (uint32_t pc = pc0; pc < pc1 && !cx.aborted; ++pc) {
+    const uint32_t nslot = uni((uint32_t)p.nslot);
+    uint32_t slot = 0;  // buffer set of instruction pc (rotates with the gather wave's)
+    for (uint32_t pc = pc0; pc < pc1 && !cx.aborted; ++pc, slot = slot + 1 == nslot ? 0 : slot + 1) {
         const u32x4 raw = next;
         if (pc + 1 < pc1) next = iq[pc + 1];
         Inst in;
@@ -1406,16 +1427,16 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
         cx.t_acq = cx.t_in = cx.t_mid = t_start;
         cx.t_ring = 0;
         const uint32_t r = pc - pc0;
-        LDS float* xb = r & 1 ? s.xbuf[1] : s.xbuf[0];
+        LDS float* xb = xslot(s, p, slot);
         switch (in.op) {
         case OP_ATTENTION: op_attention_t<HEAD_DIM>(cx, s, seq, r, in, xb, sp); break;
         case OP_ATTN_REDUCE: op_reduce(cx, s, r, in, xb); break;
         default: {
             const int ku = in.op == OP_O_PROJ_RES ? p.ku_q : in.op == OP_DOWN_RES ? p.ku_f : p.ku_h;
-            if (p.B != 1) op_gemv<0>(cx, s, st, r, in, xb, sp, da);
-            else if (ku == 4) op_gemv<4>(cx, s, st, r, in, xb, sp, da);
-            else if (ku == 2) op_gemv<2>(cx, s, st, r, in, xb, sp, da);
-            else op_gemv<0>(cx, s, st, r, in, xb, sp, da);
+            if (p.B != 1) op_gemv<0>(cx, s, st, r, slot, in, xb, sp, da);
+            else if (ku == 4) op_gemv<4>(cx, s, st, r, slot, in, xb, sp, da);
+            else if (ku == 2) op_gemv<2>(cx, s, st, r, slot, in, xb, sp, da);
+            else op_gemv<0>(cx, s, st, r, slot, in, xb, sp, da);
             break;
         }
         }

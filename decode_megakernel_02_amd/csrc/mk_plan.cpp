@@ -140,9 +140,11 @@ int build_plan(const mk_config& c, int ncu, Plan& p, std::string& err) {
     if (c.n_splits) {
         p.n_split = c.n_splits;
     } else {
-        // one attention unit per CU when the context is long enough
+        // at most one attention unit per CU, and about 64 keys per split or more:
+        // a split costs a fixed latency (one 64-key block per wave, a merge) and
+        // every extra split adds work to the reduce (measured best at 1K context)
         int by_cu = std::max(1, ncu / (p.B * p.Hkv));
-        int by_len = std::max(1, ceil_div(p.max_seq, 32));
+        int by_len = std::max(1, ceil_div(p.max_seq, 64));
         p.n_split = std::min(std::min(by_cu, by_len), 64);
     }
     if (p.n_split > 256) {
