@@ -351,12 +351,15 @@ static int step_args_ok(mk_handle* h, const int32_t* tokens, const int32_t* posi
     return MK_OK;
 }
 
+// handles created with profiling or tracing run the instrumented kernel build
+static uint32_t instr_flag(const mk_handle* h) { return (h->hp.prof || h->hp.trace) ? KF_INSTRUMENTED : 0u; }
+
 int mk_decode_step(mk_handle* h, const int32_t* tokens, const int32_t* positions, void* kv_cache, float* logits,
                    void* stream) {
     int rc = step_args_ok(h, tokens, positions, kv_cache, logits);
     if (rc != MK_OK) return rc;
     hipError_t e = launch_step(h->dparams, h->hp.D, h->hp.ncu, h->lds_bytes, tokens, positions, kv_cache, logits, -1,
-                               KF_BUMP_EPOCH, (hipStream_t)stream);
+                               KF_BUMP_EPOCH | instr_flag(h), (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(h, HipError{e, "mk_step_kernel launch"});
     return MK_OK;
 }
@@ -368,7 +371,7 @@ int mk_decode_step_multikernel(mk_handle* h, const int32_t* tokens, const int32_
     const int ns = h->hp.n_stages;
     for (int st = 0; st < ns; ++st) {
         hipError_t e = launch_step(h->dparams, h->hp.D, h->hp.ncu, h->lds_bytes, tokens, positions, kv_cache, logits, st,
-                                   st == ns - 1 ? KF_BUMP_EPOCH : 0u, (hipStream_t)stream);
+                                   (st == ns - 1 ? KF_BUMP_EPOCH : 0u) | instr_flag(h), (hipStream_t)stream);
         if (e != hipSuccess) return hip_fail(h, HipError{e, "mk_step_kernel stage launch"});
     }
     return MK_OK;

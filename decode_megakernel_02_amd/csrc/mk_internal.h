@@ -104,6 +104,7 @@ struct Params {
 
 // Kernel launch flags.
 constexpr uint32_t KF_BUMP_EPOCH = 1u;  // last launch of a step: advance the per-workgroup epoch
+constexpr uint32_t KF_INSTRUMENTED = 2u;  // run the kernel build that records profile counters / timelines
 constexpr int PROF_SLOTS = 8;          // counters per wave
 // Timeline record per instruction (100 MHz real-time clock): [0] op | layer << 8 |
 // a << 16 | b << 32 | cu << 48, then per compute wave w at [1 + 6w]: start,

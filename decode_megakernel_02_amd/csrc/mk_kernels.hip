@@ -37,6 +37,11 @@ typedef GLB void glb_void;
 // change during a launch, and no LDS or global store can alias them, so the
 // compiler keeps loaded fields instead of re-reading them after every store.
 typedef const __attribute__((address_space(4))) Params CParams;
+// The instruction queues never change during a launch either: read through the
+// constant address space they become scalar loads, which are waited for with
+// the LDS/scalar counter instead of the vector-memory counter (a vector load
+// would make the wave wait for its own outstanding stores as well).
+#define CONST_AS __attribute__((address_space(4)))
 
 template <class T>
 __device__ __forceinline__ T gld(const T* p) {
@@ -257,7 +262,7 @@ __device__ __forceinline__ bool keep_waiting(Ctx& cx, uint32_t& spins, uint32_t 
 
 // ---------------------------------------------------------------- LDS map --
 
-constexpr int SYNC_WORDS = 2 * NW + 4 + MAX_SLOTS * MAX_BATCH;  // counters + ss, zeroed at launch
+constexpr int SYNC_WORDS = 3 * NW + 4 + MAX_SLOTS * MAX_BATCH;  // counters + ss, zeroed at launch
 static_assert(SYNC_WORDS <= 64, "sync words precede the prefetch dump");  // dump: words 64..127 of 512 B
 
 struct Lds {
@@ -267,7 +272,7 @@ struct Lds {
     LDS uint32_t* consumed; // [NW] units consumed
     LDS uint32_t* bar;      // compute-wave barrier counter
     LDS uint32_t* gathered; // instructions of this launch whose inputs are staged
-    LDS uint32_t* done;     // instruction completions of the compute waves (NW per instruction)
+    LDS uint32_t* done;     // [NW] instructions each compute wave has finished
     LDS float* ss;          // [MAX_SLOTS][MAX_BATCH] sum of squares of each x buffer's raw input rows
     LDS uint32_t* pf_dump;  // [64] landing words of the cache-prefetch touches (never read)
     LDS float* side0;       // nslot side buffers (side_floats each): epilogue inputs staged with x buffer i
@@ -282,8 +287,8 @@ __device__ __forceinline__ Lds lds_map(LDS uint8_t* smem, CParams& p) {
     m.consumed = sync + NW;
     m.bar = sync + 2 * NW;
     m.gathered = sync + 2 * NW + 1;
-    m.done = sync + 2 * NW + 2;
-    m.ss = (LDS float*)(sync + 2 * NW + 4);
+    m.done = sync + 2 * NW + 4;
+    m.ss = (LDS float*)(sync + 3 * NW + 4);
     m.pf_dump = sync + 64;
     m.side0 = (LDS float*)(smem + off + (size_t)p.nslot * p.xbuf_bytes + 512);
     return m;
@@ -920,15 +925,18 @@ __device__ __forceinline__ void gatherer(Ctx& cx, const Lds& s, const Step& sp, 
                                          uint32_t pc1) {
     CParams& p = *cx.p;
     __builtin_amdgcn_s_setprio(MK_LOADER_PRIO);
-    const GLB u32x4* iq = (const GLB u32x4*)(p.insts + qb);
+    const CONST_AS u32x4* iq = (const CONST_AS u32x4*)(p.insts + uni(qb));
     const uint32_t nslot = uni((uint32_t)p.nslot);
     uint32_t slot = 0;
     for (uint32_t pc = pc0; pc < pc1; ++pc, slot = slot + 1 == nslot ? 0 : slot + 1) {
         const uint32_t r = pc - pc0;
         const u32x4 raw = iq[pc];
         if (r >= nslot) {  // buffer set `slot` held instruction r - nslot: wait until every compute wave is done with it
+            // (one counter per wave: a wave with less work in an instruction may
+            // run ahead, so a shared count could reach the total too early)
+            const uint32_t need = r - nslot + 1;
             uint32_t spins = 0;
-            while (uni(lds_ld(s.done)) < NW * (r - nslot + 1))
+            while (any_lane(cx.lane < NW && lds_ld(s.done + (cx.lane < NW ? cx.lane : 0)) < need))
                 if (!keep_waiting<2>(cx, spins, 0x60000000u | r)) break;
         }
         if (uni(cx.aborted)) break;
@@ -937,8 +945,10 @@ __device__ __forceinline__ void gatherer(Ctx& cx, const Lds& s, const Step& sp, 
         cx.op = in.op;
         const uint64_t t0 = cx.trace ? rtime() : 0;
         cx.t_acq = t0;
-        gather_inst(cx, sp, in, xslot(s, p, slot), s.ss + slot * MAX_BATCH);
+        // side inputs first: each was complete before the main input's producers
+        // began, so their round trip never waits behind the main poll
         if (p.side_floats) gather_side(cx, sp, in, sslot(s, p, slot));
+        gather_inst(cx, sp, in, xslot(s, p, slot), s.ss + slot * MAX_BATCH);
         if (uni(cx.aborted)) break;
         CBAR();
         if (cx.lane == 0) lds_st(s.gathered, r + 1);  // after the staged data (LDS requests of a wave stay ordered)
@@ -1319,8 +1329,10 @@ __device__ __forceinline__ void op_reduce(Ctx& cx, const Lds& s, uint32_t r, con
 
 // stage < 0: run the whole queue (one launch per step); stage >= 0: only that
 // stage's instructions (one launch per op and layer).  One instantiation per
-// head size.
-template <int HEAD_DIM>
+// head size, each with and without the profile/timeline instrumentation (its
+// bookkeeping costs registers and scalar work on every instruction, so the
+// plain build leaves it out entirely).
+template <int HEAD_DIM, bool INSTR>
 __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const int32_t* tokens,
                                           const int32_t* positions, uint16_t* kv, float* logits, int stage,
                                           uint32_t flags) {
@@ -1334,8 +1346,8 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
     cx.aborted = false;
     cx.pc = 0;
     cx.op = 0;
-    cx.prof = p.prof != nullptr;
-    cx.trace = p.trace != nullptr;
+    cx.prof = INSTR && p.prof != nullptr;
+    cx.trace = INSTR && p.trace != nullptr;
     cx.t_in = cx.t_acq = cx.t_mid = cx.t_ring = 0;
     for (int k = 0; k < 8; ++k) cx.cnt[k] = 0;
     const uint64_t t_kernel = cx.prof ? cycles() : 0;
@@ -1407,7 +1419,7 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
     for (int k = 0; k < DREG; ++k) da.r[k] = 0.f;
     // instructions are fetched one ahead so the fetch latency overlaps the
     // current instruction
-    const GLB u32x4* iq = (const GLB u32x4*)(p.insts + qb);
+    const CONST_AS u32x4* iq = (const CONST_AS u32x4*)(p.insts + uni(qb));
     u32x4 next = pc0 < pc1 ? iq[pc0] : u32x4{0, 0, 0, 0};
     const uint32_t nslot = uni((uint32_t)p.nslot);
     uint32_t slot = 0;  // buffer set of instruction pc (rotates with the gather wave's)
@@ -1442,7 +1454,7 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
         }
         // this wave is done with the instruction's staged inputs
         CBAR();
-        if (cx.lane == 0) __hip_atomic_fetch_add(s.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (cx.lane == 0) lds_st(s.done + wave, pc - pc0 + 1);
         if (cx.trace && cx.lane == 0) {
             GLB uint64_t* r = (GLB uint64_t*)p.trace + (size_t)(qb + pc) * TRACE_SLOTS;
             if (wave == 0)
@@ -1462,19 +1474,19 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
 }
 
 // The whole step in one launch (every workgroup runs its full queue).
-template <int HEAD_DIM>
+template <int HEAD_DIM, bool INSTR>
 __global__ void __launch_bounds__(WG_THREADS, 1)
 mk_decode_kernel(const Params* __restrict__ pp, const int32_t* tokens, const int32_t* positions, uint16_t* kv,
                  float* logits, int stage, uint32_t flags) {
-    step_body<HEAD_DIM>(pp, tokens, positions, kv, logits, -1, flags);
+    step_body<HEAD_DIM, INSTR>(pp, tokens, positions, kv, logits, -1, flags);
 }
 
 // One stage of the step (one op of one layer) per launch.
-template <int HEAD_DIM>
+template <int HEAD_DIM, bool INSTR>
 __global__ void __launch_bounds__(WG_THREADS, 1)
 mk_stage_kernel(const Params* __restrict__ pp, const int32_t* tokens, const int32_t* positions, uint16_t* kv,
                 float* logits, int stage, uint32_t flags) {
-    step_body<HEAD_DIM>(pp, tokens, positions, kv, logits, stage, flags);
+    step_body<HEAD_DIM, INSTR>(pp, tokens, positions, kv, logits, stage, flags);
 }
 
 // ------------------------------------------------------------ pack kernel --
@@ -1563,17 +1575,22 @@ hipError_t launch_step(const Params* dev_params, int head_dim, int ncu, size_t l
     uint16_t* kv16 = (uint16_t*)kv;
     void* args[] = {(void*)&dev_params, (void*)&tokens, (void*)&positions, (void*)&kv16, (void*)&logits,
                     (void*)&stage, (void*)&flags};
+    const bool instr = (flags & KF_INSTRUMENTED) != 0;
     if (stage < 0) {
-        const void* fn = head_dim == 64 ? (const void*)mk_decode_kernel<64> : (const void*)mk_decode_kernel<128>;
+        const void* fn = head_dim == 64 ? (instr ? (const void*)mk_decode_kernel<64, true> : (const void*)mk_decode_kernel<64, false>)
+                                        : (instr ? (const void*)mk_decode_kernel<128, true> : (const void*)mk_decode_kernel<128, false>);
         return hipLaunchCooperativeKernel(fn, dim3(ncu), dim3(WG_THREADS), args, (unsigned)lds_bytes, stream);
     }
-    const void* fn = head_dim == 64 ? (const void*)mk_stage_kernel<64> : (const void*)mk_stage_kernel<128>;
+    const void* fn = head_dim == 64 ? (instr ? (const void*)mk_stage_kernel<64, true> : (const void*)mk_stage_kernel<64, false>)
+                                    : (instr ? (const void*)mk_stage_kernel<128, true> : (const void*)mk_stage_kernel<128, false>);
     return hipLaunchKernel(fn, dim3(ncu), dim3(WG_THREADS), args, lds_bytes, stream);
 }
 
 hipError_t set_step_kernel_lds(size_t lds_bytes) {
-    const void* fns[] = {(const void*)mk_decode_kernel<64>, (const void*)mk_decode_kernel<128>,
-                         (const void*)mk_stage_kernel<64>, (const void*)mk_stage_kernel<128>};
+    const void* fns[] = {(const void*)mk_decode_kernel<64, false>, (const void*)mk_decode_kernel<128, false>,
+                         (const void*)mk_stage_kernel<64, false>,  (const void*)mk_stage_kernel<128, false>,
+                         (const void*)mk_decode_kernel<64, true>,  (const void*)mk_decode_kernel<128, true>,
+                         (const void*)mk_stage_kernel<64, true>,   (const void*)mk_stage_kernel<128, true>};
     for (const void* fn : fns) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
         if (e != hipSuccess) return e;

@@ -190,7 +190,19 @@ int build_plan(const mk_config& c, int ncu, Plan& p, std::string& err) {
         mark(st + 3);
         b.tiles(OP_O_PROJ_RES, l, p.H);
         mark(st + 4);
-        b.tiles(OP_RMS_UP_GATE, l, p.F);
+        // up/gate rows go chunk by chunk: every CU computes its share of
+        // K-chunk 0 of the down projection first, then of chunk 1, ..., so a
+        // chunk is complete after the matching fraction of the stage instead
+        // of after the whole stage, and the down instructions of the early
+        // chunks find their inputs ready
+        for (int cch = 0; cch < p.n_chunk; ++cch) {
+            const int c0 = p.chunk_begin[cch], len = p.chunk_begin[cch + 1] - c0;
+            for (int t = 0; t < ncu; ++t) {
+                int r0 = (int)((long long)len * t / ncu), r1 = (int)((long long)len * (t + 1) / ncu);
+                if (r1 > r0)
+                    b.q[t].push_back(Inst{OP_RMS_UP_GATE, (uint16_t)l, (uint32_t)(c0 + r0), (uint32_t)(r1 - r0), 0, 0});
+            }
+        }
         mark(st + 5);
         // down projection: a CU owns rows [r0, r1) for every K-chunk, one
         // instruction per chunk, each waiting only for its chunk of the SwiGLU output

@@ -5,6 +5,7 @@ Each case pre-fills the cache with seeded N(0, 1) bf16 rows (identical bytes on
 both sides), runs a few greedy steps through the C ABI and compares every step
 with the teacher-forced CPU oracle to the same bar as the other parity tests.
 """
+import dataclasses
 import os
 
 import numpy as np
@@ -18,14 +19,14 @@ pytestmark = pytest.mark.gpu
 THREADS = min(32, os.cpu_count() or 1)
 
 
-def run_and_compare(shape, weights, batch, prompt_lens, steps, label, multikernel=False):
+def run_and_compare(shape, weights, batch, prompt_lens, steps, label, multikernel=False, n_chunks=0):
     P = np.asarray(prompt_lens, dtype=np.int32)
     max_seq = int(P.max()) + steps + 1
     kv = synth.make_kv_cache(shape, batch, max_seq, int(P.max()))
     # rows with shorter prompts: slots [P_b, max) stay unused (the step writes slot P_b and
     # attends to 0..P_b), so the extra filled slots of those rows are never read
     first = synth.make_first_tokens(shape.vocab, batch)
-    dec = H.GpuDecoder(shape, weights, batch, max_seq, kv_init=kv)
+    dec = H.GpuDecoder(shape, weights, batch, max_seq, n_chunks=n_chunks, kv_init=kv)
     try:
         run = dec.greedy(first, P, steps, multikernel)
     finally:
@@ -58,3 +59,14 @@ def test_llama8b_head_dim_128():
     shape = synth.LLAMA_8B
     weights = synth.make_weights(shape)
     run_and_compare(shape, weights, 1, [1024], 2, "llama8b")
+
+
+@pytest.mark.parametrize("n_chunks", [8, 16])
+def test_uneven_rows_per_wave(n_chunks):
+    """Down-projection chunks of 1024 or 512 rows give each CU 4 or 2 up/gate
+    rows per instruction, so half or more of the compute waves have no row in
+    those instructions and run ahead of the others; the staged-input buffers
+    must still not be refilled while a slower wave reads them."""
+    shape = dataclasses.replace(synth.LLAMA_1B, n_layers=2, vocab=4096)
+    weights = synth.make_weights(shape)
+    run_and_compare(shape, weights, 1, [64], 2, f"llama1b-dims 2 layers, {n_chunks} chunks", n_chunks=n_chunks)
