@@ -68,6 +68,21 @@ __device__ __forceinline__ float2 gld_f2(const float* p) {
     const u32x2 v = *(const GLB u32x2*)p;
     return make_float2(__uint_as_float(v.x), __uint_as_float(v.y));
 }
+// Waits until none of this wave's vector-memory operations is outstanding, as
+// an instruction the compiler's wait-insertion pass sees (so it stops tracking
+// earlier loads).  gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15.
+__device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// A load whose value is waited for on the spot.  Used on rarely taken paths of
+// the compute waves: a load left outstanding across a branch join makes the
+// compiler wait for the whole vector-memory counter at a later register
+// reuse, and on gfx9 that counter includes the wave's own stores, whose
+// acknowledgement from the coherent memory level takes microseconds.
+template <class T>
+__device__ __forceinline__ T gld_now(const T* p) {
+    const T v = gld(p);
+    vm_drain();
+    return v;
+}
 template <class T>
 __device__ __forceinline__ void gst(T* p, T v) {
     *(GLB T*)p = v;
@@ -159,28 +174,13 @@ __device__ __forceinline__ uint32_t asm_lds_ld(uint32_t a) {
 __device__ __forceinline__ void asm_lds_st(uint32_t a, uint32_t v) {
     asm volatile("ds_write_b32 %0, %1" ::"v"(a), "v"(v) : "memory");
 }
-// wait until at most n vector-memory operations of this wave are outstanding
-__device__ __forceinline__ void wait_vm_le(uint32_t n) {
-    switch (n) {
-    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
-    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
-    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
-    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
-    case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
-    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
-    case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
-    case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
-    case 11: asm volatile("s_waitcnt vmcnt(11)" ::: "memory"); break;
-    case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
-    case 13: asm volatile("s_waitcnt vmcnt(13)" ::: "memory"); break;
-    case 14: asm volatile("s_waitcnt vmcnt(14)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
-    }
-}
-static_assert(MAXOUT <= 16, "wait_vm_le covers 0..15");
+// wait until at most MK_KEEP (or no) vector-memory operations of this wave are outstanding
+#define MK_STR2(x) #x
+#define MK_STR(x) MK_STR2(x)
+__device__ __forceinline__ void wait_vm_keep() { asm volatile("s_waitcnt vmcnt(" MK_STR(MK_KEEP) ")" ::: "memory"); }
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+static_assert(MAXOUT <= 32, "the loader's stream-id FIFO holds 32 entries");
+static_assert(MAXOUT <= 63, "vmcnt counts at most 63 operations");
 
 // ------------------------------------------------------------ wave context --
 
@@ -248,7 +248,7 @@ template <int SLEEP = MK_SLEEP>
 __device__ __forceinline__ bool keep_waiting(Ctx& cx, uint32_t& spins, uint32_t detail) {
     if (uni(cx.aborted)) return false;
     ++spins;
-    if ((spins & 63u) == 0u && abort_flag(cx.p)) {
+    if ((spins & 1023u) == 0u && abort_flag(cx.p)) {
         cx.aborted = true;
         return false;
     }
@@ -435,7 +435,8 @@ __device__ __forceinline__ void loader(Ctx& cx, const Lds& s, int w0, const uint
         return sid == 0 ? load_stream_issue(a, ru, max)
                         : sid == 1 ? load_stream_issue(b, ru, max) : load_stream_issue(c, ru, max);
     };
-    uint32_t fifo = 0, out = 0, spins = 0, turn = 0;
+    uint64_t fifo = 0;  // 2-bit stream id per outstanding unit, oldest in the low bits
+    uint32_t out = 0, spins = 0, turn = 0;
     while (a.done < a.n || b.done < b.n || c.done < c.n) {
         while (out < (uint32_t)MAXOUT) {
             const uint32_t max = MAXOUT - out < ISSUE_BATCH ? MAXOUT - out : ISSUE_BATCH;
@@ -448,13 +449,13 @@ __device__ __forceinline__ void loader(Ctx& cx, const Lds& s, int w0, const uint
                     __builtin_amdgcn_global_load_lds((const glb_void*)(pf_src + (size_t)pf_k * (NW * UNIT_BYTES)),
                                                      (lds_void*)(uintptr_t)pf_dump, 4, 0, 0);
                     ++pf_k;
-                    fifo |= 3u << (2 * out);
+                    fifo |= 3ull << (2 * out);
                     ++out;
                     continue;
                 }
                 break;
             }
-            fifo |= (sid * (0x55u & ((1u << (2 * k)) - 1u))) << (2 * out);  // k entries of sid
+            fifo |= (uint64_t)(sid * (0x55u & ((1u << (2 * k)) - 1u))) << (2 * out);  // k entries of sid
             out += k;
             turn = sid == 2 ? 0 : sid + 1;
         }
@@ -463,15 +464,16 @@ __device__ __forceinline__ void loader(Ctx& cx, const Lds& s, int w0, const uint
             const bool blocked = out < (uint32_t)MAXOUT;
             const uint32_t keep = blocked ? 0u : KEEP_IN_FLIGHT;
             const uint64_t t0 = cx.prof ? cycles() : 0;
-            wait_vm_le(keep);
+            if (blocked) wait_vm_all();
+            else wait_vm_keep();
             if (cx.prof) cx.cnt[1] += cycles() - t0;
             const uint32_t k = out - keep;
-            const uint32_t f = k >= 16 ? fifo : fifo & ((1u << (2 * k)) - 1u);
-            const uint32_t lo = f & 0x55555555u, hi = (f >> 1) & 0x55555555u;
-            const uint32_t n1 = (uint32_t)__builtin_popcount(lo & ~hi), n2 = (uint32_t)__builtin_popcount(hi & ~lo);
-            const uint32_t n3 = (uint32_t)__builtin_popcount(lo & hi);  // prefetch touches
+            const uint64_t f = k >= 32 ? fifo : fifo & ((1ull << (2 * k)) - 1ull);
+            const uint64_t lo = f & 0x5555555555555555ull, hi = (f >> 1) & 0x5555555555555555ull;
+            const uint32_t n1 = (uint32_t)__builtin_popcountll(lo & ~hi), n2 = (uint32_t)__builtin_popcountll(hi & ~lo);
+            const uint32_t n3 = (uint32_t)__builtin_popcountll(lo & hi);  // prefetch touches
             const uint32_t n0 = k - n1 - n2 - n3;
-            fifo = k >= 16 ? 0u : fifo >> (2 * k);
+            fifo = k >= 32 ? 0ull : fifo >> (2 * k);
             out = keep;
             if (n0) asm_lds_st(a.a_landed, a.done += n0);
             if (n1) asm_lds_st(b.a_landed, b.done += n1);
@@ -999,7 +1001,7 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
     if (cx.aborted) return;
     float scale = 1.f;
     if ((in.op == OP_RMS_QKV_ROPE || in.op == OP_RMS_LM_HEAD || in.op == OP_RMS_UP_GATE) && cx.lane < B)
-        scale = 1.0f / sqrtf(s.ss[slot * MAX_BATCH + cx.lane] / (float)H + p.eps);
+        scale = rsqrtf(s.ss[slot * MAX_BATCH + cx.lane] * (1.0f / (float)H) + p.eps);
 
     XSlice<KU == 0 ? 1 : KU> xs;
     const uint32_t ru = __builtin_amdgcn_readfirstlane((uint32_t)p.ring_units);
@@ -1035,7 +1037,7 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
                 if (t < (G + 1) * half) {  // q or k: rotate the pair (ii, ii + D/2)
                     const int ii = t < G * half ? t % half : t - G * half;
                     const float2 cs = sd ? make_float2(sd[b * D + 2 * ii], sd[b * D + 2 * ii + 1])
-                                         : gld_f2(p.rope + ((size_t)pos * half + ii) * 2);
+                                         : [&] { const float2 c = gld_f2(p.rope + ((size_t)pos * half + ii) * 2); vm_drain(); return c; }();
                     const float r1 = y1 * cs.x - y2 * cs.y, r2 = y2 * cs.x + y1 * cs.y;
                     uint64_t* blk = p.qkv + (((size_t)l * B + b) * p.Hkv + g) * (size_t)(G + 2) * D;
                     if (t < G * half) {
@@ -1070,7 +1072,7 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
             if (sd) {
                 if (lane_row) hin = sd[b * nrg + i];
             } else if (lane_row) {
-                if (l == 0) hin = bf2f(gld(p.embed + (size_t)sp.tok * H + rg));
+                if (l == 0) hin = bf2f(gld_now(p.embed + (size_t)sp.tok * H + rg));
                 else hin = wait_word(cx, p.hout + ((size_t)(l - 1) * B + b) * H + rg);
             }
             dot1(o);
@@ -1096,7 +1098,7 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
                 if (ri < DREG)
                     prev = ri == 0 ? da.r[0] : ri == 1 ? da.r[1] : ri == 2 ? da.r[2] : da.r[3];
                 else if (lane_row)
-                    prev = gld(acc);
+                    prev = gld_now(acc);
             }
             dot1(o);
             const float v = o.mine[0] + prev;
@@ -1441,7 +1443,10 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
         const uint32_t r = pc - pc0;
         LDS float* xb = xslot(s, p, slot);
         switch (in.op) {
-        case OP_ATTENTION: op_attention_t<HEAD_DIM>(cx, s, seq, r, in, xb, sp); break;
+        case OP_ATTENTION:
+            op_attention_t<HEAD_DIM>(cx, s, seq, r, in, xb, sp);
+            vm_drain();  // no load of the attention body stays tracked into the next instruction
+            break;
         case OP_ATTN_REDUCE: op_reduce(cx, s, r, in, xb); break;
         default: {
             const int ku = in.op == OP_O_PROJ_RES ? p.ku_q : in.op == OP_DOWN_RES ? p.ku_f : p.ku_h;
