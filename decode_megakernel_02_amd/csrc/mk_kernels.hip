@@ -720,10 +720,18 @@ __device__ __forceinline__ void gather_region(Ctx& cx, const uint64_t* base, int
             }
         }
         if (cx.trace) cx.t_acq = rtime();  // every tag current
+        // put(kb, ...) stores pair k = kb + 2 * lane, kb = k0 + 128 j; a full
+        // round needs no per-pair bounds test
+        if (k0 + 128 * NB <= n) {
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const int k = k0 + j * 128 + 2 * cx.lane;
-            if (k < n) put(k, __uint_as_float(w[j].x), __uint_as_float(w[j].z), GAIN ? g[j] : 0x3f803f80u);
+            for (int j = 0; j < NB; ++j)
+                put(k0 + j * 128, __uint_as_float(w[j].x), __uint_as_float(w[j].z), GAIN ? g[j] : 0x3f803f80u);
+        } else {
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const int k = k0 + j * 128 + 2 * cx.lane;
+                if (k < n) put(k0 + j * 128, __uint_as_float(w[j].x), __uint_as_float(w[j].z), GAIN ? g[j] : 0x3f803f80u);
+            }
         }
     }
 }
@@ -742,10 +750,10 @@ __device__ __forceinline__ void gather_x(Ctx& cx, int B, int K, int kpad, Row&& 
         // lane l stores pairs k = k0 + 2l (k0 a multiple of 128): one base address per lane
         LDS float* xl = xb + xidx(xs, b, 2 * cx.lane);
         gather_region<GATHER_NB, GAIN>(cx, row(b), K, gain,
-                                      [&](int k, float v0, float v1, uint32_t gp) {
+                                      [&](int kb, float v0, float v1, uint32_t gp) {
                                           ss = fmaf(v0, v0, ss);
                                           ss = fmaf(v1, v1, ss);
-                                          LDS float* x = xl + (k - 2 * cx.lane) / 2;  // k, k+1 adjacent
+                                          LDS float* x = xl + (kb >> 1);  // k, k+1 adjacent
                                           x[0] = v0 * bf_lo(gp);
                                           x[1] = v1 * bf_hi(gp);
                                       });
@@ -892,7 +900,8 @@ __device__ __forceinline__ void gather_inst(Ctx& cx, const Step& sp, const Inst&
         const int b = in.a, g = in.b, D = p.D, nq = p.G * D;
         const uint64_t* src = p.qkv + (((size_t)l * B + b) * p.Hkv + g) * (size_t)(p.G + 2) * D;
         const float sc = p.inv_sqrt_d;
-        gather_region<GATHER_NB_ATTN, false>(cx, src, nq + 2 * D, nullptr, [&](int i, float v0, float v1, uint32_t) {
+        gather_region<GATHER_NB_ATTN, false>(cx, src, nq + 2 * D, nullptr, [&](int kb, float v0, float v1, uint32_t) {
+            const int i = kb + 2 * cx.lane;
             const float f = i < nq ? sc : 1.f;  // nq even: a pair never straddles q and k
             xb[i] = v0 * f;
             xb[i + 1] = v1 * f;
@@ -902,7 +911,8 @@ __device__ __forceinline__ void gather_inst(Ctx& cx, const Step& sp, const Inst&
     default: {  // OP_ATTN_REDUCE: the n_split partials (m, l, o[D]) of (row, head)
         const int b = in.a, head = in.b, W = p.D + 2;
         const uint64_t* src = p.part + (((size_t)l * B + b) * p.Hq + head) * p.n_split * W;
-        gather_region<GATHER_NB, false>(cx, src, p.n_split * W, nullptr, [&](int i, float v0, float v1, uint32_t) {
+        gather_region<GATHER_NB, false>(cx, src, p.n_split * W, nullptr, [&](int kb, float v0, float v1, uint32_t) {
+                                           const int i = kb + 2 * cx.lane;
                                            xb[i] = v0;
                                            xb[i + 1] = v1;
                                        });
