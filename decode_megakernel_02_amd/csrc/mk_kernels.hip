@@ -1200,8 +1200,8 @@ __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& 
     const uint16_t* Vc = sp.kv + ((((size_t)l * 2 + 1) * B + b) * p.Hkv + g) * (size_t)p.max_seq * D;
     const int nkeys = j1 - j0;
 
-    // K rows written by earlier steps do not depend on this step: load the
-    // first block's first 64 dims before waiting for q.  Rows are handled in
+    // K and V rows written by earlier steps do not depend on this step: load
+    // the first block's first 64 dims before waiting for q.  Rows are handled in
     // 64-dim halves (eight 16-byte chunks) to bound register use.
     uint4 kr[8], vr[8];
     auto load_half = [&](uint4 (&r)[8], const uint16_t* base, int kb, int h) {
@@ -1221,7 +1221,12 @@ __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& 
                               (hi.x >> 16) | (hi.y & 0xffff0000u), (hi.z >> 16) | (hi.w & 0xffff0000u));
         }
     };
-    if (sub * 64 < nkeys) load_half(kr, Kc, sub, 0);
+    // (with 64-dim heads V of that block too: its load then overlaps the wait
+    // instead of following the softmax; 128-dim heads lack the registers)
+    if (sub * 64 < nkeys) {
+        load_half(kr, Kc, sub, 0);
+        if (NH == 1) load_half(vr, Vc, sub, 0);
+    }
 
     // q of the group's heads (pre-scaled), then the new K and V rows, staged by the gather wave
     wait_inputs(cx, s, r);
@@ -1257,7 +1262,7 @@ __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& 
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
             CBAR();
-            load_half(vr, Vc, kb, h);
+            if (NH != 1 || kb != sub) load_half(vr, Vc, kb, h);
             if (is_new) pack_lds(vr, vn + h * 64);
             o[h] = o[h] * corr + pv_reduce_scatter64(vr, e, cx.lane);
         }
