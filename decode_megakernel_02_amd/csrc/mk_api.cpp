@@ -19,7 +19,8 @@ hipError_t launch_step(const Params* dev_params, int head_dim, int ncu, size_t l
                        hipStream_t stream);
 hipError_t set_step_kernel_lds(size_t lds_bytes);
 hipError_t launch_pack(const void* rows, uint32_t n, const uint16_t* const* mats, uint8_t* dst, hipStream_t stream);
-hipError_t launch_greedy(const float* logits, int B, int V, int32_t* tokens, int32_t* positions, hipStream_t stream);
+hipError_t launch_greedy(const float* logits, int B, int V, int32_t* tokens, int32_t* positions, uint64_t* part,
+                         uint32_t* cnt, hipStream_t stream);
 }  // namespace mk
 
 using namespace mk;
@@ -33,6 +34,8 @@ struct mk_handle {
     size_t lds_bytes = 0;
     bool loaded = false;
     std::string last_error;
+    uint64_t* greedy_part = nullptr;  // [B][GREEDY_BLOCKS] per-slice (value, index) pairs
+    uint32_t* greedy_cnt = nullptr;   // [B] finished slices of the current call (zero between calls)
 };
 
 static thread_local std::string g_create_error;
@@ -270,6 +273,9 @@ int mk_create(const mk_config* cfg, mk_handle** out) {
         HIPCHK(hipMemset(hp.epoch, 0, (size_t)ncu * 4));
         hp.error = dalloc<uint32_t>(h, 8);
         HIPCHK(hipMemset(hp.error, 0, 32));
+        h->greedy_part = dalloc<uint64_t>(h, (size_t)B * GREEDY_BLOCKS);
+        h->greedy_cnt = dalloc<uint32_t>(h, (size_t)B);
+        HIPCHK(hipMemset(h->greedy_cnt, 0, (size_t)B * 4));
         h->dparams = dalloc<Params>(h, 1);
         HIPCHK(hipMemcpy(h->dparams, &hp, sizeof hp, hipMemcpyHostToDevice));
         HIPCHK(set_step_kernel_lds(h->lds_bytes));
@@ -379,7 +385,8 @@ int mk_decode_step_multikernel(mk_handle* h, const int32_t* tokens, const int32_
 
 int mk_greedy_advance(mk_handle* h, const float* logits, int32_t* tokens, int32_t* positions, void* stream) {
     if (!h || !logits || !tokens || !positions) return fail(h, MK_ERR_INVALID_ARG, "null argument");
-    hipError_t e = launch_greedy(logits, h->hp.B, h->hp.V, tokens, positions, (hipStream_t)stream);
+    hipError_t e = launch_greedy(logits, h->hp.B, h->hp.V, tokens, positions, h->greedy_part, h->greedy_cnt,
+                                 (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(h, HipError{e, "mk_greedy_kernel launch"});
     return MK_OK;
 }

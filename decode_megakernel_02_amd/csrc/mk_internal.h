@@ -17,6 +17,7 @@ constexpr int MAX_BATCH = 8;
 constexpr int LDS_BYTES = 160 * 1024; // gfx950 LDS per CU
 constexpr int SIDE_MAX_FLOATS = 2048; // cap of one LDS side buffer (epilogue inputs)
 constexpr int MAX_SLOTS = 3;          // staged-input buffer sets
+constexpr int GREEDY_BLOCKS = 32;     // workgroups per batch row of the greedy argmax
 
 // Fused ops, in the order they appear inside one layer.  The page
 // "Megakernels: Deleting the Kernel Boundary to Win Back Microseconds"

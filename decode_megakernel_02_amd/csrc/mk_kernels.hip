@@ -1534,53 +1534,83 @@ __global__ void __launch_bounds__(256) mk_pack_kernel(const PackRowDev* rows, ui
 
 // ------------------------------------------------------------ greedy step --
 
-// One workgroup per batch row: tokens[b] = argmax_v logits[b][v] (lowest index
-// among equal maxima), positions[b] += 1.  Reads the row once with 16-byte
-// loads; the (value, index) pairs are reduced in LDS.
-constexpr int GREEDY_THREADS = 1024;
+// tokens[b] = argmax_v logits[b][v] (lowest index among equal maxima, NaN
+// never wins, an all-NaN row gives 0), positions[b] += 1.  GREEDY_BLOCKS
+// workgroups share a row: each reduces its slice to a (value, index) pair,
+// and the last one to finish (a device-scope counter per row) reduces the
+// pairs and writes the token.  The counter is reset by that last workgroup,
+// so the next call starts from zero.
+constexpr int GREEDY_THREADS = 256;
+struct ArgMax {
+    float v;
+    int i;
+};
+__device__ __forceinline__ void argmax_take(ArgMax& a, float v, int i) {
+    if (v > a.v || (v == a.v && i < a.i)) {
+        a.v = v;
+        a.i = i;
+    }
+}
+__device__ __forceinline__ ArgMax argmax_block(ArgMax a, ArgMax* sh) {
+    for (int off = 32; off >= 1; off >>= 1) argmax_take(a, __shfl_xor(a.v, off), __shfl_xor(a.i, off));
+    const int t = threadIdx.x;
+    if ((t & 63) == 0) sh[t >> 6] = a;
+    __syncthreads();
+    if (t == 0)
+        for (int w = 1; w < GREEDY_THREADS / 64; ++w) argmax_take(a, sh[w].v, sh[w].i);
+    return a;  // complete in thread 0
+}
 __global__ void __launch_bounds__(GREEDY_THREADS) mk_greedy_kernel(const float* logits, int V, int32_t* tokens,
-                                                                    int32_t* positions) {
-    __shared__ float sv[GREEDY_THREADS / 64];
-    __shared__ int si[GREEDY_THREADS / 64];
-    const int b = blockIdx.x, t = threadIdx.x;
+                                                                    int32_t* positions, uint64_t* part, uint32_t* cnt) {
+    __shared__ ArgMax sh[GREEDY_THREADS / 64];
+    __shared__ bool last;
+    const int b = blockIdx.y, blk = blockIdx.x, nb = gridDim.x, t = threadIdx.x;
     const float* row = logits + (size_t)b * V;
-    float best = -__builtin_inff();
-    int bi = 0x7fffffff;
-    auto take = [&](float v, int i) {
-        if (v > best || (v == best && i < bi)) {
-            best = v;
-            bi = i;
-        }
-    };
-    const int V4 = ((uintptr_t)row & 15) == 0 ? V / 4 : 0;  // rows of odd V may be unaligned
-    for (int c = t; c < V4; c += GREEDY_THREADS) {
-        const f32x4 v = *(const GLB f32x4*)(row + 4 * c);
-        take(v.x, 4 * c);
-        take(v.y, 4 * c + 1);
-        take(v.z, 4 * c + 2);
-        take(v.w, 4 * c + 3);
+    // slice [v0, v1), 4-aligned when the row is 16-byte aligned
+    const int per = ((V + nb - 1) / nb + 3) & ~3;
+    const int v0 = blk * per < V ? blk * per : V, v1 = v0 + per < V ? v0 + per : V;
+    ArgMax a{-__builtin_inff(), 0x7fffffff};
+    const bool vec = ((uintptr_t)row & 15) == 0;
+    const int n4 = vec ? (v1 - v0) / 4 : 0;
+    for (int c = t; c < n4; c += GREEDY_THREADS) {
+        const f32x4 x = *(const GLB f32x4*)(row + v0 + 4 * c);
+        const int i = v0 + 4 * c;
+        argmax_take(a, x.x, i);
+        argmax_take(a, x.y, i + 1);
+        argmax_take(a, x.z, i + 2);
+        argmax_take(a, x.w, i + 3);
     }
-    for (int i = 4 * V4 + t; i < V; i += GREEDY_THREADS) take(gld(row + i), i);
-    // wave reduction, then across waves
-    for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(best, off);
-        const int oi = __shfl_xor(bi, off);
-        take(ov, oi);
-    }
-    if ((t & 63) == 0) {
-        sv[t >> 6] = best;
-        si[t >> 6] = bi;
+    for (int i = v0 + 4 * n4 + t; i < v1; i += GREEDY_THREADS) argmax_take(a, gld(row + i), i);
+    a = argmax_block(a, sh);
+    if (t == 0) {
+        __hip_atomic_store((GLB uint64_t*)&part[(size_t)b * nb + blk], ((uint64_t)(uint32_t)a.i << 32) | __float_as_uint(a.v),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // the pair is ordered before the count (release); the last arrival
+        // orders its reads after it (acquire)
+        const uint32_t old = __hip_atomic_fetch_add(&cnt[b], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        last = old == (uint32_t)nb - 1;
     }
     __syncthreads();
+    if (!last) return;
+    ArgMax f{-__builtin_inff(), 0x7fffffff};
+    for (int k = t; k < nb; k += GREEDY_THREADS) {
+        const uint64_t w = __hip_atomic_load((GLB uint64_t*)&part[(size_t)b * nb + k], __ATOMIC_ACQUIRE,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        argmax_take(f, __uint_as_float((uint32_t)w), (int)(w >> 32));
+    }
+    __syncthreads();
+    f = argmax_block(f, sh);
     if (t == 0) {
-        for (int w = 1; w < GREEDY_THREADS / 64; ++w) take(sv[w], si[w]);
-        tokens[b] = bi == 0x7fffffff ? 0 : bi;  // all-NaN row: token 0
+        tokens[b] = f.i == 0x7fffffff ? 0 : f.i;
         positions[b] += 1;
+        __hip_atomic_store(&cnt[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
-hipError_t launch_greedy(const float* logits, int B, int V, int32_t* tokens, int32_t* positions, hipStream_t stream) {
-    hipLaunchKernelGGL(mk_greedy_kernel, dim3(B), dim3(GREEDY_THREADS), 0, stream, logits, V, tokens, positions);
+hipError_t launch_greedy(const float* logits, int B, int V, int32_t* tokens, int32_t* positions, uint64_t* part,
+                         uint32_t* cnt, hipStream_t stream) {
+    hipLaunchKernelGGL(mk_greedy_kernel, dim3(GREEDY_BLOCKS, B), dim3(GREEDY_THREADS), 0, stream, logits, V, tokens,
+                       positions, part, cnt);
     return hipGetLastError();
 }
 

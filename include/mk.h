@@ -136,7 +136,10 @@ int mk_decode_step_multikernel(mk_handle* h, const int32_t* tokens, const int32_
  * device int32[B] (the next step's inputs).  Asynchronous; NaN logits never
  * win a comparison (an all-NaN row yields token 0).  Greedy decoding is the
  * setting of the speed-of-light figures on the Gemma TPU megakernel page
- * (withhopper.com); the tie-break is torch.argmax's.                       */
+ * (withhopper.com); the tie-break is torch.argmax's.  Uses a small per-handle
+ * device scratch area (per-slice partial maxima and a per-row counter that
+ * each call leaves at zero): calls on one handle must not overlap in time
+ * (issue them on one stream).                                              */
 int mk_greedy_advance(mk_handle* h, const float* logits, int32_t* tokens, int32_t* positions, void* stream);
 
 /* Frees everything the handle owns.  NULL is accepted. */

@@ -32,3 +32,32 @@ def test_greedy_matches_argmax(batch, vocab):
         assert ref[0] == vocab // 3
     finally:
         mk.mk_destroy(h)
+
+
+def test_greedy_repeated_calls_and_nan():
+    """Back-to-back calls on one handle (the per-row slice counter must be back
+    at zero after each call) and NaN logits: NaN never wins, an all-NaN row
+    gives token 0."""
+    import torch
+    from decode_megakernel_02_amd import mk
+    batch, vocab = 3, 128256
+    shape = synth.ModelShape("greedy", 1, 256, 4, 2, 64, 688, vocab, 1e-5, 1e4, True)
+    h = mk.mk_create(mk.make_config(shape, batch, 64))
+    try:
+        rng = np.random.default_rng(11)
+        d_tok = torch.zeros(batch, dtype=torch.int32, device="cuda")
+        d_pos = torch.zeros(batch, dtype=torch.int32, device="cuda")
+        for call in range(4):
+            lg = rng.standard_normal((batch, vocab)).astype(np.float32)
+            lg[0, rng.integers(vocab, size=500)] = np.nan
+            lg[2, :] = np.nan
+            want = np.nanargmax(np.where(np.isnan(lg[:2]), -np.inf, lg[:2]), axis=1)
+            d_lg = torch.from_numpy(lg).cuda()
+            mk.mk_greedy_advance(h, d_lg, d_tok, d_pos, mk.current_stream())
+            torch.cuda.synchronize()
+            got = d_tok.cpu().numpy()
+            assert got[0] == want[0] and got[1] == want[1], (call, got, want)
+            assert got[2] == 0
+            assert (d_pos.cpu().numpy() == call + 1).all()
+    finally:
+        mk.mk_destroy(h)
