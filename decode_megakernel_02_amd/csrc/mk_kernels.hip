@@ -97,8 +97,12 @@ __device__ __forceinline__ void gst(T* p, T v) {
 #define MK_KEEP 8
 #endif
 constexpr int MAXOUT = MK_MAXOUT;  // DMA units in flight per loader wave
-constexpr int NWL = NLOAD - 1;  // weight loader waves; the last loader wave gathers inputs
-static_assert(NW <= 3 * NWL, "a weight loader serves at most three compute waves");
+#ifndef MK_NGATHER
+#define MK_NGATHER 1
+#endif
+constexpr int NGATHER = MK_NGATHER;  // gather waves (instruction r is staged by gather wave r % NGATHER)
+constexpr int NWL = NLOAD - NGATHER; // weight loader waves
+static_assert(NW <= 4 * NWL, "a weight loader serves at most four compute waves");
 
 // ------------------------------------------------------------- primitives --
 
@@ -189,6 +193,7 @@ struct Ctx {
     int cu, wave, lane;
     uint32_t epoch;
     uint32_t pc;       // instruction index in this CU's queue (for error records)
+    uint32_t slot;     // buffer set of the current instruction's staged inputs
     uint32_t op;
     bool aborted;
     bool prof;         // accumulate cycle counters
@@ -271,10 +276,9 @@ struct Lds {
     LDS uint32_t* landed;   // [NW] units landed in each compute wave's ring
     LDS uint32_t* consumed; // [NW] units consumed
     LDS uint32_t* bar;      // compute-wave barrier counter
-    LDS uint32_t* gathered; // instructions of this launch whose inputs are staged
+    LDS uint32_t* ready;    // [MAX_SLOTS] r + 1 once instruction r's inputs are staged in buffer set r % nslot
     LDS uint32_t* done;     // [NW] instructions each compute wave has finished
     LDS float* ss;          // [MAX_SLOTS][MAX_BATCH] sum of squares of each x buffer's raw input rows
-    LDS uint32_t* pf_dump;  // [64] landing words of the cache-prefetch touches (never read)
     LDS float* side0;       // nslot side buffers (side_floats each): epilogue inputs staged with x buffer i
 };
 __device__ __forceinline__ Lds lds_map(LDS uint8_t* smem, CParams& p) {
@@ -286,10 +290,9 @@ __device__ __forceinline__ Lds lds_map(LDS uint8_t* smem, CParams& p) {
     m.landed = sync;
     m.consumed = sync + NW;
     m.bar = sync + 2 * NW;
-    m.gathered = sync + 2 * NW + 1;
+    m.ready = sync + 2 * NW + 1;
     m.done = sync + 2 * NW + 4;
     m.ss = (LDS float*)(sync + 3 * NW + 4);
-    m.pf_dump = sync + 64;
     m.side0 = (LDS float*)(smem + off + (size_t)p.nslot * p.xbuf_bytes + 512);
     return m;
 }
@@ -353,10 +356,6 @@ __device__ __forceinline__ void load_stream_init(const Ctx& cx, const Lds& s, Lo
 }
 
 constexpr uint32_t ISSUE_BATCH = 4;  // units issued per stream per turn
-#ifndef MK_PF_DIST
-#define MK_PF_DIST 0
-#endif
-constexpr uint32_t PF_DIST = MK_PF_DIST;  // cache prefetch distance in steps of NW units (0: off)
 
 // Issues up to `max` (<= ISSUE_BATCH) consecutive units of the stream, as many
 // as its ring has room for (re-reading the consumer's count only when the
@@ -389,7 +388,7 @@ static_assert(MK_KEEP < MK_MAXOUT, "a retire step must free at least one unit");
 #define MK_LOADER_SLEEP 2
 #endif
 
-// Streams the units of up to three compute waves (w, w + 3, w + 6) into their
+// Streams the units of up to four compute waves (w, w + NWL, ...) into their
 // rings.  DMA completes in issue order, so a FIFO of 2-bit stream ids (entry
 // i = stream of the i-th oldest outstanding unit) says whose units a vmcnt
 // step retires.  Units are retired in batches, keeping KEEP_IN_FLIGHT
@@ -402,62 +401,33 @@ __device__ __forceinline__ void loader(Ctx& cx, const Lds& s, int w0, const uint
                                        uint32_t pc1) {
     __builtin_amdgcn_s_setprio(MK_LOADER_PRIO);
     const uint32_t ru = uni((uint32_t)cx.p->ring_units);
-    LoadStream a, b, c;
-    const int w1 = w0 + NWL, w2 = w0 + 2 * NWL;
-    load_stream_init(cx, s, a, w0, uoff[(size_t)pc0 * NW + w0], uoff[(size_t)pc1 * NW + w0]);
-    load_stream_init(cx, s, b, w1, uoff[(size_t)pc0 * NW + w1], uoff[(size_t)pc1 * NW + w1]);
-    if (w2 < NW) load_stream_init(cx, s, c, w2, uoff[(size_t)pc0 * NW + w2], uoff[(size_t)pc1 * NW + w2]);
-    else load_stream_init(cx, s, c, w0, 0, 0);  // no third stream
-    // The last weight loader also prefetches the CU's packed weights (one
-    // contiguous region: its NW streams interleave unit by unit) up to
-    // PF_DIST steps of NW units ahead of its first stream, one 4-byte touch
-    // per 128-byte line, into a dump word of LDS: while the rings are full the
-    // HBM stream keeps filling the caches instead of idling.
-    const bool pf_on = PF_DIST > 0 && w0 == NWL - 1;
-    const GLB uint8_t* pf_src = nullptr;
-    uint32_t pf_k = 0, pf_end = 0, pf_ref = 0;
-    const uint32_t pf_dump = lds_addr(s.pf_dump);
-    if (pf_on) {
-        CParams& p = *cx.p;
-        uint32_t k0 = 0xffffffffu, k1 = 0;
-        for (int w = 0; w < NW; ++w) {
-            k0 = min(k0, uni(uoff[(size_t)pc0 * NW + w]));
-            k1 = max(k1, uni(uoff[(size_t)pc1 * NW + w]));
-        }
-        const uint64_t base = p.stream_base[cx.cu * NW];
-        const uint64_t base_u = ((uint64_t)uni((uint32_t)(base >> 32)) << 32) | uni((uint32_t)base);
-        pf_src = (const GLB uint8_t*)(p.wstream + base_u * UNIT_BYTES) + cx.lane * 128;
-        pf_k = k0;
-        pf_end = k1;
-        pf_ref = uni(uoff[(size_t)pc0 * NW + w0]);  // first unit of stream a
+    LoadStream st[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int w = w0 + k * NWL;
+        if (w < NW) load_stream_init(cx, s, st[k], w, uoff[(size_t)pc0 * NW + w], uoff[(size_t)pc1 * NW + w]);
+        else load_stream_init(cx, s, st[k], w0, 0, 0);  // no such stream
     }
     auto issue = [&](uint32_t sid, uint32_t max) -> uint32_t {
-        return sid == 0 ? load_stream_issue(a, ru, max)
-                        : sid == 1 ? load_stream_issue(b, ru, max) : load_stream_issue(c, ru, max);
+        return sid == 0 ? load_stream_issue(st[0], ru, max)
+             : sid == 1 ? load_stream_issue(st[1], ru, max)
+             : sid == 2 ? load_stream_issue(st[2], ru, max) : load_stream_issue(st[3], ru, max);
     };
     uint64_t fifo = 0;  // 2-bit stream id per outstanding unit, oldest in the low bits
     uint32_t out = 0, spins = 0, turn = 0;
-    while (a.done < a.n || b.done < b.n || c.done < c.n) {
+    while (st[0].done < st[0].n || st[1].done < st[1].n || st[2].done < st[2].n || st[3].done < st[3].n) {
         while (out < (uint32_t)MAXOUT) {
             const uint32_t max = MAXOUT - out < ISSUE_BATCH ? MAXOUT - out : ISSUE_BATCH;
-            uint32_t sid = turn;
-            uint32_t k = issue(sid, max);
-            if (!k) { sid = sid == 2 ? 0 : sid + 1; k = issue(sid, max); }
-            if (!k) { sid = sid == 2 ? 0 : sid + 1; k = issue(sid, max); }
-            if (!k) {
-                if (pf_on && pf_k < pf_end && pf_k < pf_ref + a.issued + PF_DIST) {
-                    __builtin_amdgcn_global_load_lds((const glb_void*)(pf_src + (size_t)pf_k * (NW * UNIT_BYTES)),
-                                                     (lds_void*)(uintptr_t)pf_dump, 4, 0, 0);
-                    ++pf_k;
-                    fifo |= 3ull << (2 * out);
-                    ++out;
-                    continue;
-                }
-                break;
+            uint32_t sid = turn, k = 0;
+#pragma unroll
+            for (int tries = 0; tries < 4 && k == 0; ++tries) {
+                k = issue(sid, max);
+                if (!k) sid = (sid + 1) & 3u;
             }
+            if (!k) break;
             fifo |= (uint64_t)(sid * (0x55u & ((1u << (2 * k)) - 1u))) << (2 * out);  // k entries of sid
             out += k;
-            turn = sid == 2 ? 0 : sid + 1;
+            turn = (sid + 1) & 3u;
         }
         if (out > 0) {
             // retire all but KEEP_IN_FLIGHT units (all of them when nothing more could be issued)
@@ -471,18 +441,19 @@ __device__ __forceinline__ void loader(Ctx& cx, const Lds& s, int w0, const uint
             const uint64_t f = k >= 32 ? fifo : fifo & ((1ull << (2 * k)) - 1ull);
             const uint64_t lo = f & 0x5555555555555555ull, hi = (f >> 1) & 0x5555555555555555ull;
             const uint32_t n1 = (uint32_t)__builtin_popcountll(lo & ~hi), n2 = (uint32_t)__builtin_popcountll(hi & ~lo);
-            const uint32_t n3 = (uint32_t)__builtin_popcountll(lo & hi);  // prefetch touches
+            const uint32_t n3 = (uint32_t)__builtin_popcountll(lo & hi);
             const uint32_t n0 = k - n1 - n2 - n3;
             fifo = k >= 32 ? 0ull : fifo >> (2 * k);
             out = keep;
-            if (n0) asm_lds_st(a.a_landed, a.done += n0);
-            if (n1) asm_lds_st(b.a_landed, b.done += n1);
-            if (n2) asm_lds_st(c.a_landed, c.done += n2);
+            if (n0) asm_lds_st(st[0].a_landed, st[0].done += n0);
+            if (n1) asm_lds_st(st[1].a_landed, st[1].done += n1);
+            if (n2) asm_lds_st(st[2].a_landed, st[2].done += n2);
+            if (n3) asm_lds_st(st[3].a_landed, st[3].done += n3);
             if (cx.prof) cx.cnt[3] += k;
             spins = 0;
         } else {
             const uint64_t t0 = cx.prof ? cycles() : 0;
-            const bool go_on = keep_waiting<MK_LOADER_SLEEP>(cx, spins, 0x10000000u | (a.done << 12) | b.done);
+            const bool go_on = keep_waiting<MK_LOADER_SLEEP>(cx, spins, 0x10000000u | (st[0].done << 12) | st[1].done);
             if (cx.prof) cx.cnt[2] += cycles() - t0;
             if (!go_on) break;
         }
@@ -932,15 +903,17 @@ __device__ __forceinline__ Inst decode_inst(const u32x4 raw) {
     return in;
 }
 
-// The gather wave's loop over instructions [pc0, pc1) of this CU's queue.
+// Gather wave g's loop over instructions pc0 + g, pc0 + g + NGATHER, ... of
+// this CU's queue: the gather waves take turns, so one wave's poll round trip
+// overlaps another's staging.
 __device__ __forceinline__ void gatherer(Ctx& cx, const Lds& s, const Step& sp, uint32_t qb, uint32_t pc0,
-                                         uint32_t pc1) {
+                                         uint32_t pc1, int g) {
     CParams& p = *cx.p;
     __builtin_amdgcn_s_setprio(MK_LOADER_PRIO);
     const CONST_AS u32x4* iq = (const CONST_AS u32x4*)(p.insts + uni(qb));
     const uint32_t nslot = uni((uint32_t)p.nslot);
-    uint32_t slot = 0;
-    for (uint32_t pc = pc0; pc < pc1; ++pc, slot = slot + 1 == nslot ? 0 : slot + 1) {
+    uint32_t slot = (uint32_t)g % nslot;
+    for (uint32_t pc = pc0 + g; pc < pc1; pc += NGATHER, slot = (slot + NGATHER) % nslot) {
         const uint32_t r = pc - pc0;
         const u32x4 raw = iq[pc];
         if (r >= nslot) {  // buffer set `slot` held instruction r - nslot: wait until every compute wave is done with it
@@ -963,7 +936,7 @@ __device__ __forceinline__ void gatherer(Ctx& cx, const Lds& s, const Step& sp, 
         gather_inst(cx, sp, in, xslot(s, p, slot), s.ss + slot * MAX_BATCH);
         if (uni(cx.aborted)) break;
         CBAR();
-        if (cx.lane == 0) lds_st(s.gathered, r + 1);  // after the staged data (LDS requests of a wave stay ordered)
+        if (cx.lane == 0) lds_st(s.ready + slot, r + 1);  // after the staged data (LDS requests of a wave stay ordered)
         if (cx.trace && cx.lane == 0) {
             GLB uint64_t* rec = (GLB uint64_t*)p.trace + (size_t)(qb + pc) * TRACE_SLOTS + 1 + TRACE_WAVE_SLOTS * NW;
             rec[0] = t0;
@@ -973,14 +946,14 @@ __device__ __forceinline__ void gatherer(Ctx& cx, const Lds& s, const Step& sp, 
     }
 }
 
-// Compute-wave side: wait until instruction r's inputs are staged.
+// Compute-wave side: wait until instruction r's inputs are staged (in buffer set cx.slot).
 __device__ __forceinline__ void wait_inputs(Ctx& cx, const Lds& s, uint32_t r) {
     const uint64_t t0 = cx.prof ? cycles() : 0;
     uint32_t spins = 0;
 #ifndef MK_INPUT_SLEEP
 #define MK_INPUT_SLEEP MK_SLEEP
 #endif
-    while (uni(lds_ld(s.gathered)) <= r)
+    while (uni(lds_ld(s.ready + cx.slot)) != r + 1)
         if (!keep_waiting<MK_INPUT_SLEEP>(cx, spins, 0x70000000u | r)) break;
     CBAR();
     if (cx.prof) cx.cnt[2] += cycles() - t0;
@@ -1363,6 +1336,7 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
     cx.aborted = false;
     cx.pc = 0;
     cx.op = 0;
+    cx.slot = 0;
     cx.prof = INSTR && p.prof != nullptr;
     cx.trace = INSTR && p.trace != nullptr;
     cx.t_in = cx.t_acq = cx.t_mid = cx.t_ring = 0;
@@ -1417,13 +1391,13 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
     __syncthreads();
 
     const uint32_t* uoff = p.unit_off + ((size_t)qb + cx.cu) * NW;
-    if (wave >= NW + NWL) {  // gather wave
+    if (wave >= NW + NWL) {  // gather waves
         cx.wave = wave;
-        gatherer(cx, s, sp, qb, pc0, pc1);
+        gatherer(cx, s, sp, qb, pc0, pc1, wave - NW - NWL);
         flush_prof(wave);
         return;
     }
-    if (wave >= NW) {  // weight loader of compute waves i, i + 3, i + 6
+    if (wave >= NW) {  // weight loader of compute waves i, i + NWL, i + 2 NWL, ...
         cx.wave = wave;
         loader(cx, s, wave - NW, uoff, pc0, pc1);
         flush_prof(wave);
@@ -1456,6 +1430,7 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
         cx.t_acq = cx.t_in = cx.t_mid = t_start;
         cx.t_ring = 0;
         const uint32_t r = pc - pc0;
+        cx.slot = slot;
         LDS float* xb = xslot(s, p, slot);
         switch (in.op) {
         case OP_ATTENTION:
