@@ -18,8 +18,7 @@ hipError_t launch_step(const Params* dev_params, int head_dim, int ncu, size_t l
                        const int32_t* positions, void* kv, float* logits, int stage, uint32_t flags,
                        hipStream_t stream);
 hipError_t set_step_kernel_lds(size_t lds_bytes);
-hipError_t launch_pack(const void* rows, uint32_t n, const uint16_t* const* mats, const uint16_t* const* gains,
-                       uint8_t* dst, hipStream_t stream);
+hipError_t launch_pack(const void* rows, uint32_t n, const uint16_t* const* mats, uint8_t* dst, hipStream_t stream);
 hipError_t launch_greedy(const float* logits, int B, int V, int32_t* tokens, int32_t* positions, uint64_t* part,
                          uint32_t* cnt, hipStream_t stream);
 }  // namespace mk
@@ -225,6 +224,9 @@ int mk_create(const mk_config* cfg, mk_handle** out) {
         hp.unit_off = dupload(h, p.unit_off);
         hp.stage_pc = dupload(h, p.stage_pc);
         hp.embed = dalloc<uint16_t>(h, (size_t)p.V * p.H);
+        hp.gain_attn = dalloc<uint16_t>(h, (size_t)p.L * p.H);
+        hp.gain_mlp = dalloc<uint16_t>(h, (size_t)p.L * p.H);
+        hp.gain_final = dalloc<uint16_t>(h, (size_t)p.H);
         // RoPE table: angle p * theta^(-2i/D) in double, cos/sin rounded to fp32
         {
             const int half = p.D / 2;
@@ -306,7 +308,6 @@ int mk_load_weights(mk_handle* h, const mk_weights* w, void* stream) {
     hipStream_t s = (hipStream_t)stream;
     void* d_rows = nullptr;
     void* d_mats = nullptr;
-    void* d_gains = nullptr;
     try {
         HIPCHK(hipSetDevice(h->cfg.device));
         std::vector<const uint16_t*> mats((size_t)p.n_mats(), nullptr);
@@ -321,36 +322,26 @@ int mk_load_weights(mk_handle* h, const mk_weights* w, void* stream) {
             mats[b + MAT_DOWN] = (const uint16_t*)w->w_down[l];
         }
         mats[p.lm_mat()] = (const uint16_t*)(p.tied ? w->embed : w->lm_head);
-        // RMSNorm gains are folded into the matrices that read the normalised
-        // vector (q/k/v: attention norm, gate/up: MLP norm, LM head: final norm)
-        std::vector<const uint16_t*> gains((size_t)p.n_mats(), nullptr);
-        for (int l = 0; l < p.L; ++l) {
-            const size_t b = (size_t)l * MATS_PER_LAYER;
-            gains[b + MAT_WQ] = gains[b + MAT_WK] = gains[b + MAT_WV] = (const uint16_t*)w->attn_norm[l];
-            gains[b + MAT_GATE] = gains[b + MAT_UP] = (const uint16_t*)w->mlp_norm[l];
-        }
-        gains[p.lm_mat()] = (const uint16_t*)w->final_norm;
         HIPCHK(hipMalloc(&d_rows, p.pack.size() * sizeof(PackRow)));
         HIPCHK(hipMalloc(&d_mats, mats.size() * sizeof(void*)));
-        HIPCHK(hipMalloc(&d_gains, gains.size() * sizeof(void*)));
         HIPCHK(hipMemcpyAsync(d_rows, p.pack.data(), p.pack.size() * sizeof(PackRow), hipMemcpyHostToDevice, s));
         HIPCHK(hipMemcpyAsync(d_mats, mats.data(), mats.size() * sizeof(void*), hipMemcpyHostToDevice, s));
-        HIPCHK(hipMemcpyAsync(d_gains, gains.data(), gains.size() * sizeof(void*), hipMemcpyHostToDevice, s));
-        HIPCHK(launch_pack(d_rows, (uint32_t)p.pack.size(), (const uint16_t* const*)d_mats,
-                           (const uint16_t* const*)d_gains, (uint8_t*)h->hp.wstream, s));
+        HIPCHK(launch_pack(d_rows, (uint32_t)p.pack.size(), (const uint16_t* const*)d_mats, (uint8_t*)h->hp.wstream, s));
         const size_t HB = (size_t)p.H * 2;
         HIPCHK(hipMemcpyAsync((void*)h->hp.embed, w->embed, (size_t)p.V * HB, hipMemcpyDeviceToDevice, s));
+        for (int l = 0; l < p.L; ++l) {
+            HIPCHK(hipMemcpyAsync((uint8_t*)h->hp.gain_attn + l * HB, w->attn_norm[l], HB, hipMemcpyDeviceToDevice, s));
+            HIPCHK(hipMemcpyAsync((uint8_t*)h->hp.gain_mlp + l * HB, w->mlp_norm[l], HB, hipMemcpyDeviceToDevice, s));
+        }
+        HIPCHK(hipMemcpyAsync((void*)h->hp.gain_final, w->final_norm, HB, hipMemcpyDeviceToDevice, s));
         HIPCHK(hipStreamSynchronize(s));
         HIPCHK(hipFree(d_rows));
         d_rows = nullptr;
         HIPCHK(hipFree(d_mats));
         d_mats = nullptr;
-        HIPCHK(hipFree(d_gains));
-        d_gains = nullptr;
     } catch (const HipError& e) {
         if (d_rows) (void)hipFree(d_rows);
         if (d_mats) (void)hipFree(d_mats);
-        if (d_gains) (void)hipFree(d_gains);
         return hip_fail(h, e);
     }
     static_assert(sizeof(PackRow) == 32, "PackRow matches the device pack record");

@@ -81,6 +81,9 @@ struct Params {
 
     // weights read in place
     const uint16_t* embed;         // [V][H] bf16 (token gather)
+    const uint16_t* gain_attn;     // [L][H]
+    const uint16_t* gain_mlp;      // [L][H]
+    const uint16_t* gain_final;    // [H]
     const float* rope;             // [max_seq][D/2][2] (cos, sin)
 
     // tagged activations: 64-bit words {low: fp32 bits, high: step epoch}

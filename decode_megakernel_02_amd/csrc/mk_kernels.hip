@@ -652,22 +652,26 @@ struct Step {  // per-launch batch inputs, lane b holds row b
 
 // Reads the n (even) tagged words at base, two adjacent words per lane per
 // 16-byte load and 128 * NB words per round, polling until every tag carries
-// this step's epoch; put(kb, v_k, v_k+1) stores pair k = kb + 2 * lane.  Buffer
-// loads keep the addresses in scalar registers; their range check returns
-// zeros past n.
+// this step's epoch; put(k, v_k, v_k+1, gain pair) stores them.  With GAIN,
+// the bf16 gain pair at gain + k is loaded alongside.  Buffer loads keep the
+// addresses in scalar registers; their range check returns zeros past n.
 constexpr uint32_t RSRC_WORD3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9)
 constexpr int CPOL_SC1 = 16;                 // device-coherent load: bypasses the non-coherent L2 copy
 
-template <int NB, class Put>
-__device__ __forceinline__ void gather_region(Ctx& cx, const uint64_t* base, int n, Put&& put) {
+template <int NB, bool GAIN, class Put>
+__device__ __forceinline__ void gather_region(Ctx& cx, const uint64_t* base, int n, const uint16_t* gain, Put&& put) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, n * 8, RSRC_WORD3);
+    __amdgpu_buffer_rsrc_t rg = rs;
+    if (GAIN) rg = __builtin_amdgcn_make_buffer_rsrc((void*)gain, (short)0, n * 2, RSRC_WORD3);
     const uint32_t ep = cx.epoch;
     for (int k0 = 0; k0 < n; k0 += 128 * NB) {
         u32x4 w[NB];
+        uint32_t g[NB];
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
             const int k = k0 + j * 128 + 2 * cx.lane;
             w[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, k * 8, 0, CPOL_SC1);
+            if (GAIN) g[j] = __builtin_amdgcn_raw_buffer_load_b32(rg, k * 2, 0, 0);
         }
         uint32_t spins = 0;
         while (true) {
@@ -687,15 +691,17 @@ __device__ __forceinline__ void gather_region(Ctx& cx, const uint64_t* base, int
             }
         }
         if (cx.trace) cx.t_acq = rtime();  // every tag current
-        // a full round needs no per-pair bounds test
+        // put(kb, ...) stores pair k = kb + 2 * lane, kb = k0 + 128 j; a full
+        // round needs no per-pair bounds test
         if (k0 + 128 * NB <= n) {
 #pragma unroll
-            for (int j = 0; j < NB; ++j) put(k0 + j * 128, __uint_as_float(w[j].x), __uint_as_float(w[j].z));
+            for (int j = 0; j < NB; ++j)
+                put(k0 + j * 128, __uint_as_float(w[j].x), __uint_as_float(w[j].z), GAIN ? g[j] : 0x3f803f80u);
         } else {
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 const int k = k0 + j * 128 + 2 * cx.lane;
-                if (k < n) put(k0 + j * 128, __uint_as_float(w[j].x), __uint_as_float(w[j].z));
+                if (k < n) put(k0 + j * 128, __uint_as_float(w[j].x), __uint_as_float(w[j].z), GAIN ? g[j] : 0x3f803f80u);
             }
         }
     }
@@ -704,24 +710,24 @@ __device__ __forceinline__ void gather_region(Ctx& cx, const uint64_t* base, int
 constexpr int GATHER_NB = 16;      // 16-byte loads per lane per polling round (2048 words)
 constexpr int GATHER_NB_ATTN = 6;  // (G + 2) * D <= 768 words
 
-// x[b][k] = raw[b][k] in the x-buffer layout (RMSNorm gains are folded into
-// the packed weights), plus zero padding up to kpad; ss[b] = sum_k raw[b][k]^2
-// when ss_out is given.
-template <class Row>
-__device__ __forceinline__ void gather_x(Ctx& cx, int B, int K, int kpad, Row&& row, LDS float* xb,
-                                         LDS float* ss_out) {
+// x[b][k] = raw[b][k] * gain[k] in the x-buffer layout, plus zero padding up
+// to kpad; ss[b] = sum_k raw[b][k]^2 when ss_out is given.
+template <bool GAIN, class Row>
+__device__ __forceinline__ void gather_x(Ctx& cx, int B, int K, int kpad, Row&& row, const uint16_t* gain,
+                                         LDS float* xb, LDS float* ss_out) {
     const int xs = (int)uni((uint32_t)cx.p->xstride);
     for (int b = 0; b < B; ++b) {
         float ss = 0.f;
         // lane l stores pairs k = k0 + 2l (k0 a multiple of 128): one base address per lane
         LDS float* xl = xb + xidx(xs, b, 2 * cx.lane);
-        gather_region<GATHER_NB>(cx, row(b), K, [&](int kb, float v0, float v1) {
-            ss = fmaf(v0, v0, ss);
-            ss = fmaf(v1, v1, ss);
-            LDS float* x = xl + (kb >> 1);  // k, k+1 adjacent
-            x[0] = v0;
-            x[1] = v1;
-        });
+        gather_region<GATHER_NB, GAIN>(cx, row(b), K, gain,
+                                      [&](int kb, float v0, float v1, uint32_t gp) {
+                                          ss = fmaf(v0, v0, ss);
+                                          ss = fmaf(v1, v1, ss);
+                                          LDS float* x = xl + (kb >> 1);  // k, k+1 adjacent
+                                          x[0] = v0 * bf_lo(gp);
+                                          x[1] = v1 * bf_hi(gp);
+                                      });
         for (int k = K + cx.lane; k < kpad; k += 64) xb[xidx(xs, b, k)] = 0.f;
         if (ss_out) {
             ss = wave_sum(ss);
@@ -732,7 +738,8 @@ __device__ __forceinline__ void gather_x(Ctx& cx, int B, int K, int kpad, Row&& 
 
 // Embedding rows (bf16, written before the launch: no tags) as the input of
 // the first layer's RMSNorm.
-__device__ __forceinline__ void gather_embed(Ctx& cx, const Step& sp, int kpad, LDS float* xb, LDS float* ss_out) {
+__device__ __forceinline__ void gather_embed(Ctx& cx, const Step& sp, int kpad, const uint16_t* gain, LDS float* xb,
+                                             LDS float* ss_out) {
     CParams& p = *cx.p;
     const int H = p.H, xs = (int)uni((uint32_t)p.xstride);
     for (int b = 0; b < p.B; ++b) {
@@ -740,11 +747,12 @@ __device__ __forceinline__ void gather_embed(Ctx& cx, const Step& sp, int kpad, 
         const uint32_t* row = (const uint32_t*)(p.embed + (size_t)tok * H);  // H even: bf16 pairs
         float ss = 0.f;
         for (int k0 = 0; k0 < H; k0 += 128 * GATHER_NB) {
-            uint32_t e[GATHER_NB];
+            uint32_t e[GATHER_NB], g[GATHER_NB];
 #pragma unroll
             for (int j = 0; j < GATHER_NB; ++j) {
                 const int k = k0 + j * 128 + 2 * cx.lane;
                 e[j] = k < H ? gld(row + k / 2) : 0u;
+                g[j] = k < H ? gld((const uint32_t*)(gain + k)) : 0u;
             }
 #pragma unroll
             for (int j = 0; j < GATHER_NB; ++j) {
@@ -754,8 +762,8 @@ __device__ __forceinline__ void gather_embed(Ctx& cx, const Step& sp, int kpad, 
                     ss = fmaf(v0, v0, ss);
                     ss = fmaf(v1, v1, ss);
                     LDS float* x = xb + xidx(xs, b, k);
-                    x[0] = v0;
-                    x[1] = v1;
+                    x[0] = v0 * bf_lo(g[j]);
+                    x[1] = v1 * bf_hi(g[j]);
                 }
             }
         }
@@ -828,30 +836,34 @@ __device__ __forceinline__ void gather_inst(Ctx& cx, const Step& sp, const Inst&
     case OP_RMS_QKV_ROPE:
     case OP_RMS_LM_HEAD: {
         const int src_layer = in.op == OP_RMS_LM_HEAD ? p.L : l;  // residual stream entering this layer
+        const uint16_t* gain = in.op == OP_RMS_LM_HEAD ? p.gain_final : p.gain_attn + (size_t)l * H;
         const int kpad = p.ku_h * UNIT_ELEMS;
         if (src_layer == 0) {
-            gather_embed(cx, sp, kpad, xb, ss);
+            gather_embed(cx, sp, kpad, gain, xb, ss);
         } else {
             const uint64_t* src = p.hout + (size_t)(src_layer - 1) * B * H;
-            gather_x(cx, B, H, kpad, [&](int b) { return src + (size_t)b * H; }, xb, ss);
+            gather_x<true>(cx, B, H, kpad, [&](int b) { return src + (size_t)b * H; }, gain, xb, ss);
         }
         break;
     }
     case OP_RMS_UP_GATE: {
         const uint64_t* src = p.hmid + (size_t)l * B * H;
-        gather_x(cx, B, H, p.ku_h * UNIT_ELEMS, [&](int b) { return src + (size_t)b * H; }, xb, ss);
+        gather_x<true>(cx, B, H, p.ku_h * UNIT_ELEMS, [&](int b) { return src + (size_t)b * H; },
+                       p.gain_mlp + (size_t)l * H, xb, ss);
         break;
     }
     case OP_O_PROJ_RES: {
         const int K = p.Hq * p.D;
         const uint64_t* src = p.attn + (size_t)l * B * K;
-        gather_x(cx, B, K, p.ku_q * UNIT_ELEMS, [&](int b) { return src + (size_t)b * K; }, xb, nullptr);
+        gather_x<false>(cx, B, K, p.ku_q * UNIT_ELEMS, [&](int b) { return src + (size_t)b * K; }, nullptr, xb,
+                        nullptr);
         break;
     }
     case OP_DOWN_RES: {
         const int c0 = p.chunk_begin[in.a], K = p.chunk_begin[in.a + 1] - c0;
         const uint64_t* src = p.act + (size_t)l * B * p.F + c0;
-        gather_x(cx, B, K, p.ku_f * UNIT_ELEMS, [&](int b) { return src + (size_t)b * p.F; }, xb, nullptr);
+        gather_x<false>(cx, B, K, p.ku_f * UNIT_ELEMS, [&](int b) { return src + (size_t)b * p.F; }, nullptr, xb,
+                        nullptr);
         break;
     }
     case OP_ATTENTION: {
@@ -859,7 +871,7 @@ __device__ __forceinline__ void gather_inst(Ctx& cx, const Step& sp, const Inst&
         const int b = in.a, g = in.b, D = p.D, nq = p.G * D;
         const uint64_t* src = p.qkv + (((size_t)l * B + b) * p.Hkv + g) * (size_t)(p.G + 2) * D;
         const float sc = p.inv_sqrt_d;
-        gather_region<GATHER_NB_ATTN>(cx, src, nq + 2 * D, [&](int kb, float v0, float v1) {
+        gather_region<GATHER_NB_ATTN, false>(cx, src, nq + 2 * D, nullptr, [&](int kb, float v0, float v1, uint32_t) {
             const int i = kb + 2 * cx.lane;
             const float f = i < nq ? sc : 1.f;  // nq even: a pair never straddles q and k
             xb[i] = v0 * f;
@@ -870,7 +882,7 @@ __device__ __forceinline__ void gather_inst(Ctx& cx, const Step& sp, const Inst&
     default: {  // OP_ATTN_REDUCE: the n_split partials (m, l, o[D]) of (row, head)
         const int b = in.a, head = in.b, W = p.D + 2;
         const uint64_t* src = p.part + (((size_t)l * B + b) * p.Hq + head) * p.n_split * W;
-        gather_region<GATHER_NB>(cx, src, p.n_split * W, [&](int kb, float v0, float v1) {
+        gather_region<GATHER_NB, false>(cx, src, p.n_split * W, nullptr, [&](int kb, float v0, float v1, uint32_t) {
                                            const int i = kb + 2 * cx.lane;
                                            xb[i] = v0;
                                            xb[i + 1] = v1;
@@ -1479,23 +1491,18 @@ struct PackRowDev {
     uint64_t dst_unit;
 };
 
-// One workgroup per stream row: dst[unit .. unit + kunits) = src row slice,
-// zero padded.  Rows of a matrix that reads an RMSNorm output get the norm's
-// gain folded in: w[k] * g[k], rounded to bf16 (gains[mat] is null otherwise).
+// One workgroup per stream row: dst[unit .. unit + kunits) = src row slice, zero padded.
 __global__ void __launch_bounds__(256) mk_pack_kernel(const PackRowDev* rows, uint32_t n, const uint16_t* const* mats,
-                                                      const uint16_t* const* gains, uint8_t* dst) {
+                                                      uint8_t* dst) {
     for (uint32_t r = blockIdx.x; r < n; r += gridDim.x) {
         const PackRowDev pr = rows[r];
         const uint16_t* src = mats[pr.mat] + (size_t)pr.row * pr.src_cols + pr.k0;
-        const uint16_t* gain = gains[pr.mat];
         const uint32_t n_el = pr.kunits * UNIT_ELEMS;
         for (uint32_t e = threadIdx.x; e < n_el; e += blockDim.x) {
             // element e lies in the row's unit e / 512, and consecutive units of a
             // stream are NW units apart in the packed buffer
             uint16_t* out = (uint16_t*)(dst + (pr.dst_unit + (uint64_t)(e / UNIT_ELEMS) * NW) * UNIT_BYTES);
-            uint16_t v = 0;
-            if (e < pr.klen) v = gain ? f2bf(bf2f(src[e]) * bf2f(gain[pr.k0 + e])) : src[e];
-            out[e % UNIT_ELEMS] = v;
+            out[e % UNIT_ELEMS] = e < pr.klen ? src[e] : (uint16_t)0;
         }
     }
 }
@@ -1616,11 +1623,10 @@ hipError_t set_step_kernel_lds(size_t lds_bytes) {
     return hipSuccess;
 }
 
-hipError_t launch_pack(const void* rows, uint32_t n, const uint16_t* const* mats, const uint16_t* const* gains,
-                       uint8_t* dst, hipStream_t stream) {
+hipError_t launch_pack(const void* rows, uint32_t n, const uint16_t* const* mats, uint8_t* dst, hipStream_t stream) {
     if (n == 0) return hipSuccess;
     const uint32_t grid = n < 65536 ? n : 65536;
-    hipLaunchKernelGGL(mk_pack_kernel, dim3(grid), dim3(256), 0, stream, (const PackRowDev*)rows, n, mats, gains, dst);
+    hipLaunchKernelGGL(mk_pack_kernel, dim3(grid), dim3(256), 0, stream, (const PackRowDev*)rows, n, mats, dst);
     return hipGetLastError();
 }
 

@@ -102,11 +102,7 @@ int mk_create(const mk_config* cfg, mk_handle** out);
 
 /* Copies the caller's weights (device pointers, see mk_weights) into the
  * library's packed layout on `stream`, then synchronises `stream`; the caller
- * may free its tensors afterwards.  May be called again to replace weights.
- * Each RMSNorm gain is folded into the matrices that read the normalised
- * vector (q/k/v rows: attention norm; gate/up rows: MLP norm; LM head: final
- * norm): the packed element is bf16(w[k] * g[k]), rounded to nearest even,
- * which equals RMSNorm-then-multiply up to that one rounding.              */
+ * may free its tensors afterwards.  May be called again to replace weights. */
 int mk_load_weights(mk_handle* h, const mk_weights* w, void* stream);
 
 /* Bytes of the caller-owned KV cache: bf16 [L][2 (K,V)][B][Hkv][max_seq][D],
