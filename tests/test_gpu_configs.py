@@ -70,3 +70,12 @@ def test_uneven_rows_per_wave(n_chunks):
     shape = dataclasses.replace(synth.LLAMA_1B, n_layers=2, vocab=4096)
     weights = synth.make_weights(shape)
     run_and_compare(shape, weights, 1, [64], 2, f"llama1b-dims 2 layers, {n_chunks} chunks", n_chunks=n_chunks)
+
+
+def test_llama1b_dims_nonunit_norm_gains():
+    """1B dimensions (2 layers) with RMSNorm gains 1 + N(0, 0.3): the folded
+    gains of q/k/v, gate/up and the tied LM head against the oracle."""
+    shape = dataclasses.replace(synth.LLAMA_1B, n_layers=2, vocab=4096)
+    weights = synth.make_weights(shape, gain_std=0.3)
+    stats = run_and_compare(shape, weights, 1, [64], 2, "llama1b-dims 2 layers, gains 1 + N(0, 0.3)")
+    assert stats["max_abs"] < 1e-3  # fp32 path: ~1e-5; folded-gain rounding gave ~2e-2

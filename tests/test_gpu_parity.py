@@ -15,9 +15,10 @@ from tests import helpers as H
 pytestmark = pytest.mark.gpu
 
 
-def tiny_prefill_run(multikernel: bool, n_cus: int = 0, n_splits: int = 0, batch: int = 1, seed: int = 1234):
+def tiny_prefill_run(multikernel: bool, n_cus: int = 0, n_splits: int = 0, batch: int = 1, seed: int = 1234,
+                     gain_std: float = 0.0):
     w_shape = synth.TINY
-    weights = synth.make_weights(w_shape, seed=seed)
+    weights = synth.make_weights(w_shape, seed=seed, gain_std=gain_std)
     wl = synth.WORKLOADS["tiny_b1_p32"]
     prompt = synth.make_prompts(w_shape.vocab, batch, wl.prompt)
     max_seq = wl.prompt + wl.decode
@@ -47,6 +48,22 @@ def test_tiny_prefill_and_greedy_decode_matches_oracle(multikernel):
     stats = H.compare(run, ref, "tiny")
     print("tiny", "multikernel" if multikernel else "megakernel", stats)
     assert stats["tokens_checked"] > 0
+
+
+@pytest.mark.parametrize("gain_std", [0.1, 0.5])
+@pytest.mark.parametrize("multikernel", [False, True], ids=["megakernel", "multikernel"])
+def test_tiny_nonunit_norm_gains(multikernel, gain_std):
+    """RMSNorm gains 1 + N(0, gain_std) on every norm: the library folds them
+    into the packed weights (one extra bf16 rounding per weight); parity with
+    the oracle, which applies them to the normalised vector, must still hold."""
+    weights, run, kv, max_seq = tiny_prefill_run(multikernel, gain_std=gain_std)
+    ref = H.oracle_replay(synth.TINY, weights, 1, max_seq, run)
+    stats = H.compare(run, ref, f"tiny gains {gain_std}")
+    print("tiny gains", gain_std, "multikernel" if multikernel else "megakernel", stats)
+    assert stats["tokens_checked"] > 0
+    # the fp32 path lands within ~1e-5 of the oracle here; an extra rounding
+    # step (such as folding the gains into the bf16 weights) shows up as ~5e-3
+    assert stats["max_abs"] < 1e-3
 
 
 def test_tiny_kv_cache_matches_oracle_cache():
