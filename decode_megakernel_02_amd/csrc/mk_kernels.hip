@@ -528,6 +528,7 @@ __device__ __forceinline__ float wait_word(Ctx& cx, const uint64_t* p) {
         if (!keep_waiting(cx, spins, 0x40000000u)) break;
         if (tag_of(w) != cx.epoch) w = ld_tag(p);
     }
+    vm_drain();  // leaves no load tracked past this (rarely taken) path
     return val_of(w);
 }
 
