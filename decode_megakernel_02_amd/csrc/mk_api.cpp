@@ -273,8 +273,6 @@ int mk_create(const mk_config* cfg, mk_handle** out) {
         HIPCHK(hipMemset(hp.epoch, 0, (size_t)ncu * 4));
         hp.error = dalloc<uint32_t>(h, 8);
         HIPCHK(hipMemset(hp.error, 0, 32));
-        hp.amax = dalloc<uint64_t>(h, (size_t)ncu * MAX_BATCH * 2);
-        HIPCHK(hipMemset(hp.amax, 0, (size_t)ncu * MAX_BATCH * 2 * 8));
         h->greedy_part = dalloc<uint64_t>(h, (size_t)B * GREEDY_BLOCKS);
         h->greedy_cnt = dalloc<uint32_t>(h, (size_t)B);
         HIPCHK(hipMemset(h->greedy_cnt, 0, (size_t)B * 4));
@@ -368,16 +366,6 @@ int mk_decode_step(mk_handle* h, const int32_t* tokens, const int32_t* positions
     if (rc != MK_OK) return rc;
     hipError_t e = launch_step(h->dparams, h->hp.D, h->hp.ncu, h->lds_bytes, tokens, positions, kv_cache, logits, -1,
                                KF_BUMP_EPOCH | instr_flag(h), (hipStream_t)stream);
-    if (e != hipSuccess) return hip_fail(h, HipError{e, "mk_step_kernel launch"});
-    return MK_OK;
-}
-
-int mk_decode_step_greedy(mk_handle* h, int32_t* tokens, int32_t* positions, void* kv_cache, float* logits,
-                          void* stream) {
-    int rc = step_args_ok(h, tokens, positions, kv_cache, logits);
-    if (rc != MK_OK) return rc;
-    hipError_t e = launch_step(h->dparams, h->hp.D, h->hp.ncu, h->lds_bytes, tokens, positions, kv_cache, logits, -1,
-                               KF_BUMP_EPOCH | KF_GREEDY | instr_flag(h), (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(h, HipError{e, "mk_step_kernel launch"});
     return MK_OK;
 }

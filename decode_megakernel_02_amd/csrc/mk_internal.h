@@ -99,7 +99,6 @@ struct Params {
 
     uint64_t* prof;   // [ncu][NW + NLOAD][8] cycle counters, or null
     uint64_t* trace;  // [total instructions][TRACE_SLOTS] timeline records, or null
-    uint64_t* amax;   // [ncu][MAX_BATCH][2] tagged (value, index) of each CU's LM-head rows (greedy steps)
     uint32_t* epoch;  // [ncu] per-workgroup step counter
     uint32_t* error;  // [8] device error record (code, wg, pc, op, wave, detail), abort flag at [7]
 };
@@ -107,7 +106,6 @@ struct Params {
 // Kernel launch flags.
 constexpr uint32_t KF_BUMP_EPOCH = 1u;  // last launch of a step: advance the per-workgroup epoch
 constexpr uint32_t KF_INSTRUMENTED = 2u;  // run the kernel build that records profile counters / timelines
-constexpr uint32_t KF_GREEDY = 4u;        // also pick the next tokens (argmax) and advance the positions
 constexpr int PROF_SLOTS = 8;          // counters per wave
 // Timeline record per instruction (100 MHz real-time clock): [0] op | layer << 8 |
 // a << 16 | b << 32 | cu << 48, then per compute wave w at [1 + 6w]: start,

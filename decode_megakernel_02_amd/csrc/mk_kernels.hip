@@ -640,7 +640,6 @@ struct Step {  // per-launch batch inputs, lane b holds row b
     const int32_t* positions;
     uint16_t* kv;
     float* logits;
-    bool greedy;  // pick the next tokens on device (written over tokens / positions at the end)
 };
 
 // ------------------------------------------------------------ gather wave --
@@ -745,7 +744,7 @@ __device__ __forceinline__ void gather_embed(Ctx& cx, const Step& sp, int kpad, 
     CParams& p = *cx.p;
     const int H = p.H, xs = (int)uni((uint32_t)p.xstride);
     for (int b = 0; b < p.B; ++b) {
-        const int tok = __builtin_amdgcn_readlane(sp.tok, b);
+        const int tok = gld(sp.tokens + b);
         const uint32_t* row = (const uint32_t*)(p.embed + (size_t)tok * H);  // H even: bf16 pairs
         float ss = 0.f;
         for (int k0 = 0; k0 < H; k0 += 128 * GATHER_NB) {
@@ -813,13 +812,13 @@ __device__ __forceinline__ void gather_side(Ctx& cx, const Step& sp, const Inst&
     if (in.op == OP_RMS_QKV_ROPE) {
         const int D = p.D;
         for (int b = 0; b < B; ++b) {
-            const float* rope = p.rope + (size_t)__builtin_amdgcn_readlane(sp.pos, b) * D;
+            const float* rope = p.rope + (size_t)gld(sp.positions + b) * D;
             for (int i = cx.lane; i < D; i += 64) sd[b * D + i] = gld(rope + i);
         }
     } else if (in.op == OP_O_PROJ_RES) {
         for (int b = 0; b < B; ++b) {
             if (l == 0) {
-                const uint16_t* e = p.embed + (size_t)__builtin_amdgcn_readlane(sp.tok, b) * H + rg0;
+                const uint16_t* e = p.embed + (size_t)gld(sp.tokens + b) * H + rg0;
                 for (int j = cx.lane; j < nrg; j += 64) sd[b * nrg + j] = bf2f(gld(e + j));
             } else {
                 gather_words(cx, p.hout + ((size_t)(l - 1) * B + b) * H + rg0, nrg, sd + b * nrg);
@@ -963,68 +962,6 @@ __device__ __forceinline__ void wait_inputs(Ctx& cx, const Lds& s, uint32_t r) {
     mark_inputs(cx);
 }
 
-struct ArgMax {
-    float v;
-    int i;
-};
-__device__ __forceinline__ void argmax_take(ArgMax& a, float v, int i) {
-    if (v > a.v || (v == a.v && i < a.i)) {
-        a.v = v;
-        a.i = i;
-    }
-}
-
-// Greedy selection inside the step (LM-head epilogue).  The waves of a CU
-// merge their best rows in LDS (the instruction's x buffer, free once every
-// wave has passed the barrier: the gather wave reuses it only after all of
-// them report done); wave 0 stores the CU's (value, index) pair as two tagged
-// words.  CU 0 then waits for every CU's pair, reduces them (lowest index
-// among equal maxima, NaN never wins, no candidate gives token 0) and writes
-// the next tokens and positions over this step's inputs: every workgroup read
-// those at its start, and every CU's pair is stored after its last
-// instruction, so nothing reads them again in this step.
-__device__ __forceinline__ void lm_argmax(Ctx& cx, const Lds& s, const Step& sp, LDS float* xb, ArgMax am,
-                                          uint32_t& seq) {
-    CParams& p = *cx.p;
-    const int B = p.B;
-    LDS float* sv = xb;                     // [NW][MAX_BATCH] values
-    LDS int* si = (LDS int*)(xb + NW * MAX_BATCH);  // [NW][MAX_BATCH] indices
-    cbar(cx, s, seq);                       // every wave is done reading xb
-    if (cx.lane < B) {
-        sv[cx.wave * MAX_BATCH + cx.lane] = am.v;
-        si[cx.wave * MAX_BATCH + cx.lane] = am.i;
-    }
-    cbar(cx, s, seq);
-    if (cx.wave != 0 || cx.aborted) return;
-    ArgMax cu_best{-__builtin_inff(), 0x7fffffff};
-    if (cx.lane < B)
-        for (int w = 0; w < NW; ++w) argmax_take(cu_best, sv[w * MAX_BATCH + cx.lane], si[w * MAX_BATCH + cx.lane]);
-    uint64_t* mine = p.amax + ((size_t)cx.cu * MAX_BATCH) * 2;
-    if (cx.lane < B) {
-        st_tag(mine + 2 * cx.lane, cu_best.v, cx.epoch);
-        st_tag(mine + 2 * cx.lane + 1, __int_as_float(cu_best.i), cx.epoch);
-    }
-    if (cx.cu != 0) return;
-    const int ncu = p.ncu, V = p.V;
-    for (int b = 0; b < B; ++b) {
-        ArgMax best{-__builtin_inff(), 0x7fffffff};
-        for (int c0 = 0; c0 < ncu; c0 += 64) {
-            const int c = c0 + cx.lane;
-            // CUs whose LM-head tile is empty store no pair
-            const bool has = c < ncu && (long long)V * (c + 1) / ncu > (long long)V * c / ncu;
-            const uint64_t* w = p.amax + ((size_t)(has ? c : 0) * MAX_BATCH + b) * 2;
-            const float v = has ? wait_word(cx, w) : -__builtin_inff();
-            const int i = has ? __float_as_int(wait_word(cx, w + 1)) : 0x7fffffff;
-            argmax_take(best, v, i);
-        }
-        for (int off = 32; off >= 1; off >>= 1) argmax_take(best, __shfl_xor(best.v, off), __shfl_xor(best.i, off));
-        if (cx.lane == 0 && !cx.aborted) {
-            ((int32_t*)sp.tokens)[b] = best.i == 0x7fffffff ? 0 : best.i;
-            ((int32_t*)sp.positions)[b] = __builtin_amdgcn_readlane(sp.pos, b) + 1;
-        }
-    }
-}
-
 // ------------------------------------------------------------ GEMV ops ------
 
 // Down-projection partial sums of a wave's first DREG row-groups stay in
@@ -1039,7 +976,7 @@ struct DownAcc {
 // KU == 0: general path.
 template <int KU>
 __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint32_t r, uint32_t slot, const Inst& in,
-                                        LDS float* xb, const Step& sp, DownAcc& da, uint32_t& seq) {
+                                        LDS float* xb, const Step& sp, DownAcc& da) {
     CParams& p = *cx.p;
     const int B = p.B, H = p.H, l = in.layer;
     const int ku = in.op == OP_O_PROJ_RES ? p.ku_q : in.op == OP_DOWN_RES ? p.ku_f : p.ku_h;
@@ -1068,7 +1005,6 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
     const int b = lane_row ? cx.lane : 0;
     const int nrg = (int)in.nrg;
     const LDS float* sd = p.side_floats ? sslot(s, p, slot) : nullptr;  // staged epilogue inputs
-    ArgMax am{-__builtin_inff(), 0x7fffffff};  // greedy: best LM-head row of this wave (lane b: batch row b)
     for (uint32_t ri = 0;; ++ri) {
         const uint32_t i = cx.wave + ri * NW;
         if (i >= in.nrg) break;
@@ -1164,15 +1100,12 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
         }
         default: {  // OP_RMS_LM_HEAD
             dot1(o);
-            const float lg = o.mine[0] * scale;
-            if (lane_row) gst(sp.logits + (size_t)b * p.V + rg, lg);
-            if (sp.greedy && lane_row) argmax_take(am, lg, (int)rg);
+            if (lane_row) gst(sp.logits + (size_t)b * p.V + rg, o.mine[0] * scale);
             break;
         }
         }
         if (cx.aborted) return;
     }
-    if (in.op == OP_RMS_LM_HEAD && sp.greedy) lm_argmax(cx, s, sp, xb, am, seq);
     mark_mid(cx);
 }
 
@@ -1229,7 +1162,7 @@ __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& 
     constexpr int NH = D / 64;       // 64-dim halves
     CParams& p = *cx.p;
     const int B = p.B, G = p.G, l = in.layer, b = in.a, g = in.b, split = (int)in.rg0;
-    const int pos = __builtin_amdgcn_readlane(sp.pos, b);
+    const int pos = gld(sp.positions + b);
     const int S = pos + 1;
     const int j0 = (int)((long long)split * S / p.n_split), j1 = (int)((long long)(split + 1) * S / p.n_split);
     LDS float* qs = xb;              // [G][D], pre-scaled by 1/sqrt(D)
@@ -1428,7 +1361,6 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
     sp.logits = logits;
     sp.tok = 0;
     sp.pos = 0;
-    sp.greedy = (flags & KF_GREEDY) != 0;
     {
         int bad = 0;
         uint32_t detail = 0;
@@ -1509,10 +1441,10 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
         case OP_ATTN_REDUCE: op_reduce(cx, s, r, in, xb); break;
         default: {
             const int ku = in.op == OP_O_PROJ_RES ? p.ku_q : in.op == OP_DOWN_RES ? p.ku_f : p.ku_h;
-            if (p.B != 1) op_gemv<0>(cx, s, st, r, slot, in, xb, sp, da, seq);
-            else if (ku == 4) op_gemv<4>(cx, s, st, r, slot, in, xb, sp, da, seq);
-            else if (ku == 2) op_gemv<2>(cx, s, st, r, slot, in, xb, sp, da, seq);
-            else op_gemv<0>(cx, s, st, r, slot, in, xb, sp, da, seq);
+            if (p.B != 1) op_gemv<0>(cx, s, st, r, slot, in, xb, sp, da);
+            else if (ku == 4) op_gemv<4>(cx, s, st, r, slot, in, xb, sp, da);
+            else if (ku == 2) op_gemv<2>(cx, s, st, r, slot, in, xb, sp, da);
+            else op_gemv<0>(cx, s, st, r, slot, in, xb, sp, da);
             break;
         }
         }
@@ -1585,6 +1517,16 @@ __global__ void __launch_bounds__(256) mk_pack_kernel(const PackRowDev* rows, ui
 // pairs and writes the token.  The counter is reset by that last workgroup,
 // so the next call starts from zero.
 constexpr int GREEDY_THREADS = 256;
+struct ArgMax {
+    float v;
+    int i;
+};
+__device__ __forceinline__ void argmax_take(ArgMax& a, float v, int i) {
+    if (v > a.v || (v == a.v && i < a.i)) {
+        a.v = v;
+        a.i = i;
+    }
+}
 __device__ __forceinline__ ArgMax argmax_block(ArgMax a, ArgMax* sh) {
     for (int off = 32; off >= 1; off >>= 1) argmax_take(a, __shfl_xor(a.v, off), __shfl_xor(a.i, off));
     const int t = threadIdx.x;

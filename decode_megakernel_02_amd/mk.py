@@ -54,7 +54,7 @@ class MkScheduleInfo(ctypes.Structure):
 
 EXPORTS = ["mk_create", "mk_load_weights", "mk_kv_cache_bytes", "mk_decode_step", "mk_decode_step_multikernel",
            "mk_destroy", "mk_status_string", "mk_last_error", "mk_get_device_error", "mk_get_profile",
-           "mk_schedule_inspect", "mk_get_trace", "mk_greedy_advance", "mk_decode_step_greedy"]
+           "mk_schedule_inspect", "mk_get_trace", "mk_greedy_advance"]
 MK_FLAG_PROFILE = 1
 MK_FLAG_TRACE = 2
 TRACE_SLOTS = 52
@@ -78,7 +78,6 @@ def lib():
         L.mk_kv_cache_bytes.restype = ctypes.c_size_t
         L.mk_decode_step.argtypes = [H, _P, _P, _P, _P, _P]
         L.mk_decode_step_multikernel.argtypes = [H, _P, _P, _P, _P, _P]
-        L.mk_decode_step_greedy.argtypes = [H, _P, _P, _P, _P, _P]
         L.mk_destroy.argtypes = [H]
         L.mk_status_string.argtypes = [ctypes.c_int]
         L.mk_status_string.restype = ctypes.c_char_p
@@ -89,8 +88,7 @@ def lib():
         L.mk_get_profile.argtypes = [H, _P, ctypes.c_size_t]
         L.mk_get_trace.argtypes = [H, _P, ctypes.c_size_t]
         L.mk_greedy_advance.argtypes = [H, _P, _P, _P, _P]
-        for name in ["mk_create", "mk_load_weights", "mk_decode_step", "mk_decode_step_multikernel",
-                     "mk_decode_step_greedy", "mk_destroy",
+        for name in ["mk_create", "mk_load_weights", "mk_decode_step", "mk_decode_step_multikernel", "mk_destroy",
                      "mk_get_device_error", "mk_schedule_inspect", "mk_get_profile", "mk_get_trace",
                      "mk_greedy_advance"]:
             getattr(L, name).restype = ctypes.c_int
@@ -163,12 +161,6 @@ def mk_load_weights(handle, weights: Dict[str, object], stream: Optional[int] = 
 
 def mk_decode_step(handle, tokens, positions, kv_cache, logits, stream: Optional[int] = None):
     _check(lib().mk_decode_step(handle, _ptr(tokens), _ptr(positions), _ptr(kv_cache), _ptr(logits), stream), handle)
-
-
-def mk_decode_step_greedy(handle, tokens, positions, kv_cache, logits, stream: Optional[int] = None):
-    """One step plus on-device greedy selection: tokens / positions are overwritten with the next inputs."""
-    _check(lib().mk_decode_step_greedy(handle, _ptr(tokens), _ptr(positions), _ptr(kv_cache), _ptr(logits), stream),
-           handle)
 
 
 def mk_decode_step_multikernel(handle, tokens, positions, kv_cache, logits, stream: Optional[int] = None):

@@ -129,18 +129,6 @@ int mk_decode_step(mk_handle* h, const int32_t* tokens, const int32_t* positions
 int mk_decode_step_multikernel(mk_handle* h, const int32_t* tokens, const int32_t* positions,
                                void* kv_cache, float* logits, void* stream);
 
-/* mk_decode_step followed by greedy selection inside the same launch: the
- * step writes logits and the KV rows as mk_decode_step does, then overwrites
- * tokens[b] with argmax_v logits[b][v] and positions[b] with positions[b] + 1
- * (the next step's inputs), with mk_greedy_advance's rules (lowest index
- * among equal maxima, NaN never wins, an all-NaN row yields token 0).  Each
- * CU reduces its LM-head rows and CU 0 merges the per-CU results; this is the
- * on-device greedy step of the Gemma TPU megakernel page's decode loop
- * (withhopper.com, "Megakernels for Gemma 4") and removes the separate
- * selection launch.  Invalid inputs: as mk_decode_step (nothing is written). */
-int mk_decode_step_greedy(mk_handle* h, int32_t* tokens, int32_t* positions, void* kv_cache, float* logits,
-                          void* stream);
-
 /* Greedy selection after a step (outside the step kernel): one launch on
  * `stream` that sets tokens[b] = argmax_v logits[b][v] (the lowest index among
  * equal maxima) and positions[b] += 1 for every batch row, so that back-to-back

@@ -61,40 +61,3 @@ def test_greedy_repeated_calls_and_nan():
             assert (d_pos.cpu().numpy() == call + 1).all()
     finally:
         mk.mk_destroy(h)
-
-
-@pytest.mark.parametrize("name,batch", [("tiny", 1), ("tiny", 3), ("llama1b-dims", 2)])
-def test_fused_greedy_step_matches_separate_selection(name, batch):
-    """mk_decode_step_greedy (selection inside the step) against mk_decode_step
-    followed by mk_greedy_advance, over several steps from the same state:
-    identical logits, tokens and positions at every step."""
-    import dataclasses
-    import torch
-    from tests import helpers as H
-    shape = synth.TINY if name == "tiny" else dataclasses.replace(synth.LLAMA_1B, n_layers=2, vocab=4096)
-    weights = synth.make_weights(shape)
-    P, steps = 24, 6
-    max_seq = P + steps + 2
-    kv0 = synth.make_kv_cache(shape, batch, max_seq, P)
-    first = synth.make_first_tokens(shape.vocab, batch)
-    decs = [H.GpuDecoder(shape, weights, batch, max_seq, kv_init=kv0) for _ in range(2)]
-    try:
-        from decode_megakernel_02_amd import mk
-        s = mk.current_stream()
-        for d in decs:
-            d.tokens.copy_(torch.as_tensor(first))
-            d.positions.fill_(P)
-        for i in range(steps):
-            a, b = decs
-            mk.mk_decode_step(a.h, a.tokens, a.positions, a.kv, a.logits, s)
-            mk.mk_greedy_advance(a.h, a.logits, a.tokens, a.positions, s)
-            mk.mk_decode_step_greedy(b.h, b.tokens, b.positions, b.kv, b.logits, s)
-            torch.cuda.synchronize()
-            assert mk.mk_get_device_error(b.h) is None
-            assert torch.equal(a.logits, b.logits), i
-            assert torch.equal(a.tokens, b.tokens), (i, a.tokens, b.tokens)
-            assert torch.equal(a.positions, b.positions), i
-            assert int(b.positions[0]) == P + i + 1
-    finally:
-        for d in decs:
-            d.close()
