@@ -269,6 +269,23 @@ def main():
     kern_mk = statistics.mean(a.elapsed_time(b) * 1e3 for a, b in evm)
     log(f"multikernel: {KM} steps in {wall_mk * 1e3:.1f} ms")
 
+    # ---- the device's sustained read rate (4 GiB, past the memory-side cache), best of 5
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    probe_buf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    probe_buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    probe_gbps = 0.0
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(cur)
+        mk.mk_read_probe(probe_buf, sink, ncu, stream)
+        e1.record(cur)
+        torch.cuda.synchronize()
+        probe_gbps = max(probe_gbps, probe_buf.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del probe_buf
+    torch.cuda.empty_cache()
+    log(f"read probe: {probe_gbps:.0f} GB/s")
+
     # ---- roofline of the dominant (only) kernel
     keys = R.mean_keys(P, W, K)  # the event-timed pass covers steps W .. W+K-1
     bytes_step = R.step_bytes(shape, B, keys)
@@ -296,6 +313,8 @@ def main():
                    "kernel_launches_per_step": 1},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": peak, "unit": "GB/s", "frac": achieved / peak,
                      "traffic": traffic},
+        "hbm_read_probe_GBps": probe_gbps,
+        "achieved_frac_of_read_probe": achieved / probe_gbps,
         "kernel_us_per_step": kern_mean,
         "kernel_us_median": statistics.median(kern_us),
         "bytes_per_step": bytes_step,

@@ -19,6 +19,7 @@ hipError_t launch_step(const Params* dev_params, int head_dim, int ncu, size_t l
                        hipStream_t stream);
 hipError_t set_step_kernel_lds(size_t lds_bytes);
 hipError_t launch_pack(const void* rows, uint32_t n, const uint16_t* const* mats, uint8_t* dst, hipStream_t stream);
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int ncu, hipStream_t stream);
 hipError_t launch_greedy(const float* logits, int B, int V, int32_t* tokens, int32_t* positions, uint64_t* part,
                          uint32_t* cnt, hipStream_t stream);
 }  // namespace mk
@@ -388,6 +389,14 @@ int mk_greedy_advance(mk_handle* h, const float* logits, int32_t* tokens, int32_
     hipError_t e = launch_greedy(logits, h->hp.B, h->hp.V, tokens, positions, h->greedy_part, h->greedy_cnt,
                                  (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(h, HipError{e, "mk_greedy_kernel launch"});
+    return MK_OK;
+}
+
+int mk_read_probe(const void* buf, size_t bytes, void* sink, int n_cus, void* stream) {
+    if (!buf || !sink || n_cus < 1 || n_cus > 4096 || bytes % 16 != 0 || ((uintptr_t)buf & 15) != 0)
+        return fail(nullptr, MK_ERR_INVALID_ARG, "mk_read_probe: null buffer, n_cus outside 1..4096 or unaligned size/address");
+    hipError_t e = launch_read_probe(buf, bytes, (uint32_t*)sink, n_cus, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(nullptr, HipError{e, "mk_read_probe_kernel launch"});
     return MK_OK;
 }
 

@@ -744,7 +744,7 @@ __device__ __forceinline__ void gather_embed(Ctx& cx, const Step& sp, int kpad, 
     CParams& p = *cx.p;
     const int H = p.H, xs = (int)uni((uint32_t)p.xstride);
     for (int b = 0; b < p.B; ++b) {
-        const int tok = gld(sp.tokens + b);
+        const int tok = __builtin_amdgcn_readlane(sp.tok, b);
         const uint32_t* row = (const uint32_t*)(p.embed + (size_t)tok * H);  // H even: bf16 pairs
         float ss = 0.f;
         for (int k0 = 0; k0 < H; k0 += 128 * GATHER_NB) {
@@ -812,13 +812,13 @@ __device__ __forceinline__ void gather_side(Ctx& cx, const Step& sp, const Inst&
     if (in.op == OP_RMS_QKV_ROPE) {
         const int D = p.D;
         for (int b = 0; b < B; ++b) {
-            const float* rope = p.rope + (size_t)gld(sp.positions + b) * D;
+            const float* rope = p.rope + (size_t)__builtin_amdgcn_readlane(sp.pos, b) * D;
             for (int i = cx.lane; i < D; i += 64) sd[b * D + i] = gld(rope + i);
         }
     } else if (in.op == OP_O_PROJ_RES) {
         for (int b = 0; b < B; ++b) {
             if (l == 0) {
-                const uint16_t* e = p.embed + (size_t)gld(sp.tokens + b) * H + rg0;
+                const uint16_t* e = p.embed + (size_t)__builtin_amdgcn_readlane(sp.tok, b) * H + rg0;
                 for (int j = cx.lane; j < nrg; j += 64) sd[b * nrg + j] = bf2f(gld(e + j));
             } else {
                 gather_words(cx, p.hout + ((size_t)(l - 1) * B + b) * H + rg0, nrg, sd + b * nrg);
@@ -1162,7 +1162,7 @@ __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& 
     constexpr int NH = D / 64;       // 64-dim halves
     CParams& p = *cx.p;
     const int B = p.B, G = p.G, l = in.layer, b = in.a, g = in.b, split = (int)in.rg0;
-    const int pos = gld(sp.positions + b);
+    const int pos = __builtin_amdgcn_readlane(sp.pos, b);
     const int S = pos + 1;
     const int j0 = (int)((long long)split * S / p.n_split), j1 = (int)((long long)(split + 1) * S / p.n_split);
     LDS float* qs = xb;              // [G][D], pre-scaled by 1/sqrt(D)
@@ -1587,6 +1587,36 @@ hipError_t launch_greedy(const float* logits, int B, int V, int32_t* tokens, int
                          uint32_t* cnt, hipStream_t stream) {
     hipLaunchKernelGGL(mk_greedy_kernel, dim3(GREEDY_BLOCKS, B), dim3(GREEDY_THREADS), 0, stream, logits, V, tokens,
                        positions, part, cnt);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------ read probe --
+
+// Streams `bytes` from buf once (16-byte loads, eight in flight per lane): the
+// achievable HBM read rate that a step's weight stream competes for.
+__global__ void __launch_bounds__(512) mk_read_probe_kernel(const uint8_t* buf, size_t bytes, uint32_t* sink) {
+    const size_t n16 = bytes / 16;
+    const size_t nthreads = (size_t)gridDim.x * blockDim.x;
+    const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    // thread t reads chunks t, t + nthreads, ...: every wave reads 1 KiB contiguous per load
+    uint32_t acc = 0;
+    size_t i = t;
+    for (; i + 7 * nthreads < n16; i += 8 * nthreads) {
+        u32x4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = *(const GLB u32x4*)(buf + (i + k * nthreads) * 16);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+    }
+    for (; i < n16; i += nthreads) {
+        const u32x4 v = *(const GLB u32x4*)(buf + i * 16);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    if (acc == 0x9e3779b9u) sink[0] = acc;  // keeps the loads; practically never taken
+}
+
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int ncu, hipStream_t stream) {
+    hipLaunchKernelGGL(mk_read_probe_kernel, dim3(ncu * 4), dim3(512), 0, stream, (const uint8_t*)buf, bytes, sink);
     return hipGetLastError();
 }
 

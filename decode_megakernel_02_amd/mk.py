@@ -54,7 +54,7 @@ class MkScheduleInfo(ctypes.Structure):
 
 EXPORTS = ["mk_create", "mk_load_weights", "mk_kv_cache_bytes", "mk_decode_step", "mk_decode_step_multikernel",
            "mk_destroy", "mk_status_string", "mk_last_error", "mk_get_device_error", "mk_get_profile",
-           "mk_schedule_inspect", "mk_get_trace", "mk_greedy_advance"]
+           "mk_schedule_inspect", "mk_get_trace", "mk_greedy_advance", "mk_read_probe"]
 MK_FLAG_PROFILE = 1
 MK_FLAG_TRACE = 2
 TRACE_SLOTS = 52
@@ -78,6 +78,7 @@ def lib():
         L.mk_kv_cache_bytes.restype = ctypes.c_size_t
         L.mk_decode_step.argtypes = [H, _P, _P, _P, _P, _P]
         L.mk_decode_step_multikernel.argtypes = [H, _P, _P, _P, _P, _P]
+        L.mk_read_probe.argtypes = [_P, ctypes.c_size_t, _P, ctypes.c_int, _P]
         L.mk_destroy.argtypes = [H]
         L.mk_status_string.argtypes = [ctypes.c_int]
         L.mk_status_string.restype = ctypes.c_char_p
@@ -90,7 +91,7 @@ def lib():
         L.mk_greedy_advance.argtypes = [H, _P, _P, _P, _P]
         for name in ["mk_create", "mk_load_weights", "mk_decode_step", "mk_decode_step_multikernel", "mk_destroy",
                      "mk_get_device_error", "mk_schedule_inspect", "mk_get_profile", "mk_get_trace",
-                     "mk_greedy_advance"]:
+                     "mk_greedy_advance", "mk_read_probe"]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -161,6 +162,11 @@ def mk_load_weights(handle, weights: Dict[str, object], stream: Optional[int] = 
 
 def mk_decode_step(handle, tokens, positions, kv_cache, logits, stream: Optional[int] = None):
     _check(lib().mk_decode_step(handle, _ptr(tokens), _ptr(positions), _ptr(kv_cache), _ptr(logits), stream), handle)
+
+
+def mk_read_probe(buf, sink, n_cus: int, stream: Optional[int] = None):
+    """One streaming read of the device tensor `buf` (asynchronous)."""
+    _check(lib().mk_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), n_cus, stream))
 
 
 def mk_decode_step_multikernel(handle, tokens, positions, kv_cache, logits, stream: Optional[int] = None):

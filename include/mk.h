@@ -142,6 +142,18 @@ int mk_decode_step_multikernel(mk_handle* h, const int32_t* tokens, const int32_
  * (issue them on one stream).                                              */
 int mk_greedy_advance(mk_handle* h, const float* logits, int32_t* tokens, int32_t* positions, void* stream);
 
+/* Measurement support: reads `bytes` (a multiple of 16) at the 16-byte aligned
+ * device address `buf` once, as 4 * n_cus workgroups of 512 threads with
+ * 16-byte loads, eight in flight per thread, on `stream` (asynchronous; time
+ * it with events).  `sink`: device memory of at least 4 bytes that the kernel
+ * may write.  The floor of a decode step is the time to read every weight
+ * once at the memory's read rate (the page "Megakernels: Deleting the Kernel
+ * Boundary to Win Back Microseconds", section "Where the microseconds go");
+ * this gives the rate the device actually sustains, next to its data-sheet
+ * peak.  Needs no handle; MK_ERR_INVALID_ARG on null/unaligned arguments or
+ * n_cus outside 1..4096.                                                   */
+int mk_read_probe(const void* buf, size_t bytes, void* sink, int n_cus, void* stream);
+
 /* Frees everything the handle owns.  NULL is accepted. */
 int mk_destroy(mk_handle* h);
 
