@@ -95,6 +95,14 @@ def test_null_arguments():
     assert L.mk_decode_step(None, None, None, None, None, None) == mk.MK_ERR_INVALID_ARG
     assert L.mk_decode_step_multikernel(None, None, None, None, None, None) == mk.MK_ERR_INVALID_ARG
     assert L.mk_load_weights(None, None, None) == mk.MK_ERR_INVALID_ARG
+    assert L.mk_greedy_advance(None, None, None, None, None) == mk.MK_ERR_INVALID_ARG
+    # the read probe checks its arguments before any device call
+    sink = ctypes.c_void_p(64)
+    assert L.mk_read_probe(None, 16, sink, 1, None) == mk.MK_ERR_INVALID_ARG
+    assert L.mk_read_probe(ctypes.c_void_p(256), 24, sink, 1, None) == mk.MK_ERR_INVALID_ARG
+    assert L.mk_read_probe(ctypes.c_void_p(264), 16, sink, 1, None) == mk.MK_ERR_INVALID_ARG
+    assert L.mk_read_probe(ctypes.c_void_p(256), 16, sink, 0, None) == mk.MK_ERR_INVALID_ARG
+    assert L.mk_read_probe(ctypes.c_void_p(256), 16, sink, 4097, None) == mk.MK_ERR_INVALID_ARG
 
 
 def test_kv_cache_bytes():
