@@ -269,8 +269,49 @@ def main():
     kern_mk = statistics.mean(a.elapsed_time(b) * 1e3 for a, b in evm)
     log(f"multikernel: {KM} steps in {wall_mk * 1e3:.1f} ms")
 
-    # ---- the device's sustained read rate (4 GiB, past the memory-side cache), best of 5
     ncu = torch.cuda.get_device_properties(0).multi_processor_count
+
+    # ---- the same loops captured once as HIP graphs (one replay = step + argmax), and the
+    # launch cost alone: as many empty kernels as the per-op step launches, eager and in a graph
+    def graph_us(flags, n):
+        g = mk.mk_graph_create(h, tokens, positions, kv, logits, 1, flags)
+        try:
+            positions.fill_(P)
+            for _ in range(3):
+                mk.mk_graph_launch(g, stream)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(cur)
+            for _ in range(n):
+                mk.mk_graph_launch(g, stream)
+            e1.record(cur)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / n
+        finally:
+            mk.mk_graph_destroy(g)
+
+    n_launch = shape.n_layers * 6 + 1
+    graph_mk = graph_us(mk.MK_GRAPH_MULTIKERNEL, KM)
+    check_device()
+    try:
+        graph_mega = graph_us(0, KM)
+        check_device()
+    except mk.MkError as e:  # the runtime may refuse to capture a cooperative launch
+        graph_mega = None
+        log(f"single-launch step not capturable: {e}")
+    graph_empty = graph_us(mk.MK_GRAPH_EMPTY, 20)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    mk.mk_empty_launches(n_launch, ncu, 768, stream)
+    e0.record(cur)
+    for _ in range(20):
+        mk.mk_empty_launches(n_launch, ncu, 768, stream)
+    e1.record(cur)
+    torch.cuda.synchronize()
+    eager_empty = e0.elapsed_time(e1) * 1e3 / 20
+    log(f"graphs: per-op step {graph_mk:.1f} us, single-launch step {graph_mega} us; "
+        f"{n_launch} empty launches: eager {eager_empty:.1f} us, graph {graph_empty:.1f} us")
+
+    # ---- the device's sustained read rate (4 GiB, past the memory-side cache), best of 5
     probe_buf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
     probe_buf.fill_(1)
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -321,7 +362,12 @@ def main():
         "floor_us_per_step": R.floor_us(bytes_step),
         "multikernel": {"ms_per_step": wall_mk / KM * 1e3, "tokens_per_s": B * KM / wall_mk,
                         "kernel_us_per_step": kern_mk, "launches_per_step": shape.n_layers * 6 + 1,
-                        "megakernel_speedup": kern_mk / kern_mean},
+                        "megakernel_speedup": kern_mk / kern_mean,
+                        "graph_us_per_step": graph_mk, "megakernel_speedup_vs_graph": graph_mk / (wall / K * 1e6)},
+        "graph": {"megakernel_us_per_step": graph_mega, "per_op_us_per_step": graph_mk,
+                  "note": "one replay = one decode step + the argmax launch, captured once, replayed back to back"},
+        "launch_overhead": {"launches": n_launch, "blocks": ncu, "threads": 768, "eager_empty_us": eager_empty,
+                            "graph_empty_us": graph_empty},
         "kernel_source_hash": kernel_source_hash(),
     }
     if args.cpu_steps > 0:

@@ -20,6 +20,7 @@ hipError_t launch_step(const Params* dev_params, int head_dim, int ncu, size_t l
 hipError_t set_step_kernel_lds(size_t lds_bytes);
 hipError_t launch_pack(const void* rows, uint32_t n, const uint16_t* const* mats, uint8_t* dst, hipStream_t stream);
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int ncu, hipStream_t stream);
+hipError_t launch_empty(int n_blocks, int n_threads, hipStream_t stream);
 hipError_t launch_greedy(const float* logits, int B, int V, int32_t* tokens, int32_t* positions, uint64_t* part,
                          uint32_t* cnt, hipStream_t stream);
 }  // namespace mk
@@ -397,6 +398,99 @@ int mk_read_probe(const void* buf, size_t bytes, void* sink, int n_cus, void* st
         return fail(nullptr, MK_ERR_INVALID_ARG, "mk_read_probe: null buffer, n_cus outside 1..4096 or unaligned size/address");
     hipError_t e = launch_read_probe(buf, bytes, (uint32_t*)sink, n_cus, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(nullptr, HipError{e, "mk_read_probe_kernel launch"});
+    return MK_OK;
+}
+
+int mk_empty_launches(int n_launches, int n_blocks, int n_threads, void* stream) {
+    if (n_launches < 1 || n_launches > 100000 || n_blocks < 1 || n_blocks > 65536 || n_threads < 1 || n_threads > 1024)
+        return fail(nullptr, MK_ERR_INVALID_ARG, "mk_empty_launches: count, blocks or threads out of range");
+    for (int i = 0; i < n_launches; ++i) {
+        hipError_t e = launch_empty(n_blocks, n_threads, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(nullptr, HipError{e, "mk_empty_kernel launch"});
+    }
+    return MK_OK;
+}
+
+// ------------------------------------------------------------ graphs ------
+
+struct mk_graph {
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+};
+
+static void graph_free(mk_graph* g) {
+    if (!g) return;
+    if (g->exec) (void)hipGraphExecDestroy(g->exec);
+    if (g->graph) (void)hipGraphDestroy(g->graph);
+    delete g;
+}
+
+int mk_graph_create(mk_handle* h, int32_t* tokens, int32_t* positions, void* kv_cache, float* logits, int n_steps,
+                    uint32_t flags, mk_graph** out) {
+    if (!out) return fail(h, MK_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    int rc = step_args_ok(h, tokens, positions, kv_cache, logits);
+    if (rc != MK_OK) return rc;
+    if (n_steps < 1 || n_steps > 4096) return fail(h, MK_ERR_INVALID_ARG, "n_steps outside 1..4096");
+    if (flags & ~(MK_GRAPH_MULTIKERNEL | MK_GRAPH_EMPTY)) return fail(h, MK_ERR_INVALID_ARG, "unknown graph flag");
+    mk_graph* g = new (std::nothrow) mk_graph;
+    if (!g) return fail(h, MK_ERR_OOM, "host allocation failed");
+    hipStream_t cs = nullptr;
+    try {
+        // captured on a private stream (the legacy default stream cannot be captured)
+        HIPCHK(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
+        HIPCHK(hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal));
+        const int ns = h->hp.n_stages;
+        HipError first{hipSuccess, ""};
+        for (int i = 0; i < n_steps && first.e == hipSuccess; ++i) {
+            if (flags & MK_GRAPH_EMPTY) {
+                for (int st = 0; st < ns && first.e == hipSuccess; ++st)
+                    first = HipError{launch_empty(h->hp.ncu, WG_THREADS, cs), "mk_empty_kernel launch"};
+                continue;
+            }
+            if (flags & MK_GRAPH_MULTIKERNEL) {
+                for (int st = 0; st < ns && first.e == hipSuccess; ++st)
+                    first = HipError{launch_step(h->dparams, h->hp.D, h->hp.ncu, h->lds_bytes, tokens, positions,
+                                                 kv_cache, logits, st,
+                                                 (st == ns - 1 ? KF_BUMP_EPOCH : 0u) | instr_flag(h), cs),
+                                     "mk_step_kernel stage launch"};
+            } else {
+                first = HipError{launch_step(h->dparams, h->hp.D, h->hp.ncu, h->lds_bytes, tokens, positions, kv_cache,
+                                             logits, -1, KF_BUMP_EPOCH | instr_flag(h), cs),
+                                 "mk_step_kernel launch"};
+            }
+            if (first.e == hipSuccess)
+                first = HipError{launch_greedy(logits, h->hp.B, h->hp.V, tokens, positions, h->greedy_part,
+                                               h->greedy_cnt, cs),
+                                 "mk_greedy_kernel launch"};
+        }
+        hipGraph_t graph = nullptr;
+        const hipError_t ec = hipStreamEndCapture(cs, &graph);  // ends the capture whatever happened above
+        g->graph = graph;
+        if (first.e != hipSuccess) throw first;
+        if (ec != hipSuccess) throw HipError{ec, "hipStreamEndCapture"};
+        HIPCHK(hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0));
+        HIPCHK(hipStreamDestroy(cs));
+        cs = nullptr;
+    } catch (const HipError& e) {
+        if (cs) (void)hipStreamDestroy(cs);
+        graph_free(g);
+        (void)hipGetLastError();
+        return hip_fail(h, e);
+    }
+    *out = g;
+    return MK_OK;
+}
+
+int mk_graph_launch(mk_graph* g, void* stream) {
+    if (!g || !g->exec) return fail(nullptr, MK_ERR_INVALID_ARG, "graph is NULL");
+    hipError_t e = hipGraphLaunch(g->exec, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(nullptr, HipError{e, "hipGraphLaunch"});
+    return MK_OK;
+}
+
+int mk_graph_destroy(mk_graph* g) {
+    graph_free(g);
     return MK_OK;
 }
 

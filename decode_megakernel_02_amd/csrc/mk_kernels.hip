@@ -1615,6 +1615,14 @@ __global__ void __launch_bounds__(512) mk_read_probe_kernel(const uint8_t* buf, 
     if (acc == 0x9e3779b9u) sink[0] = acc;  // keeps the loads; practically never taken
 }
 
+// A kernel that does nothing: the launch and dispatch cost alone.
+__global__ void __launch_bounds__(1024) mk_empty_kernel() {}
+
+hipError_t launch_empty(int n_blocks, int n_threads, hipStream_t stream) {
+    hipLaunchKernelGGL(mk_empty_kernel, dim3(n_blocks), dim3(n_threads), 0, stream);
+    return hipGetLastError();
+}
+
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int ncu, hipStream_t stream) {
     hipLaunchKernelGGL(mk_read_probe_kernel, dim3(ncu * 4), dim3(512), 0, stream, (const uint8_t*)buf, bytes, sink);
     return hipGetLastError();

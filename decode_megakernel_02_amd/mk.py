@@ -54,9 +54,12 @@ class MkScheduleInfo(ctypes.Structure):
 
 EXPORTS = ["mk_create", "mk_load_weights", "mk_kv_cache_bytes", "mk_decode_step", "mk_decode_step_multikernel",
            "mk_destroy", "mk_status_string", "mk_last_error", "mk_get_device_error", "mk_get_profile",
-           "mk_schedule_inspect", "mk_get_trace", "mk_greedy_advance", "mk_read_probe"]
+           "mk_schedule_inspect", "mk_get_trace", "mk_greedy_advance", "mk_read_probe", "mk_empty_launches",
+           "mk_graph_create", "mk_graph_launch", "mk_graph_destroy"]
 MK_FLAG_PROFILE = 1
 MK_FLAG_TRACE = 2
+MK_GRAPH_MULTIKERNEL = 1
+MK_GRAPH_EMPTY = 2
 TRACE_SLOTS = 52
 PROF_WAVES = 12  # 8 compute + 4 loader waves per workgroup
 PROF_SLOTS = 8
@@ -89,9 +92,14 @@ def lib():
         L.mk_get_profile.argtypes = [H, _P, ctypes.c_size_t]
         L.mk_get_trace.argtypes = [H, _P, ctypes.c_size_t]
         L.mk_greedy_advance.argtypes = [H, _P, _P, _P, _P]
+        L.mk_empty_launches.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _P]
+        L.mk_graph_create.argtypes = [H, _P, _P, _P, _P, ctypes.c_int, ctypes.c_uint32, ctypes.POINTER(ctypes.c_void_p)]
+        L.mk_graph_launch.argtypes = [ctypes.c_void_p, _P]
+        L.mk_graph_destroy.argtypes = [ctypes.c_void_p]
         for name in ["mk_create", "mk_load_weights", "mk_decode_step", "mk_decode_step_multikernel", "mk_destroy",
                      "mk_get_device_error", "mk_schedule_inspect", "mk_get_profile", "mk_get_trace",
-                     "mk_greedy_advance", "mk_read_probe"]:
+                     "mk_greedy_advance", "mk_read_probe", "mk_empty_launches", "mk_graph_create",
+                     "mk_graph_launch", "mk_graph_destroy"]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -167,6 +175,27 @@ def mk_decode_step(handle, tokens, positions, kv_cache, logits, stream: Optional
 def mk_read_probe(buf, sink, n_cus: int, stream: Optional[int] = None):
     """One streaming read of the device tensor `buf` (asynchronous)."""
     _check(lib().mk_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), n_cus, stream))
+
+
+def mk_empty_launches(n_launches: int, n_blocks: int, n_threads: int, stream: Optional[int] = None):
+    """n_launches launches of an empty kernel (asynchronous; for timing launch cost)."""
+    _check(lib().mk_empty_launches(n_launches, n_blocks, n_threads, stream))
+
+
+def mk_graph_create(handle, tokens, positions, kv_cache, logits, n_steps: int, flags: int = 0):
+    """A HIP graph of n_steps greedy decode steps on these device buffers (see include/mk.h)."""
+    g = ctypes.c_void_p()
+    _check(lib().mk_graph_create(handle, _ptr(tokens), _ptr(positions), _ptr(kv_cache), _ptr(logits), n_steps, flags,
+                                 ctypes.byref(g)), handle)
+    return g
+
+
+def mk_graph_launch(graph, stream: Optional[int] = None):
+    _check(lib().mk_graph_launch(graph, stream))
+
+
+def mk_graph_destroy(graph):
+    _check(lib().mk_graph_destroy(graph))
 
 
 def mk_decode_step_multikernel(handle, tokens, positions, kv_cache, logits, stream: Optional[int] = None):

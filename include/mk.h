@@ -154,6 +154,41 @@ int mk_greedy_advance(mk_handle* h, const float* logits, int32_t* tokens, int32_
  * n_cus outside 1..4096.                                                   */
 int mk_read_probe(const void* buf, size_t bytes, void* sink, int n_cus, void* stream);
 
+/* Measurement support: enqueues n_launches (1..100000) launches of an empty
+ * kernel with n_blocks (1..65536) workgroups of n_threads (1..1024) threads
+ * on `stream`, so that their cost can be timed next to the per-op path's
+ * launches (the per-launch overhead of the page "Megakernels: Deleting the
+ * Kernel Boundary to Win Back Microseconds", section "Where the microseconds
+ * go").  Needs no handle; MK_ERR_INVALID_ARG when out of range.            */
+int mk_empty_launches(int n_launches, int n_blocks, int n_threads, void* stream);
+
+/* A decode loop captured once as a HIP graph and replayed with one call.
+ * mk_graph_create records n_steps (1..4096) greedy steps, each one decode
+ * step followed by mk_greedy_advance's kernel, on a private stream of its
+ * own and instantiates the graph; nothing runs until mk_graph_launch.  The
+ * four device pointers are baked into the graph (same meaning as for
+ * mk_decode_step; tokens and positions are advanced on device by every
+ * step), so every replay continues from whatever they hold when it starts.
+ * flags: 0 = the single-launch step; MK_GRAPH_MULTIKERNEL = the per-op
+ * launches of mk_decode_step_multikernel (launch cost without the host's
+ * launch path, the replay point next to "one launch, one interpreter" of the
+ * megakernel page); MK_GRAPH_EMPTY = as many empty-kernel launches as the
+ * per-op step has, with the step's grid shape, and no greedy kernel (the
+ * graph launch overhead alone; the buffers are not touched).  The graph
+ * holds no memset nodes.  Replays on one handle must be ordered on one
+ * stream, like steps.  *out is NULL on error.  MK_ERR_HIP when the runtime
+ * refuses the capture (for instance of the cooperative single-launch step);
+ * the handle stays usable.  The graph must be destroyed before its handle. */
+#define MK_GRAPH_MULTIKERNEL 1u
+#define MK_GRAPH_EMPTY 2u
+typedef struct mk_graph mk_graph;
+int mk_graph_create(mk_handle* h, int32_t* tokens, int32_t* positions, void* kv_cache,
+                    float* logits, int n_steps, uint32_t flags, mk_graph** out);
+/* Enqueues one replay of the graph on `stream` (asynchronous). */
+int mk_graph_launch(mk_graph* g, void* stream);
+/* Frees the graph.  NULL is accepted. */
+int mk_graph_destroy(mk_graph* g);
+
 /* Frees everything the handle owns.  NULL is accepted. */
 int mk_destroy(mk_handle* h);
 

@@ -103,6 +103,16 @@ def test_null_arguments():
     assert L.mk_read_probe(ctypes.c_void_p(264), 16, sink, 1, None) == mk.MK_ERR_INVALID_ARG
     assert L.mk_read_probe(ctypes.c_void_p(256), 16, sink, 0, None) == mk.MK_ERR_INVALID_ARG
     assert L.mk_read_probe(ctypes.c_void_p(256), 16, sink, 4097, None) == mk.MK_ERR_INVALID_ARG
+    # launch probe and graph entry points check their arguments before any device call
+    assert L.mk_empty_launches(0, 1, 64, None) == mk.MK_ERR_INVALID_ARG
+    assert L.mk_empty_launches(1, 0, 64, None) == mk.MK_ERR_INVALID_ARG
+    assert L.mk_empty_launches(1, 1, 1025, None) == mk.MK_ERR_INVALID_ARG
+    g = ctypes.c_void_p(1)
+    assert L.mk_graph_create(None, None, None, None, None, 1, 0, ctypes.byref(g)) == mk.MK_ERR_INVALID_ARG
+    assert g.value is None
+    assert L.mk_graph_create(None, None, None, None, None, 1, 0, None) == mk.MK_ERR_INVALID_ARG
+    assert L.mk_graph_launch(None, None) == mk.MK_ERR_INVALID_ARG
+    assert L.mk_graph_destroy(None) == mk.MK_OK
 
 
 def test_kv_cache_bytes():
