@@ -893,6 +893,22 @@ __device__ __forceinline__ void gather_inst(Ctx& cx, const Step& sp, const Inst&
     }
 }
 
+// Consecutive instructions of one CU that read the same full input vector
+// (the up/gate chunks of a layer, several row tiles of one GEMV op) share it:
+// the gather wave copies it from the buffer set it staged last instead of
+// polling it from global memory again (one round trip saved per instruction).
+__device__ __forceinline__ uint32_t input_key(const Inst& in) {
+    const bool whole = in.op == OP_RMS_QKV_ROPE || in.op == OP_RMS_UP_GATE || in.op == OP_RMS_LM_HEAD ||
+                       in.op == OP_O_PROJ_RES;
+    return whole ? (uint32_t)in.op | ((uint32_t)in.layer << 8) : 0u;
+}
+
+__device__ __forceinline__ void copy_staged(const Ctx& cx, const LDS float* from, LDS float* to, int n,
+                                            const LDS float* ss_from, LDS float* ss_to, int B) {
+    for (int i = cx.lane * 4; i < n; i += 64 * 4) *(LDS f32x4*)(to + i) = *(const LDS f32x4*)(from + i);
+    if (cx.lane < B) ss_to[cx.lane] = ss_from[cx.lane];
+}
+
 __device__ __forceinline__ Inst decode_inst(const u32x4 raw) {
     Inst in;
     in.op = (uint16_t)(raw.x & 0xffffu);
@@ -914,6 +930,7 @@ __device__ __forceinline__ void gatherer(Ctx& cx, const Lds& s, const Step& sp, 
     const CONST_AS u32x4* iq = (const CONST_AS u32x4*)(p.insts + uni(qb));
     const uint32_t nslot = uni((uint32_t)p.nslot);
     uint32_t slot = (uint32_t)g % nslot;
+    uint32_t prev_key = 0, prev_slot = 0;  // input of the instruction this wave staged last
     for (uint32_t pc = pc0 + g; pc < pc1; pc += NGATHER, slot = (slot + NGATHER) % nslot) {
         const uint32_t r = pc - pc0;
         const u32x4 raw = iq[pc];
@@ -934,7 +951,15 @@ __device__ __forceinline__ void gatherer(Ctx& cx, const Lds& s, const Step& sp, 
         // side inputs first: each was complete before the main input's producers
         // began, so their round trip never waits behind the main poll
         if (p.side_floats) gather_side(cx, sp, in, sslot(s, p, slot));
-        gather_inst(cx, sp, in, xslot(s, p, slot), s.ss + slot * MAX_BATCH);
+        const uint32_t key = input_key(in);
+        if (NGATHER == 1 && key != 0 && key == prev_key)  // its buffer set still holds it: the
+            // wave refills a set only nslot instructions later, after this copy
+            copy_staged(cx, xslot(s, p, prev_slot), xslot(s, p, slot), p.B * (int)uni((uint32_t)p.xstride),
+                        s.ss + prev_slot * MAX_BATCH, s.ss + slot * MAX_BATCH, p.B);
+        else
+            gather_inst(cx, sp, in, xslot(s, p, slot), s.ss + slot * MAX_BATCH);
+        prev_key = key;
+        prev_slot = slot;
         if (uni(cx.aborted)) break;
         CBAR();
         if (cx.lane == 0) lds_st(s.ready + slot, r + 1);  // after the staged data (LDS requests of a wave stay ordered)

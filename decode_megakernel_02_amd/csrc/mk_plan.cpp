@@ -428,6 +428,36 @@ bool check_plan(const Plan& p, std::string& err) {
                 }
         }
     }
+    // --- pack table: every entry reads inside its source matrix and writes inside the buffer
+    auto mat_shape = [&](uint32_t mat, uint32_t& rows, uint32_t& cols) {
+        if (mat == (uint32_t)p.lm_mat()) {
+            rows = p.V;
+            cols = p.H;
+            return true;
+        }
+        if (mat >= (uint32_t)p.lm_mat()) return false;
+        const uint32_t QD = p.Hq * p.D, KD = p.Hkv * p.D;
+        switch (mat % MATS_PER_LAYER) {
+        case MAT_WQ: rows = QD; cols = p.H; break;
+        case MAT_WK: case MAT_WV: rows = KD; cols = p.H; break;
+        case MAT_WO: rows = p.H; cols = QD; break;
+        case MAT_GATE: case MAT_UP: rows = p.F; cols = p.H; break;
+        default: rows = p.H; cols = p.F; break;  // MAT_DOWN
+        }
+        return true;
+    };
+    for (size_t i = 0; i < p.pack.size(); ++i) {
+        const PackRow& r = p.pack[i];
+        uint32_t rows = 0, cols = 0;
+        if (!mat_shape(r.mat, rows, cols) || r.src_cols != cols || (uint64_t)r.k0 + r.klen > cols ||
+            r.row >= rows || r.kunits == 0 || (uint64_t)r.klen > (uint64_t)r.kunits * UNIT_ELEMS ||
+            r.dst_unit + (uint64_t)(r.kunits - 1) * NW >= p.total_units) {
+            snprintf(buf, sizeof buf, "pack entry %zu out of bounds (mat %u row %u k0 %u klen %u)", i, r.mat, r.row,
+                     r.k0, r.klen);
+            err = buf;
+            return false;
+        }
+    }
     // --- stream layout: pack rows tile every stream exactly
     uint64_t units = 0, stream_units = 0;
     for (const PackRow& r : p.pack) units += r.kunits;
