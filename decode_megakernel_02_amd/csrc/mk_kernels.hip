@@ -597,40 +597,54 @@ __device__ __forceinline__ void rowgroup_dot_b1(Ctx& cx, const Lds& s, Stream& s
 }
 
 // Dot products of one row-group (NROWS = 1 or 2 rows of ku units each) with x
-// for every batch row (x read from LDS); general path for any batch size.
-template <int NROWS>
+// for each of the NB batch rows (x read from LDS); the path for batch sizes
+// above one.  NB is a template parameter so that a unit's 2 NB x loads are
+// issued together and its NB product chains interleave.
+template <int NROWS, int NB>
 __device__ __forceinline__ void rowgroup_dot(Ctx& cx, const Lds& s, Stream& st, const LDS float* xb, int ku,
                                              RowOut& out) {
-    CParams& p = *cx.p;
-    const int B = p.B, xs = (int)uni((uint32_t)p.xstride);
+    const int xs = (int)uni((uint32_t)cx.p->xstride);
 #pragma unroll
     for (int r = 0; r < NROWS; ++r) {
-        float acc[MAX_BATCH];
+        float acc[NB];
 #pragma unroll
-        for (int b = 0; b < MAX_BATCH; ++b) acc[b] = 0.f;
+        for (int b = 0; b < NB; ++b) acc[b] = 0.f;
         for (int u = 0; u < ku; ++u) {
             const uint4 w = ring_take(cx, s, st);
-            const int c = u * 64 + cx.lane;  // 8-element chunk index
+            const LDS float* xl = xb + 4 * (u * 64 + cx.lane);  // 8-element chunk u * 64 + lane
+            float4 lo[NB], hi[NB];
 #pragma unroll
-            for (int b = 0; b < MAX_BATCH; ++b) {
-                if (b < B) {
-                    const LDS float* xr = xb + b * xs;
-                    const float4 lo = lds_f4(xr + 4 * c), hi = lds_f4(xr + 4 * ((xs >> 3) + c));
-                    acc[b] += dot8(w, lo, hi);
-                }
+            for (int b = 0; b < NB; ++b) {
+                lo[b] = lds_f4(xl + b * xs);
+                hi[b] = lds_f4(xl + b * xs + (xs >> 1));
             }
+#pragma unroll
+            for (int b = 0; b < NB; ++b) acc[b] += dot8(w, lo[b], hi[b]);
             ring_advance(cx, st);
             if ((u & 3) == 3 || u == ku - 1) ring_release(cx, s, st);
         }
         float mine = 0.f;
 #pragma unroll
-        for (int b = 0; b < MAX_BATCH; ++b) {
-            if (b < B) {
-                const float t = wave_sum(acc[b]);
-                mine = cx.lane == b ? t : mine;
-            }
+        for (int b = 0; b < NB; ++b) {
+            const float t = wave_sum(acc[b]);
+            mine = cx.lane == b ? t : mine;
         }
         out.mine[r] = mine;
+    }
+}
+
+template <int NROWS>
+__device__ __forceinline__ void rowgroup_dot_batch(Ctx& cx, const Lds& s, Stream& st, const LDS float* xb, int ku,
+                                                   RowOut& out) {
+    switch (cx.p->B) {
+    case 1: rowgroup_dot<NROWS, 1>(cx, s, st, xb, ku, out); break;
+    case 2: rowgroup_dot<NROWS, 2>(cx, s, st, xb, ku, out); break;
+    case 3: rowgroup_dot<NROWS, 3>(cx, s, st, xb, ku, out); break;
+    case 4: rowgroup_dot<NROWS, 4>(cx, s, st, xb, ku, out); break;
+    case 5: rowgroup_dot<NROWS, 5>(cx, s, st, xb, ku, out); break;
+    case 6: rowgroup_dot<NROWS, 6>(cx, s, st, xb, ku, out); break;
+    case 7: rowgroup_dot<NROWS, 7>(cx, s, st, xb, ku, out); break;
+    default: rowgroup_dot<NROWS, 8>(cx, s, st, xb, ku, out); break;
     }
 }
 
@@ -1017,11 +1031,11 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
     if constexpr (KU > 0) load_xslice<KU>(cx, xb, __builtin_amdgcn_readfirstlane(p.xstride), xs);
     auto dot1 = [&](RowOut& o) {
         if constexpr (KU > 0) rowgroup_dot_b1<KU, 1>(cx, s, st, xs, ru, o);
-        else rowgroup_dot<1>(cx, s, st, xb, ku, o);
+        else rowgroup_dot_batch<1>(cx, s, st, xb, ku, o);
     };
     auto dot2 = [&](RowOut& o) {
         if constexpr (KU > 0) rowgroup_dot_b1<KU, 2>(cx, s, st, xs, ru, o);
-        else rowgroup_dot<2>(cx, s, st, xb, ku, o);
+        else rowgroup_dot_batch<2>(cx, s, st, xb, ku, o);
     };
 
     // ---- this wave's row-groups; lane b < B finishes batch row b
