@@ -116,24 +116,65 @@ def write_stats_summary(stats_csv, workload, command):
     return path
 
 
-def cpu_baseline(shape, weights, kv_host, first_tok, prompt, n_steps: int):
+def cpu_baseline(shape, weights, kv_host, first_toks, prompt, n_steps: int, threads: int = 0):
+    """The oracle on the host cores: n_steps greedy steps of every batch row after one warm-up
+    step; threads = 0 uses every core (at most 64)."""
     import numpy as np
 
     import oracle
-    threads = max(1, min(64, os.cpu_count() or 1))
-    orc = oracle.Oracle(shape, weights, 1, kv_host.shape[4])
+    threads = threads or max(1, min(64, os.cpu_count() or 1))
+    B = kv_host.shape[2]
+    orc = oracle.Oracle(shape, weights, B, kv_host.shape[4])
     cache = kv_host.copy()
-    tok = np.array([first_tok], dtype=np.int32)
-    orc.decode_step(cache, tok, np.array([prompt], dtype=np.int32), threads)  # warm-up
+    tok = np.asarray(first_toks, dtype=np.int32).reshape(B)
+    orc.decode_step(cache, tok, np.full(B, prompt, dtype=np.int32), threads)  # warm-up
     t0 = time.perf_counter()
     for i in range(n_steps):
-        lg = orc.decode_step(cache, tok, np.array([prompt + 1 + i], dtype=np.int32), threads)
-        tok = np.array([int(np.argmax(lg[0]))], dtype=np.int32)
+        lg = orc.decode_step(cache, tok, np.full(B, prompt + 1 + i, dtype=np.int32), threads)
+        tok = np.argmax(lg, axis=1).astype(np.int32)
     dt = (time.perf_counter() - t0) / n_steps
-    return {"value": 1.0 / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n_steps} greedy decode steps of the same workload after 1 warm-up step "
+    return {"value": B / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_steps} greedy decode steps of the same workload (batch {B}) after 1 warm-up step "
                       f"(fp64 C oracle, {threads} threads, rows split across threads); "
                       f"{dt * 1e3:.1f} ms/step"}
+
+
+def write_stage_summary(trace_csv, workload, command):
+    """Per-op durations of the per-op-launch path from a rocprofv3 --kernel-trace run: the stage
+    launches of a step come in op order (six per layer, then the LM head), so a launch's position
+    in its step names its op; also the idle gap between consecutive launches of a step."""
+    import csv
+    import synth
+    shape = synth.WORKLOADS[workload].model
+    n = shape.n_layers * 6 + 1
+    ops = ["RMS_QKV_ROPE", "ATTENTION", "ATTN_REDUCE", "O_PROJ_RES", "RMS_UP_GATE", "DOWN_RES"]
+    rows = [r for r in csv.DictReader(open(trace_csv)) if "mk_stage_kernel" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    if not rows or len(rows) % n:
+        raise SystemExit(f"{len(rows)} stage launches is not a multiple of {n}")
+    dur, gap = {}, {}
+    for i, r in enumerate(rows):
+        j = i % n
+        op = "RMS_LM_HEAD" if j == n - 1 else ops[j % 6]
+        dur.setdefault(op, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        if j:
+            gap.setdefault(op, []).append((int(r["Start_Timestamp"]) - int(rows[i - 1]["End_Timestamp"])) / 1e3)
+    steps = len(rows) // n
+    total = sum(sum(v) for v in dur.values()) / steps
+    path = os.path.join(ROOT, "profiles", f"stage_durations_mk_stage_kernel_{workload}.md")
+    with open(path, "w") as fh:
+        fh.write(f"# Per-op launches of the decode step, workload {workload} (rocprofv3 --kernel-trace)\n\n")
+        fh.write(f"Command: `{command}`\n\n")
+        fh.write(f"{steps} steps of {n} launches; kernel time {total:.1f} us per step.\n\n")
+        fh.write("| op | launches per step | average us | us per step | share % | average gap before, us |\n"
+                 "|---|---|---|---|---|---|\n")
+        for op in ops + ["RMS_LM_HEAD"]:
+            v = dur[op]
+            per_step = sum(v) / steps
+            g = gap.get(op, [])
+            fh.write(f"| {op} | {len(v) // steps} | {sum(v) / len(v):.2f} | {per_step:.1f} | "
+                     f"{100 * per_step / total:.1f} | {sum(g) / len(g) if g else 0:.2f} |\n")
+    return path
 
 
 def main():
@@ -148,12 +189,32 @@ def main():
                     help="write the profiles/ kernel-duration summary from a rocprofv3 --stats run and exit")
     ap.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
                     help="write the profiles/ traffic summary from two rocprofv3 counter passes and exit")
+    ap.add_argument("--stage-summary", nargs=2, metavar=("TRACE_CSV", "COMMAND"),
+                    help="write the profiles/ per-op table of the per-op-launch path from a rocprofv3 "
+                         "--kernel-trace run and exit")
+    ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: every core, at most 64)")
+    ap.add_argument("--cpu-only", action="store_true",
+                    help="time only the CPU oracle on the workload and print it as one JSON line")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (3 launches), the reference "
                          "kernel for scaling HBM byte counters")
     args = ap.parse_args()
     if args.stats_summary:
         print(write_stats_summary(args.stats_summary[0], args.workload, args.stats_summary[1]))
+        return
+    if args.stage_summary:
+        print(write_stage_summary(args.stage_summary[0], args.workload, args.stage_summary[1]))
+        return
+    if args.cpu_only:
+        import synth
+        wl = synth.WORKLOADS[args.workload]
+        t0 = time.perf_counter()
+        weights = synth.make_weights(wl.model)
+        kv_host = synth.make_kv_cache(wl.model, wl.batch, wl.prompt + args.cpu_steps + 2, wl.prompt)
+        log(f"inputs generated in {time.perf_counter() - t0:.1f}s")
+        cb = cpu_baseline(wl.model, weights, kv_host, synth.make_first_tokens(wl.model.vocab, wl.batch), wl.prompt,
+                          max(1, args.cpu_steps), args.cpu_threads)
+        print(json.dumps({"workload": args.workload, "cpu_baseline": cb}), flush=True)
         return
     if args.traffic_summary:
         print(write_traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.workload,
@@ -372,7 +433,7 @@ def main():
     }
     if args.cpu_steps > 0:
         log("timing the CPU oracle")
-        out["cpu_baseline"] = cpu_baseline(shape, weights, kv_host, int(first[0]), P, args.cpu_steps)
+        out["cpu_baseline"] = cpu_baseline(shape, weights, kv_host, first, P, args.cpu_steps, args.cpu_threads)
     mk.mk_destroy(h)
     print(json.dumps(out), flush=True)
 
