@@ -198,8 +198,9 @@ int mk_create(const mk_config* cfg, mk_handle** out) {
             const long budget = (long)LDS_BYTES - nslot * (long)(xb + side_bytes) - (long)sync_bytes;
             return (int)std::min<long>(32, budget / (NW * UNIT_BYTES));
         };
-        // three buffer sets when the rings keep at least 12 slots, else two
-        int nslot = rings_for(3) >= std::max(ring_need, 12) ? 3 : 2;
+        // three buffer sets when the rings keep at least 12 slots, else two; one when two
+        // would leave the rings under 4 slots (large batch x hidden)
+        int nslot = rings_for(3) >= std::max(ring_need, 12) ? 3 : rings_for(2) >= 4 ? 2 : 1;
         const int ring_units = rings_for(nslot);
         if (ring_units < ring_need) {
             delete h;
@@ -346,7 +347,7 @@ int mk_load_weights(mk_handle* h, const mk_weights* w, void* stream) {
         if (d_mats) (void)hipFree(d_mats);
         return hip_fail(h, e);
     }
-    static_assert(sizeof(PackRow) == 32, "PackRow matches the device pack record");
+    static_assert(sizeof(PackRow) == 40, "PackRow matches the device pack record");
     h->loaded = true;
     h->last_error.clear();
     return MK_OK;

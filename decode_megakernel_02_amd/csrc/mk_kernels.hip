@@ -604,6 +604,40 @@ template <int NROWS, int NB>
 __device__ __forceinline__ void rowgroup_dot(Ctx& cx, const Lds& s, Stream& st, const LDS float* xb, int ku,
                                              RowOut& out) {
     const int xs = (int)uni((uint32_t)cx.p->xstride);
+    if constexpr (NROWS == 2) {  // the rows' units alternate in the stream: one x read serves both
+        float a0[NB], a1[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) a0[b] = a1[b] = 0.f;
+        for (int u = 0; u < ku; ++u) {
+            const uint4 w0 = ring_take(cx, s, st);
+            ring_advance(cx, st);
+            const uint4 w1 = ring_take(cx, s, st);
+            ring_advance(cx, st);
+            const LDS float* xl = xb + 4 * (u * 64 + cx.lane);
+            float4 lo[NB], hi[NB];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                lo[b] = lds_f4(xl + b * xs);
+                hi[b] = lds_f4(xl + b * xs + (xs >> 1));
+            }
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                a0[b] += dot8(w0, lo[b], hi[b]);
+                a1[b] += dot8(w1, lo[b], hi[b]);
+            }
+            if ((u & 1) == 1 || u == ku - 1) ring_release(cx, s, st);
+        }
+        float m0 = 0.f, m1 = 0.f;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const float t0 = wave_sum(a0[b]), t1 = wave_sum(a1[b]);
+            m0 = cx.lane == b ? t0 : m0;
+            m1 = cx.lane == b ? t1 : m1;
+        }
+        out.mine[0] = m0;
+        out.mine[1] = m1;
+        return;
+    }
 #pragma unroll
     for (int r = 0; r < NROWS; ++r) {
         float acc[NB];
@@ -1480,10 +1514,9 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
         case OP_ATTN_REDUCE: op_reduce(cx, s, r, in, xb); break;
         default: {
             const int ku = in.op == OP_O_PROJ_RES ? p.ku_q : in.op == OP_DOWN_RES ? p.ku_f : p.ku_h;
-            if (p.B != 1) op_gemv<0>(cx, s, st, r, slot, in, xb, sp, da);
+            if (!batch1_path(p.B, ku)) op_gemv<0>(cx, s, st, r, slot, in, xb, sp, da);
             else if (ku == 4) op_gemv<4>(cx, s, st, r, slot, in, xb, sp, da);
-            else if (ku == 2) op_gemv<2>(cx, s, st, r, slot, in, xb, sp, da);
-            else op_gemv<0>(cx, s, st, r, slot, in, xb, sp, da);
+            else op_gemv<2>(cx, s, st, r, slot, in, xb, sp, da);
             break;
         }
         }
@@ -1527,7 +1560,7 @@ mk_stage_kernel(const Params* __restrict__ pp, const int32_t* tokens, const int3
 // ------------------------------------------------------------ pack kernel --
 
 struct PackRowDev {
-    uint32_t mat, row, k0, klen, src_cols, kunits;
+    uint32_t mat, row, k0, klen, src_cols, kunits, ustride, reserved;
     uint64_t dst_unit;
 };
 
@@ -1541,7 +1574,8 @@ __global__ void __launch_bounds__(256) mk_pack_kernel(const PackRowDev* rows, ui
         for (uint32_t e = threadIdx.x; e < n_el; e += blockDim.x) {
             // element e lies in the row's unit e / 512, and consecutive units of a
             // stream are NW units apart in the packed buffer
-            uint16_t* out = (uint16_t*)(dst + (pr.dst_unit + (uint64_t)(e / UNIT_ELEMS) * NW) * UNIT_BYTES);
+            uint16_t* out =
+                (uint16_t*)(dst + (pr.dst_unit + (uint64_t)(e / UNIT_ELEMS) * NW * pr.ustride) * UNIT_BYTES);
             out[e % UNIT_ELEMS] = e < pr.klen ? src[e] : (uint16_t)0;
         }
     }

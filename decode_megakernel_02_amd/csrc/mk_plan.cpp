@@ -276,11 +276,17 @@ int build_plan(const mk_config& c, int ncu, Plan& p, std::string& err) {
             for (uint32_t i = 0; i < in.nrg; ++i) {
                 int nrows = b.rows_of(in, in.rg0 + i, rr);
                 uint64_t& cur = cursor[(size_t)cu * NW + i % NW];  // unit index within the wave's stream
+                // general GEMV path: the two rows of a row-group alternate unit by unit, so that
+                // each x slice read from LDS serves both rows
+                const bool inter = nrows == 2 && !batch1_path(p.B, (int)ku);
                 for (int k = 0; k < nrows; ++k) {
+                    const uint64_t first = inter ? cur + k : cur;
                     p.pack.push_back(PackRow{rr[k].mat, rr[k].row, rr[k].k0, rr[k].klen, rr[k].cols, ku,
-                                             p.stream_base[(size_t)cu * NW + i % NW] + cur * NW});
-                    cur += ku;
+                                             inter ? 2u : 1u, 0u,
+                                             p.stream_base[(size_t)cu * NW + i % NW] + first * NW});
+                    if (!inter) cur += ku;
                 }
+                if (inter) cur += 2 * (uint64_t)ku;
             }
         }
     }
@@ -451,7 +457,8 @@ bool check_plan(const Plan& p, std::string& err) {
         uint32_t rows = 0, cols = 0;
         if (!mat_shape(r.mat, rows, cols) || r.src_cols != cols || (uint64_t)r.k0 + r.klen > cols ||
             r.row >= rows || r.kunits == 0 || (uint64_t)r.klen > (uint64_t)r.kunits * UNIT_ELEMS ||
-            r.dst_unit + (uint64_t)(r.kunits - 1) * NW >= p.total_units) {
+            (r.ustride != 1 && r.ustride != 2) ||
+            r.dst_unit + (uint64_t)(r.kunits - 1) * NW * r.ustride >= p.total_units) {
             snprintf(buf, sizeof buf, "pack entry %zu out of bounds (mat %u row %u k0 %u klen %u)", i, r.mat, r.row,
                      r.k0, r.klen);
             err = buf;

@@ -22,7 +22,11 @@ struct PackRow {
     uint32_t klen;
     uint32_t src_cols;   // row length of the source matrix
     uint32_t kunits;
-    uint64_t dst_unit;   // absolute unit index in the packed buffer (first unit; later units every NW)
+    uint32_t ustride;    // stream units from one of the row's units to the next (2: interleaved with
+                         // the other row of its row-group)
+    uint32_t reserved;
+    uint64_t dst_unit;   // absolute unit index in the packed buffer (first unit; later units every
+                         // ustride * NW)
 };
 
 struct Plan {
