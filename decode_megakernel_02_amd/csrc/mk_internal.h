@@ -33,12 +33,12 @@ enum Op : uint16_t {
     OP_RMS_LM_HEAD = 7,   // final RMSNorm + LM head rows
 };
 
-constexpr int STAGES_PER_LAYER = 6;
+constexpr int STAGES_PER_LAYER = 6;  // QKV, ATTN, REDUCE, O, UPGATE, DOWN; LM head last
 
 // GEMV rows of ku units take the batch-1 path (x slice in registers, a row's units read
 // together) for these shapes, else the general path; the pack layout depends on it (the
 // general path reads the two rows of a row-group alternately, unit by unit).
-constexpr bool batch1_path(int B, int ku) { return B == 1 && (ku == 2 || ku == 4); }  // QKV, ATTN, REDUCE, O, UPGATE, DOWN; LM head last
+constexpr bool batch1_path(int B, int ku) { return B == 1 && (ku == 2 || ku == 4); }
 
 // One queue entry (16 bytes).  GEMV ops: row-groups [rg0, rg0 + nrg) of the
 // op's row-group space, distributed round-robin over the NW compute waves
