@@ -21,7 +21,7 @@ class OrcConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in
                 ["n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim", "ffn", "vocab",
                  "batch", "max_seq", "tied"]] + [("rms_eps", ctypes.c_double),
-                                                 ("rope_theta", ctypes.c_double)]
+                                                 ("rope_theta", ctypes.c_double), ("fp8", ctypes.c_int)]
 
 
 class OrcWeights(ctypes.Structure):
@@ -51,6 +51,13 @@ def lib():
         L.orc_decode_step.argtypes = [ctypes.POINTER(OrcConfig), ctypes.POINTER(OrcWeights),
                                       _P, _P, _P, _P, ctypes.c_int]
         L.orc_decode_step.restype = ctypes.c_int
+        L.orc_e4m3_to_double.argtypes = [ctypes.c_uint8]
+        L.orc_e4m3_to_double.restype = ctypes.c_double
+        L.orc_e4m3_round.argtypes = [ctypes.c_double]
+        L.orc_e4m3_round.restype = ctypes.c_uint8
+        L.orc_fp8_scale.argtypes = [_P, ctypes.c_size_t]
+        L.orc_fp8_scale.restype = ctypes.c_float
+        L.orc_gemv_fp8.argtypes = [_P, ctypes.c_int, ctypes.c_int, _P, _P, ctypes.c_int]
         L.orc_argmax.argtypes = [_P, ctypes.c_int]
         L.orc_argmax.restype = ctypes.c_int
         _lib = L
@@ -90,6 +97,27 @@ def gemv(W_bits, x, nthreads: int = 1) -> np.ndarray:
     return y
 
 
+def e4m3_to_double(code: int) -> float:
+    return lib().orc_e4m3_to_double(int(code))
+
+
+def e4m3_round(x: float) -> int:
+    return int(lib().orc_e4m3_round(float(x)))
+
+
+def fp8_scale(W_bits) -> float:
+    W = _u16(W_bits)
+    return float(lib().orc_fp8_scale(W.ctypes.data, W.size))
+
+
+def gemv_fp8(W_bits, x, nthreads: int = 1) -> np.ndarray:
+    W, x = _u16(W_bits), _f64(x)
+    rows, cols = W.shape
+    y = np.empty(rows, dtype=np.float64)
+    lib().orc_gemv_fp8(W.ctypes.data, rows, cols, x.ctypes.data, y.ctypes.data, nthreads)
+    return y
+
+
 def rope(v, pos: int, theta: float) -> np.ndarray:
     v = _f64(v).copy()
     lib().orc_rope(v.ctypes.data, v.size, pos, theta)
@@ -111,11 +139,11 @@ def silu(z: float) -> float:
 class Oracle:
     """Holds weight pointers (the numpy arrays stay referenced) for repeated steps."""
 
-    def __init__(self, shape, weights: Dict[str, object], batch: int, max_seq: int):
+    def __init__(self, shape, weights: Dict[str, object], batch: int, max_seq: int, fp8: bool = False):
         self.shape = shape
         self.cfg = OrcConfig(shape.n_layers, shape.hidden, shape.n_q_heads, shape.n_kv_heads,
                              shape.head_dim, shape.ffn, shape.vocab, batch, max_seq,
-                             1 if shape.tied else 0, shape.rms_eps, shape.rope_theta)
+                             1 if shape.tied else 0, shape.rms_eps, shape.rope_theta, 1 if fp8 else 0)
         self._keep = weights
         L = shape.n_layers
         w = OrcWeights()

@@ -65,12 +65,53 @@ void orc_rmsnorm(const double *h, const uint16_t *gain, int n, double eps, doubl
     for (int i = 0; i < n; ++i) out[i] = h[i] * inv * orc_bf16_to_double(gain[i]);
 }
 
+/*
+ * OCP 8-bit floating point E4M3 ("FP8"): sign, 4-bit exponent with bias 7 and
+ * 3 mantissa bits; exponent 0 holds the subnormals m * 2^-9; there are no
+ * infinities and S.1111.111 is NaN, so the largest finite value is
+ * 1.75 * 2^8 = 448.
+ */
+double orc_e4m3_to_double(uint8_t code) {
+    const int s = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double v = e ? ldexp(1.0 + m / 8.0, e - 7) : ldexp((double)m, -9);
+    return s ? -v : v;
+}
+
+/* Round to the nearest representable value: the spacing of E4M3 values is
+ * 2^(e-3) in the binade [2^e, 2^(e+1)) for e >= -6, and 2^-9 below 2^-6. */
+uint8_t orc_e4m3_round(double x) {
+    const uint8_t sign = signbit(x) ? 0x80 : 0;
+    const double a = fabs(x);
+    if (a >= 448.0) return sign | 0x7E;
+    const int e = a >= ldexp(1.0, -6) ? ilogb(a) : -6;
+    const double step = ldexp(1.0, e - 3);
+    const double v = nearbyint(a / step) * step; /* a / step is exact; ties to even */
+    if (v == 0.0) return sign;
+    if (v < ldexp(1.0, -6)) return sign | (uint8_t)(v / ldexp(1.0, -9)); /* subnormal */
+    const int E = ilogb(v);
+    const int m = (int)((v / ldexp(1.0, E) - 1.0) * 8.0);
+    return sign | (uint8_t)(((E + 7) << 3) | m);
+}
+
+float orc_fp8_scale(const uint16_t *W, size_t n) {
+    double amax = 0.0;
+    for (size_t i = 0; i < n; ++i) {
+        const double a = fabs(orc_bf16_to_double(W[i]));
+        if (a > amax) amax = a;
+    }
+    if (amax == 0.0) return 1.0f;
+    return (float)amax / 448.0f;
+}
+
 typedef struct {
     const uint16_t *W;
     int cols;
     const double *x;
     double *y;
     int r0, r1;
+    int fp8;
+    float scale;
 } gemv_job;
 
 static void *gemv_rows(void *p) {
@@ -78,14 +119,32 @@ static void *gemv_rows(void *p) {
     for (int r = j->r0; r < j->r1; ++r) {
         const uint16_t *row = j->W + (size_t)r * j->cols;
         double acc = 0.0;
-        for (int c = 0; c < j->cols; ++c) acc += orc_bf16_to_double(row[c]) * j->x[c];
+        if (j->fp8) {
+            for (int c = 0; c < j->cols; ++c) {
+                const float q = (float)orc_bf16_to_double(row[c]) / j->scale;
+                acc += (double)j->scale * orc_e4m3_to_double(orc_e4m3_round(q)) * j->x[c];
+            }
+        } else {
+            for (int c = 0; c < j->cols; ++c) acc += orc_bf16_to_double(row[c]) * j->x[c];
+        }
         j->y[r] = acc;
     }
     return NULL;
 }
 
+static void gemv_any(const uint16_t *W, int rows, int cols, const double *x, double *y, int nthreads, int fp8);
+
 /* Matrix-vector product with bf16 weights; the thread split does not change any row's sum. */
 void orc_gemv(const uint16_t *W, int rows, int cols, const double *x, double *y, int nthreads) {
+    gemv_any(W, rows, cols, x, y, nthreads, 0);
+}
+
+void orc_gemv_fp8(const uint16_t *W, int rows, int cols, const double *x, double *y, int nthreads) {
+    gemv_any(W, rows, cols, x, y, nthreads, 1);
+}
+
+static void gemv_any(const uint16_t *W, int rows, int cols, const double *x, double *y, int nthreads, int fp8) {
+    const float scale = fp8 ? orc_fp8_scale(W, (size_t)rows * cols) : 1.0f;
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;
     if (nthreads > rows / 64 + 1) nthreads = rows / 64 + 1;
@@ -96,7 +155,7 @@ void orc_gemv(const uint16_t *W, int rows, int cols, const double *x, double *y,
     for (int t = 0; t < nthreads; ++t) {
         int r0 = t * per < rows ? t * per : rows;
         int r1 = r0 + per < rows ? r0 + per : rows;
-        jobs[t] = (gemv_job){W, cols, x, y, r0, r1};
+        jobs[t] = (gemv_job){W, cols, x, y, r0, r1, fp8, scale};
     }
     for (int t = 1; t < nthreads; ++t) {
         if (jobs[t].r0 >= jobs[t].r1) continue;
@@ -220,9 +279,9 @@ int orc_decode_step(const orc_config *c, const orc_weights *w, uint16_t *kv_cach
         for (int l = 0; l < c->n_layers; ++l) {
             /* attention block: RMS norm, Q/K/V projections, RoPE on q and k */
             orc_rmsnorm(h, w->attn_norm[l], H, c->rms_eps, x);
-            orc_gemv(w->wq[l], QD, H, x, q, nthreads);
-            orc_gemv(w->wk[l], KD, H, x, k, nthreads);
-            orc_gemv(w->wv[l], KD, H, x, v, nthreads);
+            gemv_any(w->wq[l], QD, H, x, q, nthreads, c->fp8);
+            gemv_any(w->wk[l], KD, H, x, k, nthreads, c->fp8);
+            gemv_any(w->wv[l], KD, H, x, v, nthreads, c->fp8);
             for (int hd = 0; hd < Hq; ++hd) orc_rope(q + hd * D, D, p, c->rope_theta);
             for (int g = 0; g < Hkv; ++g) orc_rope(k + g * D, D, p, c->rope_theta);
             /* append this position's K and V (bf16) to the cache */
@@ -241,19 +300,19 @@ int orc_decode_step(const orc_config *c, const orc_weights *w, uint16_t *kv_cach
                               cache_rows(c, kv_cache, l, 1, b, g), p + 1, D, o + hd * D);
             }
             /* output projection and residual */
-            orc_gemv(w->wo[l], H, QD, o, proj, nthreads);
+            gemv_any(w->wo[l], H, QD, o, proj, nthreads, c->fp8);
             for (int i = 0; i < H; ++i) h[i] += proj[i];
             /* MLP block: RMS norm, SwiGLU, down projection and residual */
             orc_rmsnorm(h, w->mlp_norm[l], H, c->rms_eps, x);
-            orc_gemv(w->w_gate[l], F, H, x, gate, nthreads);
-            orc_gemv(w->w_up[l], F, H, x, up, nthreads);
+            gemv_any(w->w_gate[l], F, H, x, gate, nthreads, c->fp8);
+            gemv_any(w->w_up[l], F, H, x, up, nthreads, c->fp8);
             for (int i = 0; i < F; ++i) gate[i] = orc_silu(gate[i]) * up[i];
-            orc_gemv(w->w_down[l], H, F, gate, proj, nthreads);
+            gemv_any(w->w_down[l], H, F, gate, proj, nthreads, c->fp8);
             for (int i = 0; i < H; ++i) h[i] += proj[i];
         }
         /* final RMS norm and LM head (the embedding matrix when tied) */
         orc_rmsnorm(h, w->final_norm, H, c->rms_eps, x);
-        orc_gemv(c->tied ? w->embed : w->lm_head, V, H, x, logits + (size_t)b * V, nthreads);
+        gemv_any(c->tied ? w->embed : w->lm_head, V, H, x, logits + (size_t)b * V, nthreads, c->fp8);
     }
     free(h); free(x); free(q); free(k); free(v); free(o); free(proj); free(gate); free(up);
     return ORC_OK;

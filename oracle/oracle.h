@@ -21,6 +21,7 @@
 #ifndef MK_ORACLE_H
 #define MK_ORACLE_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -33,6 +34,8 @@ typedef struct {
     int max_seq;   /* cache slots per (layer, K/V, row, group) */
     int tied;      /* 1: LM head weight is the embedding matrix */
     double rms_eps, rope_theta;
+    int fp8;       /* 1: every projection matrix and the LM head are used as their FP8
+                      quantisation (orc_gemv_fp8); the embedding lookup stays bf16 */
 } orc_config;
 
 /* Host pointers, bf16 bit patterns, row-major nn.Linear layout [out][in]. */
@@ -62,6 +65,19 @@ uint16_t orc_bf16_round(double x);
 void orc_rmsnorm(const double *h, const uint16_t *gain, int n, double eps, double *out);
 /* y[r] = sum_c W[r][c] * x[c]; rows split over `nthreads` threads, each row summed in c order. */
 void orc_gemv(const uint16_t *W, int rows, int cols, const double *x, double *y, int nthreads);
+/* OCP FP8 E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinities, S.1111.111 is NaN): the value of a code. */
+double orc_e4m3_to_double(uint8_t code);
+/* Code of the E4M3 value nearest to the finite x, ties to the even mantissa;
+ * |x| >= 448 gives +-448 (the largest finite value). */
+uint8_t orc_e4m3_round(double x);
+/* Per-matrix FP8 scale: fp32(amax / 448) with amax the largest |w| of the n
+ * bf16 weights (1 when every weight is zero). */
+float orc_fp8_scale(const uint16_t *W, size_t n);
+/* y[r] = sum_c (s * e4m3(fp32(W[r][c]) / s)) * x[c] with s = orc_fp8_scale(W):
+ * the product with the matrix's FP8 quantisation (fp32 division, as the
+ * quantiser computes it).  Same threading and summation order as orc_gemv. */
+void orc_gemv_fp8(const uint16_t *W, int rows, int cols, const double *x, double *y, int nthreads);
 /* Rotate-half RoPE of one head vector at position `pos`. */
 void orc_rope(double *v, int head_dim, int pos, double theta);
 /* Softmax attention of one query over n_keys bf16 K/V rows (row stride head_dim). */
