@@ -18,7 +18,9 @@ hipError_t launch_step(const Params* dev_params, int head_dim, int ncu, size_t l
                        const int32_t* positions, void* kv, float* logits, int stage, uint32_t flags,
                        hipStream_t stream);
 hipError_t set_step_kernel_lds(size_t lds_bytes);
-hipError_t launch_pack(const void* rows, uint32_t n, const uint16_t* const* mats, uint8_t* dst, hipStream_t stream);
+hipError_t launch_pack(const void* rows, uint32_t n, const uint16_t* const* mats, uint8_t* dst, int fp8,
+                       const float* scales, hipStream_t stream);
+hipError_t launch_amax(const uint16_t* w, size_t n, uint32_t* out, hipStream_t stream);
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int ncu, hipStream_t stream);
 hipError_t launch_empty(int n_blocks, int n_threads, hipStream_t stream);
 hipError_t launch_greedy(const float* logits, int B, int V, int32_t* tokens, int32_t* positions, uint64_t* part,
@@ -38,6 +40,7 @@ struct mk_handle {
     std::string last_error;
     uint64_t* greedy_part = nullptr;  // [B][GREEDY_BLOCKS] per-slice (value, index) pairs
     uint32_t* greedy_cnt = nullptr;   // [B] finished slices of the current call (zero between calls)
+    uint32_t* amax_bits = nullptr;    // FP8: [n_mats] largest |w| per matrix (bf16 bits), at load time
 };
 
 static thread_local std::string g_create_error;
@@ -179,7 +182,7 @@ int mk_create(const mk_config* cfg, mk_handle** out) {
             return fail(nullptr, rc, err);
         }
         // LDS: rings, nslot x buffers (also scratch of attention/reduce), sync words, nslot side buffers
-        const int xstride = std::max(std::max(p.ku_h, p.ku_q), p.ku_f) * UNIT_ELEMS;
+        const int xstride = std::max(std::max(p.ku_h, p.ku_q), p.ku_f) * p.epu;
         size_t xb = (size_t)p.B * xstride * 4;
         const size_t attn_scratch = (size_t)(p.G * p.D + 2 * p.D + NW * (p.D + 2) + NW * 64) * 4;
         const size_t red_scratch = (size_t)p.n_split * (p.D + 2) * 4;
@@ -219,6 +222,11 @@ int mk_create(const mk_config* cfg, mk_handle** out) {
         hp.spin_limit = 1u << 25;
         for (int i = 0; i <= p.n_chunk; ++i) hp.chunk_begin[i] = p.chunk_begin[i];
         hp.n_stages = p.n_stages;
+        hp.fp8 = p.fp8 ? 1 : 0;
+        if (p.fp8) {
+            hp.wscale = dalloc<float>(h, (size_t)p.n_mats());
+            h->amax_bits = dalloc<uint32_t>(h, (size_t)p.n_mats());
+        }
 
         hp.wstream = dalloc<uint8_t>(h, (size_t)p.total_units * UNIT_BYTES);
         hp.stream_base = dupload(h, p.stream_base);
@@ -329,7 +337,31 @@ int mk_load_weights(mk_handle* h, const mk_weights* w, void* stream) {
         HIPCHK(hipMalloc(&d_mats, mats.size() * sizeof(void*)));
         HIPCHK(hipMemcpyAsync(d_rows, p.pack.data(), p.pack.size() * sizeof(PackRow), hipMemcpyHostToDevice, s));
         HIPCHK(hipMemcpyAsync(d_mats, mats.data(), mats.size() * sizeof(void*), hipMemcpyHostToDevice, s));
-        HIPCHK(launch_pack(d_rows, (uint32_t)p.pack.size(), (const uint16_t* const*)d_mats, (uint8_t*)h->hp.wstream, s));
+        if (p.fp8) {
+            // per-matrix scale fp32(max|w| / 448): the largest magnitude as bf16 bits (magnitudes of
+            // finite bf16 values order like their bits with the sign cleared), then on the host
+            const int nm = p.n_mats();
+            HIPCHK(hipMemsetAsync(h->amax_bits, 0, (size_t)nm * 4, s));
+            for (int m = 0; m < nm; ++m) {
+                uint32_t rows = 0, cols = 0;
+                p.mat_shape((uint32_t)m, rows, cols);
+                HIPCHK(launch_amax(mats[(size_t)m], (size_t)rows * cols, h->amax_bits + m, s));
+            }
+            std::vector<uint32_t> bits((size_t)nm);
+            HIPCHK(hipMemcpyAsync(bits.data(), h->amax_bits, (size_t)nm * 4, hipMemcpyDeviceToHost, s));
+            HIPCHK(hipStreamSynchronize(s));
+            std::vector<float> scale((size_t)nm);
+            for (int m = 0; m < nm; ++m) {
+                uint32_t f = bits[(size_t)m] << 16;
+                float amax;
+                std::memcpy(&amax, &f, 4);
+                scale[(size_t)m] = amax == 0.0f ? 1.0f : amax / 448.0f;
+            }
+            HIPCHK(hipMemcpyAsync((void*)h->hp.wscale, scale.data(), (size_t)nm * 4, hipMemcpyHostToDevice, s));
+            HIPCHK(hipStreamSynchronize(s));  // the host vector goes out of scope
+        }
+        HIPCHK(launch_pack(d_rows, (uint32_t)p.pack.size(), (const uint16_t* const*)d_mats, (uint8_t*)h->hp.wstream,
+                           p.fp8 ? 1 : 0, h->hp.wscale, s));
         const size_t HB = (size_t)p.H * 2;
         HIPCHK(hipMemcpyAsync((void*)h->hp.embed, w->embed, (size_t)p.V * HB, hipMemcpyDeviceToDevice, s));
         for (int l = 0; l < p.L; ++l) {
@@ -360,8 +392,10 @@ static int step_args_ok(mk_handle* h, const int32_t* tokens, const int32_t* posi
     return MK_OK;
 }
 
-// handles created with profiling or tracing run the instrumented kernel build
-static uint32_t instr_flag(const mk_handle* h) { return (h->hp.prof || h->hp.trace) ? KF_INSTRUMENTED : 0u; }
+// handles created with profiling or tracing run the instrumented kernel build, FP8 handles the FP8 one
+static uint32_t instr_flag(const mk_handle* h) {
+    return ((h->hp.prof || h->hp.trace) ? KF_INSTRUMENTED : 0u) | (h->hp.fp8 ? KF_FP8 : 0u);
+}
 
 int mk_decode_step(mk_handle* h, const int32_t* tokens, const int32_t* positions, void* kv_cache, float* logits,
                    void* stream) {

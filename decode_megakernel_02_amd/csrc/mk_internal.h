@@ -35,10 +35,19 @@ enum Op : uint16_t {
 
 constexpr int STAGES_PER_LAYER = 6;  // QKV, ATTN, REDUCE, O, UPGATE, DOWN; LM head last
 
+// Weight matrices: layer matrices at layer * MATS_PER_LAYER + kind, the LM head last.
+enum MatKind : uint32_t { MAT_WQ = 0, MAT_WK, MAT_WV, MAT_WO, MAT_GATE, MAT_UP, MAT_DOWN, MATS_PER_LAYER };
+constexpr int FP8_UNIT_ELEMS = 1024;  // FP8 codes per unit
+
 // GEMV rows of ku units take the batch-1 path (x slice in registers, a row's units read
 // together) for these shapes, else the general path; the pack layout depends on it (the
 // general path reads the two rows of a row-group alternately, unit by unit).
-constexpr bool batch1_path(int B, int ku) { return B == 1 && (ku == 2 || ku == 4); }
+#if defined(__HIP__)
+#define MK_INLINE __attribute__((host, device, always_inline)) inline  // inlined into the kernels' dispatch
+#else
+#define MK_INLINE inline
+#endif
+MK_INLINE constexpr bool batch1_path(int B, int ku, bool fp8) { return B == 1 && (ku == 2 || (ku == 4 && !fp8)); }
 
 // One queue entry (16 bytes).  GEMV ops: row-groups [rg0, rg0 + nrg) of the
 // op's row-group space, distributed round-robin over the NW compute waves
@@ -106,11 +115,15 @@ struct Params {
     uint64_t* trace;  // [total instructions][TRACE_SLOTS] timeline records, or null
     uint32_t* epoch;  // [ncu] per-workgroup step counter
     uint32_t* error;  // [8] device error record (code, wg, pc, op, wave, detail), abort flag at [7]
+
+    const float* wscale;  // FP8 weights: [L * MATS_PER_LAYER + 1] per-matrix scales (LM head last)
+    int32_t fp8;          // weights packed as FP8 codes (units of 1024 elements)
 };
 
 // Kernel launch flags.
 constexpr uint32_t KF_BUMP_EPOCH = 1u;  // last launch of a step: advance the per-workgroup epoch
 constexpr uint32_t KF_INSTRUMENTED = 2u;  // run the kernel build that records profile counters / timelines
+constexpr uint32_t KF_FP8 = 4u;           // run the kernel build for FP8 weights
 constexpr int PROF_SLOTS = 8;          // counters per wave
 // Timeline record per instruction (100 MHz real-time clock): [0] op | layer << 8 |
 // a << 16 | b << 32 | cu << 48, then per compute wave w at [1 + 6w]: start,

@@ -520,6 +520,33 @@ __device__ __forceinline__ float dot8(const uint4 w, const float4 a, const float
     return s;
 }
 
+// One unit of FP8 codes: lane c holds the 16 codes of elements 16c .. 16c+15 of
+// the unit, i.e. x chunks 2c (a0: elements 0-3, b0: 4-7) and 2c+1 (a1, b1).
+// The conversion instruction decodes OCP E4M3 (checked against the format
+// table on this device); the per-matrix scale is applied to the row sum.
+__device__ __forceinline__ float dot16_fp8(const uint4 w, const float4 a0, const float4 b0, const float4 a1,
+                                           const float4 b1) {
+    const auto c0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false), c1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
+    const auto c2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false), c3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
+    const auto c4 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.z, false), c5 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.z, true);
+    const auto c6 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.w, false), c7 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.w, true);
+    // four independent chains of four (a single chain of sixteen is latency-bound)
+    float s0 = c0[0] * a0.x, s1 = c2[0] * b0.x, s2 = c4[0] * a1.x, s3 = c6[0] * b1.x;
+    s0 = fmaf(c0[1], a0.y, s0);
+    s1 = fmaf(c2[1], b0.y, s1);
+    s2 = fmaf(c4[1], a1.y, s2);
+    s3 = fmaf(c6[1], b1.y, s3);
+    s0 = fmaf(c1[0], a0.z, s0);
+    s1 = fmaf(c3[0], b0.z, s1);
+    s2 = fmaf(c5[0], a1.z, s2);
+    s3 = fmaf(c7[0], b1.z, s3);
+    s0 = fmaf(c1[1], a0.w, s0);
+    s1 = fmaf(c3[1], b0.w, s1);
+    s2 = fmaf(c5[1], a1.w, s2);
+    s3 = fmaf(c7[1], b1.w, s3);
+    return (s0 + s1) + (s2 + s3);
+}
+
 // Poll a single tagged word (epilogue inputs that were produced long before).
 __device__ __forceinline__ float wait_word(Ctx& cx, const uint64_t* p) {
     uint64_t w = ld_tag(p);
@@ -554,23 +581,35 @@ __device__ __forceinline__ void ring_wait(Ctx& cx, const Lds& s, Stream& st, uin
 // Batch-1 row dot products with this wave's x slice in registers: the KU
 // units of a row are read from the ring together and accumulated in KU
 // independent chains.
-template <int KU>
+template <int NC>
 struct XSlice {
-    float4 lo[KU], hi[KU];
+    float4 lo[NC], hi[NC];
 };
 
-template <int KU>
-__device__ __forceinline__ void load_xslice(const Ctx& cx, const LDS float* xb, int xstride, XSlice<KU>& x) {
+// x chunks (8 elements) of this lane for KU units: chunk u * 64 + lane (bf16
+// units), chunks 2 (u * 64 + lane) and 2 (u * 64 + lane) + 1 (FP8 units)
+template <int KU, bool FP8>
+__device__ __forceinline__ void load_xslice(const Ctx& cx, const LDS float* xb, int xstride,
+                                            XSlice<FP8 ? 2 * KU : KU>& x) {
+    if constexpr (FP8) {
 #pragma unroll
-    for (int u = 0; u < KU; ++u) {
-        x.lo[u] = lds_f4(xb + 4 * (u * 64 + cx.lane));
-        x.hi[u] = lds_f4(xb + 4 * ((xstride >> 3) + u * 64 + cx.lane));
+        for (int c = 0; c < 2 * KU; ++c) {
+            const int q = 2 * ((c >> 1) * 64 + cx.lane) + (c & 1);
+            x.lo[c] = lds_f4(xb + 4 * q);
+            x.hi[c] = lds_f4(xb + 4 * ((xstride >> 3) + q));
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+            x.lo[u] = lds_f4(xb + 4 * (u * 64 + cx.lane));
+            x.hi[u] = lds_f4(xb + 4 * ((xstride >> 3) + u * 64 + cx.lane));
+        }
     }
 }
 
-template <int KU, int NROWS>
-__device__ __forceinline__ void rowgroup_dot_b1(Ctx& cx, const Lds& s, Stream& st, const XSlice<KU>& x, uint32_t ru,
-                                                RowOut& out) {
+template <int KU, int NROWS, bool FP8>
+__device__ __forceinline__ void rowgroup_dot_b1(Ctx& cx, const Lds& s, Stream& st,
+                                                const XSlice<FP8 ? 2 * KU : KU>& x, uint32_t ru, RowOut& out) {
 #pragma unroll
     for (int r = 0; r < NROWS; ++r) {
         ring_wait(cx, s, st, st.unit + KU);
@@ -583,7 +622,10 @@ __device__ __forceinline__ void rowgroup_dot_b1(Ctx& cx, const Lds& s, Stream& s
         }
         float acc[KU];
 #pragma unroll
-        for (int u = 0; u < KU; ++u) acc[u] = dot8(w[u], x.lo[u], x.hi[u]);
+        for (int u = 0; u < KU; ++u) {
+            if constexpr (FP8) acc[u] = dot16_fp8(w[u], x.lo[2 * u], x.hi[2 * u], x.lo[2 * u + 1], x.hi[2 * u + 1]);
+            else acc[u] = dot8(w[u], x.lo[u], x.hi[u]);
+        }
         float sum = acc[0];
 #pragma unroll
         for (int u = 1; u < KU; ++u) sum += acc[u];
@@ -600,7 +642,18 @@ __device__ __forceinline__ void rowgroup_dot_b1(Ctx& cx, const Lds& s, Stream& s
 // for each of the NB batch rows (x read from LDS); the path for batch sizes
 // above one.  NB is a template parameter so that a unit's 2 NB x loads are
 // issued together and its NB product chains interleave.
-template <int NROWS, int NB>
+// x of one unit for batch row b: (lo, hi) of chunk u * 64 + lane (bf16), and
+// for FP8 units also (lo2, hi2) of the next chunk
+template <bool FP8>
+__device__ __forceinline__ float unit_dot(const uint4 w, const LDS float* xl, int xs, int b) {
+    const LDS float* xr = xl + b * xs;
+    if constexpr (FP8)
+        return dot16_fp8(w, lds_f4(xr), lds_f4(xr + (xs >> 1)), lds_f4(xr + 4), lds_f4(xr + (xs >> 1) + 4));
+    else
+        return dot8(w, lds_f4(xr), lds_f4(xr + (xs >> 1)));
+}
+
+template <int NROWS, int NB, bool FP8>
 __device__ __forceinline__ void rowgroup_dot(Ctx& cx, const Lds& s, Stream& st, const LDS float* xb, int ku,
                                              RowOut& out) {
     const int xs = (int)uni((uint32_t)cx.p->xstride);
@@ -613,17 +666,29 @@ __device__ __forceinline__ void rowgroup_dot(Ctx& cx, const Lds& s, Stream& st, 
             ring_advance(cx, st);
             const uint4 w1 = ring_take(cx, s, st);
             ring_advance(cx, st);
-            const LDS float* xl = xb + 4 * (u * 64 + cx.lane);
-            float4 lo[NB], hi[NB];
+            const LDS float* xl = xb + 4 * (FP8 ? 2 * (u * 64 + cx.lane) : u * 64 + cx.lane);
+            if constexpr (FP8) {
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                lo[b] = lds_f4(xl + b * xs);
-                hi[b] = lds_f4(xl + b * xs + (xs >> 1));
-            }
+                for (int b = 0; b < NB; ++b) {
+                    const LDS float* xr = xl + b * xs;
+                    const float4 l0 = lds_f4(xr), h0 = lds_f4(xr + (xs >> 1)), l1 = lds_f4(xr + 4),
+                                 h1 = lds_f4(xr + (xs >> 1) + 4);
+                    a0[b] += dot16_fp8(w0, l0, h0, l1, h1);
+                    a1[b] += dot16_fp8(w1, l0, h0, l1, h1);
+                    CBAR();  // one batch row's x live at a time (register budget)
+                }
+            } else {
+                float4 lo[NB], hi[NB];
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                a0[b] += dot8(w0, lo[b], hi[b]);
-                a1[b] += dot8(w1, lo[b], hi[b]);
+                for (int b = 0; b < NB; ++b) {
+                    lo[b] = lds_f4(xl + b * xs);
+                    hi[b] = lds_f4(xl + b * xs + (xs >> 1));
+                }
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    a0[b] += dot8(w0, lo[b], hi[b]);
+                    a1[b] += dot8(w1, lo[b], hi[b]);
+                }
             }
             if ((u & 1) == 1 || u == ku - 1) ring_release(cx, s, st);
         }
@@ -645,15 +710,23 @@ __device__ __forceinline__ void rowgroup_dot(Ctx& cx, const Lds& s, Stream& st, 
         for (int b = 0; b < NB; ++b) acc[b] = 0.f;
         for (int u = 0; u < ku; ++u) {
             const uint4 w = ring_take(cx, s, st);
-            const LDS float* xl = xb + 4 * (u * 64 + cx.lane);  // 8-element chunk u * 64 + lane
-            float4 lo[NB], hi[NB];
+            const LDS float* xl = xb + 4 * (FP8 ? 2 * (u * 64 + cx.lane) : u * 64 + cx.lane);
+            if constexpr (FP8) {
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                lo[b] = lds_f4(xl + b * xs);
-                hi[b] = lds_f4(xl + b * xs + (xs >> 1));
+                for (int b = 0; b < NB; ++b) {
+                    acc[b] += unit_dot<true>(w, xl, xs, b);
+                    CBAR();  // one batch row's x live at a time (register budget)
+                }
+            } else {
+                float4 lo[NB], hi[NB];
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    lo[b] = lds_f4(xl + b * xs);
+                    hi[b] = lds_f4(xl + b * xs + (xs >> 1));
+                }
+#pragma unroll
+                for (int b = 0; b < NB; ++b) acc[b] += dot8(w, lo[b], hi[b]);
             }
-#pragma unroll
-            for (int b = 0; b < NB; ++b) acc[b] += dot8(w, lo[b], hi[b]);
             ring_advance(cx, st);
             if ((u & 3) == 3 || u == ku - 1) ring_release(cx, s, st);
         }
@@ -667,18 +740,27 @@ __device__ __forceinline__ void rowgroup_dot(Ctx& cx, const Lds& s, Stream& st, 
     }
 }
 
-template <int NROWS>
+template <int NROWS, bool FP8>
 __device__ __forceinline__ void rowgroup_dot_batch(Ctx& cx, const Lds& s, Stream& st, const LDS float* xb, int ku,
                                                    RowOut& out) {
+    if constexpr (FP8) {  // FP8 handles take at most four batch rows (register budget)
+        switch (cx.p->B) {
+        case 1: rowgroup_dot<NROWS, 1, true>(cx, s, st, xb, ku, out); break;
+        case 2: rowgroup_dot<NROWS, 2, true>(cx, s, st, xb, ku, out); break;
+        case 3: rowgroup_dot<NROWS, 3, true>(cx, s, st, xb, ku, out); break;
+        default: rowgroup_dot<NROWS, 4, true>(cx, s, st, xb, ku, out); break;
+        }
+        return;
+    }
     switch (cx.p->B) {
-    case 1: rowgroup_dot<NROWS, 1>(cx, s, st, xb, ku, out); break;
-    case 2: rowgroup_dot<NROWS, 2>(cx, s, st, xb, ku, out); break;
-    case 3: rowgroup_dot<NROWS, 3>(cx, s, st, xb, ku, out); break;
-    case 4: rowgroup_dot<NROWS, 4>(cx, s, st, xb, ku, out); break;
-    case 5: rowgroup_dot<NROWS, 5>(cx, s, st, xb, ku, out); break;
-    case 6: rowgroup_dot<NROWS, 6>(cx, s, st, xb, ku, out); break;
-    case 7: rowgroup_dot<NROWS, 7>(cx, s, st, xb, ku, out); break;
-    default: rowgroup_dot<NROWS, 8>(cx, s, st, xb, ku, out); break;
+    case 1: rowgroup_dot<NROWS, 1, FP8>(cx, s, st, xb, ku, out); break;
+    case 2: rowgroup_dot<NROWS, 2, FP8>(cx, s, st, xb, ku, out); break;
+    case 3: rowgroup_dot<NROWS, 3, FP8>(cx, s, st, xb, ku, out); break;
+    case 4: rowgroup_dot<NROWS, 4, FP8>(cx, s, st, xb, ku, out); break;
+    case 5: rowgroup_dot<NROWS, 5, FP8>(cx, s, st, xb, ku, out); break;
+    case 6: rowgroup_dot<NROWS, 6, FP8>(cx, s, st, xb, ku, out); break;
+    case 7: rowgroup_dot<NROWS, 7, FP8>(cx, s, st, xb, ku, out); break;
+    default: rowgroup_dot<NROWS, 8, FP8>(cx, s, st, xb, ku, out); break;
     }
 }
 
@@ -877,8 +959,12 @@ __device__ __forceinline__ void gather_side(Ctx& cx, const Step& sp, const Inst&
     }
 }
 
+
 // Stages the inputs of one instruction in xb (see the op bodies for layouts).
+// (FP8 weights: units of 1024 elements, so the zero padding of x covers those)
+template <bool FP8>
 __device__ __forceinline__ void gather_inst(Ctx& cx, const Step& sp, const Inst& in, LDS float* xb, LDS float* ss) {
+    constexpr int EPU = FP8 ? FP8_UNIT_ELEMS : UNIT_ELEMS;
     CParams& p = *cx.p;
     const int B = p.B, H = p.H, l = in.layer;
     switch (in.op) {
@@ -886,7 +972,7 @@ __device__ __forceinline__ void gather_inst(Ctx& cx, const Step& sp, const Inst&
     case OP_RMS_LM_HEAD: {
         const int src_layer = in.op == OP_RMS_LM_HEAD ? p.L : l;  // residual stream entering this layer
         const uint16_t* gain = in.op == OP_RMS_LM_HEAD ? p.gain_final : p.gain_attn + (size_t)l * H;
-        const int kpad = p.ku_h * UNIT_ELEMS;
+        const int kpad = p.ku_h * EPU;
         if (src_layer == 0) {
             gather_embed(cx, sp, kpad, gain, xb, ss);
         } else {
@@ -897,21 +983,21 @@ __device__ __forceinline__ void gather_inst(Ctx& cx, const Step& sp, const Inst&
     }
     case OP_RMS_UP_GATE: {
         const uint64_t* src = p.hmid + (size_t)l * B * H;
-        gather_x<true>(cx, B, H, p.ku_h * UNIT_ELEMS, [&](int b) { return src + (size_t)b * H; },
+        gather_x<true>(cx, B, H, p.ku_h * EPU, [&](int b) { return src + (size_t)b * H; },
                        p.gain_mlp + (size_t)l * H, xb, ss);
         break;
     }
     case OP_O_PROJ_RES: {
         const int K = p.Hq * p.D;
         const uint64_t* src = p.attn + (size_t)l * B * K;
-        gather_x<false>(cx, B, K, p.ku_q * UNIT_ELEMS, [&](int b) { return src + (size_t)b * K; }, nullptr, xb,
+        gather_x<false>(cx, B, K, p.ku_q * EPU, [&](int b) { return src + (size_t)b * K; }, nullptr, xb,
                         nullptr);
         break;
     }
     case OP_DOWN_RES: {
         const int c0 = p.chunk_begin[in.a], K = p.chunk_begin[in.a + 1] - c0;
         const uint64_t* src = p.act + (size_t)l * B * p.F + c0;
-        gather_x<false>(cx, B, K, p.ku_f * UNIT_ELEMS, [&](int b) { return src + (size_t)b * p.F; }, nullptr, xb,
+        gather_x<false>(cx, B, K, p.ku_f * EPU, [&](int b) { return src + (size_t)b * p.F; }, nullptr, xb,
                         nullptr);
         break;
     }
@@ -971,6 +1057,7 @@ __device__ __forceinline__ Inst decode_inst(const u32x4 raw) {
 // Gather wave g's loop over instructions pc0 + g, pc0 + g + NGATHER, ... of
 // this CU's queue: the gather waves take turns, so one wave's poll round trip
 // overlaps another's staging.
+template <bool FP8>
 __device__ __forceinline__ void gatherer(Ctx& cx, const Lds& s, const Step& sp, uint32_t qb, uint32_t pc0,
                                          uint32_t pc1, int g) {
     CParams& p = *cx.p;
@@ -1005,7 +1092,7 @@ __device__ __forceinline__ void gatherer(Ctx& cx, const Lds& s, const Step& sp, 
             copy_staged(cx, xslot(s, p, prev_slot), xslot(s, p, slot), p.B * (int)uni((uint32_t)p.xstride),
                         s.ss + prev_slot * MAX_BATCH, s.ss + slot * MAX_BATCH, p.B);
         else
-            gather_inst(cx, sp, in, xslot(s, p, slot), s.ss + slot * MAX_BATCH);
+            gather_inst<FP8>(cx, sp, in, xslot(s, p, slot), s.ss + slot * MAX_BATCH);
         prev_key = key;
         prev_slot = slot;
         if (uni(cx.aborted)) break;
@@ -1047,7 +1134,7 @@ struct DownAcc {
 
 // KU > 0: batch-1 path with KU units per row (x slice in registers);
 // KU == 0: general path.
-template <int KU>
+template <int KU, bool FP8>
 __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint32_t r, uint32_t slot, const Inst& in,
                                         LDS float* xb, const Step& sp, DownAcc& da) {
     CParams& p = *cx.p;
@@ -1060,16 +1147,22 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
     if ((in.op == OP_RMS_QKV_ROPE || in.op == OP_RMS_LM_HEAD || in.op == OP_RMS_UP_GATE) && cx.lane < B)
         scale = rsqrtf(s.ss[slot * MAX_BATCH + cx.lane] * (1.0f / (float)H) + p.eps);
 
-    XSlice<KU == 0 ? 1 : KU> xs;
+    XSlice<KU == 0 ? 1 : (FP8 ? 2 * KU : KU)> xs;
     const uint32_t ru = __builtin_amdgcn_readfirstlane((uint32_t)p.ring_units);
-    if constexpr (KU > 0) load_xslice<KU>(cx, xb, __builtin_amdgcn_readfirstlane(p.xstride), xs);
+    if constexpr (KU > 0) load_xslice<KU, FP8>(cx, xb, __builtin_amdgcn_readfirstlane(p.xstride), xs);
     auto dot1 = [&](RowOut& o) {
-        if constexpr (KU > 0) rowgroup_dot_b1<KU, 1>(cx, s, st, xs, ru, o);
-        else rowgroup_dot_batch<1>(cx, s, st, xb, ku, o);
+        if constexpr (KU > 0) rowgroup_dot_b1<KU, 1, FP8>(cx, s, st, xs, ru, o);
+        else rowgroup_dot_batch<1, FP8>(cx, s, st, xb, ku, o);
     };
     auto dot2 = [&](RowOut& o) {
-        if constexpr (KU > 0) rowgroup_dot_b1<KU, 2>(cx, s, st, xs, ru, o);
-        else rowgroup_dot_batch<2>(cx, s, st, xb, ku, o);
+        if constexpr (KU > 0) rowgroup_dot_b1<KU, 2, FP8>(cx, s, st, xs, ru, o);
+        else rowgroup_dot_batch<2, FP8>(cx, s, st, xb, ku, o);
+    };
+    // FP8 weights: each row sum times the scale of the row's matrix
+    auto fp8_scale = [&](RowOut& o, uint32_t kind0, uint32_t kind1) {
+        const float* wsc = p.wscale + (size_t)l * MATS_PER_LAYER;
+        o.mine[0] *= wsc[kind0];
+        o.mine[1] *= wsc[kind1];
     };
 
     // ---- this wave's row-groups; lane b < B finishes batch row b
@@ -1086,6 +1179,11 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
         switch (in.op) {
         case OP_RMS_QKV_ROPE: {
             dot2(o);
+            if constexpr (FP8) {  // the pair's matrix: q, k or v rows of its KV group
+                const int PGf = (p.G + 2) * half, tf = rg % PGf;
+                const uint32_t kind = tf < p.G * half ? MAT_WQ : tf < (p.G + 1) * half ? MAT_WK : MAT_WV;
+                fp8_scale(o, kind, kind);
+            }
             if (lane_row) {
                 const int pos = sp.pos;
                 const float y1 = o.mine[0] * scale, y2 = o.mine[1] * scale;
@@ -1133,11 +1231,13 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
                 else hin = wait_word(cx, p.hout + ((size_t)(l - 1) * B + b) * H + rg);
             }
             dot1(o);
+            if constexpr (FP8) fp8_scale(o, MAT_WO, MAT_WO);
             if (lane_row) st_tag(p.hmid + ((size_t)l * B + b) * H + rg, hin + o.mine[0], cx.epoch);
             break;
         }
         case OP_RMS_UP_GATE: {
             dot2(o);
+            if constexpr (FP8) fp8_scale(o, MAT_GATE, MAT_UP);
             if (lane_row) {
                 const float gt = o.mine[0] * scale, up = o.mine[1] * scale;
                 const float a = gt / (1.0f + __expf(-gt)) * up;  // silu(gate) * up
@@ -1158,6 +1258,7 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
                     prev = gld_now(acc);
             }
             dot1(o);
+            if constexpr (FP8) fp8_scale(o, MAT_DOWN, MAT_DOWN);
             const float v = o.mine[0] + prev;
             if (last) {
                 if (lane_row) st_tag(p.hout + ((size_t)l * B + b) * H + rg, hm + v, cx.epoch);
@@ -1171,8 +1272,9 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
             }
             break;
         }
-        default: {  // OP_RMS_LM_HEAD
+        default: {  // OP_RMS_LM_HEAD (its scale follows the last layer's matrices)
             dot1(o);
+            if constexpr (FP8) fp8_scale(o, (uint32_t)(p.L - l) * MATS_PER_LAYER, 0u);
             if (lane_row) gst(sp.logits + (size_t)b * p.V + rg, o.mine[0] * scale);
             break;
         }
@@ -1396,7 +1498,7 @@ __device__ __forceinline__ void op_reduce(Ctx& cx, const Lds& s, uint32_t r, con
 // head size, each with and without the profile/timeline instrumentation (its
 // bookkeeping costs registers and scalar work on every instruction, so the
 // plain build leaves it out entirely).
-template <int HEAD_DIM, bool INSTR>
+template <int HEAD_DIM, bool INSTR, bool FP8>
 __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const int32_t* tokens,
                                           const int32_t* positions, uint16_t* kv, float* logits, int stage,
                                           uint32_t flags) {
@@ -1467,7 +1569,7 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
     const uint32_t* uoff = p.unit_off + ((size_t)qb + cx.cu) * NW;
     if (wave >= NW + NWL) {  // gather waves
         cx.wave = wave;
-        gatherer(cx, s, sp, qb, pc0, pc1, wave - NW - NWL);
+        gatherer<FP8>(cx, s, sp, qb, pc0, pc1, wave - NW - NWL);
         flush_prof(wave);
         return;
     }
@@ -1514,9 +1616,9 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
         case OP_ATTN_REDUCE: op_reduce(cx, s, r, in, xb); break;
         default: {
             const int ku = in.op == OP_O_PROJ_RES ? p.ku_q : in.op == OP_DOWN_RES ? p.ku_f : p.ku_h;
-            if (!batch1_path(p.B, ku)) op_gemv<0>(cx, s, st, r, slot, in, xb, sp, da);
-            else if (ku == 4) op_gemv<4>(cx, s, st, r, slot, in, xb, sp, da);
-            else op_gemv<2>(cx, s, st, r, slot, in, xb, sp, da);
+            if (!batch1_path(p.B, ku, FP8)) op_gemv<0, FP8>(cx, s, st, r, slot, in, xb, sp, da);
+            else if (!FP8 && ku == 4) op_gemv<FP8 ? 2 : 4, FP8>(cx, s, st, r, slot, in, xb, sp, da);
+            else op_gemv<2, FP8>(cx, s, st, r, slot, in, xb, sp, da);
             break;
         }
         }
@@ -1542,19 +1644,19 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
 }
 
 // The whole step in one launch (every workgroup runs its full queue).
-template <int HEAD_DIM, bool INSTR>
+template <int HEAD_DIM, bool INSTR, bool FP8 = false>
 __global__ void __launch_bounds__(WG_THREADS, 1)
 mk_decode_kernel(const Params* __restrict__ pp, const int32_t* tokens, const int32_t* positions, uint16_t* kv,
                  float* logits, int stage, uint32_t flags) {
-    step_body<HEAD_DIM, INSTR>(pp, tokens, positions, kv, logits, -1, flags);
+    step_body<HEAD_DIM, INSTR, FP8>(pp, tokens, positions, kv, logits, -1, flags);
 }
 
 // One stage of the step (one op of one layer) per launch.
-template <int HEAD_DIM, bool INSTR>
+template <int HEAD_DIM, bool INSTR, bool FP8 = false>
 __global__ void __launch_bounds__(WG_THREADS, 1)
 mk_stage_kernel(const Params* __restrict__ pp, const int32_t* tokens, const int32_t* positions, uint16_t* kv,
                 float* logits, int stage, uint32_t flags) {
-    step_body<HEAD_DIM, INSTR>(pp, tokens, positions, kv, logits, stage, flags);
+    step_body<HEAD_DIM, INSTR, FP8>(pp, tokens, positions, kv, logits, stage, flags);
 }
 
 // ------------------------------------------------------------ pack kernel --
@@ -1564,11 +1666,59 @@ struct PackRowDev {
     uint64_t dst_unit;
 };
 
-// One workgroup per stream row: dst[unit .. unit + kunits) = src row slice, zero padded.
+// OCP E4M3 code of the value nearest to x (ties to the even mantissa), +-448
+// for |x| >= 448: below 2^-6 the spacing is 2^-9 (subnormals, and 8 * 2^-9 is
+// the smallest normal's code 0x08); above, the 23-bit fp32 mantissa is
+// rounded to 3 bits.
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const float a = fabsf(x);
+    if (!(a < 448.f)) return sign | 0x7Eu;
+    if (a < 0x1p-6f) return sign | (uint32_t)rintf(a * 512.f);
+    int e = (int)((u >> 23) & 0xffu) - 127;  // -6 .. 8
+    uint32_t q = (u >> 20) & 7u;
+    const uint32_t low = u & 0xfffffu;
+    if (low > 0x80000u || (low == 0x80000u && (q & 1u))) ++q;
+    if (q == 8u) {
+        q = 0;
+        ++e;
+    }
+    if (e > 8 || (e == 8 && q == 7u)) return sign | 0x7Eu;
+    return sign | ((uint32_t)(e + 7) << 3) | q;
+}
+
+// Largest |w| of n bf16 weights as bf16 bits (sign cleared: finite bf16
+// magnitudes order like their bits), folded into *out with an atomic max.
+__global__ void __launch_bounds__(256) mk_amax_kernel(const uint16_t* w, size_t n, uint32_t* out) {
+    uint32_t m = 0;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+        const uint32_t v = w[i] & 0x7fffu;
+        m = v > m ? v : m;
+    }
+    for (int d = 32; d >= 1; d >>= 1) {
+        const uint32_t o = (uint32_t)__shfl_xor((int)m, d);
+        m = o > m ? o : m;
+    }
+    if ((threadIdx.x & 63) == 0) atomicMax(out, m);
+}
+
+// One workgroup per stream row: dst[unit .. unit + kunits) = src row slice, zero padded;
+// with fp8, the codes of fp32(w / scale[mat]) (1024 per unit) instead of the bf16 values.
 __global__ void __launch_bounds__(256) mk_pack_kernel(const PackRowDev* rows, uint32_t n, const uint16_t* const* mats,
-                                                      uint8_t* dst) {
+                                                      uint8_t* dst, int fp8, const float* scales) {
     for (uint32_t r = blockIdx.x; r < n; r += gridDim.x) {
         const PackRowDev pr = rows[r];
+        if (fp8) {
+            const uint16_t* src = mats[pr.mat] + (size_t)pr.row * pr.src_cols + pr.k0;
+            const float sc = scales[pr.mat];
+            const uint32_t n_el = pr.kunits * FP8_UNIT_ELEMS;
+            for (uint32_t e = threadIdx.x; e < n_el; e += blockDim.x) {
+                uint8_t* out = dst + (pr.dst_unit + (uint64_t)(e / FP8_UNIT_ELEMS) * NW * pr.ustride) * UNIT_BYTES;
+                out[e % FP8_UNIT_ELEMS] = e < pr.klen ? (uint8_t)e4m3_code(bf2f(src[e]) / sc) : (uint8_t)0;
+            }
+            continue;
+        }
         const uint16_t* src = mats[pr.mat] + (size_t)pr.row * pr.src_cols + pr.k0;
         const uint32_t n_el = pr.kunits * UNIT_ELEMS;
         for (uint32_t e = threadIdx.x; e < n_el; e += blockDim.x) {
@@ -1712,14 +1862,19 @@ hipError_t launch_step(const Params* dev_params, int head_dim, int ncu, size_t l
     uint16_t* kv16 = (uint16_t*)kv;
     void* args[] = {(void*)&dev_params, (void*)&tokens, (void*)&positions, (void*)&kv16, (void*)&logits,
                     (void*)&stage, (void*)&flags};
-    const bool instr = (flags & KF_INSTRUMENTED) != 0;
+    const bool instr = (flags & KF_INSTRUMENTED) != 0, fp8 = (flags & KF_FP8) != 0;
+    if (fp8 && instr) return hipErrorInvalidValue;  // no instrumented FP8 build
     if (stage < 0) {
-        const void* fn = head_dim == 64 ? (instr ? (const void*)mk_decode_kernel<64, true> : (const void*)mk_decode_kernel<64, false>)
-                                        : (instr ? (const void*)mk_decode_kernel<128, true> : (const void*)mk_decode_kernel<128, false>);
+        const void* fn =
+            fp8 ? (head_dim == 64 ? (const void*)mk_decode_kernel<64, false, true> : (const void*)mk_decode_kernel<128, false, true>)
+            : head_dim == 64 ? (instr ? (const void*)mk_decode_kernel<64, true> : (const void*)mk_decode_kernel<64, false>)
+                             : (instr ? (const void*)mk_decode_kernel<128, true> : (const void*)mk_decode_kernel<128, false>);
         return hipLaunchCooperativeKernel(fn, dim3(ncu), dim3(WG_THREADS), args, (unsigned)lds_bytes, stream);
     }
-    const void* fn = head_dim == 64 ? (instr ? (const void*)mk_stage_kernel<64, true> : (const void*)mk_stage_kernel<64, false>)
-                                    : (instr ? (const void*)mk_stage_kernel<128, true> : (const void*)mk_stage_kernel<128, false>);
+    const void* fn =
+        fp8 ? (head_dim == 64 ? (const void*)mk_stage_kernel<64, false, true> : (const void*)mk_stage_kernel<128, false, true>)
+        : head_dim == 64 ? (instr ? (const void*)mk_stage_kernel<64, true> : (const void*)mk_stage_kernel<64, false>)
+                         : (instr ? (const void*)mk_stage_kernel<128, true> : (const void*)mk_stage_kernel<128, false>);
     return hipLaunchKernel(fn, dim3(ncu), dim3(WG_THREADS), args, lds_bytes, stream);
 }
 
@@ -1727,7 +1882,9 @@ hipError_t set_step_kernel_lds(size_t lds_bytes) {
     const void* fns[] = {(const void*)mk_decode_kernel<64, false>, (const void*)mk_decode_kernel<128, false>,
                          (const void*)mk_stage_kernel<64, false>,  (const void*)mk_stage_kernel<128, false>,
                          (const void*)mk_decode_kernel<64, true>,  (const void*)mk_decode_kernel<128, true>,
-                         (const void*)mk_stage_kernel<64, true>,   (const void*)mk_stage_kernel<128, true>};
+                         (const void*)mk_stage_kernel<64, true>,   (const void*)mk_stage_kernel<128, true>,
+                         (const void*)mk_decode_kernel<64, false, true>, (const void*)mk_decode_kernel<128, false, true>,
+                         (const void*)mk_stage_kernel<64, false, true>,  (const void*)mk_stage_kernel<128, false, true>};
     for (const void* fn : fns) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
         if (e != hipSuccess) return e;
@@ -1735,10 +1892,19 @@ hipError_t set_step_kernel_lds(size_t lds_bytes) {
     return hipSuccess;
 }
 
-hipError_t launch_pack(const void* rows, uint32_t n, const uint16_t* const* mats, uint8_t* dst, hipStream_t stream) {
+hipError_t launch_pack(const void* rows, uint32_t n, const uint16_t* const* mats, uint8_t* dst, int fp8,
+                       const float* scales, hipStream_t stream) {
     if (n == 0) return hipSuccess;
     const uint32_t grid = n < 65536 ? n : 65536;
-    hipLaunchKernelGGL(mk_pack_kernel, dim3(grid), dim3(256), 0, stream, (const PackRowDev*)rows, n, mats, dst);
+    hipLaunchKernelGGL(mk_pack_kernel, dim3(grid), dim3(256), 0, stream, (const PackRowDev*)rows, n, mats, dst, fp8,
+                       scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_amax(const uint16_t* w, size_t n, uint32_t* out, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    const size_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(mk_amax_kernel, dim3(blocks < 4096 ? (uint32_t)blocks : 4096u), dim3(256), 0, stream, w, n, out);
     return hipGetLastError();
 }
 

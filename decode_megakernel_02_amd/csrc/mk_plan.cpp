@@ -41,6 +41,9 @@ int validate_config(const mk_config& c, std::string& err) {
     if (NW % G) return unsup("n_q_heads / n_kv_heads must divide 8");
     if (c.hidden % 8 || c.ffn % 8) return unsup("hidden and ffn must be multiples of 8");
     if (c.batch > MAX_BATCH) return unsup("batch must be <= 8");
+    if ((c.flags & MK_FLAG_FP8_WEIGHTS) && (c.flags & (MK_FLAG_PROFILE | MK_FLAG_TRACE)))
+        return unsup("FP8 weights cannot be combined with profiling or tracing");
+    if ((c.flags & MK_FLAG_FP8_WEIGHTS) && c.batch > 4) return unsup("FP8 weights take batch <= 4");
     if (c.n_chunks > 16) return unsup("n_chunks must be <= 16");
     if (c.hidden > 16384 || c.ffn > 65536) return unsup("hidden <= 16384 and ffn <= 65536");
     if ((long long)c.max_seq > (1LL << 24)) return unsup("max_seq <= 2^24");
@@ -151,8 +154,10 @@ int build_plan(const mk_config& c, int ncu, Plan& p, std::string& err) {
         err = "n_splits must be <= 256";
         return MK_ERR_UNSUPPORTED_SHAPE;
     }
-    p.ku_h = ceil_div(p.H, UNIT_ELEMS);
-    p.ku_q = ceil_div(p.Hq * p.D, UNIT_ELEMS);
+    p.fp8 = (c.flags & MK_FLAG_FP8_WEIGHTS) != 0;
+    p.epu = p.fp8 ? FP8_UNIT_ELEMS : UNIT_ELEMS;
+    p.ku_h = ceil_div(p.H, p.epu);
+    p.ku_q = ceil_div(p.Hq * p.D, p.epu);
     int maxc = 0;
     for (int i = 0; i <= p.n_chunk; ++i) {
         // chunk boundaries on multiples of 8 elements
@@ -160,7 +165,7 @@ int build_plan(const mk_config& c, int ncu, Plan& p, std::string& err) {
         if (i == p.n_chunk) p.chunk_begin[i] = p.F;
         if (i) maxc = std::max(maxc, p.chunk_begin[i] - p.chunk_begin[i - 1]);
     }
-    p.ku_f = ceil_div(maxc, UNIT_ELEMS);
+    p.ku_f = ceil_div(maxc, p.epu);
     p.n_stages = p.L * STAGES_PER_LAYER + 1;
 
     Builder b(p);
@@ -278,7 +283,7 @@ int build_plan(const mk_config& c, int ncu, Plan& p, std::string& err) {
                 uint64_t& cur = cursor[(size_t)cu * NW + i % NW];  // unit index within the wave's stream
                 // general GEMV path: the two rows of a row-group alternate unit by unit, so that
                 // each x slice read from LDS serves both rows
-                const bool inter = nrows == 2 && !batch1_path(p.B, (int)ku);
+                const bool inter = nrows == 2 && !batch1_path(p.B, (int)ku, p.fp8);
                 for (int k = 0; k < nrows; ++k) {
                     const uint64_t first = inter ? cur + k : cur;
                     p.pack.push_back(PackRow{rr[k].mat, rr[k].row, rr[k].k0, rr[k].klen, rr[k].cols, ku,
@@ -435,28 +440,11 @@ bool check_plan(const Plan& p, std::string& err) {
         }
     }
     // --- pack table: every entry reads inside its source matrix and writes inside the buffer
-    auto mat_shape = [&](uint32_t mat, uint32_t& rows, uint32_t& cols) {
-        if (mat == (uint32_t)p.lm_mat()) {
-            rows = p.V;
-            cols = p.H;
-            return true;
-        }
-        if (mat >= (uint32_t)p.lm_mat()) return false;
-        const uint32_t QD = p.Hq * p.D, KD = p.Hkv * p.D;
-        switch (mat % MATS_PER_LAYER) {
-        case MAT_WQ: rows = QD; cols = p.H; break;
-        case MAT_WK: case MAT_WV: rows = KD; cols = p.H; break;
-        case MAT_WO: rows = p.H; cols = QD; break;
-        case MAT_GATE: case MAT_UP: rows = p.F; cols = p.H; break;
-        default: rows = p.H; cols = p.F; break;  // MAT_DOWN
-        }
-        return true;
-    };
     for (size_t i = 0; i < p.pack.size(); ++i) {
         const PackRow& r = p.pack[i];
         uint32_t rows = 0, cols = 0;
-        if (!mat_shape(r.mat, rows, cols) || r.src_cols != cols || (uint64_t)r.k0 + r.klen > cols ||
-            r.row >= rows || r.kunits == 0 || (uint64_t)r.klen > (uint64_t)r.kunits * UNIT_ELEMS ||
+        if (!p.mat_shape(r.mat, rows, cols) || r.src_cols != cols || (uint64_t)r.k0 + r.klen > cols ||
+            r.row >= rows || r.kunits == 0 || (uint64_t)r.klen > (uint64_t)r.kunits * p.epu ||
             (r.ustride != 1 && r.ustride != 2) ||
             r.dst_unit + (uint64_t)(r.kunits - 1) * NW * r.ustride >= p.total_units) {
             snprintf(buf, sizeof buf, "pack entry %zu out of bounds (mat %u row %u k0 %u klen %u)", i, r.mat, r.row,

@@ -11,8 +11,7 @@
 
 namespace mk {
 
-// Source matrices of the pack table.  Layer matrices: layer * MATS_PER_LAYER + kind.
-enum MatKind : uint32_t { MAT_WQ = 0, MAT_WK, MAT_WV, MAT_WO, MAT_GATE, MAT_UP, MAT_DOWN, MATS_PER_LAYER };
+// Source matrices of the pack table: MatKind (mk_internal.h), layer * MATS_PER_LAYER + kind.
 
 // One row of one stream: copy src[row][k0 .. k0+klen) (bf16), zero-pad to kunits*512.
 struct PackRow {
@@ -36,6 +35,8 @@ struct Plan {
     float eps = 0, theta = 0;
     // schedule parameters
     int ncu = 0, n_split = 0, n_chunk = 0;
+    bool fp8 = false;
+    int epu = UNIT_ELEMS;                // weight elements per unit (1024 with FP8 codes)
     int ku_h = 0, ku_q = 0, ku_f = 0;
     int chunk_begin[17] = {0};
     int n_stages = 0;
@@ -51,6 +52,24 @@ struct Plan {
     std::vector<PackRow> pack;
 
     int lm_mat() const { return L * MATS_PER_LAYER; }
+    // rows and columns of source matrix `mat`; false for an index past the LM head
+    bool mat_shape(uint32_t mat, uint32_t& rows, uint32_t& cols) const {
+        if (mat == (uint32_t)lm_mat()) {
+            rows = V;
+            cols = H;
+            return true;
+        }
+        if (mat > (uint32_t)lm_mat()) return false;
+        const uint32_t QD = Hq * D, KD = Hkv * D;
+        switch (mat % MATS_PER_LAYER) {
+        case MAT_WQ: rows = QD; cols = H; break;
+        case MAT_WK: case MAT_WV: rows = KD; cols = H; break;
+        case MAT_WO: rows = H; cols = QD; break;
+        case MAT_GATE: case MAT_UP: rows = F; cols = H; break;
+        default: rows = H; cols = F; break;  // MAT_DOWN
+        }
+        return true;
+    }
     int n_mats() const { return L * MATS_PER_LAYER + 1; }
 };
 

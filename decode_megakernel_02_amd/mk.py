@@ -58,6 +58,7 @@ EXPORTS = ["mk_create", "mk_load_weights", "mk_kv_cache_bytes", "mk_decode_step"
            "mk_graph_create", "mk_graph_launch", "mk_graph_destroy"]
 MK_FLAG_PROFILE = 1
 MK_FLAG_TRACE = 2
+MK_FLAG_FP8_WEIGHTS = 4
 MK_GRAPH_MULTIKERNEL = 1
 MK_GRAPH_EMPTY = 2
 TRACE_SLOTS = 52

@@ -49,12 +49,13 @@ class GpuDecoder:
     """A handle plus its device buffers; steps through mk_decode_step(_multikernel)."""
 
     def __init__(self, shape: synth.ModelShape, weights, batch: int, max_seq: int, n_cus: int = 0,
-                 n_splits: int = 0, n_chunks: int = 0, kv_init: Optional[np.ndarray] = None):
+                 n_splits: int = 0, n_chunks: int = 0, kv_init: Optional[np.ndarray] = None, flags: int = 0):
         import torch
         from decode_megakernel_02_amd import mk
         self.mk, self.torch = mk, torch
         self.shape, self.B, self.max_seq = shape, batch, max_seq
-        self.cfg = mk.make_config(shape, batch, max_seq, n_cus=n_cus, n_splits=n_splits, n_chunks=n_chunks)
+        self.cfg = mk.make_config(shape, batch, max_seq, n_cus=n_cus, n_splits=n_splits, n_chunks=n_chunks,
+                                  flags=flags)
         self.h = mk.mk_create(self.cfg)
         self.dw = device_weights(weights)
         mk.mk_load_weights(self.h, self.dw, mk.current_stream())
@@ -106,10 +107,10 @@ class GpuDecoder:
 
 
 def oracle_replay(shape, weights, batch, max_seq, run: Run, kv_init: Optional[np.ndarray] = None,
-                  nthreads: int = 8) -> List[np.ndarray]:
+                  nthreads: int = 8, fp8: bool = False) -> List[np.ndarray]:
     """Teacher-forced oracle logits for the exact inputs the GPU saw."""
     import oracle
-    orc = oracle.Oracle(shape, weights, batch, max_seq)
+    orc = oracle.Oracle(shape, weights, batch, max_seq, fp8=fp8)
     cache = (np.zeros(synth.kv_cache_shape(shape, batch, max_seq), dtype=np.uint16) if kv_init is None
              else kv_init.copy())
     return [orc.decode_step(cache, t, p, nthreads) for t, p in zip(run.tokens, run.positions)]
