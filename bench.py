@@ -193,6 +193,8 @@ def main():
                     help="write the profiles/ per-op table of the per-op-launch path from a rocprofv3 "
                          "--kernel-trace run and exit")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: every core, at most 64)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="FP8 (E4M3, per-matrix scale) weights instead of bf16 (a variant, not the headline)")
     ap.add_argument("--cpu-only", action="store_true",
                     help="time only the CPU oracle on the workload and print it as one JSON line")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -261,7 +263,7 @@ def main():
     dw = {"embed": up(weights["embed"]), "final_norm": up(weights["final_norm"]),
           "lm_head": up(weights["lm_head"]) if weights["lm_head"] is not None else None,
           "layers": [{k: up(v) for k, v in L.items()} for L in weights["layers"]]}
-    cfg = mk.make_config(shape, B, max_seq)
+    cfg = mk.make_config(shape, B, max_seq, flags=mk.MK_FLAG_FP8_WEIGHTS if args.fp8 else 0)
     h = mk.mk_create(cfg)
     stream = mk.current_stream()
     mk.mk_load_weights(h, dw, stream)
@@ -390,10 +392,10 @@ def main():
 
     # ---- roofline of the dominant (only) kernel
     keys = R.mean_keys(P, W, K)  # the event-timed pass covers steps W .. W+K-1
-    bytes_step = R.step_bytes(shape, B, keys)
+    bytes_step = R.step_bytes(shape, B, keys, 1 if args.fp8 else 2)
     achieved = bytes_step / (kern_mean * 1e-6) / 1e9
     peak = R.MI355X_HBM_PEAK_GBPS
-    traffic = measured_traffic(args.workload)
+    traffic = None if args.fp8 else measured_traffic(args.workload)  # counters were taken for bf16
     ms_per_step = wall / K * 1e3
 
     out = {
@@ -407,11 +409,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8-e4m3 weights" if args.fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": f"{shape.name}, batch {B}, {P}-token synthetic KV prefill, greedy decode",
                    "batch": B, "prompt_tokens": P, "decode_steps": K, "kv_prefill": "seeded N(0,1) bf16 rows",
-                   "weights": "seeded N(0,0.02) bf16, norm gains 1.0", "accumulate": "fp32",
+                   "weights": "seeded N(0,0.02) bf16, norm gains 1.0" + (
+                       ", projections and LM head quantised to FP8 E4M3 with one scale per matrix" if args.fp8 else ""),
+                   "accumulate": "fp32",
                    "kernel_launches_per_step": 1},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": peak, "unit": "GB/s", "frac": achieved / peak,
                      "traffic": traffic},

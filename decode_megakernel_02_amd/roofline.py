@@ -11,14 +11,15 @@ from __future__ import annotations
 MI355X_HBM_PEAK_GBPS = 8000.0  # published HBM3E peak, GB/s
 
 
-def weight_bytes_read(shape, batch: int) -> int:
-    """bf16 weight bytes streamed per step: every layer matrix and norm gain,
-    the LM head (the embedding matrix when tied) and the final norm gain,
-    plus one embedding row per batch row."""
+def weight_bytes_read(shape, batch: int, matrix_bytes: int = 2) -> int:
+    """Weight bytes streamed per step: every layer matrix (matrix_bytes per element:
+    2 for bf16, 1 for FP8 codes), every norm gain (bf16), the LM head (the embedding
+    matrix when tied; a matrix too) and the final norm gain, plus one bf16 embedding
+    row per batch row."""
     H, D = shape.hidden, shape.head_dim
-    per_layer = (shape.n_q_heads * D * H + 2 * shape.n_kv_heads * D * H + H * shape.n_q_heads * D
-                 + 3 * shape.ffn * H + 2 * H)
-    return 2 * (shape.n_layers * per_layer + shape.vocab * H + H + batch * H)
+    mats = (shape.n_q_heads * D * H + 2 * shape.n_kv_heads * D * H + H * shape.n_q_heads * D
+            + 3 * shape.ffn * H)
+    return matrix_bytes * (shape.n_layers * mats + shape.vocab * H) + 2 * (shape.n_layers * 2 * H + H + batch * H)
 
 
 def kv_bytes_read(shape, batch: int, keys: float) -> float:
@@ -26,8 +27,8 @@ def kv_bytes_read(shape, batch: int, keys: float) -> float:
     return batch * keys * shape.n_layers * 2 * shape.n_kv_heads * shape.head_dim * 2
 
 
-def step_bytes(shape, batch: int, keys: float) -> float:
-    return weight_bytes_read(shape, batch) + kv_bytes_read(shape, batch, keys)
+def step_bytes(shape, batch: int, keys: float, matrix_bytes: int = 2) -> float:
+    return weight_bytes_read(shape, batch, matrix_bytes) + kv_bytes_read(shape, batch, keys)
 
 
 def mean_keys(prompt: int, first_step: int, n_steps: int) -> float:
