@@ -34,7 +34,6 @@ int validate_config(const mk_config& c, std::string& err) {
         return bad("every dimension must be positive");
     if (!(c.rms_eps >= 0.0f) || !(c.rope_theta > 0.0f)) return bad("rms_eps >= 0 and rope_theta > 0 required");
     if (c.n_cus < 0 || c.n_splits < 0 || c.n_chunks < 0) return bad("n_cus, n_splits, n_chunks must be >= 0");
-    if (c.hidden != c.n_q_heads * c.head_dim) return unsup("hidden must equal n_q_heads * head_dim");
     if (c.n_q_heads % c.n_kv_heads) return unsup("n_kv_heads must divide n_q_heads");
     if (c.head_dim != 64 && c.head_dim != 128) return unsup("head_dim must be 64 or 128");
     int G = c.n_q_heads / c.n_kv_heads;
@@ -46,6 +45,7 @@ int validate_config(const mk_config& c, std::string& err) {
     if ((c.flags & MK_FLAG_FP8_WEIGHTS) && c.batch > 4) return unsup("FP8 weights take batch <= 4");
     if (c.n_chunks > 16) return unsup("n_chunks must be <= 16");
     if (c.hidden > 16384 || c.ffn > 65536) return unsup("hidden <= 16384 and ffn <= 65536");
+    if ((long long)c.n_q_heads * c.head_dim > 16384) return unsup("n_q_heads * head_dim <= 16384");
     if ((long long)c.max_seq > (1LL << 24)) return unsup("max_seq <= 2^24");
     return MK_OK;
 }

@@ -48,7 +48,7 @@ typedef enum {
  * LM head (the embedding matrix when tied_embeddings).                    */
 typedef struct {
     int32_t n_layers;
-    int32_t hidden;          /* H; must equal n_q_heads * head_dim */
+    int32_t hidden;          /* H; n_q_heads * head_dim may differ (a tensor-parallel shard) */
     int32_t n_q_heads;
     int32_t n_kv_heads;      /* divides n_q_heads */
     int32_t head_dim;        /* D: 64 or 128 */

@@ -110,6 +110,11 @@ LLAMA_1B = ModelShape("llama-3.2-1b-shaped", 16, 2048, 32, 8, 64, 8192, 128256, 
                       500000.0, True)
 LLAMA_8B = ModelShape("llama-3.1-8b-shaped", 32, 4096, 32, 8, 128, 14336, 128256, 1e-5,
                       500000.0, False)
+# one GPU's share of the 1B shape under 8-way tensor parallelism with one KV
+# group per GPU: 4 query heads, 1 K/V head, F/8 gate/up rows (and down
+# columns), V/8 rows of the tied embedding / LM head; the hidden size stays H
+LLAMA_1B_TP8_SHARD = ModelShape("llama-3.2-1b-tp8-shard", 16, 2048, 4, 1, 64, 1024, 16032, 1e-5,
+                                500000.0, True)
 
 WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
     Workload("tiny_b1_p32", TINY, 1, 32, 16, "real"),
@@ -119,6 +124,7 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
     Workload("llama1b_b1_p8192", LLAMA_1B, 1, 8192, 128, "synthetic"),
     Workload("llama1b_b1_p32768", LLAMA_1B, 1, 32768, 128, "synthetic"),
     Workload("llama8b_b1_p1024", LLAMA_8B, 1, 1024, 128, "synthetic"),
+    Workload("llama1b_tp8shard_b1_p1024", LLAMA_1B_TP8_SHARD, 1, 1024, 256, "synthetic"),
 ]}
 
 WEIGHT_SEED = 1234

@@ -41,6 +41,7 @@ def test_status_strings():
     ("TINY", 1, 64, 1), ("TINY", 2, 64, 7), ("TINY", 8, 1024, 256), ("TINY", 3, 40, 64),
     ("LLAMA_1B", 1, 1040, 256), ("LLAMA_1B", 4, 1040, 256), ("LLAMA_1B", 8, 1040, 256),
     ("LLAMA_1B", 1, 32784, 256), ("LLAMA_1B", 1, 1040, 200), ("LLAMA_8B", 1, 1040, 256),
+    ("LLAMA_1B_TP8_SHARD", 1, 1040, 256), ("LLAMA_1B_TP8_SHARD", 4, 1040, 256),
 ])
 def test_schedule_is_valid(shape_name, batch, max_seq, ncus):
     shape = getattr(synth, shape_name)
@@ -65,10 +66,13 @@ def test_schedule_is_valid(shape_name, batch, max_seq, ncus):
     assert info.max_stream_bytes_per_wave * 8 * ncus >= info.packed_weight_bytes
 
 
-def test_schedule_balances_weight_streams():
-    info = mk.mk_schedule_inspect(mk.make_config(synth.LLAMA_1B, 1, 1040), 256)
+@pytest.mark.parametrize("shape_name,bound", [("LLAMA_1B", 1.1), ("LLAMA_8B", 1.12)])
+def test_schedule_balances_weight_streams(shape_name, bound):
+    """The eight compute waves of a CU get nearly equal weight streams at the
+    full-size shapes."""
+    info = mk.mk_schedule_inspect(mk.make_config(getattr(synth, shape_name), 1, 1040), 256)
     mean = info.packed_weight_bytes / (256 * 8)
-    assert info.max_stream_bytes_per_wave <= 1.1 * mean
+    assert info.max_stream_bytes_per_wave <= bound * mean
 
 
 @pytest.mark.parametrize("field,value", [

@@ -1,5 +1,7 @@
 """GPU parity at the other benchmark shapes: batch 4 and 8, long contexts
-(8K and 32K tokens in the cache) and the 8B shape (head_dim 128, untied head).
+(8K and 32K tokens in the cache), the 8B shape (head_dim 128, untied head) and
+one GPU's share of the 1B shape under 8-way tensor parallelism (hidden size
+2048 with 4 query heads, so n_q_heads * head_dim differs from it).
 
 Each case pre-fills the cache with seeded N(0, 1) bf16 rows (identical bytes on
 both sides), runs a few greedy steps through the C ABI and compares every step
@@ -79,3 +81,15 @@ def test_llama1b_dims_nonunit_norm_gains():
     weights = synth.make_weights(shape, gain_std=0.3)
     stats = run_and_compare(shape, weights, 1, [64], 2, "llama1b-dims 2 layers, gains 1 + N(0, 0.3)")
     assert stats["max_abs"] < 1e-3  # fp32 path: ~1e-5; folded-gain rounding gave ~2e-2
+
+
+@pytest.mark.parametrize("batch,multikernel", [(1, False), (4, False), (4, True)])
+def test_llama1b_tp8_shard(batch, multikernel):
+    """The per-GPU shape of an 8-way tensor-parallel 1B model (one KV group,
+    F/8, V/8): attention output width 256 against hidden size 2048, so the
+    O projection reads a 256-wide input and the up/gate instructions hold a
+    single row pair."""
+    shape = synth.LLAMA_1B_TP8_SHARD
+    weights = synth.make_weights(shape)
+    run_and_compare(shape, weights, batch, [1024 - 5 * b for b in range(batch)], 2,
+                    f"llama1b tp8 shard b{batch}" + (" multikernel" if multikernel else ""), multikernel)
