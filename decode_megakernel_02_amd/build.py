@@ -30,7 +30,8 @@ def _run(cmd, verbose):
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     objs = []
-    for src, lang in [("mk_kernels.hip", []), ("mk_api.cpp", ["-x", "hip"]), ("mk_plan.cpp", ["-x", "hip"])]:
+    for src, lang in [("mk_kernels.hip", []), ("mk_prefill.hip", []), ("mk_api.cpp", ["-x", "hip"]),
+                      ("mk_plan.cpp", ["-x", "hip"])]:
         obj = os.path.join(BUILD, src + ".o")
         _run(["hipcc"] + HIP_FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj], verbose)
         objs.append(obj)

@@ -23,6 +23,7 @@ hipError_t launch_pack(const void* rows, uint32_t n, const uint16_t* const* mats
 hipError_t launch_amax(const uint16_t* w, size_t n, uint32_t* out, hipStream_t stream);
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int ncu, hipStream_t stream);
 hipError_t launch_empty(int n_blocks, int n_threads, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_greedy(const float* logits, int B, int V, int32_t* tokens, int32_t* positions, uint64_t* part,
                          uint32_t* cnt, hipStream_t stream);
 }  // namespace mk
@@ -574,6 +575,80 @@ int mk_get_trace(mk_handle* h, uint64_t* records, size_t n) {
         HIPCHK(hipDeviceSynchronize());
         HIPCHK(hipMemcpy(records, h->hp.trace, need * 8, hipMemcpyDeviceToHost));
     } catch (const HipError& e) {
+        return hip_fail(h, e);
+    }
+    return MK_OK;
+}
+
+int mk_prefill(mk_handle* h, const mk_weights* w, const int32_t* tokens, int32_t n_tokens, void* kv_cache,
+               float* logits, void* stream) {
+    if (!h) return fail(nullptr, MK_ERR_INVALID_ARG, "handle is NULL");
+    if (!w || !tokens || !kv_cache || !logits) return fail(h, MK_ERR_INVALID_ARG, "null argument");
+    const Params& p = h->hp;
+    if (h->cfg.flags & MK_FLAG_FP8_WEIGHTS)
+        return fail(h, MK_ERR_UNSUPPORTED_SHAPE, "prefill runs on bf16 weights; the handle decodes FP8 weights");
+    if (n_tokens < 1 || n_tokens > h->cfg.max_seq) return fail(h, MK_ERR_INVALID_ARG, "n_tokens must be in [1, max_seq]");
+    const bool tied = h->cfg.tied_embeddings != 0;
+    if (!w->embed || !w->final_norm || (!tied && !w->lm_head) || !w->attn_norm || !w->wq || !w->wk || !w->wv ||
+        !w->wo || !w->mlp_norm || !w->w_gate || !w->w_up || !w->w_down)
+        return fail(h, MK_ERR_INVALID_ARG, "a weight pointer is NULL");
+    auto aligned = [](const void* q) { return q && ((uintptr_t)q & 15u) == 0; };
+    bool ok = aligned(w->embed) && aligned(w->final_norm) && (tied || aligned(w->lm_head)) &&
+              aligned(tokens) && aligned(kv_cache) && aligned(logits);
+    for (int l = 0; l < p.L && ok; ++l)
+        ok = aligned(w->attn_norm[l]) && aligned(w->wq[l]) && aligned(w->wk[l]) && aligned(w->wv[l]) &&
+             aligned(w->wo[l]) && aligned(w->mlp_norm[l]) && aligned(w->w_gate[l]) && aligned(w->w_up[l]) &&
+             aligned(w->w_down[l]);
+    if (!ok) return fail(h, MK_ERR_INVALID_ARG, "every pointer must be non-NULL and 16-byte aligned");
+    const size_t B = p.B, P = (size_t)n_tokens, M = B * P, H = p.H, QD = (size_t)p.Hq * p.D, KD = (size_t)p.Hkv * p.D;
+    const size_t F = p.F;
+    const size_t floats = M * (2 * H + QD + 2 * KD + QD + 2 * F);
+    hipStream_t s = (hipStream_t)stream;
+    void* ws = nullptr;
+    try {
+        HIPCHK(hipSetDevice(h->cfg.device));
+        if (hipMalloc(&ws, floats * 4 + 256) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(h, MK_ERR_OOM, "prefill workspace allocation failed");
+        }
+        std::vector<const uint16_t*> ptrs((size_t)9 * p.L);
+        const void* const* src[9] = {w->attn_norm, w->wq, w->wk, w->wv, w->wo, w->mlp_norm, w->w_gate, w->w_up, w->w_down};
+        for (int k = 0; k < 9; ++k)
+            for (int l = 0; l < p.L; ++l) ptrs[(size_t)k * p.L + l] = (const uint16_t*)src[k][l];
+        PrefillArgs a{};
+        a.L = p.L; a.H = p.H; a.Hq = p.Hq; a.Hkv = p.Hkv; a.D = p.D; a.F = p.F; a.V = p.V; a.B = p.B;
+        a.P = n_tokens; a.max_seq = h->cfg.max_seq; a.eps = h->cfg.rms_eps;
+        a.tokens = tokens;
+        a.embed = (const uint16_t*)w->embed;
+        a.final_norm = (const uint16_t*)w->final_norm;
+        a.lm_head = (const uint16_t*)(tied ? w->embed : w->lm_head);
+        a.attn_norm = &ptrs[0]; a.wq = &ptrs[(size_t)p.L]; a.wk = &ptrs[(size_t)2 * p.L]; a.wv = &ptrs[(size_t)3 * p.L];
+        a.wo = &ptrs[(size_t)4 * p.L]; a.mlp_norm = &ptrs[(size_t)5 * p.L]; a.w_gate = &ptrs[(size_t)6 * p.L];
+        a.w_up = &ptrs[(size_t)7 * p.L]; a.w_down = &ptrs[(size_t)8 * p.L];
+        a.rope = p.rope;
+        a.kv = (uint16_t*)kv_cache;
+        a.logits = logits;
+        float* f = (float*)ws;
+        a.X = f; f += M * H;
+        a.A = f; f += M * H;
+        a.QKV = f; f += M * (QD + 2 * KD);
+        a.O = f; f += M * QD;
+        a.G = f; f += M * F;
+        a.U = f; f += M * F;
+        a.bad = (uint32_t*)f;
+        HIPCHK(hipMemsetAsync(a.bad, 0, 4, s));
+        HIPCHK(launch_prefill(a, s));
+        uint32_t bad = 0;
+        HIPCHK(hipMemcpyAsync(&bad, a.bad, 4, hipMemcpyDeviceToHost, s));
+        HIPCHK(hipStreamSynchronize(s));
+        HIPCHK(hipFree(ws));
+        ws = nullptr;
+        if (bad) return fail(h, MK_ERR_INVALID_ARG, "a prompt token is outside [0, vocab)");
+    } catch (const HipError& e) {
+        if (ws) {
+            (void)hipStreamSynchronize(s);
+            (void)hipFree(ws);
+        }
         return hip_fail(h, e);
     }
     return MK_OK;

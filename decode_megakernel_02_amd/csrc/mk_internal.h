@@ -134,4 +134,31 @@ constexpr int TRACE_WAVE_SLOTS = 6;
 constexpr int TRACE_SLOTS = 1 + TRACE_WAVE_SLOTS * NW + 3;
 
 
+// Batched prefill (mk_prefill): shapes, the caller's bf16 weights (per-layer
+// arrays are host arrays of device pointers) and a workspace of fp32 rows
+// (M = B * P): X [M][H] residual, A [M][H] normalised input, QKV
+// [M][Hq*D + 2*Hkv*D], O [M][Hq*D], G and U [M][F]; bad: token-range flag.
+struct PrefillArgs {
+    int L, H, Hq, Hkv, D, F, V, B, P, max_seq;
+    float eps;
+    const int32_t* tokens;  // [B][P]
+    const uint16_t* embed;
+    const uint16_t* final_norm;
+    const uint16_t* lm_head;  // the embedding when tied
+    const uint16_t* const* attn_norm;
+    const uint16_t* const* wq;
+    const uint16_t* const* wk;
+    const uint16_t* const* wv;
+    const uint16_t* const* wo;
+    const uint16_t* const* mlp_norm;
+    const uint16_t* const* w_gate;
+    const uint16_t* const* w_up;
+    const uint16_t* const* w_down;
+    const float* rope;  // [max_seq][D/2][2]
+    uint16_t* kv;
+    float* logits;  // [B][V]
+    float *X, *A, *QKV, *O, *G, *U;
+    uint32_t* bad;
+};
+
 }  // namespace mk

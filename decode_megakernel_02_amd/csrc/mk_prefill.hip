@@ -1,0 +1,273 @@
+// Batched prefill: one forward pass over every position of a prompt that
+// fills the KV cache and yields the logits of the last position.  The opening
+// section of "One Token, 2,400 Kernel Launches" contrasts this phase (the
+// whole prompt at once, compute-saturated) with token-by-token decode; the
+// math per position is the same Llama layer as the decode step, so the result
+// equals running the decode step at positions 0 .. P-1 with the prompt tokens
+// (up to fp32 rounding order).
+//
+// Rows are (batch row, position) pairs, so every projection is a dense
+// contraction C[M][N] = A[M][K] * W[N][K]^T with M = B * P: those run on the
+// fp32 matrix cores (v_mfma_f32_16x16x4f32, fp32 activations against bf16
+// weights widened in LDS).  RMSNorm, RoPE + cache append, causal attention and
+// SwiGLU are small vector kernels between them, all on the caller's stream.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <algorithm>
+#include "mk_internal.h"
+
+namespace mk {
+namespace pf {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN
+__device__ __forceinline__ uint16_t to_bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float wsum(float x) {
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+__device__ __forceinline__ float wmax(float x) {
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+
+// X[m][:] = E[tokens[m]]; an id outside [0, V) gives a zero row and sets *bad
+__global__ void __launch_bounds__(256) embed(const int32_t* tok, int H, int V, const uint16_t* E, float* X,
+                                             uint32_t* bad) {
+    const int m = blockIdx.x;
+    int t = tok[m];
+    if (t < 0 || t >= V) {
+        if (threadIdx.x == 0) atomicOr(bad, 1u);
+        t = -1;
+    }
+    for (int i = threadIdx.x; i < H; i += blockDim.x)
+        X[(size_t)m * H + i] = t < 0 ? 0.f : bf(E[(size_t)t * H + i]);
+}
+
+// A[r][:] = X[r][:] * rsqrt(mean(X[r]^2) + eps) * gain, one row per block
+__global__ void __launch_bounds__(256) rmsnorm(const float* X, size_t ldx, int H, const uint16_t* gain, float eps,
+                                               float* A, size_t lda) {
+    __shared__ float red[4];
+    const float* x = X + (size_t)blockIdx.x * ldx;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < H; i += 256) ss += x[i] * x[i];
+    ss = wsum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float sc = rsqrtf((red[0] + red[1] + red[2] + red[3]) * (1.0f / (float)H) + eps);
+    float* a = A + (size_t)blockIdx.x * lda;
+    for (int i = threadIdx.x; i < H; i += 256) a[i] = x[i] * sc * bf(gain[i]);
+}
+
+// C[M][N] (row stride ldc) = or += A[M][K] (stride lda) * W[N][K]^T.
+// 64 x 64 tile per block of 4 waves, each wave a 32 x 32 quarter as 2 x 2
+// MFMA 16x16 tiles; K in steps of 32 staged through LDS.  K, lda and the
+// pointers are multiples of 8 elements (the config guarantees it), so the
+// staging loads are whole float4 / 8 x bf16 vectors, inside or outside K.
+constexpr int TM = 64, TN = 64, TK = 32;
+__global__ void __launch_bounds__(256) gemm(const float* A, int lda, const uint16_t* W, int K, float* C, int ldc,
+                                            int M, int N, int accumulate) {
+    __shared__ float As[TM][TK + 1];
+    __shared__ float Ws[TN][TK + 1];
+    const int m0 = blockIdx.y * TM, n0 = blockIdx.x * TN;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
+    f32x4 acc[2][2];
+    for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < K; k0 += TK) {
+        // A: 64 rows x 32 floats = 512 float4, two per thread
+        for (int e = tid; e < TM * TK / 4; e += 256) {
+            const int r = e / (TK / 4), c = (e % (TK / 4)) * 4;
+            const int gm = m0 + r, gk = k0 + c;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (gm < M && gk < K) v = *(const float4*)(A + (size_t)gm * lda + gk);
+            As[r][c] = v.x;
+            As[r][c + 1] = v.y;
+            As[r][c + 2] = v.z;
+            As[r][c + 3] = v.w;
+        }
+        // W: 64 rows x 32 bf16 = 256 vectors of 8, one per thread
+        {
+            const int r = tid / (TK / 8), c = (tid % (TK / 8)) * 8;
+            const int gn = n0 + r, gk = k0 + c;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (gn < N && gk < K) v = *(const uint4*)(W + (size_t)gn * K + gk);
+            const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+            for (int i = 0; i < 4; ++i) {
+                Ws[r][c + 2 * i] = __uint_as_float(q[i] << 16);
+                Ws[r][c + 2 * i + 1] = __uint_as_float(q[i] & 0xffff0000u);
+            }
+        }
+        __syncthreads();
+        // 16x16x4 operands: lane l holds A[row l % 16][k l / 16] and
+        // B[k l / 16][col l % 16]; the result's lane l holds rows 4 (l / 16) + j
+        // of column l % 16
+        for (int kk = 0; kk < TK; kk += 4) {
+            const int kr = kk + (lane >> 4);
+            const float a0 = As[wm + (lane & 15)][kr], a1 = As[wm + 16 + (lane & 15)][kr];
+            const float b0 = Ws[wn + (lane & 15)][kr], b1 = Ws[wn + 16 + (lane & 15)][kr];
+            acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc[0][0], 0, 0, 0);
+            acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc[0][1], 0, 0, 0);
+            acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b0, acc[1][0], 0, 0, 0);
+            acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc[1][1], 0, 0, 0);
+        }
+        __syncthreads();
+    }
+    for (int ti = 0; ti < 2; ++ti)
+        for (int tj = 0; tj < 2; ++tj)
+            for (int j = 0; j < 4; ++j) {
+                const int r = m0 + wm + ti * 16 + 4 * (lane >> 4) + j, c = n0 + wn + tj * 16 + (lane & 15);
+                if (r < M && c < N) {
+                    float* p = C + (size_t)r * ldc + c;
+                    *p = accumulate ? *p + acc[ti][tj][j] : acc[ti][tj][j];
+                }
+            }
+}
+
+// Row m = b * P + t of QKV ([q heads | k heads | v heads], fp32): RoPE on the
+// q and k heads at position t (rotate-half pairs, cos/sin from the handle's
+// table), then k and v rounded to bf16 into cache slot t of layer `layer`.
+__global__ void __launch_bounds__(256) rope_kv(float* QKV, int ld, int B, int P, int Hq, int Hkv, int D,
+                                               const float* rope, uint16_t* kv, int layer, int max_seq) {
+    const int m = blockIdx.x, b = m / P, t = m % P, half = D / 2;
+    float* row = QKV + (size_t)m * ld;
+    const int QD = Hq * D, KD = Hkv * D;
+    for (int e = threadIdx.x; e < (Hq + Hkv) * half; e += 256) {
+        const int head = e / half, i = e % half;
+        float* x = row + (size_t)head * D;
+        const float c = rope[((size_t)t * half + i) * 2], s = rope[((size_t)t * half + i) * 2 + 1];
+        const float u = x[i], w = x[i + half];
+        x[i] = u * c - w * s;
+        x[i + half] = w * c + u * s;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < KD; e += 256) {
+        const int g = e / D, d = e % D;
+        const size_t kslot = ((((size_t)layer * 2 + 0) * B + b) * Hkv + g) * (size_t)max_seq + t;
+        const size_t vslot = ((((size_t)layer * 2 + 1) * B + b) * Hkv + g) * (size_t)max_seq + t;
+        kv[kslot * D + d] = to_bf(row[QD + e]);
+        kv[vslot * D + d] = to_bf(row[QD + KD + e]);
+    }
+}
+
+// Causal attention of query (row m, head h) over cache slots 0 .. t of its KV
+// group: one wave each, keys in blocks of 64 (lane j scores key j of the
+// block), online softmax across blocks, lane d accumulating output dims
+// d, d + 64.  O[m][h * D + d] = sum_j softmax(q . k_j / sqrt(D))_j v_j[d].
+template <int D>
+__global__ void __launch_bounds__(256) attention(const float* QKV, int ld, const uint16_t* kv, int B, int P, int Hq,
+                                                 int Hkv, int layer, int max_seq, float* O, int ldo) {
+    constexpr int NC = D / 64;
+    __shared__ float qs[4][D];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wid = blockIdx.x * 4 + w;
+    if (wid >= B * P * Hq) return;  // the whole wave leaves; no block barrier follows
+    const int head = wid % Hq, m = wid / Hq, b = m / P, t = m % P, g = head / (Hq / Hkv);
+    const float* q = QKV + (size_t)m * ld + (size_t)head * D;
+    for (int d = lane; d < D; d += 64) qs[w][d] = q[d];
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    const uint16_t* Kb = kv + ((((size_t)layer * 2 + 0) * B + b) * Hkv + g) * (size_t)max_seq * D;
+    const uint16_t* Vb = kv + ((((size_t)layer * 2 + 1) * B + b) * Hkv + g) * (size_t)max_seq * D;
+    const float scale = rsqrtf((float)D);
+    float mx = -__builtin_inff(), l = 0.f, o[NC];
+    for (int c = 0; c < NC; ++c) o[c] = 0.f;
+    for (int j0 = 0; j0 <= t; j0 += 64) {
+        const int j = j0 + lane;
+        float s = -__builtin_inff();
+        if (j <= t) {
+            const uint4* kr = (const uint4*)(Kb + (size_t)j * D);
+            float acc = 0.f;
+            for (int u = 0; u < D / 8; ++u) {
+                const uint4 v = kr[u];
+                const float* qq = &qs[w][u * 8];
+                acc = fmaf(__uint_as_float(v.x << 16), qq[0], acc);
+                acc = fmaf(__uint_as_float(v.x & 0xffff0000u), qq[1], acc);
+                acc = fmaf(__uint_as_float(v.y << 16), qq[2], acc);
+                acc = fmaf(__uint_as_float(v.y & 0xffff0000u), qq[3], acc);
+                acc = fmaf(__uint_as_float(v.z << 16), qq[4], acc);
+                acc = fmaf(__uint_as_float(v.z & 0xffff0000u), qq[5], acc);
+                acc = fmaf(__uint_as_float(v.w << 16), qq[6], acc);
+                acc = fmaf(__uint_as_float(v.w & 0xffff0000u), qq[7], acc);
+            }
+            s = acc * scale;
+        }
+        const float nm = fmaxf(mx, wmax(s));  // lane 0's key j0 <= t, so nm is finite
+        const float p = j <= t ? __expf(s - nm) : 0.f;
+        const float corr = __expf(mx - nm);
+        l = l * corr + wsum(p);
+        for (int c = 0; c < NC; ++c) o[c] *= corr;
+        const int nk = t - j0 + 1 < 64 ? t - j0 + 1 : 64;
+        for (int jj = 0; jj < nk; ++jj) {
+            const float pj = __shfl(p, jj);
+            const uint16_t* vr = Vb + (size_t)(j0 + jj) * D;
+            for (int c = 0; c < NC; ++c) o[c] = fmaf(pj, bf(vr[lane + 64 * c]), o[c]);
+        }
+        mx = nm;
+    }
+    const float inv = 1.0f / l;
+    for (int c = 0; c < NC; ++c) O[(size_t)m * ldo + (size_t)head * D + lane + 64 * c] = o[c] * inv;
+}
+
+// G[i] = silu(G[i]) * U[i]
+__global__ void __launch_bounds__(256) swiglu(float* G, const float* U, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+        const float gt = G[i];
+        G[i] = gt / (1.0f + __expf(-gt)) * U[i];
+    }
+}
+
+void run_gemm(const float* A, int lda, const uint16_t* W, int K, float* C, int ldc, int M, int N, int acc,
+              hipStream_t s) {
+    const dim3 grid((unsigned)((N + TN - 1) / TN), (unsigned)((M + TM - 1) / TM));
+    hipLaunchKernelGGL(gemm, grid, dim3(256), 0, s, A, lda, W, K, C, ldc, M, N, acc);
+}
+
+}  // namespace pf
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
+    using namespace pf;
+    const int B = a.B, P = a.P, M = B * P, H = a.H, D = a.D, F = a.F, V = a.V;
+    const int QD = a.Hq * D, KD = a.Hkv * D, NQKV = QD + 2 * KD;
+    hipLaunchKernelGGL(embed, dim3(M), dim3(256), 0, s, a.tokens, H, V, a.embed, a.X, a.bad);
+    for (int l = 0; l < a.L; ++l) {
+        hipLaunchKernelGGL(rmsnorm, dim3(M), dim3(256), 0, s, a.X, (size_t)H, H, a.attn_norm[l], a.eps, a.A,
+                           (size_t)H);
+        run_gemm(a.A, H, a.wq[l], H, a.QKV, NQKV, M, QD, 0, s);
+        run_gemm(a.A, H, a.wk[l], H, a.QKV + QD, NQKV, M, KD, 0, s);
+        run_gemm(a.A, H, a.wv[l], H, a.QKV + QD + KD, NQKV, M, KD, 0, s);
+        hipLaunchKernelGGL(rope_kv, dim3(M), dim3(256), 0, s, a.QKV, NQKV, B, P, a.Hq, a.Hkv, D, a.rope, a.kv, l,
+                           a.max_seq);
+        const unsigned nat = (unsigned)(((size_t)M * a.Hq + 3) / 4);
+        if (D == 64)
+            hipLaunchKernelGGL(attention<64>, dim3(nat), dim3(256), 0, s, a.QKV, NQKV, a.kv, B, P, a.Hq, a.Hkv, l,
+                               a.max_seq, a.O, QD);
+        else
+            hipLaunchKernelGGL(attention<128>, dim3(nat), dim3(256), 0, s, a.QKV, NQKV, a.kv, B, P, a.Hq, a.Hkv, l,
+                               a.max_seq, a.O, QD);
+        run_gemm(a.O, QD, a.wo[l], QD, a.X, H, M, H, 1, s);  // h += W_o attn
+        hipLaunchKernelGGL(rmsnorm, dim3(M), dim3(256), 0, s, a.X, (size_t)H, H, a.mlp_norm[l], a.eps, a.A,
+                           (size_t)H);
+        run_gemm(a.A, H, a.w_gate[l], H, a.G, F, M, F, 0, s);
+        run_gemm(a.A, H, a.w_up[l], H, a.U, F, M, F, 0, s);
+        const size_t n = (size_t)M * F;
+        hipLaunchKernelGGL(swiglu, dim3((unsigned)std::min<size_t>((n + 255) / 256, 65536)), dim3(256), 0, s, a.G,
+                           a.U, n);
+        run_gemm(a.G, F, a.w_down[l], F, a.X, H, M, H, 1, s);  // h += W_down a
+    }
+    // last position of each row: final RMSNorm, then the LM head
+    hipLaunchKernelGGL(rmsnorm, dim3(B), dim3(256), 0, s, a.X + (size_t)(P - 1) * H, (size_t)P * H, H, a.final_norm,
+                       a.eps, a.A, (size_t)H);
+    run_gemm(a.A, H, a.lm_head, H, a.logits, V, B, V, 0, s);
+    return hipGetLastError();
+}
+
+}  // namespace mk

@@ -55,7 +55,7 @@ class MkScheduleInfo(ctypes.Structure):
 EXPORTS = ["mk_create", "mk_load_weights", "mk_kv_cache_bytes", "mk_decode_step", "mk_decode_step_multikernel",
            "mk_destroy", "mk_status_string", "mk_last_error", "mk_get_device_error", "mk_get_profile",
            "mk_schedule_inspect", "mk_get_trace", "mk_greedy_advance", "mk_read_probe", "mk_empty_launches",
-           "mk_graph_create", "mk_graph_launch", "mk_graph_destroy"]
+           "mk_graph_create", "mk_graph_launch", "mk_graph_destroy", "mk_prefill"]
 MK_FLAG_PROFILE = 1
 MK_FLAG_TRACE = 2
 MK_FLAG_FP8_WEIGHTS = 4
@@ -97,10 +97,11 @@ def lib():
         L.mk_graph_create.argtypes = [H, _P, _P, _P, _P, ctypes.c_int, ctypes.c_uint32, ctypes.POINTER(ctypes.c_void_p)]
         L.mk_graph_launch.argtypes = [ctypes.c_void_p, _P]
         L.mk_graph_destroy.argtypes = [ctypes.c_void_p]
+        L.mk_prefill.argtypes = [H, ctypes.POINTER(MkWeights), _P, ctypes.c_int32, _P, _P, _P]
         for name in ["mk_create", "mk_load_weights", "mk_decode_step", "mk_decode_step_multikernel", "mk_destroy",
                      "mk_get_device_error", "mk_schedule_inspect", "mk_get_profile", "mk_get_trace",
                      "mk_greedy_advance", "mk_read_probe", "mk_empty_launches", "mk_graph_create",
-                     "mk_graph_launch", "mk_graph_destroy"]:
+                     "mk_graph_launch", "mk_graph_destroy", "mk_prefill"]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -167,6 +168,30 @@ def mk_load_weights(handle, weights: Dict[str, object], stream: Optional[int] = 
         arrays[kind] = arr
         setattr(w, kind, ctypes.cast(arr, ctypes.POINTER(_P)))
     _check(lib().mk_load_weights(handle, ctypes.byref(w), stream), handle)
+
+
+def _weights_struct(weights: Dict[str, object]):
+    layers: List[Dict[str, object]] = weights["layers"]
+    L = len(layers)
+    keep = []
+    w = MkWeights()
+    w.embed = _ptr(weights["embed"])
+    w.final_norm = _ptr(weights["final_norm"])
+    w.lm_head = _ptr(weights["lm_head"]) if weights.get("lm_head") is not None else None
+    for kind in ["attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down"]:
+        arr = (_P * L)(*[_ptr(layers[l][kind]) for l in range(L)])
+        keep.append(arr)
+        setattr(w, kind, ctypes.cast(arr, ctypes.POINTER(_P)))
+    return w, keep
+
+
+def mk_prefill(handle, weights: Dict[str, object], tokens, n_tokens: int, kv_cache, logits,
+               stream: Optional[int] = None):
+    """Batched prefill of positions 0 .. n_tokens-1 (tokens: device int32 [B][n_tokens]); synchronous."""
+    w, keep = _weights_struct(weights)
+    _check(lib().mk_prefill(handle, ctypes.byref(w), _ptr(tokens), int(n_tokens), _ptr(kv_cache), _ptr(logits),
+                            stream), handle)
+    del keep
 
 
 def mk_decode_step(handle, tokens, positions, kv_cache, logits, stream: Optional[int] = None):

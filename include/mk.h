@@ -101,7 +101,7 @@ typedef struct mk_handle mk_handle;
 /* Validates `cfg`, queries the device, builds the per-CU instruction queues
  * and the packed-weight layout, and allocates all library-owned device
  * memory (packed weights, queues, activation scratch, RoPE table).  On error
- * *out is set to NULL.  Shape limits: H = Hq*D, Hq % Hkv == 0, D in {64,128},
+ * *out is set to NULL.  Shape limits: Hq*D <= 16384, Hq % Hkv == 0, D in {64,128},
  * (Hq/Hkv) divides 8, H and F multiples of 8, 1 <= batch <= 8.            */
 int mk_create(const mk_config* cfg, mk_handle** out);
 
@@ -195,6 +195,26 @@ int mk_graph_launch(mk_graph* g, void* stream);
 int mk_graph_destroy(mk_graph* g);
 
 /* Frees everything the handle owns.  NULL is accepted. */
+/* Batched prefill ("One Token, 2,400 Kernel Launches", opening section: the
+ * prompt is one compute-bound pass, decode the token-by-token phase): runs
+ * the model over positions 0 .. n_tokens-1 of every batch row at once.
+ *   w:        the caller's bf16 weights, as for mk_load_weights (device
+ *             pointers, 16-byte aligned); read during the call only.
+ *   tokens:   device int32 [B][n_tokens], ids in [0, vocab).
+ *   kv_cache: the caller's cache; slots [0, n_tokens) of every (layer, K/V,
+ *             row, group) are written, bf16 rounded to nearest even.
+ *   logits:   device fp32 [B][vocab], the last position's logits.
+ * Equals mk_decode_step at positions 0 .. n_tokens-1 with the same tokens,
+ * up to fp32 rounding order (the projections run on the fp32 matrix cores).
+ * Synchronous: allocates an fp32 workspace of B*n_tokens*(2H + 2*Hq*D +
+ * 2*Hkv*D + 2F) floats, runs on `stream`, waits for it and frees it.
+ * MK_ERR_INVALID_ARG: null or unaligned pointer, n_tokens outside
+ * [1, max_seq], or (after the run) a token outside [0, vocab) — its rows
+ * are then computed from a zero embedding.  MK_ERR_UNSUPPORTED_SHAPE for
+ * an MK_FLAG_FP8_WEIGHTS handle; MK_ERR_OOM when the workspace does not fit. */
+int mk_prefill(mk_handle* h, const mk_weights* w, const int32_t* tokens, int32_t n_tokens, void* kv_cache,
+               float* logits, void* stream);
+
 int mk_destroy(mk_handle* h);
 
 /* Static description of a status code. */

@@ -97,6 +97,7 @@ def test_null_arguments():
     assert L.mk_schedule_inspect(None, 8, None) == mk.MK_ERR_INVALID_ARG
     assert L.mk_destroy(None) == mk.MK_OK
     assert L.mk_decode_step(None, None, None, None, None, None) == mk.MK_ERR_INVALID_ARG
+    assert L.mk_prefill(None, None, None, 0, None, None, None) == mk.MK_ERR_INVALID_ARG
     assert L.mk_decode_step_multikernel(None, None, None, None, None, None) == mk.MK_ERR_INVALID_ARG
     assert L.mk_load_weights(None, None, None) == mk.MK_ERR_INVALID_ARG
     assert L.mk_greedy_advance(None, None, None, None, None) == mk.MK_ERR_INVALID_ARG

@@ -1,0 +1,93 @@
+"""Batched prefill (mk_prefill) against the oracle run token by token.
+
+The oracle's decode step at positions 0 .. P-1 with the prompt tokens is the
+plain definition of what a prefill computes: the KV cache slots [0, P) and
+the logits of position P-1.  Compared here: the logits to the usual bar, the
+cache to the decode path's cache bar (max |d| <= 2e-2 max(1, max |ref|), over
+90 % of the bf16 values bit-equal: a value near a rounding boundary may round
+the other way), and greedy decode steps
+continued from the prefilled cache, against the oracle continuing from its own.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import synth
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+def bf16_to_f32(a):
+    return (a.astype(np.uint32) << 16).view(np.float32)
+
+
+def prefill_and_compare(shape, batch, P, decode_steps, label):
+    import torch
+    import oracle
+    from decode_megakernel_02_amd import mk
+    weights = synth.make_weights(shape)
+    max_seq = P + decode_steps + 1
+    prompts = synth.make_prompts(shape.vocab, batch, P)
+    dec = H.GpuDecoder(shape, weights, batch, max_seq)
+    try:
+        toks = torch.as_tensor(np.ascontiguousarray(prompts, dtype=np.int32)).cuda()
+        mk.mk_prefill(dec.h, dec.dw, toks, P, dec.kv, dec.logits, mk.current_stream())
+        torch.cuda.synchronize()
+        gpu_logits = dec.logits.cpu().numpy().copy()
+        gpu_kv = dec.kv_host().copy()
+        nxt = np.argmax(gpu_logits, axis=1).astype(np.int32)
+        run = dec.greedy(nxt, np.full(batch, P, dtype=np.int32), decode_steps)
+    finally:
+        dec.close()
+    orc = oracle.Oracle(shape, weights, batch, max_seq)
+    cache = np.zeros(synth.kv_cache_shape(shape, batch, max_seq), dtype=np.uint16)
+    ref = None
+    for t in range(P):
+        ref = orc.decode_step(cache, prompts[:, t].astype(np.int32), np.full(batch, t, dtype=np.int32), 8)
+    stats = H.compare(H.Run([prompts[:, -1]], [np.full(batch, P - 1)], [gpu_logits]), [ref], label + " prefill")
+    g = bf16_to_f32(gpu_kv[..., :P, :])
+    o = bf16_to_f32(cache[..., :P, :])
+    # the decode path's cache bar: rounding-order differences flip some bf16 roundings
+    kv_err = float(np.max(np.abs(g - o)))
+    assert kv_err <= 2e-2 * max(1.0, float(np.max(np.abs(o)))), (label, kv_err)
+    frac_equal = float(np.mean(gpu_kv[..., :P, :] == cache[..., :P, :]))
+    assert frac_equal > 0.9, (label, frac_equal)
+    # decode continues from the prefilled cache; the oracle continues from its own
+    H.compare(run, H.oracle_replay(shape, weights, batch, max_seq, run, kv_init=cache), label + " decode")
+    print(label, stats, "kv max|d|", kv_err, "bit-equal fraction", frac_equal, flush=True)
+
+
+@pytest.mark.parametrize("batch,P", [(1, 1), (2, 37), (3, 130)])
+def test_tiny_prefill_matches_token_by_token_oracle(batch, P):
+    prefill_and_compare(synth.TINY, batch, P, 3, f"tiny b{batch} p{P}")
+
+
+def test_llama1b_dims_prefill():
+    """1B dimensions (2 layers, 4096-token vocabulary): 64-row tiles over a
+    ragged 100-position prompt, 32 query heads over 8 KV groups."""
+    shape = dataclasses.replace(synth.LLAMA_1B, n_layers=2, vocab=4096)
+    prefill_and_compare(shape, 2, 100, 2, "llama1b-dims 2 layers p100")
+
+
+def test_llama8b_dims_prefill_head_dim_128():
+    shape = dataclasses.replace(synth.LLAMA_8B, n_layers=1, vocab=4096, hidden=1024, ffn=2048, n_q_heads=8,
+                                n_kv_heads=2)
+    prefill_and_compare(shape, 1, 70, 2, "head_dim 128, untied, p70")
+
+
+def test_prefill_rejects_out_of_range_token():
+    import torch
+    from decode_megakernel_02_amd import mk
+    shape = synth.TINY
+    dec = H.GpuDecoder(shape, synth.make_weights(shape), 1, 16)
+    try:
+        toks = torch.tensor([[1, 2, shape.vocab, 3]], dtype=torch.int32, device="cuda")
+        with pytest.raises(mk.MkError) as e:
+            mk.mk_prefill(dec.h, dec.dw, toks, 4, dec.kv, dec.logits, mk.current_stream())
+        assert e.value.code == mk.MK_ERR_INVALID_ARG
+        with pytest.raises(mk.MkError):
+            mk.mk_prefill(dec.h, dec.dw, toks, 17, dec.kv, dec.logits, mk.current_stream())  # > max_seq
+    finally:
+        dec.close()
