@@ -197,6 +197,8 @@ def main():
                     help="FP8 (E4M3, per-matrix scale) weights instead of bf16 (a variant, not the headline)")
     ap.add_argument("--cpu-only", action="store_true",
                     help="time only the CPU oracle on the workload and print it as one JSON line")
+    ap.add_argument("--prefill", action="store_true",
+                    help="time batched prefill (mk_prefill) of the workload's prompt instead of decode; one JSON line")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (3 launches), the reference "
                          "kernel for scaling HBM byte counters")
@@ -267,6 +269,30 @@ def main():
     h = mk.mk_create(cfg)
     stream = mk.current_stream()
     mk.mk_load_weights(h, dw, stream)
+    if args.prefill:  # whole-prompt pass: W untimed and K timed calls of mk_prefill (each synchronous)
+        kvz = torch.zeros(mk.mk_kv_cache_bytes(cfg) // 2, dtype=torch.int16, device="cuda")
+        ptoks = torch.as_tensor(synth.make_prompts(shape.vocab, B, P)).cuda()
+        lg = torch.empty(B, shape.vocab, dtype=torch.float32, device="cuda")
+        for _ in range(max(W, 1)):
+            mk.mk_prefill(h, dw, ptoks, P, kvz, lg, stream)
+        ts = []
+        for _ in range(K):
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            mk.mk_prefill(h, dw, ptoks, P, kvz, lg, stream)
+            ts.append(time.perf_counter() - t1)
+        med = float(np.median(ts))
+        QD, KD = shape.n_q_heads * shape.head_dim, shape.n_kv_heads * shape.head_dim
+        flops = 2.0 * B * P * shape.n_layers * shape.hidden * (QD + 2 * KD + QD + 3 * shape.ffn) + 2.0 * B * shape.vocab * shape.hidden
+        print(json.dumps({"metric": "prefill_tokens_per_s", "value": B * P / med, "unit": "tokens/s", "n_gpus": 1,
+                          "steps": K, "warmup": W, "ms_per_step": med * 1e3, "higher_is_better": True,
+                          "dtype": "f32 (bf16 weights)", "data": "synthetic",
+                          "config": {"workload": args.workload, "batch": B, "prompt": P},
+                          "roofline": {"bound": "mfma", "achieved": flops / med / 1e12, "peak": 157.3,
+                                       "unit": "TFLOP/s", "frac": flops / med / 1e12 / 157.3, "traffic": None}}),
+              flush=True)
+        mk.mk_destroy(h)
+        return
     del dw
     torch.cuda.empty_cache()
     kv = up(kv_host.reshape(-1))
