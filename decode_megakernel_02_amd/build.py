@@ -28,13 +28,16 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False) -> str:
+    from concurrent.futures import ThreadPoolExecutor
     os.makedirs(BUILD, exist_ok=True)
-    objs = []
-    for src, lang in [("mk_kernels.hip", []), ("mk_prefill.hip", []), ("mk_api.cpp", ["-x", "hip"]),
-                      ("mk_plan.cpp", ["-x", "hip"])]:
-        obj = os.path.join(BUILD, src + ".o")
-        _run(["hipcc"] + HIP_FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj], verbose)
-        objs.append(obj)
+    units = [("mk_kernels.hip", []), ("mk_prefill.hip", []), ("mk_api.cpp", ["-x", "hip"]),
+             ("mk_plan.cpp", ["-x", "hip"])]
+    objs = [os.path.join(BUILD, src + ".o") for src, _ in units]
+    # the translation units are independent: compile them side by side
+    with ThreadPoolExecutor(len(units)) as ex:
+        for f in [ex.submit(_run, ["hipcc"] + HIP_FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj], verbose)
+                  for (src, lang), obj in zip(units, objs)]:
+            f.result()
     tmp = LIB + ".tmp"
     _run(["hipcc", "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs, verbose)
     os.replace(tmp, LIB)

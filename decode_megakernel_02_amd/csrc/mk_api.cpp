@@ -150,6 +150,24 @@ int mk_schedule_inspect(const mk_config* cfg, int32_t n_cus, mk_schedule_info* o
     return MK_OK;
 }
 
+int mk_schedule_selftest(const mk_config* cfg, int32_t n_cus, int32_t mutation) {
+    if (!cfg || n_cus < 1 || mutation < 0 || mutation > 4)
+        return fail(nullptr, MK_ERR_INVALID_ARG, "null config, n_cus < 1 or mutation outside 0..4");
+    Plan p;
+    std::string err;
+    try {
+        const int rc = build_plan(*cfg, n_cus, p, err);
+        if (rc != MK_OK) return fail(nullptr, rc, err);
+        if (mutation && !mutate_plan(p, mutation == 4 ? 3 : mutation))
+            return fail(nullptr, MK_ERR_INVALID_ARG, "the schedule has no place for this defect");
+        if (!check_plan(p, err, mutation != 4)) return fail(nullptr, MK_ERR_UNSUPPORTED_SHAPE, err);
+    } catch (const std::bad_alloc&) {
+        return fail(nullptr, MK_ERR_OOM, "host allocation failed");
+    }
+    g_create_error.clear();
+    return MK_OK;
+}
+
 int mk_create(const mk_config* cfg, mk_handle** out) {
     if (!out) return fail(nullptr, MK_ERR_INVALID_ARG, "out is NULL");
     *out = nullptr;

@@ -5,11 +5,12 @@
 
 namespace mk {
 
-// Workgroup shape: one workgroup per CU, NW compute waves and NLOAD loader
-// waves; each loader streams the packed weights of NW / NLOAD compute waves
-// into their LDS rings.
+// Workgroup shape: one workgroup per CU, NW compute waves and NLOAD helper
+// waves: NLOAD - 1 weight loaders (each streams the packed weights of up to
+// four compute waves into their LDS rings) and one gather wave (stages the
+// cross-CU inputs of each instruction).
 constexpr int NW = 8;                 // compute waves
-constexpr int NLOAD = 4;              // loader waves, each serving two compute waves
+constexpr int NLOAD = 4;              // helper waves: 3 weight loaders + 1 gather wave
 constexpr int WG_THREADS = 64 * (NW + NLOAD);
 constexpr int UNIT_BYTES = 1024;      // one DMA: 64 lanes x 16 B
 constexpr int UNIT_ELEMS = 512;       // bf16 per unit

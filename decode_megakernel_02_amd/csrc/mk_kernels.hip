@@ -1,10 +1,11 @@
 // Device code for gfx950 (MI355X): the persistent decode interpreter, its op
 // bodies, and the weight-pack kernel.
 //
-// One workgroup per CU runs 8 compute waves and 8 loader waves.  Loader wave i
-// streams compute wave i's packed weights (a contiguous byte stream laid out at
-// load time in exactly the order wave i consumes them) from HBM into a private
-// LDS ring with global->LDS DMA, ahead of the dependency waits: weights never
+// One workgroup per CU runs 8 compute waves, 3 weight-loader waves and 1
+// gather wave.  Loader wave i streams the packed weights of compute waves i,
+// i + 3 and i + 6 (each a byte stream laid out at load time in exactly the
+// order that wave consumes it) from HBM into the waves' private LDS rings with
+// global->LDS DMA, ahead of the dependency waits: weights never
 // depend on activations, so the next instructions' loads overlap the tail of
 // the current one (the page "Megakernels: Deleting the Kernel Boundary to Win
 // Back Microseconds", sections "One launch, one interpreter" and "Correctness
@@ -774,9 +775,9 @@ struct Step {  // per-launch batch inputs, lane b holds row b
 
 // ------------------------------------------------------------ gather wave --
 //
-// The last loader wave stages every instruction's cross-CU inputs in an LDS
-// x buffer one instruction ahead of the compute waves (the two buffers
-// alternate by instruction), so the compute waves start each instruction
+// The gather wave stages every instruction's cross-CU inputs in one of nslot
+// (1 to 3) LDS buffer sets, up to nslot - 1 instructions ahead of the compute
+// waves (the sets rotate by instruction), so the compute waves start each instruction
 // with a single LDS counter check instead of polling remote memory and
 // meeting at a barrier.  For RMSNorm inputs it also sums the squares of the
 // raw rows and stores x * gain.

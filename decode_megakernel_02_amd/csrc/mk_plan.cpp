@@ -300,7 +300,7 @@ int build_plan(const mk_config& c, int ncu, Plan& p, std::string& err) {
 
 // ---------------------------------------------------------------- checking --
 
-bool check_plan(const Plan& p, std::string& err) {
+bool check_plan(const Plan& p, std::string& err, bool check_order) {
     char buf[256];
     const int ncu = p.ncu, L = p.L, B = p.B;
     const int n_pairs = (p.Hq + 2 * p.Hkv) * p.D / 2;
@@ -340,7 +340,7 @@ bool check_plan(const Plan& p, std::string& err) {
                 err = buf;
                 return false;
             }
-            if (stage < last_stage) {
+            if (check_order && stage < last_stage) {
                 snprintf(buf, sizeof buf, "CU %d: queue not in stage order at pc %u", cu, i - p.queue_begin[cu]);
                 err = buf;
                 return false;
@@ -463,6 +463,46 @@ bool check_plan(const Plan& p, std::string& err) {
         err = buf;
         return false;
     }
+    return true;
+}
+
+bool mutate_plan(Plan& p, int mutation) {
+    const int ncu = p.ncu;
+    std::vector<std::vector<Inst>> q(ncu);
+    for (int cu = 0; cu < ncu; ++cu)
+        q[cu].assign(p.insts.begin() + p.queue_begin[cu], p.insts.begin() + p.queue_begin[cu + 1]);
+    // the first queue that has a place for the defect
+    bool done = false;
+    for (int cu = 0; cu < ncu && !done; ++cu) {
+        std::vector<Inst>& qc = q[cu];
+        if (qc.empty()) continue;
+        if (mutation == 1) {
+            std::vector<Inst>& qb = q[(cu + 1) % ncu];
+            qb.insert(qb.begin() + (qb.empty() ? 0 : 1), qc.front());
+            done = true;
+        } else if (mutation == 2) {
+            for (size_t i = 0; i < qc.size() && !done; ++i)
+                if (qc[i].op == OP_RMS_UP_GATE) {
+                    qc.erase(qc.begin() + i);
+                    done = true;
+                }
+        } else if (mutation == 3) {
+            size_t last_dn = qc.size();
+            for (size_t i = 0; i < qc.size(); ++i)
+                if (qc[i].op == OP_DOWN_RES) last_dn = i;
+            if (last_dn + 1 < qc.size()) {
+                std::swap(qc[last_dn], qc[last_dn + 1]);
+                done = true;
+            }
+        }
+    }
+    if (!done) return false;
+    p.insts.clear();
+    for (int cu = 0; cu < ncu; ++cu) {
+        p.queue_begin[cu] = (uint32_t)p.insts.size();
+        p.insts.insert(p.insts.end(), q[cu].begin(), q[cu].end());
+    }
+    p.queue_begin[ncu] = (uint32_t)p.insts.size();
     return true;
 }
 

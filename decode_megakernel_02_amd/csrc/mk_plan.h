@@ -79,9 +79,18 @@ int validate_config(const mk_config& cfg, std::string& err);
 // Builds the queues and stream layout for `ncu` workgroups.
 int build_plan(const mk_config& cfg, int ncu, Plan& out, std::string& err);
 
-// Checks that every output is produced exactly once per step and simulates the
-// queues (each instruction runs once everything it reads has been produced);
-// returns false with a message on a coverage hole, a duplicate or a deadlock.
-bool check_plan(const Plan& p, std::string& err);
+// Checks that every output is produced exactly once per step, that every queue
+// is in stage order (check_order), and simulates the queues (each instruction
+// runs once everything it reads has been produced); returns false with a
+// message on a coverage hole, a duplicate, an out-of-order queue or a deadlock.
+bool check_plan(const Plan& p, std::string& err, bool check_order = true);
+
+// Deliberate schedule defects for testing check_plan, planted in the first
+// queue that has a place for them: 1 duplicates the queue's first instruction
+// into the next CU's queue, 2 removes its first up/gate instruction, 3 swaps
+// its last down-projection instruction with the later-stage instruction after
+// it (the queue then waits on its own later work).  Returns false if no queue
+// has a place for the defect.
+bool mutate_plan(Plan& p, int mutation);
 
 }  // namespace mk

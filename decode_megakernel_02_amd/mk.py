@@ -55,7 +55,7 @@ class MkScheduleInfo(ctypes.Structure):
 EXPORTS = ["mk_create", "mk_load_weights", "mk_kv_cache_bytes", "mk_decode_step", "mk_decode_step_multikernel",
            "mk_destroy", "mk_status_string", "mk_last_error", "mk_get_device_error", "mk_get_profile",
            "mk_schedule_inspect", "mk_get_trace", "mk_greedy_advance", "mk_read_probe", "mk_empty_launches",
-           "mk_graph_create", "mk_graph_launch", "mk_graph_destroy", "mk_prefill"]
+           "mk_graph_create", "mk_graph_launch", "mk_graph_destroy", "mk_prefill", "mk_schedule_selftest"]
 MK_FLAG_PROFILE = 1
 MK_FLAG_TRACE = 2
 MK_FLAG_FP8_WEIGHTS = 4
@@ -90,6 +90,7 @@ def lib():
         L.mk_last_error.restype = ctypes.c_char_p
         L.mk_get_device_error.argtypes = [H, ctypes.POINTER(MkDeviceError)]
         L.mk_schedule_inspect.argtypes = [ctypes.POINTER(MkConfig), ctypes.c_int32, ctypes.POINTER(MkScheduleInfo)]
+        L.mk_schedule_selftest.argtypes = [ctypes.POINTER(MkConfig), ctypes.c_int32, ctypes.c_int32]
         L.mk_get_profile.argtypes = [H, _P, ctypes.c_size_t]
         L.mk_get_trace.argtypes = [H, _P, ctypes.c_size_t]
         L.mk_greedy_advance.argtypes = [H, _P, _P, _P, _P]
@@ -101,7 +102,7 @@ def lib():
         for name in ["mk_create", "mk_load_weights", "mk_decode_step", "mk_decode_step_multikernel", "mk_destroy",
                      "mk_get_device_error", "mk_schedule_inspect", "mk_get_profile", "mk_get_trace",
                      "mk_greedy_advance", "mk_read_probe", "mk_empty_launches", "mk_graph_create",
-                     "mk_graph_launch", "mk_graph_destroy", "mk_prefill"]:
+                     "mk_graph_launch", "mk_graph_destroy", "mk_prefill", "mk_schedule_selftest"]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -148,6 +149,12 @@ def mk_schedule_inspect(cfg: MkConfig, n_cus: int) -> MkScheduleInfo:
     info = MkScheduleInfo()
     _check(lib().mk_schedule_inspect(ctypes.byref(cfg), n_cus, ctypes.byref(info)))
     return info
+
+
+def mk_schedule_selftest(cfg: MkConfig, n_cus: int, mutation: int) -> int:
+    """Runs the schedule validator on a schedule with a planted defect (see include/mk.h);
+    returns the status code (MK_OK: accepted) without raising."""
+    return int(lib().mk_schedule_selftest(ctypes.byref(cfg), n_cus, mutation))
 
 
 def _ptr(t) -> int:

@@ -194,7 +194,6 @@ int mk_graph_launch(mk_graph* g, void* stream);
 /* Frees the graph.  NULL is accepted. */
 int mk_graph_destroy(mk_graph* g);
 
-/* Frees everything the handle owns.  NULL is accepted. */
 /* Batched prefill ("One Token, 2,400 Kernel Launches", opening section: the
  * prompt is one compute-bound pass, decode the token-by-token phase): runs
  * the model over positions 0 .. n_tokens-1 of every batch row at once.
@@ -215,6 +214,7 @@ int mk_graph_destroy(mk_graph* g);
 int mk_prefill(mk_handle* h, const mk_weights* w, const int32_t* tokens, int32_t n_tokens, void* kv_cache,
                float* logits, void* stream);
 
+/* Frees everything the handle owns.  NULL is accepted. */
 int mk_destroy(mk_handle* h);
 
 /* Static description of a status code. */
@@ -283,6 +283,23 @@ typedef struct {
 } mk_schedule_info;
 
 int mk_schedule_inspect(const mk_config* cfg, int32_t n_cus, mk_schedule_info* out);
+
+/* Host-only self-test of the schedule validator (the hand-built dependency
+ * graph is what "Megakernels: Deleting the Kernel Boundary to Win Back
+ * Microseconds", section "The catch", names as the hard part to debug):
+ * builds the schedule for `cfg` on `n_cus` CUs, plants one defect, and runs
+ * the validator on the result, in the first queue (lowest CU) that has a place
+ * for it.  mutation: 0 none; 1 the queue's first instruction duplicated into
+ * the next CU's queue (an output produced twice); 2 its first up/gate
+ * instruction removed (an output never produced); 3 its last down-projection
+ * instruction swapped with the later-stage instruction that follows it (a
+ * queue that waits on its own later work), caught by the
+ * stage-order check; 4 the same defect with the stage-order check switched
+ * off, so that only the dependency simulation can catch it (as a deadlock).
+ * Returns MK_OK if the validator accepts the schedule, MK_ERR_UNSUPPORTED_SHAPE
+ * with its message in mk_last_error(NULL) if it rejects it, MK_ERR_INVALID_ARG
+ * for a bad argument or a schedule without a place for the defect.  Needs no GPU. */
+int mk_schedule_selftest(const mk_config* cfg, int32_t n_cus, int32_t mutation);
 
 #ifdef __cplusplus
 }

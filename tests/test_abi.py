@@ -129,3 +129,25 @@ def test_kv_cache_bytes():
         assert mk.mk_kv_cache_bytes(cfg) == 2 * n
     bad = mk.make_config(synth.TINY, 0, 64)
     assert mk.mk_kv_cache_bytes(bad) == 0
+
+
+@pytest.mark.parametrize("shape_name,batch,ncus", [("TINY", 1, 256), ("TINY", 3, 7), ("LLAMA_1B", 1, 256),
+                                                  ("LLAMA_1B", 4, 64)])
+def test_validator_rejects_planted_schedule_defects(shape_name, batch, ncus):
+    """A duplicate, a hole and a queue that waits on its own later work are each rejected, the last
+    one both by the stage-order check and, with that check off, by the dependency simulation."""
+    shape = getattr(synth, shape_name)
+    cfg = mk.make_config(shape, batch, 256)
+    assert mk.mk_schedule_selftest(cfg, ncus, 0) == mk.MK_OK
+    expect = {1: "produced 2 times", 2: "produced 0 times", 3: "not in stage order", 4: "deadlock"}
+    for mutation, text in expect.items():
+        rc = mk.mk_schedule_selftest(cfg, ncus, mutation)
+        assert rc == mk.MK_ERR_UNSUPPORTED_SHAPE, (mutation, rc)
+        assert text in mk.mk_last_error(), (mutation, mk.mk_last_error())
+
+
+def test_validator_selftest_argument_errors():
+    cfg = mk.make_config(synth.TINY, 1, 64)
+    assert mk.mk_schedule_selftest(cfg, 0, 0) == mk.MK_ERR_INVALID_ARG
+    assert mk.mk_schedule_selftest(cfg, 4, 9) == mk.MK_ERR_INVALID_ARG
+    assert mk.lib().mk_schedule_selftest(None, 4, 0) == mk.MK_ERR_INVALID_ARG

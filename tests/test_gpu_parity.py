@@ -53,9 +53,9 @@ def test_tiny_prefill_and_greedy_decode_matches_oracle(multikernel):
 @pytest.mark.parametrize("gain_std", [0.1, 0.5])
 @pytest.mark.parametrize("multikernel", [False, True], ids=["megakernel", "multikernel"])
 def test_tiny_nonunit_norm_gains(multikernel, gain_std):
-    """RMSNorm gains 1 + N(0, gain_std) on every norm: the library folds them
-    into the packed weights (one extra bf16 rounding per weight); parity with
-    the oracle, which applies them to the normalised vector, must still hold."""
+    """RMSNorm gains 1 + N(0, gain_std) on every norm: the gather wave applies
+    them to the staged input in fp32 (x * gain), the oracle to the normalised
+    vector; the two agree up to fp32 rounding, well inside the parity bar."""
     weights, run, kv, max_seq = tiny_prefill_run(multikernel, gain_std=gain_std)
     ref = H.oracle_replay(synth.TINY, weights, 1, max_seq, run)
     stats = H.compare(run, ref, f"tiny gains {gain_std}")
