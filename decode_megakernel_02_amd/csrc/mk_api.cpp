@@ -26,6 +26,8 @@ hipError_t launch_empty(int n_blocks, int n_threads, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_greedy(const float* logits, int B, int V, int32_t* tokens, int32_t* positions, uint64_t* part,
                          uint32_t* cnt, hipStream_t stream);
+hipError_t launch_litmus(uint64_t* buf, int npairs, int rounds, int words, uint32_t spin_limit, uint32_t* result,
+                         hipStream_t stream);
 }  // namespace mk
 
 using namespace mk;
@@ -45,6 +47,7 @@ struct mk_handle {
 };
 
 static thread_local std::string g_create_error;
+static constexpr uint32_t DEFAULT_SPIN_LIMIT = 1u << 25;  // polls before a wait gives up (seconds)
 
 namespace {
 
@@ -238,7 +241,7 @@ int mk_create(const mk_config* cfg, mk_handle** out) {
         hp.side_floats = (int)(side_bytes / 4);
         hp.nslot = nslot;
         hp.eps = p.eps; hp.inv_sqrt_d = (float)(1.0 / std::sqrt((double)p.D));
-        hp.spin_limit = 1u << 25;
+        hp.spin_limit = DEFAULT_SPIN_LIMIT;
         for (int i = 0; i <= p.n_chunk; ++i) hp.chunk_begin[i] = p.chunk_begin[i];
         hp.n_stages = p.n_stages;
         hp.fp8 = p.fp8 ? 1 : 0;
@@ -439,6 +442,31 @@ int mk_decode_step_multikernel(mk_handle* h, const int32_t* tokens, const int32_
     return MK_OK;
 }
 
+int mk_set_spin_limit(mk_handle* h, uint32_t spins) {
+    if (!h) return fail(nullptr, MK_ERR_INVALID_ARG, "handle is NULL");
+    h->hp.spin_limit = spins ? spins : DEFAULT_SPIN_LIMIT;
+    try {
+        HIPCHK(hipSetDevice(h->cfg.device));
+        HIPCHK(hipDeviceSynchronize());  // no step may be reading the parameter block
+        HIPCHK(hipMemcpy(&h->dparams->spin_limit, &h->hp.spin_limit, sizeof(uint32_t), hipMemcpyHostToDevice));
+    } catch (const HipError& e) {
+        return hip_fail(h, e);
+    }
+    return MK_OK;
+}
+
+int mk_debug_stage(mk_handle* h, int32_t stage, const int32_t* tokens, const int32_t* positions, void* kv_cache,
+                   float* logits, void* stream) {
+    int rc = step_args_ok(h, tokens, positions, kv_cache, logits);
+    if (rc != MK_OK) return rc;
+    if (stage < 0 || stage >= h->hp.n_stages) return fail(h, MK_ERR_INVALID_ARG, "stage outside [0, n_stages)");
+    // the epoch advances, so nothing this launch writes is ever taken for a later step's data
+    hipError_t e = launch_step(h->dparams, h->hp.D, h->hp.ncu, h->lds_bytes, tokens, positions, kv_cache, logits,
+                               stage, KF_BUMP_EPOCH | instr_flag(h), (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(h, HipError{e, "mk_step_kernel stage launch"});
+    return MK_OK;
+}
+
 int mk_greedy_advance(mk_handle* h, const float* logits, int32_t* tokens, int32_t* positions, void* stream) {
     if (!h || !logits || !tokens || !positions) return fail(h, MK_ERR_INVALID_ARG, "null argument");
     hipError_t e = launch_greedy(logits, h->hp.B, h->hp.V, tokens, positions, h->greedy_part, h->greedy_cnt,
@@ -453,6 +481,36 @@ int mk_read_probe(const void* buf, size_t bytes, void* sink, int n_cus, void* st
     hipError_t e = launch_read_probe(buf, bytes, (uint32_t*)sink, n_cus, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(nullptr, HipError{e, "mk_read_probe_kernel launch"});
     return MK_OK;
+}
+
+int mk_litmus(int device, int32_t n_pairs, int32_t rounds, int32_t words, uint32_t spin_limit, uint32_t* result) {
+    if (n_pairs < 1 || n_pairs > 512 || rounds < 1 || rounds > (1 << 20) || words < 1 || words > 1024 || !result)
+        return fail(nullptr, MK_ERR_INVALID_ARG, "mk_litmus: n_pairs 1..512, rounds 1..2^20, words 1..1024, result non-NULL");
+    const size_t nres = 3 + 3 * (size_t)n_pairs;
+    uint64_t* buf = nullptr;
+    uint32_t* dres = nullptr;
+    hipStream_t s = nullptr;
+    int rc = MK_OK;
+    try {
+        HIPCHK(hipSetDevice(device));
+        HIPCHK(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
+        HIPCHK(hipMalloc(&buf, (size_t)n_pairs * 2 * words * 8));
+        HIPCHK(hipMalloc(&dres, nres * 4));
+        HIPCHK(hipMemsetAsync(buf, 0, (size_t)n_pairs * 2 * words * 8, s));
+        HIPCHK(hipMemsetAsync(dres, 0, nres * 4, s));
+        HIPCHK(launch_litmus(buf, n_pairs, rounds, words, spin_limit, dres, s));
+        HIPCHK(hipMemcpyAsync(result, dres, nres * 4, hipMemcpyDeviceToHost, s));
+        HIPCHK(hipStreamSynchronize(s));
+    } catch (const HipError& e) {
+        rc = hip_fail(nullptr, e);
+    }
+    if (s) {
+        (void)hipStreamSynchronize(s);
+        (void)hipStreamDestroy(s);
+    }
+    if (buf) (void)hipFree(buf);
+    if (dres) (void)hipFree(dres);
+    return rc;
 }
 
 int mk_empty_launches(int n_launches, int n_blocks, int n_threads, void* stream) {

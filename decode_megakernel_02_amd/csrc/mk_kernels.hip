@@ -1814,6 +1814,99 @@ hipError_t launch_greedy(const float* logits, int B, int V, int32_t* tokens, int
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------ litmus ------
+
+// Litmus test of the tagged-word protocol and ping-pong latency probe.  Pair
+// p is workgroup p (ping) and workgroup npairs + p (pong); with round-robin
+// dispatch over the XCDs the two share an XCD exactly when npairs is a
+// multiple of their number.  In round r the ping writes `words` tagged words
+// {value f(p, r, k), tag r + 1} with the same agent-coherent stores as the
+// step kernel; the pong polls them with the same loads until every tag is
+// r + 1, checks every value that arrived with the tag, and answers with
+// {g(p, r, k), r + 1}, which the ping polls and checks before its next round.
+// A value that is not the one stored with its tag counts as a mismatch; a
+// poll that exceeds spin_limit counts as a timeout and ends the pair's run.
+// result: [0] mismatches, [1] timeouts, [2] completed round trips, then per
+// pair [3 + 3p] ticks of the 100 MHz clock the ping spent, [4 + 3p] ping XCC,
+// [5 + 3p] pong XCC.
+__device__ __forceinline__ uint32_t litmus_value(uint32_t pair, uint32_t r, uint32_t k, uint32_t dir) {
+    uint32_t x = pair * 0x9E3779B1u ^ (r + 1u) * 0x85EBCA77u ^ k * 0xC2B2AE3Du ^ dir * 0x27D4EB2Fu;
+    x ^= x >> 15;
+    x *= 0x2C1B3C6Du;
+    x ^= x >> 12;
+    return x;
+}
+__device__ __forceinline__ uint32_t xcc_id() {
+    // HW_REG_XCC_ID (hardware register 20), bits 3:0
+    return (uint32_t)__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xfu;
+}
+constexpr int LITMUS_MAX_WORDS = 1024;  // 16 words per lane
+__global__ void __launch_bounds__(64) mk_litmus_kernel(uint64_t* buf, int npairs, int rounds, int words,
+                                                       uint32_t spin_limit, uint32_t* result) {
+    const int wg = blockIdx.x, lane = threadIdx.x;
+    const bool ping = wg < npairs;
+    const uint32_t pair = (uint32_t)(ping ? wg : wg - npairs);
+    uint64_t* fwd = buf + (size_t)pair * 2 * words;  // ping -> pong
+    uint64_t* back = fwd + words;                    // pong -> ping
+    uint32_t mism = 0, timeouts = 0, done = 0;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    auto send = [&](uint64_t* dst, uint32_t r, uint32_t dir) {
+        for (int k = lane; k < words; k += 64) st_tag(dst + k, __uint_as_float(litmus_value(pair, r, k, dir)), r + 1u);
+    };
+    // polls src until every tag is r + 1; false on timeout
+    auto recv = [&](const uint64_t* src, uint32_t r, uint32_t dir) -> bool {
+        uint64_t w[LITMUS_MAX_WORDS / 64];
+#pragma unroll
+        for (int j = 0; j < LITMUS_MAX_WORDS / 64; ++j) w[j] = lane + 64 * j < words ? ld_tag(src + lane + 64 * j) : 0;
+        uint32_t spins = 0;
+        while (true) {
+            bool stale = false;
+#pragma unroll
+            for (int j = 0; j < LITMUS_MAX_WORDS / 64; ++j) stale |= lane + 64 * j < words && tag_of(w[j]) != r + 1u;
+            if (!any_lane(stale)) break;
+            if (++spins > spin_limit) return false;
+            __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+            for (int j = 0; j < LITMUS_MAX_WORDS / 64; ++j)
+                if (lane + 64 * j < words && tag_of(w[j]) != r + 1u) w[j] = ld_tag(src + lane + 64 * j);
+        }
+#pragma unroll
+        for (int j = 0; j < LITMUS_MAX_WORDS / 64; ++j)
+            if (lane + 64 * j < words && __float_as_uint(val_of(w[j])) != litmus_value(pair, r, lane + 64 * j, dir)) ++mism;
+        return true;
+    };
+    for (int r = 0; r < rounds; ++r) {
+        if (ping) {
+            send(fwd, (uint32_t)r, 0);
+            if (!recv(back, (uint32_t)r, 1)) { ++timeouts; break; }
+        } else {
+            if (!recv(fwd, (uint32_t)r, 0)) { ++timeouts; break; }
+            send(back, (uint32_t)r, 1);
+        }
+        ++done;
+    }
+    const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+    for (int o = 32; o >= 1; o >>= 1) mism += (uint32_t)__shfl_xor((int)mism, o);
+    if (lane == 0) {
+        atomicAdd(&result[0], mism);
+        atomicAdd(&result[1], uni(timeouts));
+        if (ping) {
+            atomicAdd(&result[2], done);
+            result[3 + 3 * pair] = (uint32_t)(t1 - t0);
+            result[4 + 3 * pair] = xcc_id();
+        } else {
+            result[5 + 3 * pair] = xcc_id();
+        }
+    }
+}
+
+hipError_t launch_litmus(uint64_t* buf, int npairs, int rounds, int words, uint32_t spin_limit, uint32_t* result,
+                         hipStream_t stream) {
+    void* args[] = {(void*)&buf, (void*)&npairs, (void*)&rounds, (void*)&words, (void*)&spin_limit, (void*)&result};
+    // every pair waits on its partner: the grid must be resident at once
+    return hipLaunchCooperativeKernel((const void*)mk_litmus_kernel, dim3(2 * npairs), dim3(64), args, 0, stream);
+}
+
 // ------------------------------------------------------------ read probe --
 
 // Streams `bytes` from buf once (16-byte loads, eight in flight per lane): the

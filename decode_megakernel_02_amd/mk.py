@@ -55,7 +55,8 @@ class MkScheduleInfo(ctypes.Structure):
 EXPORTS = ["mk_create", "mk_load_weights", "mk_kv_cache_bytes", "mk_decode_step", "mk_decode_step_multikernel",
            "mk_destroy", "mk_status_string", "mk_last_error", "mk_get_device_error", "mk_get_profile",
            "mk_schedule_inspect", "mk_get_trace", "mk_greedy_advance", "mk_read_probe", "mk_empty_launches",
-           "mk_graph_create", "mk_graph_launch", "mk_graph_destroy", "mk_prefill", "mk_schedule_selftest"]
+           "mk_graph_create", "mk_graph_launch", "mk_graph_destroy", "mk_prefill", "mk_schedule_selftest", "mk_litmus", "mk_set_spin_limit",
+           "mk_debug_stage"]
 MK_FLAG_PROFILE = 1
 MK_FLAG_TRACE = 2
 MK_FLAG_FP8_WEIGHTS = 4
@@ -90,6 +91,9 @@ def lib():
         L.mk_last_error.restype = ctypes.c_char_p
         L.mk_get_device_error.argtypes = [H, ctypes.POINTER(MkDeviceError)]
         L.mk_schedule_inspect.argtypes = [ctypes.POINTER(MkConfig), ctypes.c_int32, ctypes.POINTER(MkScheduleInfo)]
+        L.mk_set_spin_limit.argtypes = [H, ctypes.c_uint32]
+        L.mk_debug_stage.argtypes = [H, ctypes.c_int32, _P, _P, _P, _P, _P]
+        L.mk_litmus.argtypes = [ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint32, _P]
         L.mk_schedule_selftest.argtypes = [ctypes.POINTER(MkConfig), ctypes.c_int32, ctypes.c_int32]
         L.mk_get_profile.argtypes = [H, _P, ctypes.c_size_t]
         L.mk_get_trace.argtypes = [H, _P, ctypes.c_size_t]
@@ -102,7 +106,7 @@ def lib():
         for name in ["mk_create", "mk_load_weights", "mk_decode_step", "mk_decode_step_multikernel", "mk_destroy",
                      "mk_get_device_error", "mk_schedule_inspect", "mk_get_profile", "mk_get_trace",
                      "mk_greedy_advance", "mk_read_probe", "mk_empty_launches", "mk_graph_create",
-                     "mk_graph_launch", "mk_graph_destroy", "mk_prefill", "mk_schedule_selftest"]:
+                     "mk_graph_launch", "mk_graph_destroy", "mk_prefill", "mk_schedule_selftest", "mk_litmus", "mk_set_spin_limit", "mk_debug_stage"]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -155,6 +159,16 @@ def mk_schedule_selftest(cfg: MkConfig, n_cus: int, mutation: int) -> int:
     """Runs the schedule validator on a schedule with a planted defect (see include/mk.h);
     returns the status code (MK_OK: accepted) without raising."""
     return int(lib().mk_schedule_selftest(ctypes.byref(cfg), n_cus, mutation))
+
+
+def mk_litmus(n_pairs: int, rounds: int, words: int, spin_limit: int = 1 << 22, device: int = 0):
+    """Runs the tagged-word litmus (see include/mk.h); returns (mismatches, timeouts, round_trips,
+    per-pair ticks [n_pairs], ping XCC ids [n_pairs], pong XCC ids [n_pairs])."""
+    import numpy as np
+    res = np.zeros(3 + 3 * n_pairs, dtype=np.uint32)
+    _check(lib().mk_litmus(device, n_pairs, rounds, words, spin_limit, res.ctypes.data))
+    per = res[3:].reshape(n_pairs, 3)
+    return int(res[0]), int(res[1]), int(res[2]), per[:, 0].copy(), per[:, 1].copy(), per[:, 2].copy()
 
 
 def _ptr(t) -> int:
@@ -238,6 +252,15 @@ def mk_decode_step_multikernel(handle, tokens, positions, kv_cache, logits, stre
 
 def mk_greedy_advance(handle, logits, tokens, positions, stream: Optional[int] = None):
     _check(lib().mk_greedy_advance(handle, _ptr(logits), _ptr(tokens), _ptr(positions), stream), handle)
+
+
+def mk_set_spin_limit(handle, spins: int):
+    _check(lib().mk_set_spin_limit(handle, spins), handle)
+
+
+def mk_debug_stage(handle, stage: int, tokens, positions, kv_cache, logits, stream: Optional[int] = None):
+    _check(lib().mk_debug_stage(handle, stage, _ptr(tokens), _ptr(positions), _ptr(kv_cache), _ptr(logits), stream),
+           handle)
 
 
 def mk_get_device_error(handle) -> Optional[MkDeviceError]:

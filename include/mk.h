@@ -239,6 +239,26 @@ typedef struct {
  * clears it.  Returns MK_OK, or MK_ERR_DEVICE when a record was present.  */
 int mk_get_device_error(mk_handle* h, mk_device_error* out);
 
+/* Watchdog of the bounded waits ("Megakernels: Deleting the Kernel Boundary
+ * to Win Back Microseconds", section "The catch": a hand-rolled dependency
+ * graph that is wrong hangs instead of failing).  Every wait in the step
+ * kernels polls at most `spins` times (0 restores the default of 2^25, a few
+ * seconds), then writes an error record with code 1 (the workgroup, queue
+ * position, opcode, wave and what it waited for), raises an abort flag that
+ * every other waiting wave sees, and the grid drains normally.  Synchronises
+ * the device.  The setting stays with the handle.                          */
+int mk_set_spin_limit(mk_handle* h, uint32_t spins);
+
+/* Diagnostics: launches stage `stage` (0 .. 6L: six per layer in op order,
+ * then the LM head) of the per-op path on its own, as one kernel on `stream`.
+ * A stage whose producers did not run in the same step waits for inputs that
+ * never arrive; with a small spin limit (mk_set_spin_limit) this exercises the
+ * watchdog.  The handle's step counter advances, so nothing the launch writes
+ * is taken for a later step's data; the KV slot of a QKV stage and the logits
+ * of the LM-head stage may be overwritten.                                */
+int mk_debug_stage(mk_handle* h, int32_t stage, const int32_t* tokens, const int32_t* positions,
+                   void* kv_cache, float* logits, void* stream);
+
 /* Per-wave cycle counters of the last step (handle created with
  * MK_FLAG_PROFILE): counters[(cu * 12 + wave) * 8 + k], 8 x uint64 per wave,
  * waves 0..7 compute, 8..11 loaders.  Compute k: 0 cycles in the kernel,
@@ -265,6 +285,23 @@ int mk_get_profile(mk_handle* h, uint64_t* counters, size_t n);
  * `n` is the capacity in elements; synchronises the device.  Returns
  * MK_ERR_STATE when tracing is off.                                        */
 int mk_get_trace(mk_handle* h, uint64_t* records, size_t n);
+
+/* Litmus test of the tagged-word dependency protocol across CUs, and a probe
+ * of its cross-CU latency (the hazard that "Megakernels: Deleting the Kernel
+ * Boundary to Win Back Microseconds", section "Correctness without the free
+ * barrier", warns about: a consumer must never see data older than the
+ * producer's store).  n_pairs (1..512) pairs of single-wave workgroups, pair
+ * p = workgroups p and n_pairs + p (on the same XCD of the round-robin
+ * dispatch exactly when n_pairs is a multiple of the XCD count), play
+ * `rounds` (1..2^20) round trips of `words` (1..1024) tagged words each way,
+ * written and polled with the step kernel's own store and load primitives;
+ * every value that arrives with the round's tag is checked.  Polls give up
+ * after spin_limit sleeps (a timeout ends that pair's run).  Writes, to the
+ * HOST array result[3 + 3 * n_pairs]: [0] mismatched values, [1] timeouts,
+ * [2] completed round trips, then per pair: ticks (100 MHz) the ping side
+ * spent, ping XCC id, pong XCC id.  Allocates and frees its own buffers,
+ * runs on a private stream and waits for it.                              */
+int mk_litmus(int device, int32_t n_pairs, int32_t rounds, int32_t words, uint32_t spin_limit, uint32_t* result);
 
 /* Host-only inspection of the schedule for `cfg` on `n_cus` CUs: builds it,
  * checks that every output row / unit is produced exactly once and that the
