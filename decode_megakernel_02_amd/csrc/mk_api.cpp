@@ -242,6 +242,7 @@ int mk_create(const mk_config* cfg, mk_handle** out) {
         hp.nslot = nslot;
         hp.eps = p.eps; hp.inv_sqrt_d = (float)(1.0 / std::sqrt((double)p.D));
         hp.spin_limit = DEFAULT_SPIN_LIMIT;
+
         for (int i = 0; i <= p.n_chunk; ++i) hp.chunk_begin[i] = p.chunk_begin[i];
         hp.n_stages = p.n_stages;
         hp.fp8 = p.fp8 ? 1 : 0;

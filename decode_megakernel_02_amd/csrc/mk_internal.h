@@ -6,11 +6,11 @@
 namespace mk {
 
 // Workgroup shape: one workgroup per CU, NW compute waves and NLOAD helper
-// waves: NLOAD - 1 weight loaders (each streams the packed weights of up to
-// four compute waves into their LDS rings) and one gather wave (stages the
-// cross-CU inputs of each instruction).
+// waves: one weight loader (streams the packed weights of every compute wave
+// into their LDS rings) and one gather wave (stages the cross-CU inputs of
+// each instruction).
 constexpr int NW = 8;                 // compute waves
-constexpr int NLOAD = 4;              // helper waves: 3 weight loaders + 1 gather wave
+constexpr int NLOAD = 2;              // helper waves: 1 weight loader + 1 gather wave
 constexpr int WG_THREADS = 64 * (NW + NLOAD);
 constexpr int UNIT_BYTES = 1024;      // one DMA: 64 lanes x 16 B
 constexpr int UNIT_ELEMS = 512;       // bf16 per unit
@@ -52,7 +52,8 @@ MK_INLINE constexpr bool batch1_path(int B, int ku, bool fp8) { return B == 1 &&
 
 // One queue entry (16 bytes).  GEMV ops: row-groups [rg0, rg0 + nrg) of the
 // op's row-group space, distributed round-robin over the NW compute waves
-// (row-group i goes to wave i % NW).  DOWN_RES: a = chunk.
+// (row-group i goes to wave i % NW); b = the instruction's unit-rows (the
+// most weight units any one wave reads in it).  DOWN_RES: a = chunk.
 // ATTENTION: a = batch row, b = KV group, rg0 = split.
 // ATTN_REDUCE: a = batch row, b = query head.
 struct Inst {

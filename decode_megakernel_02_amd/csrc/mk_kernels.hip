@@ -91,19 +91,9 @@ __device__ __forceinline__ void gst(T* p, T v) {
 
 #define CBAR() asm volatile("" ::: "memory")
 
-#ifndef MK_MAXOUT
-#define MK_MAXOUT 16
-#endif
-#ifndef MK_KEEP
-#define MK_KEEP 8
-#endif
-constexpr int MAXOUT = MK_MAXOUT;  // DMA units in flight per loader wave
-#ifndef MK_NGATHER
-#define MK_NGATHER 1
-#endif
-constexpr int NGATHER = MK_NGATHER;  // gather waves (instruction r is staged by gather wave r % NGATHER)
-constexpr int NWL = NLOAD - NGATHER; // weight loader waves
-static_assert(NW <= 4 * NWL, "a weight loader serves at most four compute waves");
+constexpr int NGATHER = 1;  // gather waves
+constexpr int NWL = 1;      // weight loader waves
+static_assert(NLOAD == NWL + NGATHER, "one loader wave and one gather wave");
 
 // ------------------------------------------------------------- primitives --
 
@@ -179,13 +169,7 @@ __device__ __forceinline__ uint32_t asm_lds_ld(uint32_t a) {
 __device__ __forceinline__ void asm_lds_st(uint32_t a, uint32_t v) {
     asm volatile("ds_write_b32 %0, %1" ::"v"(a), "v"(v) : "memory");
 }
-// wait until at most MK_KEEP (or no) vector-memory operations of this wave are outstanding
-#define MK_STR2(x) #x
-#define MK_STR(x) MK_STR2(x)
-__device__ __forceinline__ void wait_vm_keep() { asm volatile("s_waitcnt vmcnt(" MK_STR(MK_KEEP) ")" ::: "memory"); }
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-static_assert(MAXOUT <= 32, "the loader's stream-id FIFO holds 32 entries");
-static_assert(MAXOUT <= 63, "vmcnt counts at most 63 operations");
 
 // ------------------------------------------------------------ wave context --
 
@@ -274,7 +258,7 @@ static_assert(SYNC_WORDS <= 64, "sync words precede the prefetch dump");  // dum
 struct Lds {
     LDS uint8_t* ring;      // [NW][ring_units][1024]
     LDS float* xbuf0;       // nslot x buffers of xbuf_bytes each, back to back
-    LDS uint32_t* landed;   // [NW] units landed in each compute wave's ring
+    LDS uint32_t* landed;   // [0]: unit-rows landed in every compute wave's ring ([1 .. NW) unused)
     LDS uint32_t* consumed; // [NW] units consumed
     LDS uint32_t* bar;      // compute-wave barrier counter
     LDS uint32_t* ready;    // [MAX_SLOTS] r + 1 once instruction r's inputs are staged in buffer set r % nslot
@@ -329,138 +313,127 @@ __device__ __forceinline__ void cbar(Ctx& cx, const Lds& s, uint32_t& seq) {
 
 // ------------------------------------------------------------- loader wave --
 
-// One compute wave's stream as seen by its loader.  Every field is wave
-// uniform (scalar registers).
-struct LoadStream {
-    const uint8_t* src;   // this lane's 16 bytes of the next unit to issue
-    uint32_t ring_lds;    // LDS byte address of the ring
-    uint32_t n, issued, done, slot, consumed;
-    uint32_t a_landed, a_consumed;
-};
-
-__device__ __forceinline__ void load_stream_init(const Ctx& cx, const Lds& s, LoadStream& ls, int w, uint32_t ub,
-                                                 uint32_t ue) {
-    CParams& p = *cx.p;
-    // the loaded values are the same in every lane: make that visible to the
-    // compiler so the loader's loop state lives in scalar registers
-    ub = __builtin_amdgcn_readfirstlane(ub);
-    ue = __builtin_amdgcn_readfirstlane(ue);
-    const uint64_t base = p.stream_base[cx.cu * NW + w];
-    const uint64_t base_u = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32)) << 32) |
-                            __builtin_amdgcn_readfirstlane((uint32_t)base);
-    ls.src = p.wstream + (base_u + (uint64_t)ub * NW) * UNIT_BYTES + cx.lane * 16;
-    ls.ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(s.ring + (size_t)w * p.ring_units * UNIT_BYTES));
-    ls.n = ue - ub;
-    ls.issued = ls.done = ls.slot = ls.consumed = 0;
-    ls.a_landed = lds_addr(&s.landed[w]);
-    ls.a_consumed = lds_addr(&s.consumed[w]);
-}
-
-constexpr uint32_t ISSUE_BATCH = 4;  // units issued per stream per turn
-
-// Issues up to `max` (<= ISSUE_BATCH) consecutive units of the stream, as many
-// as its ring has room for (re-reading the consumer's count only when the
-// ring looks too full); returns how many.
-__device__ __forceinline__ uint32_t load_stream_issue(LoadStream& ls, uint32_t ru, uint32_t max) {
-    if (ls.issued >= ls.n) return 0;
-    if (ls.issued + max > ls.consumed + ru) ls.consumed = uni(asm_lds_ld(ls.a_consumed));
-    uint32_t k = ls.consumed + ru - ls.issued;
-    k = k < max ? k : max;
-    k = k < ls.n - ls.issued ? k : ls.n - ls.issued;
-#pragma unroll
-    for (uint32_t i = 0; i < ISSUE_BATCH; ++i) {
-        if (i < k) {
-            __builtin_amdgcn_global_load_lds((const glb_void*)ls.src,
-                                             (lds_void*)(uintptr_t)(ls.ring_lds + ls.slot * UNIT_BYTES), 16, 0, 0);
-            ls.src += NW * UNIT_BYTES;
-            ls.slot = ls.slot + 1 == ru ? 0 : ls.slot + 1;
-        }
-    }
-    ls.issued += k;
-    return k;
-}
-
-constexpr uint32_t KEEP_IN_FLIGHT = MK_KEEP;  // units left outstanding when retiring a batch
-static_assert(MK_KEEP < MK_MAXOUT, "a retire step must free at least one unit");
+// One loader wave streams the weights of all NW compute waves.  Unit u of
+// compute wave w's stream is packed at stream_base[cu * NW + w] + u * NW.
+// The loader walks the CU's instructions in queue order and issues each GEMV
+// instruction's units as unit-rows: row j holds unit j of the instruction for
+// every compute wave, DMA'd into that wave's ring slot (row index) % ring_units.
+// An instruction has as many rows as the wave with the most units in it
+// needs (field b of the instruction); a wave with fewer units gets a spare
+// unit (any resident 1 KiB of the packed buffer) in the rest of its rows and
+// skips them.  So row r maps to the same instruction in every ring, one
+// `landed` counter (rows fully arrived) serves every wave, and a row is issued
+// only when every ring has its slot free (each compute wave publishes how many
+// rows it has consumed).  Weights never depend on activations, so the loader
+// runs ahead across instruction and layer boundaries as far as the rings
+// allow (the page "Megakernels: Deleting the Kernel Boundary to Win Back
+// Microseconds", section "Correctness without the free barrier": the next
+// instruction's loads start early).  Its loop costs a few scalar instructions
+// per unit: it shares a SIMD with compute waves at raised priority, so every
+// instruction it spends is taken from them.
 #ifndef MK_LOADER_PRIO
 #define MK_LOADER_PRIO 2
 #endif
 #ifndef MK_LOADER_SLEEP
-#define MK_LOADER_SLEEP 2
+#define MK_LOADER_SLEEP 1
 #endif
+#ifndef MK_LD_ROWS
+#define MK_LD_ROWS 7
+#endif
+#ifndef MK_LD_KEEP
+#define MK_LD_KEEP 3
+#endif
+constexpr uint32_t LD_ROWS = MK_LD_ROWS;  // unit-rows in flight (NW DMAs each; vmcnt counts at most 63)
+constexpr uint32_t LD_KEEP = MK_LD_KEEP;  // unit-rows left in flight when retiring
+static_assert(LD_ROWS * NW <= 63 && LD_KEEP < LD_ROWS, "DMA accounting");
+// s_waitcnt immediate (gfx9 layout) that waits for vmcnt <= n only: vmcnt bits 3:0 and 15:14,
+// expcnt 6:4 and lgkmcnt 11:8 at their maxima
+constexpr int vmcnt_imm(int n) { return ((n >> 4) << 14) | 0xF00 | 0x70 | (n & 15); }
+static_assert(vmcnt_imm(0) == 0x0F70, "matches the encoding of vm_drain");
 
-// Streams the units of up to four compute waves (w, w + NWL, ...) into their
-// rings.  DMA completes in issue order, so a FIFO of 2-bit stream ids (entry
-// i = stream of the i-th oldest outstanding unit) says whose units a vmcnt
-// step retires.  Units are retired in batches, keeping KEEP_IN_FLIGHT
-// outstanding while the rings have room.  The loader never blocks while DMA
-// is in flight: when every ring is full it retires what is outstanding
-// instead, so it cannot wait on a compute wave in a cycle.  It runs at raised
-// instruction priority so the compute waves' polling cannot starve it of
-// issue slots.
-__device__ __forceinline__ void loader(Ctx& cx, const Lds& s, int w0, const uint32_t* uoff, uint32_t pc0,
-                                       uint32_t pc1) {
+__device__ __forceinline__ void loader(Ctx& cx, const Lds& s, const uint32_t* uoff, uint32_t pc0, uint32_t pc1) {
     __builtin_amdgcn_s_setprio(MK_LOADER_PRIO);
-    const uint32_t ru = uni((uint32_t)cx.p->ring_units);
-    LoadStream st[4];
+    CParams& p = *cx.p;
+    const uint32_t ru = uni((uint32_t)p.ring_units);
+    const uint8_t* base[NW];  // wave-uniform: unit 0 of compute wave w's stream
+    uint32_t cur[NW];         // wave w's first unit of the instruction being streamed
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int w = w0 + k * NWL;
-        if (w < NW) load_stream_init(cx, s, st[k], w, uoff[(size_t)pc0 * NW + w], uoff[(size_t)pc1 * NW + w]);
-        else load_stream_init(cx, s, st[k], w0, 0, 0);  // no such stream
+    for (int w = 0; w < NW; ++w) {
+        const uint64_t b = p.stream_base[cx.cu * NW + w];
+        const uint64_t bu = ((uint64_t)uni((uint32_t)(b >> 32)) << 32) | uni((uint32_t)b);
+        base[w] = p.wstream + bu * UNIT_BYTES;
+        cur[w] = uni(uoff[(size_t)pc0 * NW + w]);
     }
-    auto issue = [&](uint32_t sid, uint32_t max) -> uint32_t {
-        return sid == 0 ? load_stream_issue(st[0], ru, max)
-             : sid == 1 ? load_stream_issue(st[1], ru, max)
-             : sid == 2 ? load_stream_issue(st[2], ru, max) : load_stream_issue(st[3], ru, max);
+    // spare source of padding rows: unit 0 of the CU's region (it exists whenever a row is issued)
+    const uint8_t* spare = base[0];
+    const uint32_t voff = (uint32_t)cx.lane * 16;  // this lane's 16 bytes of a unit
+    const uint32_t ring0 = uni(lds_addr(s.ring));
+    const uint32_t a_landed = uni(lds_addr(&s.landed[0]));
+    uint32_t u = 0, slot = 0, published = 0;
+    uint32_t room = ru;  // rows below `room` have a free slot in every ring (nothing consumed yet)
+    uint32_t spins = 0;
+    bool stop = false;
+    auto publish = [&](uint32_t v) {
+        published = v;
+        asm_lds_st(a_landed, v);
     };
-    uint64_t fifo = 0;  // 2-bit stream id per outstanding unit, oldest in the low bits
-    uint32_t out = 0, spins = 0, turn = 0;
-    while (st[0].done < st[0].n || st[1].done < st[1].n || st[2].done < st[2].n || st[3].done < st[3].n) {
-        while (out < (uint32_t)MAXOUT) {
-            const uint32_t max = MAXOUT - out < ISSUE_BATCH ? MAXOUT - out : ISSUE_BATCH;
-            uint32_t sid = turn, k = 0;
+    for (uint32_t pc = pc0; pc < pc1 && !stop; ++pc) {
+        uint32_t nxt[NW], rows = 0;
 #pragma unroll
-            for (int tries = 0; tries < 4 && k == 0; ++tries) {
-                k = issue(sid, max);
-                if (!k) sid = (sid + 1) & 3u;
+        for (int w = 0; w < NW; ++w) {
+            nxt[w] = uni(uoff[(size_t)(pc + 1) * NW + w]);
+            rows = nxt[w] - cur[w] > rows ? nxt[w] - cur[w] : rows;
+        }
+        for (uint32_t j = 0; j < rows;) {
+            if (u >= room) {
+                uint32_t m = 0xffffffffu;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    const uint32_t c = uni(asm_lds_ld(lds_addr(&s.consumed[w])));
+                    m = c < m ? c : m;
+                }
+                room = m + ru;
+                if (u >= room) {
+                    const uint64_t t0 = cx.prof ? cycles() : 0;
+                    if (published < u) {  // hand over what is in flight before waiting on the consumers
+                        wait_vm_all();
+                        publish(u);
+                    } else if (!keep_waiting<MK_LOADER_SLEEP>(cx, spins, 0x10000000u | u)) {
+                        stop = true;
+                        break;
+                    }
+                    if (cx.prof) cx.cnt[2] += cycles() - t0;
+                    continue;
+                }
+                spins = 0;
             }
-            if (!k) break;
-            fifo |= (uint64_t)(sid * (0x55u & ((1u << (2 * k)) - 1u))) << (2 * out);  // k entries of sid
-            out += k;
-            turn = (sid + 1) & 3u;
+            const uint32_t dst = ring0 + slot * UNIT_BYTES;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const uint32_t unit = cur[w] + j;
+                const uint8_t* src = unit < nxt[w] ? base[w] + (size_t)unit * (NW * UNIT_BYTES) : spare;
+                __builtin_amdgcn_global_load_lds((const glb_void*)(src + voff),
+                                                 (lds_void*)(uintptr_t)(dst + (uint32_t)w * ru * UNIT_BYTES), 16, 0, 0);
+            }
+            slot = slot + 1 == ru ? 0 : slot + 1;
+            ++u;
+            ++j;
+            if (cx.prof) {
+                cx.cnt[3] += NW;
+                cx.cnt[4] += 1;
+            }
+            if (u - published >= LD_ROWS) {  // retire all but the LD_KEEP newest rows
+                const uint64_t t0 = cx.prof ? cycles() : 0;
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(LD_KEEP * NW));
+                publish(u - LD_KEEP);
+                if (cx.prof) cx.cnt[1] += cycles() - t0;
+            }
         }
-        if (out > 0) {
-            // retire all but KEEP_IN_FLIGHT units (all of them when nothing more could be issued)
-            const bool blocked = out < (uint32_t)MAXOUT;
-            const uint32_t keep = blocked ? 0u : KEEP_IN_FLIGHT;
-            const uint64_t t0 = cx.prof ? cycles() : 0;
-            if (blocked) wait_vm_all();
-            else wait_vm_keep();
-            if (cx.prof) cx.cnt[1] += cycles() - t0;
-            const uint32_t k = out - keep;
-            const uint64_t f = k >= 32 ? fifo : fifo & ((1ull << (2 * k)) - 1ull);
-            const uint64_t lo = f & 0x5555555555555555ull, hi = (f >> 1) & 0x5555555555555555ull;
-            const uint32_t n1 = (uint32_t)__builtin_popcountll(lo & ~hi), n2 = (uint32_t)__builtin_popcountll(hi & ~lo);
-            const uint32_t n3 = (uint32_t)__builtin_popcountll(lo & hi);
-            const uint32_t n0 = k - n1 - n2 - n3;
-            fifo = k >= 32 ? 0ull : fifo >> (2 * k);
-            out = keep;
-            if (n0) asm_lds_st(st[0].a_landed, st[0].done += n0);
-            if (n1) asm_lds_st(st[1].a_landed, st[1].done += n1);
-            if (n2) asm_lds_st(st[2].a_landed, st[2].done += n2);
-            if (n3) asm_lds_st(st[3].a_landed, st[3].done += n3);
-            if (cx.prof) cx.cnt[3] += k;
-            spins = 0;
-        } else {
-            const uint64_t t0 = cx.prof ? cycles() : 0;
-            const bool go_on = keep_waiting<MK_LOADER_SLEEP>(cx, spins, 0x10000000u | (st[0].done << 12) | st[1].done);
-            if (cx.prof) cx.cnt[2] += cycles() - t0;
-            if (!go_on) break;
-        }
-        if (cx.prof) cx.cnt[4] += 1;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) cur[w] = nxt[w];
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vm_all();
+    publish(u);
 }
 
 // ------------------------------------------------------------ compute side --
@@ -487,7 +460,7 @@ __device__ __forceinline__ uint4 ring_take(Ctx& cx, const Lds& s, Stream& st) {
         const uint64_t t0 = cx.prof ? cycles() : 0;
         const uint64_t r0 = cx.trace ? rtime() : 0;
         uint32_t spins = 0;
-        while ((st.landed = uni(lds_ld(&s.landed[cx.wave]))) <= st.unit)
+        while ((st.landed = uni(lds_ld(&s.landed[0]))) <= st.unit)
             if (!keep_waiting(cx, spins, 0x20000000u | st.unit)) break;
         CBAR();
         if (cx.prof) cx.cnt[1] += cycles() - t0;
@@ -572,7 +545,7 @@ __device__ __forceinline__ void ring_wait(Ctx& cx, const Lds& s, Stream& st, uin
     const uint64_t t0 = cx.prof ? cycles() : 0;
     const uint64_t r0 = cx.trace ? rtime() : 0;
     uint32_t spins = 0;
-    while ((st.landed = uni(lds_ld(&s.landed[cx.wave]))) < need)
+    while ((st.landed = uni(lds_ld(&s.landed[0]))) < need)
         if (!keep_waiting(cx, spins, 0x20000000u | st.unit)) break;
     CBAR();
     if (cx.prof) cx.cnt[1] += cycles() - t0;
@@ -1141,6 +1114,7 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
     CParams& p = *cx.p;
     const int B = p.B, H = p.H, l = in.layer;
     const int ku = in.op == OP_O_PROJ_RES ? p.ku_q : in.op == OP_DOWN_RES ? p.ku_f : p.ku_h;
+    const uint32_t row_end = st.unit + in.b;  // the instruction's unit-rows end here in every ring
     // x = raw input * gain, staged by the gather wave; lane b: RMSNorm scale of batch row b
     wait_inputs(cx, s, r);
     if (cx.aborted) return;
@@ -1281,6 +1255,13 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
         }
         }
         if (cx.aborted) return;
+    }
+    // rows of this instruction that hold no units of this wave: skip them
+    if (st.unit < row_end) {
+        const uint32_t ru = uni((uint32_t)p.ring_units);
+        st.slot = (st.slot + (row_end - st.unit)) % ru;
+        st.unit = row_end;
+        ring_release(cx, s, st);
     }
     mark_mid(cx);
 }
@@ -1574,9 +1555,9 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
         flush_prof(wave);
         return;
     }
-    if (wave >= NW) {  // weight loader of compute waves i, i + NWL, i + 2 NWL, ...
+    if (wave >= NW) {  // the weight loader of every compute wave
         cx.wave = wave;
-        loader(cx, s, wave - NW, uoff, pc0, pc1);
+        loader(cx, s, uoff, pc0, pc1);
         flush_prof(wave);
         return;
     }

@@ -258,6 +258,26 @@ int build_plan(const mk_config& c, int ncu, Plan& p, std::string& err) {
         }
         for (int w = 0; w < NW; ++w) p.stream_len[(size_t)cu * NW + w] = len[w];
     }
+    // The loader streams a GEMV instruction's units as unit-rows (unit j of every compute wave at
+    // once), as many as the wave with the most units in it needs; the other waves skip the rest.
+    // The row count goes into field b of the instruction, so every wave knows where it ends.
+    for (int cu = 0; cu < ncu; ++cu) {
+        const size_t qb = p.queue_begin[cu];
+        for (size_t pc = 0; pc < b.q[cu].size(); ++pc) {
+            Inst& in = p.insts[qb + pc];
+            if (in.op == OP_ATTENTION || in.op == OP_ATTN_REDUCE) continue;
+            uint32_t rows = 0;
+            for (int w = 0; w < NW; ++w) {
+                const size_t i0 = (qb + cu + pc) * NW + w, i1 = (qb + cu + pc + 1) * NW + w;
+                rows = std::max(rows, p.unit_off[i1] - p.unit_off[i0]);
+            }
+            if (rows > 0xffffu) {
+                err = "an instruction holds more than 65535 weight units per wave";
+                return MK_ERR_UNSUPPORTED_SHAPE;
+            }
+            in.b = (uint16_t)rows;
+        }
+    }
     // A CU's NW streams are interleaved unit by unit: unit k of wave w sits at
     // cu_base + k * NW + w, so the CU's concurrent reads stay inside one
     // advancing window of NW units (HBM row locality).

@@ -63,7 +63,7 @@ MK_FLAG_FP8_WEIGHTS = 4
 MK_GRAPH_MULTIKERNEL = 1
 MK_GRAPH_EMPTY = 2
 TRACE_SLOTS = 52
-PROF_WAVES = 12  # 8 compute + 4 loader waves per workgroup
+PROF_WAVES = 10  # 8 compute waves, the loader and the gather wave per workgroup
 PROF_SLOTS = 8
 
 _lib = None
@@ -273,7 +273,7 @@ def mk_get_device_error(handle) -> Optional[MkDeviceError]:
 
 
 def mk_get_profile(handle, n_cus: int):
-    """Cycle counters of the last step as a numpy array [n_cus][12][8] (uint64)."""
+    """Cycle counters of the last step as a numpy array [n_cus][10][8] (uint64)."""
     import numpy as np
     out = np.zeros((n_cus, PROF_WAVES, PROF_SLOTS), dtype=np.uint64)
     _check(lib().mk_get_profile(handle, out.ctypes.data, out.size), handle)

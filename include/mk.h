@@ -260,12 +260,13 @@ int mk_debug_stage(mk_handle* h, int32_t stage, const int32_t* tokens, const int
                    void* kv_cache, float* logits, void* stream);
 
 /* Per-wave cycle counters of the last step (handle created with
- * MK_FLAG_PROFILE): counters[(cu * 12 + wave) * 8 + k], 8 x uint64 per wave,
- * waves 0..7 compute, 8..11 loaders.  Compute k: 0 cycles in the kernel,
+ * MK_FLAG_PROFILE): counters[(cu * 10 + wave) * 8 + k], 8 x uint64 per wave,
+ * waves 0..7 compute, 8 the weight loader, 9 the gather wave (only k = 0).
+ * Compute k: 0 cycles in the kernel,
  * 1 waiting for weight units, 2 waiting for tagged inputs, 3 in workgroup
  * barriers, 4 units read, 5 barriers passed, 6 barrier polls, 7 barriers
  * this wave completed last.  Loader k: 0 cycles in the kernel, 1 waiting for
- * DMA completion, 2 idle with full rings, 3 units loaded, 4 loop iterations.
+ * DMA completion, 2 waiting for ring space, 3 units loaded, 4 unit-rows.
  * `n` is the capacity of `counters` in elements; synchronises the device.
  * Returns MK_ERR_STATE when profiling is off.                             */
 int mk_get_profile(mk_handle* h, uint64_t* counters, size_t n);
