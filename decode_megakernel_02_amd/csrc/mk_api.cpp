@@ -217,10 +217,14 @@ int mk_create(const mk_config* cfg, mk_handle** out) {
         size_t side = std::max((size_t)p.B * p.D, (size_t)p.B * max_rows);
         if (side > SIDE_MAX_FLOATS) side = 0;  // too many rows per CU: epilogues read global memory
         const size_t side_bytes = (side * 4 + 15) / 16 * 16;
+        // launch-resident rows: the step's RoPE rows [B][D], and (with side buffers) the CU's
+        // residual rows [B][max_rows], which the single-launch step keeps in LDS across ops
+        const int res_stride = side ? (int)max_rows : 0;
+        const size_t keep_bytes = ((size_t)p.B * p.D * 4 + (size_t)p.B * res_stride * 4 + 15) / 16 * 16;
         // the batch-1 path reads a whole row of units at once; the general path one unit at a time
         const int ring_need = p.B == 1 ? std::max(2, std::max(std::max(p.ku_h, p.ku_q), p.ku_f)) : 2;
         auto rings_for = [&](int nslot) {
-            const long budget = (long)LDS_BYTES - nslot * (long)(xb + side_bytes) - (long)sync_bytes;
+            const long budget = (long)LDS_BYTES - nslot * (long)(xb + side_bytes) - (long)sync_bytes - (long)keep_bytes;
             return (int)std::min<long>(32, budget / (NW * UNIT_BYTES));
         };
         // three buffer sets when the rings keep at least 12 slots, else two; one when two
@@ -231,7 +235,7 @@ int mk_create(const mk_config* cfg, mk_handle** out) {
             delete h;
             return fail(nullptr, MK_ERR_UNSUPPORTED_SHAPE, "batch x hidden too large for the LDS budget");
         }
-        h->lds_bytes = (size_t)NW * ring_units * UNIT_BYTES + nslot * (xb + side_bytes) + sync_bytes;
+        h->lds_bytes = (size_t)NW * ring_units * UNIT_BYTES + nslot * (xb + side_bytes) + sync_bytes + keep_bytes;
 
         Params& hp = h->hp;
         hp.L = p.L; hp.H = p.H; hp.Hq = p.Hq; hp.Hkv = p.Hkv; hp.D = p.D; hp.F = p.F; hp.V = p.V; hp.B = p.B;
@@ -240,6 +244,7 @@ int mk_create(const mk_config* cfg, mk_handle** out) {
         hp.ring_units = ring_units; hp.xbuf_bytes = (int)xb; hp.ncu = ncu;
         hp.side_floats = (int)(side_bytes / 4);
         hp.nslot = nslot;
+        hp.res_stride = res_stride;
         hp.eps = p.eps; hp.inv_sqrt_d = (float)(1.0 / std::sqrt((double)p.D));
         hp.spin_limit = DEFAULT_SPIN_LIMIT;
 

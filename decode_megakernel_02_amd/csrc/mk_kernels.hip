@@ -181,6 +181,7 @@ struct Ctx {
     uint32_t slot;     // buffer set of the current instruction's staged inputs
     uint32_t op;
     bool aborted;
+    bool resident;     // one launch for the whole step: the CU's residual rows stay in LDS between ops
     bool prof;         // accumulate cycle counters
     bool trace;        // write timeline records
     uint64_t t_acq;    // real time at which the current instruction's cross-CU inputs were loaded
@@ -265,6 +266,8 @@ struct Lds {
     LDS uint32_t* done;     // [NW] instructions each compute wave has finished
     LDS float* ss;          // [MAX_SLOTS][MAX_BATCH] sum of squares of each x buffer's raw input rows
     LDS float* side0;       // nslot side buffers (side_floats each): epilogue inputs staged with x buffer i
+    LDS float* rope;        // [B][D] (cos, sin) pairs of the step's positions, loaded once per launch
+    LDS float* res;         // [B][res_stride] the CU's residual rows (O and down-projection tile)
 };
 __device__ __forceinline__ Lds lds_map(LDS uint8_t* smem, CParams& p) {
     Lds m;
@@ -279,6 +282,8 @@ __device__ __forceinline__ Lds lds_map(LDS uint8_t* smem, CParams& p) {
     m.done = sync + 2 * NW + 4;
     m.ss = (LDS float*)(sync + 3 * NW + 4);
     m.side0 = (LDS float*)(smem + off + (size_t)p.nslot * p.xbuf_bytes + 512);
+    m.rope = m.side0 + (size_t)p.nslot * p.side_floats;
+    m.res = m.rope + (size_t)p.B * p.D;
     return m;
 }
 // buffer set `slot` of the staged inputs
@@ -914,12 +919,9 @@ __device__ __forceinline__ void gather_side(Ctx& cx, const Step& sp, const Inst&
     CParams& p = *cx.p;
     const int B = p.B, H = p.H, l = in.layer, nrg = (int)in.nrg, rg0 = (int)in.rg0;
     if (in.op == OP_RMS_QKV_ROPE) {
-        const int D = p.D;
-        for (int b = 0; b < B; ++b) {
-            const float* rope = p.rope + (size_t)__builtin_amdgcn_readlane(sp.pos, b) * D;
-            for (int i = cx.lane; i < D; i += 64) sd[b * D + i] = gld(rope + i);
-        }
+        return;  // the step's RoPE rows were loaded at launch
     } else if (in.op == OP_O_PROJ_RES) {
+        if (cx.resident && l > 0) return;  // the residual rows are the CU's own, kept in LDS
         for (int b = 0; b < B; ++b) {
             if (l == 0) {
                 const uint16_t* e = p.embed + (size_t)__builtin_amdgcn_readlane(sp.tok, b) * H + rg0;
@@ -928,7 +930,7 @@ __device__ __forceinline__ void gather_side(Ctx& cx, const Step& sp, const Inst&
                 gather_words(cx, p.hout + ((size_t)(l - 1) * B + b) * H + rg0, nrg, sd + b * nrg);
             }
         }
-    } else if (in.op == OP_DOWN_RES && in.a == p.n_chunk - 1) {
+    } else if (in.op == OP_DOWN_RES && in.a == p.n_chunk - 1 && !cx.resident) {
         for (int b = 0; b < B; ++b) gather_words(cx, p.hmid + ((size_t)l * B + b) * H + rg0, nrg, sd + b * nrg);
     }
 }
@@ -1040,6 +1042,16 @@ __device__ __forceinline__ void gatherer(Ctx& cx, const Lds& s, const Step& sp, 
     const uint32_t nslot = uni((uint32_t)p.nslot);
     uint32_t slot = (uint32_t)g % nslot;
     uint32_t prev_key = 0, prev_slot = 0;  // input of the instruction this wave staged last
+    {
+        // the (cos, sin) rows of the step's positions, for every QKV epilogue of the launch (read
+        // after the ready flag of a QKV instruction, which this wave publishes later)
+        const int D = p.D;
+        for (int b = 0; b < p.B; ++b) {
+            const float* rope = p.rope + (size_t)__builtin_amdgcn_readlane(sp.pos, b) * D;
+            for (int i = cx.lane; i < D; i += 64) s.rope[b * D + i] = gld(rope + i);
+        }
+        vm_drain();
+    }
     for (uint32_t pc = pc0 + g; pc < pc1; pc += NGATHER, slot = (slot + NGATHER) % nslot) {
         const uint32_t r = pc - pc0;
         const u32x4 raw = iq[pc];
@@ -1166,8 +1178,7 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
                 const int g = rg / PG, t = rg % PG;
                 if (t < (G + 1) * half) {  // q or k: rotate the pair (ii, ii + D/2)
                     const int ii = t < G * half ? t % half : t - G * half;
-                    const float2 cs = sd ? make_float2(sd[b * D + 2 * ii], sd[b * D + 2 * ii + 1])
-                                         : [&] { const float2 c = gld_f2(p.rope + ((size_t)pos * half + ii) * 2); vm_drain(); return c; }();
+                    const float2 cs = make_float2(s.rope[b * D + 2 * ii], s.rope[b * D + 2 * ii + 1]);
                     const float r1 = y1 * cs.x - y2 * cs.y, r2 = y2 * cs.x + y1 * cs.y;
                     uint64_t* blk = p.qkv + (((size_t)l * B + b) * p.Hkv + g) * (size_t)(G + 2) * D;
                     if (t < G * half) {
@@ -1199,15 +1210,20 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
         case OP_O_PROJ_RES: {
             // residual stream entering layer l (complete before this layer's QKV began)
             float hin = 0.f;
-            if (sd) {
-                if (lane_row) hin = sd[b * nrg + i];
-            } else if (lane_row) {
-                if (l == 0) hin = bf2f(gld_now(p.embed + (size_t)sp.tok * H + rg));
+            LDS float* res = s.res + (size_t)b * p.res_stride + i;  // this CU's row i (its own down-proj output)
+            if (lane_row) {
+                if (cx.resident && l > 0) hin = *res;
+                else if (sd) hin = sd[b * nrg + i];
+                else if (l == 0) hin = bf2f(gld_now(p.embed + (size_t)sp.tok * H + rg));
                 else hin = wait_word(cx, p.hout + ((size_t)(l - 1) * B + b) * H + rg);
             }
             dot1(o);
             if constexpr (FP8) fp8_scale(o, MAT_WO, MAT_WO);
-            if (lane_row) st_tag(p.hmid + ((size_t)l * B + b) * H + rg, hin + o.mine[0], cx.epoch);
+            if (lane_row) {
+                const float hm = hin + o.mine[0];
+                st_tag(p.hmid + ((size_t)l * B + b) * H + rg, hm, cx.epoch);
+                if (cx.resident) *res = hm;  // read back by the last down-proj chunk of this layer
+            }
             break;
         }
         case OP_RMS_UP_GATE: {
@@ -1223,7 +1239,9 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
         case OP_DOWN_RES: {
             const bool first = in.a == 0, last = in.a == p.n_chunk - 1;
             float hm = 0.f;
-            if (last && lane_row) hm = sd ? sd[b * nrg + i] : wait_word(cx, p.hmid + ((size_t)l * B + b) * H + rg);
+            LDS float* res = s.res + (size_t)b * p.res_stride + i;  // this CU's row i (its own O-proj output)
+            if (last && lane_row)
+                hm = cx.resident ? *res : sd ? sd[b * nrg + i] : wait_word(cx, p.hmid + ((size_t)l * B + b) * H + rg);
             float* acc = p.dacc + (size_t)b * H + rg;  // global accumulator: this wave's lane b only
             float prev = 0.f;
             if (!first) {
@@ -1236,7 +1254,10 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
             if constexpr (FP8) fp8_scale(o, MAT_DOWN, MAT_DOWN);
             const float v = o.mine[0] + prev;
             if (last) {
-                if (lane_row) st_tag(p.hout + ((size_t)l * B + b) * H + rg, hm + v, cx.epoch);
+                if (lane_row) {
+                    st_tag(p.hout + ((size_t)l * B + b) * H + rg, hm + v, cx.epoch);
+                    if (cx.resident) *res = hm + v;  // the residual entering the next layer's O-proj
+                }
             } else if (ri < DREG) {
                 if (ri == 0) da.r[0] = v;
                 else if (ri == 1) da.r[1] = v;
@@ -1492,6 +1513,7 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
     cx.lane = threadIdx.x & 63;
     const int wave = (int)uni(threadIdx.x >> 6);
     cx.aborted = false;
+    cx.resident = stage < 0 && pp->res_stride > 0;
     cx.pc = 0;
     cx.op = 0;
     cx.slot = 0;
