@@ -44,10 +44,13 @@ struct mk_handle {
     uint64_t* greedy_part = nullptr;  // [B][GREEDY_BLOCKS] per-slice (value, index) pairs
     uint32_t* greedy_cnt = nullptr;   // [B] finished slices of the current call (zero between calls)
     uint32_t* amax_bits = nullptr;    // FP8: [n_mats] largest |w| per matrix (bf16 bits), at load time
+    void* prefill_ws = nullptr;       // mk_prefill's workspace, kept between calls
+    size_t prefill_ws_bytes = 0;
 };
 
 static thread_local std::string g_create_error;
 static constexpr uint32_t DEFAULT_SPIN_LIMIT = 1u << 25;  // polls before a wait gives up (seconds)
+static constexpr size_t PREFILL_WS_MAX = (size_t)512 << 20;  // largest workspace mk_prefill keeps
 
 namespace {
 
@@ -662,8 +665,10 @@ int mk_get_trace(mk_handle* h, uint64_t* records, size_t n) {
     return MK_OK;
 }
 
-int mk_prefill(mk_handle* h, const mk_weights* w, const int32_t* tokens, int32_t n_tokens, void* kv_cache,
-               float* logits, void* stream) {
+// Shared argument checks and launch arguments of mk_prefill / mk_prefill_static; chunk and the
+// workspace pointers are filled in by the caller.
+static int prefill_args(mk_handle* h, const mk_weights* w, const int32_t* tokens, int32_t n_tokens, void* kv_cache,
+                        float* logits, PrefillArgs& a) {
     if (!h) return fail(nullptr, MK_ERR_INVALID_ARG, "handle is NULL");
     if (!w || !tokens || !kv_cache || !logits) return fail(h, MK_ERR_INVALID_ARG, "null argument");
     const Params& p = h->hp;
@@ -682,55 +687,79 @@ int mk_prefill(mk_handle* h, const mk_weights* w, const int32_t* tokens, int32_t
              aligned(w->wo[l]) && aligned(w->mlp_norm[l]) && aligned(w->w_gate[l]) && aligned(w->w_up[l]) &&
              aligned(w->w_down[l]);
     if (!ok) return fail(h, MK_ERR_INVALID_ARG, "every pointer must be non-NULL and 16-byte aligned");
-    const size_t B = p.B, P = (size_t)n_tokens, M = B * P, H = p.H, QD = (size_t)p.Hq * p.D, KD = (size_t)p.Hkv * p.D;
-    const size_t F = p.F;
-    const size_t floats = M * (2 * H + QD + 2 * KD + QD + 2 * F);
+    a = PrefillArgs{};
+    a.L = p.L; a.H = p.H; a.Hq = p.Hq; a.Hkv = p.Hkv; a.D = p.D; a.F = p.F; a.V = p.V; a.B = p.B;
+    a.P = n_tokens; a.max_seq = h->cfg.max_seq; a.eps = h->cfg.rms_eps;
+    a.tokens = tokens;
+    a.embed = (const uint16_t*)w->embed;
+    a.final_norm = (const uint16_t*)w->final_norm;
+    a.lm_head = (const uint16_t*)(tied ? w->embed : w->lm_head);
+    a.attn_norm = w->attn_norm; a.wq = w->wq; a.wk = w->wk; a.wv = w->wv; a.wo = w->wo;
+    a.mlp_norm = w->mlp_norm; a.w_gate = w->w_gate; a.w_up = w->w_up; a.w_down = w->w_down;
+    a.rope = p.rope;
+    a.kv = (uint16_t*)kv_cache;
+    a.logits = logits;
+    return MK_OK;
+}
+
+// Carves the chunk workspace (rows of prefill_row_floats) out of ws.
+static void prefill_carve(PrefillArgs& a, void* ws) {
+    const size_t M = (size_t)a.B * a.chunk, H = a.H, QD = (size_t)a.Hq * a.D, KD = (size_t)a.Hkv * a.D;
+    float* f = (float*)ws;
+    a.X = f; f += M * H;
+    a.A = f; f += M * H;
+    a.QKV = f; f += M * (QD + 2 * KD);
+    a.O = f; f += M * QD;
+    a.G = f; f += M * a.F;
+    a.U = f; f += M * a.F;
+    a.bad = (uint32_t*)f;
+}
+
+int mk_prefill(mk_handle* h, const mk_weights* w, const int32_t* tokens, int32_t n_tokens, void* kv_cache,
+               float* logits, void* stream) {
+    PrefillArgs a;
+    int rc = prefill_args(h, w, tokens, n_tokens, kv_cache, logits, a);
+    if (rc != MK_OK) return rc;
+    const Params& p = h->hp;
+    const size_t row = prefill_row_floats(p.H, p.Hq, p.Hkv, p.D, p.F) * 4;
+    // as many positions per chunk as the kept workspace allows (all of them when it fits)
+    const size_t per_pos = (size_t)p.B * row;
+    size_t chunk = std::min<size_t>((size_t)n_tokens, std::max<size_t>(1, (PREFILL_WS_MAX - 256) / per_pos));
+    const size_t need = chunk * per_pos + 256;
     hipStream_t s = (hipStream_t)stream;
-    void* ws = nullptr;
     try {
         HIPCHK(hipSetDevice(h->cfg.device));
-        if (hipMalloc(&ws, floats * 4 + 256) != hipSuccess) {
-            (void)hipGetLastError();
-            return fail(h, MK_ERR_OOM, "prefill workspace allocation failed");
+        if (h->prefill_ws_bytes < need) {  // grow the kept workspace (the only allocation)
+            if (h->prefill_ws) {
+                HIPCHK(hipStreamSynchronize(s));
+                for (auto it = h->allocs.begin(); it != h->allocs.end(); ++it)
+                    if (*it == h->prefill_ws) {
+                        h->allocs.erase(it);
+                        break;
+                    }
+                (void)hipFree(h->prefill_ws);
+                h->prefill_ws = nullptr;
+                h->prefill_ws_bytes = 0;
+            }
+            void* ws = nullptr;
+            if (hipMalloc(&ws, need) != hipSuccess) {
+                (void)hipGetLastError();
+                return fail(h, MK_ERR_OOM, "prefill workspace allocation failed");
+            }
+            h->allocs.push_back(ws);
+            h->prefill_ws = ws;
+            h->prefill_ws_bytes = need;
         }
-        std::vector<const uint16_t*> ptrs((size_t)9 * p.L);
-        const void* const* src[9] = {w->attn_norm, w->wq, w->wk, w->wv, w->wo, w->mlp_norm, w->w_gate, w->w_up, w->w_down};
-        for (int k = 0; k < 9; ++k)
-            for (int l = 0; l < p.L; ++l) ptrs[(size_t)k * p.L + l] = (const uint16_t*)src[k][l];
-        PrefillArgs a{};
-        a.L = p.L; a.H = p.H; a.Hq = p.Hq; a.Hkv = p.Hkv; a.D = p.D; a.F = p.F; a.V = p.V; a.B = p.B;
-        a.P = n_tokens; a.max_seq = h->cfg.max_seq; a.eps = h->cfg.rms_eps;
-        a.tokens = tokens;
-        a.embed = (const uint16_t*)w->embed;
-        a.final_norm = (const uint16_t*)w->final_norm;
-        a.lm_head = (const uint16_t*)(tied ? w->embed : w->lm_head);
-        a.attn_norm = &ptrs[0]; a.wq = &ptrs[(size_t)p.L]; a.wk = &ptrs[(size_t)2 * p.L]; a.wv = &ptrs[(size_t)3 * p.L];
-        a.wo = &ptrs[(size_t)4 * p.L]; a.mlp_norm = &ptrs[(size_t)5 * p.L]; a.w_gate = &ptrs[(size_t)6 * p.L];
-        a.w_up = &ptrs[(size_t)7 * p.L]; a.w_down = &ptrs[(size_t)8 * p.L];
-        a.rope = p.rope;
-        a.kv = (uint16_t*)kv_cache;
-        a.logits = logits;
-        float* f = (float*)ws;
-        a.X = f; f += M * H;
-        a.A = f; f += M * H;
-        a.QKV = f; f += M * (QD + 2 * KD);
-        a.O = f; f += M * QD;
-        a.G = f; f += M * F;
-        a.U = f; f += M * F;
-        a.bad = (uint32_t*)f;
+        a.chunk = (int)chunk;
+        prefill_carve(a, h->prefill_ws);
+        a.err = nullptr;
         HIPCHK(hipMemsetAsync(a.bad, 0, 4, s));
         HIPCHK(launch_prefill(a, s));
         uint32_t bad = 0;
         HIPCHK(hipMemcpyAsync(&bad, a.bad, 4, hipMemcpyDeviceToHost, s));
         HIPCHK(hipStreamSynchronize(s));
-        HIPCHK(hipFree(ws));
-        ws = nullptr;
         if (bad) return fail(h, MK_ERR_INVALID_ARG, "a prompt token is outside [0, vocab)");
     } catch (const HipError& e) {
-        if (ws) {
-            (void)hipStreamSynchronize(s);
-            (void)hipFree(ws);
-        }
         return hip_fail(h, e);
     }
     return MK_OK;

@@ -138,31 +138,40 @@ constexpr int TRACE_WAVE_SLOTS = 6;
 constexpr int TRACE_SLOTS = 1 + TRACE_WAVE_SLOTS * NW + 3;
 
 
-// Batched prefill (mk_prefill): shapes, the caller's bf16 weights (per-layer
-// arrays are host arrays of device pointers) and a workspace of fp32 rows
-// (M = B * P): X [M][H] residual, A [M][H] normalised input, QKV
-// [M][Hq*D + 2*Hkv*D], O [M][Hq*D], G and U [M][F]; bad: token-range flag.
+// Batched prefill (mk_prefill, mk_prefill_static): shapes, the caller's bf16
+// weights (per-layer pointers read on the host at launch) and a workspace of
+// fp32 rows for one chunk of positions (at most chunk positions of every
+// batch row, M = B * chunk rows): X [M][H] residual, A [M][H] normalised
+// input, QKV [M][Hq*D + 2*Hkv*D], O [M][Hq*D], G and U [M][F].  Prompt tokens
+// outside [0, V) set *bad (when non-null) and the device error record err
+// (when non-null; code 2, as a decode step does).
 struct PrefillArgs {
     int L, H, Hq, Hkv, D, F, V, B, P, max_seq;
+    int chunk;  // positions per pass through the layers
     float eps;
     const int32_t* tokens;  // [B][P]
     const uint16_t* embed;
     const uint16_t* final_norm;
     const uint16_t* lm_head;  // the embedding when tied
-    const uint16_t* const* attn_norm;
-    const uint16_t* const* wq;
-    const uint16_t* const* wk;
-    const uint16_t* const* wv;
-    const uint16_t* const* wo;
-    const uint16_t* const* mlp_norm;
-    const uint16_t* const* w_gate;
-    const uint16_t* const* w_up;
-    const uint16_t* const* w_down;
+    const void* const* attn_norm;  // host arrays of L device pointers (mk_weights)
+    const void* const* wq;
+    const void* const* wk;
+    const void* const* wv;
+    const void* const* wo;
+    const void* const* mlp_norm;
+    const void* const* w_gate;
+    const void* const* w_up;
+    const void* const* w_down;
     const float* rope;  // [max_seq][D/2][2]
     uint16_t* kv;
     float* logits;  // [B][V]
     float *X, *A, *QKV, *O, *G, *U;
     uint32_t* bad;
+    uint32_t* err;
 };
+// fp32 workspace floats of one prefill row (position of one batch row)
+inline size_t prefill_row_floats(int H, int Hq, int Hkv, int D, int F) {
+    return 2 * (size_t)H + 2 * (size_t)Hq * D + 2 * (size_t)Hkv * D + 2 * (size_t)F;
+}
 
 }  // namespace mk

@@ -38,17 +38,31 @@ __device__ __forceinline__ float wmax(float x) {
     return x;
 }
 
-// X[m][:] = E[tokens[m]]; an id outside [0, V) gives a zero row and sets *bad
-__global__ void __launch_bounds__(256) embed(const int32_t* tok, int H, int V, const uint16_t* E, float* X,
-                                             uint32_t* bad) {
-    const int m = blockIdx.x;
-    int t = tok[m];
-    if (t < 0 || t >= V) {
-        if (threadIdx.x == 0) atomicOr(bad, 1u);
-        t = -1;
+// X[m][:] = E[token of row m], row m = b * Pc + (t - t0) of the chunk; an id
+// outside [0, V) gives a zero row and is reported (*bad, and the device error
+// record as a decode step reports one: code 2, detail the batch row)
+__global__ void __launch_bounds__(256) embed(const int32_t* tokens, int P, int t0, int Pc, int H, int V,
+                                             const uint16_t* E, float* X, uint32_t* bad, uint32_t* err) {
+    const int m = blockIdx.x, b = m / Pc, t = t0 + m % Pc;
+    int tk = tokens[(size_t)b * P + t];
+    if (tk < 0 || tk >= V) {
+        if (threadIdx.x == 0) {
+            if (bad) atomicOr(bad, 1u);
+            if (err) {
+                if (atomicCAS(&err[0], 0u, 2u) == 0u) {
+                    err[1] = 0xffffffffu;  // no workgroup of a decode step
+                    err[2] = (uint32_t)t;
+                    err[3] = 0u;
+                    err[4] = 0u;
+                    err[5] = (uint32_t)b;
+                }
+                atomicOr(&err[7], 1u);
+            }
+        }
+        tk = -1;
     }
     for (int i = threadIdx.x; i < H; i += blockDim.x)
-        X[(size_t)m * H + i] = t < 0 ? 0.f : bf(E[(size_t)t * H + i]);
+        X[(size_t)m * H + i] = tk < 0 ? 0.f : bf(E[(size_t)tk * H + i]);
 }
 
 // A[r][:] = X[r][:] * rsqrt(mean(X[r]^2) + eps) * gain, one row per block
@@ -132,12 +146,12 @@ __global__ void __launch_bounds__(256) gemm(const float* A, int lda, const uint1
             }
 }
 
-// Row m = b * P + t of QKV ([q heads | k heads | v heads], fp32): RoPE on the
-// q and k heads at position t (rotate-half pairs, cos/sin from the handle's
+// Row m = b * Pc + (t - t0) of QKV ([q heads | k heads | v heads], fp32): RoPE
+// on the q and k heads at position t (rotate-half pairs, cos/sin from the handle's
 // table), then k and v rounded to bf16 into cache slot t of layer `layer`.
-__global__ void __launch_bounds__(256) rope_kv(float* QKV, int ld, int B, int P, int Hq, int Hkv, int D,
+__global__ void __launch_bounds__(256) rope_kv(float* QKV, int ld, int B, int t0, int Pc, int Hq, int Hkv, int D,
                                                const float* rope, uint16_t* kv, int layer, int max_seq) {
-    const int m = blockIdx.x, b = m / P, t = m % P, half = D / 2;
+    const int m = blockIdx.x, b = m / Pc, t = t0 + m % Pc, half = D / 2;
     float* row = QKV + (size_t)m * ld;
     const int QD = Hq * D, KD = Hkv * D;
     for (int e = threadIdx.x; e < (Hq + Hkv) * half; e += 256) {
@@ -158,19 +172,19 @@ __global__ void __launch_bounds__(256) rope_kv(float* QKV, int ld, int B, int P,
     }
 }
 
-// Causal attention of query (row m, head h) over cache slots 0 .. t of its KV
-// group: one wave each, keys in blocks of 64 (lane j scores key j of the
+// Causal attention of query (row m of the chunk, head h) over cache slots
+// 0 .. t of its KV group (earlier chunks' slots were written by their passes): one wave each, keys in blocks of 64 (lane j scores key j of the
 // block), online softmax across blocks, lane d accumulating output dims
 // d, d + 64.  O[m][h * D + d] = sum_j softmax(q . k_j / sqrt(D))_j v_j[d].
 template <int D>
-__global__ void __launch_bounds__(256) attention(const float* QKV, int ld, const uint16_t* kv, int B, int P, int Hq,
-                                                 int Hkv, int layer, int max_seq, float* O, int ldo) {
+__global__ void __launch_bounds__(256) attention(const float* QKV, int ld, const uint16_t* kv, int B, int t0, int Pc,
+                                                 int Hq, int Hkv, int layer, int max_seq, float* O, int ldo) {
     constexpr int NC = D / 64;
     __shared__ float qs[4][D];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wid = blockIdx.x * 4 + w;
-    if (wid >= B * P * Hq) return;  // the whole wave leaves; no block barrier follows
-    const int head = wid % Hq, m = wid / Hq, b = m / P, t = m % P, g = head / (Hq / Hkv);
+    if (wid >= B * Pc * Hq) return;  // the whole wave leaves; no block barrier follows
+    const int head = wid % Hq, m = wid / Hq, b = m / Pc, t = t0 + m % Pc, g = head / (Hq / Hkv);
     const float* q = QKV + (size_t)m * ld + (size_t)head * D;
     for (int d = lane; d < D; d += 64) qs[w][d] = q[d];
     __builtin_amdgcn_wave_barrier();
@@ -235,38 +249,46 @@ void run_gemm(const float* A, int lda, const uint16_t* W, int K, float* C, int l
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
     using namespace pf;
-    const int B = a.B, P = a.P, M = B * P, H = a.H, D = a.D, F = a.F, V = a.V;
+    const int B = a.B, P = a.P, H = a.H, D = a.D, F = a.F, V = a.V;
     const int QD = a.Hq * D, KD = a.Hkv * D, NQKV = QD + 2 * KD;
-    hipLaunchKernelGGL(embed, dim3(M), dim3(256), 0, s, a.tokens, H, V, a.embed, a.X, a.bad);
-    for (int l = 0; l < a.L; ++l) {
-        hipLaunchKernelGGL(rmsnorm, dim3(M), dim3(256), 0, s, a.X, (size_t)H, H, a.attn_norm[l], a.eps, a.A,
-                           (size_t)H);
-        run_gemm(a.A, H, a.wq[l], H, a.QKV, NQKV, M, QD, 0, s);
-        run_gemm(a.A, H, a.wk[l], H, a.QKV + QD, NQKV, M, KD, 0, s);
-        run_gemm(a.A, H, a.wv[l], H, a.QKV + QD + KD, NQKV, M, KD, 0, s);
-        hipLaunchKernelGGL(rope_kv, dim3(M), dim3(256), 0, s, a.QKV, NQKV, B, P, a.Hq, a.Hkv, D, a.rope, a.kv, l,
-                           a.max_seq);
-        const unsigned nat = (unsigned)(((size_t)M * a.Hq + 3) / 4);
-        if (D == 64)
-            hipLaunchKernelGGL(attention<64>, dim3(nat), dim3(256), 0, s, a.QKV, NQKV, a.kv, B, P, a.Hq, a.Hkv, l,
-                               a.max_seq, a.O, QD);
-        else
-            hipLaunchKernelGGL(attention<128>, dim3(nat), dim3(256), 0, s, a.QKV, NQKV, a.kv, B, P, a.Hq, a.Hkv, l,
-                               a.max_seq, a.O, QD);
-        run_gemm(a.O, QD, a.wo[l], QD, a.X, H, M, H, 1, s);  // h += W_o attn
-        hipLaunchKernelGGL(rmsnorm, dim3(M), dim3(256), 0, s, a.X, (size_t)H, H, a.mlp_norm[l], a.eps, a.A,
-                           (size_t)H);
-        run_gemm(a.A, H, a.w_gate[l], H, a.G, F, M, F, 0, s);
-        run_gemm(a.A, H, a.w_up[l], H, a.U, F, M, F, 0, s);
-        const size_t n = (size_t)M * F;
-        hipLaunchKernelGGL(swiglu, dim3((unsigned)std::min<size_t>((n + 255) / 256, 65536)), dim3(256), 0, s, a.G,
-                           a.U, n);
-        run_gemm(a.G, F, a.w_down[l], F, a.X, H, M, H, 1, s);  // h += W_down a
+    auto bf16 = [](const void* p) { return (const uint16_t*)p; };
+    // positions [t0, t0 + Pc) of every batch row go through all layers before the next chunk:
+    // attention reads the keys and values of earlier chunks from the cache
+    for (int t0 = 0; t0 < P; t0 += a.chunk) {
+        const int Pc = P - t0 < a.chunk ? P - t0 : a.chunk, M = B * Pc;
+        hipLaunchKernelGGL(embed, dim3(M), dim3(256), 0, s, a.tokens, P, t0, Pc, H, V, a.embed, a.X, a.bad, a.err);
+        for (int l = 0; l < a.L; ++l) {
+            hipLaunchKernelGGL(rmsnorm, dim3(M), dim3(256), 0, s, a.X, (size_t)H, H, bf16(a.attn_norm[l]), a.eps, a.A,
+                               (size_t)H);
+            run_gemm(a.A, H, bf16(a.wq[l]), H, a.QKV, NQKV, M, QD, 0, s);
+            run_gemm(a.A, H, bf16(a.wk[l]), H, a.QKV + QD, NQKV, M, KD, 0, s);
+            run_gemm(a.A, H, bf16(a.wv[l]), H, a.QKV + QD + KD, NQKV, M, KD, 0, s);
+            hipLaunchKernelGGL(rope_kv, dim3(M), dim3(256), 0, s, a.QKV, NQKV, B, t0, Pc, a.Hq, a.Hkv, D, a.rope, a.kv,
+                               l, a.max_seq);
+            const unsigned nat = (unsigned)(((size_t)M * a.Hq + 3) / 4);
+            if (D == 64)
+                hipLaunchKernelGGL(attention<64>, dim3(nat), dim3(256), 0, s, a.QKV, NQKV, a.kv, B, t0, Pc, a.Hq, a.Hkv,
+                                   l, a.max_seq, a.O, QD);
+            else
+                hipLaunchKernelGGL(attention<128>, dim3(nat), dim3(256), 0, s, a.QKV, NQKV, a.kv, B, t0, Pc, a.Hq,
+                                   a.Hkv, l, a.max_seq, a.O, QD);
+            run_gemm(a.O, QD, bf16(a.wo[l]), QD, a.X, H, M, H, 1, s);  // h += W_o attn
+            hipLaunchKernelGGL(rmsnorm, dim3(M), dim3(256), 0, s, a.X, (size_t)H, H, bf16(a.mlp_norm[l]), a.eps, a.A,
+                               (size_t)H);
+            run_gemm(a.A, H, bf16(a.w_gate[l]), H, a.G, F, M, F, 0, s);
+            run_gemm(a.A, H, bf16(a.w_up[l]), H, a.U, F, M, F, 0, s);
+            const size_t n = (size_t)M * F;
+            hipLaunchKernelGGL(swiglu, dim3((unsigned)std::min<size_t>((n + 255) / 256, 65536)), dim3(256), 0, s, a.G,
+                               a.U, n);
+            run_gemm(a.G, F, bf16(a.w_down[l]), F, a.X, H, M, H, 1, s);  // h += W_down a
+        }
+        if (t0 + Pc == P) {
+            // the last position of each row: final RMSNorm, then the LM head
+            hipLaunchKernelGGL(rmsnorm, dim3(B), dim3(256), 0, s, a.X + (size_t)(Pc - 1) * H, (size_t)Pc * H, H,
+                               a.final_norm, a.eps, a.A, (size_t)H);
+            run_gemm(a.A, H, a.lm_head, H, a.logits, V, B, V, 0, s);
+        }
     }
-    // last position of each row: final RMSNorm, then the LM head
-    hipLaunchKernelGGL(rmsnorm, dim3(B), dim3(256), 0, s, a.X + (size_t)(P - 1) * H, (size_t)P * H, H, a.final_norm,
-                       a.eps, a.A, (size_t)H);
-    run_gemm(a.A, H, a.lm_head, H, a.logits, V, B, V, 0, s);
     return hipGetLastError();
 }
 

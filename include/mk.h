@@ -196,7 +196,7 @@ int mk_graph_destroy(mk_graph* g);
 
 /* Batched prefill ("One Token, 2,400 Kernel Launches", opening section: the
  * prompt is one compute-bound pass, decode the token-by-token phase): runs
- * the model over positions 0 .. n_tokens-1 of every batch row at once.
+ * the model over positions 0 .. n_tokens-1 of every batch row.
  *   w:        the caller's bf16 weights, as for mk_load_weights (device
  *             pointers, 16-byte aligned); read during the call only.
  *   tokens:   device int32 [B][n_tokens], ids in [0, vocab).
@@ -205,12 +205,14 @@ int mk_graph_destroy(mk_graph* g);
  *   logits:   device fp32 [B][vocab], the last position's logits.
  * Equals mk_decode_step at positions 0 .. n_tokens-1 with the same tokens,
  * up to fp32 rounding order (the projections run on the fp32 matrix cores).
- * Synchronous: allocates an fp32 workspace of B*n_tokens*(2H + 2*Hq*D +
- * 2*Hkv*D + 2F) floats, runs on `stream`, waits for it and frees it.
- * MK_ERR_INVALID_ARG: null or unaligned pointer, n_tokens outside
- * [1, max_seq], or (after the run) a token outside [0, vocab) — its rows
- * are then computed from a zero embedding.  MK_ERR_UNSUPPORTED_SHAPE for
- * an MK_FLAG_FP8_WEIGHTS handle; MK_ERR_OOM when the workspace does not fit. */
+ * Positions go through the layers in chunks (attention reads the earlier
+ * chunks' keys and values from the cache), as many per chunk as a workspace
+ * of at most 512 MiB holds; the handle keeps that workspace between calls
+ * and allocates only when a call needs a larger one.  Synchronous: waits for
+ * `stream`.  MK_ERR_INVALID_ARG: null or unaligned pointer, n_tokens outside
+ * [1, max_seq], or (after the run) a token outside [0, vocab) — its rows are
+ * then computed from a zero embedding.  MK_ERR_UNSUPPORTED_SHAPE for an
+ * MK_FLAG_FP8_WEIGHTS handle; MK_ERR_OOM when the workspace does not fit.  */
 int mk_prefill(mk_handle* h, const mk_weights* w, const int32_t* tokens, int32_t n_tokens, void* kv_cache,
                float* logits, void* stream);
 
