@@ -24,6 +24,7 @@ hipError_t launch_amax(const uint16_t* w, size_t n, uint32_t* out, hipStream_t s
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int ncu, hipStream_t stream);
 hipError_t launch_empty(int n_blocks, int n_threads, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+hipError_t prefill_scratch_address(int device, void** out);
 hipError_t launch_greedy(const float* logits, int B, int V, int32_t* tokens, int32_t* positions, uint64_t* part,
                          uint32_t* cnt, hipStream_t stream);
 hipError_t launch_litmus(uint64_t* buf, int npairs, int rounds, int words, uint32_t spin_limit, uint32_t* result,
@@ -46,6 +47,7 @@ struct mk_handle {
     uint32_t* amax_bits = nullptr;    // FP8: [n_mats] largest |w| per matrix (bf16 bits), at load time
     void* prefill_ws = nullptr;       // mk_prefill's workspace, kept between calls
     size_t prefill_ws_bytes = 0;
+    void* prefill_scratch = nullptr;  // device address of this device's static prefill scratch
 };
 
 static thread_local std::string g_create_error;
@@ -192,6 +194,8 @@ int mk_create(const mk_config* cfg, mk_handle** out) {
             return fail(nullptr, MK_ERR_INVALID_ARG, "device ordinal out of range");
         }
         HIPCHK(hipSetDevice(cfg->device));
+        // this device's static prefill scratch (mk_prefill_static), looked up with the device current
+        HIPCHK(prefill_scratch_address(cfg->device, &h->prefill_scratch));
         int ncu_dev = 0;
         HIPCHK(hipDeviceGetAttribute(&ncu_dev, hipDeviceAttributeMultiprocessorCount, cfg->device));
         int ncu = cfg->n_cus ? cfg->n_cus : ncu_dev;
@@ -762,6 +766,27 @@ int mk_prefill(mk_handle* h, const mk_weights* w, const int32_t* tokens, int32_t
     } catch (const HipError& e) {
         return hip_fail(h, e);
     }
+    return MK_OK;
+}
+
+int mk_prefill_static(mk_handle* h, const mk_weights* w, const int32_t* tokens, int32_t n_tokens, void* kv_cache,
+                      float* logits, void* stream) {
+    PrefillArgs a;
+    int rc = prefill_args(h, w, tokens, n_tokens, kv_cache, logits, a);
+    if (rc != MK_OK) return rc;
+    const Params& p = h->hp;
+    const size_t per_pos = (size_t)p.B * prefill_row_floats(p.H, p.Hq, p.Hkv, p.D, p.F) * 4;
+    const size_t fit = PREFILL_SCRATCH_BYTES / per_pos;
+    if (fit == 0)
+        return fail(h, MK_ERR_UNSUPPORTED_SHAPE,
+                    "one prompt position of every batch row needs more than the 64 MiB static prefill scratch");
+    a.chunk = (int)std::min<size_t>((size_t)n_tokens, fit);
+    prefill_carve(a, h->prefill_scratch);
+    a.bad = nullptr;                     // no host readback: tokens out of range go to the error record
+    a.err = (uint32_t*)h->hp.error;
+    hipError_t e = hipSetDevice(h->cfg.device);
+    if (e == hipSuccess) e = launch_prefill(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(h, HipError{e, "prefill launch"});
     return MK_OK;
 }
 

@@ -173,5 +173,7 @@ struct PrefillArgs {
 inline size_t prefill_row_floats(int H, int Hq, int Hkv, int D, int F) {
     return 2 * (size_t)H + 2 * (size_t)Hq * D + 2 * (size_t)Hkv * D + 2 * (size_t)F;
 }
+// Static prefill scratch of every device the library runs on (mk_prefill_static).
+constexpr size_t PREFILL_SCRATCH_BYTES = (size_t)64 << 20;
 
 }  // namespace mk

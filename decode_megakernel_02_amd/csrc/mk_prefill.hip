@@ -14,6 +14,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <algorithm>
+#include <mutex>
 #include "mk_internal.h"
 
 namespace mk {
@@ -290,6 +291,28 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
         }
     }
     return hipGetLastError();
+}
+
+// The static scratch of mk_prefill_static: one array per device, for the life
+// of the process.  Its device address comes from the runtime (the array's name
+// is only a host-side stand-in), looked up once per device with that device
+// current.
+static __device__ __align__(256) uint8_t scratch[PREFILL_SCRATCH_BYTES];
+
+hipError_t prefill_scratch_address(int device, void** out) {
+    constexpr int MAX_DEVICES = 64;
+    static std::mutex mu;
+    static void* addr[MAX_DEVICES] = {};
+    if (device < 0 || device >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[device]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[device] = p;
+    }
+    *out = addr[device];
+    return hipSuccess;
 }
 
 }  // namespace mk

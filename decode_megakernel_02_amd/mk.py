@@ -56,7 +56,7 @@ EXPORTS = ["mk_create", "mk_load_weights", "mk_kv_cache_bytes", "mk_decode_step"
            "mk_destroy", "mk_status_string", "mk_last_error", "mk_get_device_error", "mk_get_profile",
            "mk_schedule_inspect", "mk_get_trace", "mk_greedy_advance", "mk_read_probe", "mk_empty_launches",
            "mk_graph_create", "mk_graph_launch", "mk_graph_destroy", "mk_prefill", "mk_schedule_selftest", "mk_litmus", "mk_set_spin_limit",
-           "mk_debug_stage"]
+           "mk_debug_stage", "mk_prefill_static"]
 MK_FLAG_PROFILE = 1
 MK_FLAG_TRACE = 2
 MK_FLAG_FP8_WEIGHTS = 4
@@ -103,10 +103,11 @@ def lib():
         L.mk_graph_launch.argtypes = [ctypes.c_void_p, _P]
         L.mk_graph_destroy.argtypes = [ctypes.c_void_p]
         L.mk_prefill.argtypes = [H, ctypes.POINTER(MkWeights), _P, ctypes.c_int32, _P, _P, _P]
+        L.mk_prefill_static.argtypes = [H, ctypes.POINTER(MkWeights), _P, ctypes.c_int32, _P, _P, _P]
         for name in ["mk_create", "mk_load_weights", "mk_decode_step", "mk_decode_step_multikernel", "mk_destroy",
                      "mk_get_device_error", "mk_schedule_inspect", "mk_get_profile", "mk_get_trace",
                      "mk_greedy_advance", "mk_read_probe", "mk_empty_launches", "mk_graph_create",
-                     "mk_graph_launch", "mk_graph_destroy", "mk_prefill", "mk_schedule_selftest", "mk_litmus", "mk_set_spin_limit", "mk_debug_stage"]:
+                     "mk_graph_launch", "mk_graph_destroy", "mk_prefill", "mk_schedule_selftest", "mk_litmus", "mk_set_spin_limit", "mk_debug_stage", "mk_prefill_static"]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -212,6 +213,15 @@ def mk_prefill(handle, weights: Dict[str, object], tokens, n_tokens: int, kv_cac
     w, keep = _weights_struct(weights)
     _check(lib().mk_prefill(handle, ctypes.byref(w), _ptr(tokens), int(n_tokens), _ptr(kv_cache), _ptr(logits),
                             stream), handle)
+    del keep
+
+
+def mk_prefill_static(handle, weights: Dict[str, object], tokens, n_tokens: int, kv_cache, logits,
+                      stream: Optional[int] = None):
+    """mk_prefill in the static scratch: no allocation, asynchronous (see include/mk.h)."""
+    w, keep = _weights_struct(weights)
+    _check(lib().mk_prefill_static(handle, ctypes.byref(w), _ptr(tokens), int(n_tokens), _ptr(kv_cache),
+                                   _ptr(logits), stream), handle)
     del keep
 
 

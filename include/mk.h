@@ -216,6 +216,21 @@ int mk_graph_destroy(mk_graph* g);
 int mk_prefill(mk_handle* h, const mk_weights* w, const int32_t* tokens, int32_t n_tokens, void* kv_cache,
                float* logits, void* stream);
 
+/* mk_prefill for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops): same arguments and results, but it
+ * allocates nothing, does not synchronise, and runs in a static 64 MiB
+ * scratch array that each device the library runs on holds until the process
+ * ends (prompts longer than fit in one pass go through in chunks).  Every
+ * call on one device shares that array: calls that overlap on one device
+ * (other streams, other handles) race.  A token outside [0, vocab) is not
+ * returned as a status: it is recorded in the handle's device error record
+ * (code 2, read with mk_get_device_error) and its rows use a zero embedding.
+ * MK_ERR_UNSUPPORTED_SHAPE when one position of every batch row needs more
+ * than 64 MiB of fp32 rows (B * (2H + 2*Hq*D + 2*Hkv*D + 2F) * 4 bytes), and
+ * for FP8 handles; MK_ERR_INVALID_ARG as mk_prefill.                       */
+int mk_prefill_static(mk_handle* h, const mk_weights* w, const int32_t* tokens, int32_t n_tokens, void* kv_cache,
+                      float* logits, void* stream);
+
 /* Frees everything the handle owns.  NULL is accepted. */
 int mk_destroy(mk_handle* h);
 
