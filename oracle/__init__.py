@@ -58,6 +58,7 @@ def lib():
         L.orc_fp8_scale.argtypes = [_P, ctypes.c_size_t]
         L.orc_fp8_scale.restype = ctypes.c_float
         L.orc_gemv_fp8.argtypes = [_P, ctypes.c_int, ctypes.c_int, _P, _P, ctypes.c_int]
+        L.orc_gemv_fp8_rows.argtypes = [_P, ctypes.c_int, ctypes.c_int, _P, _P, ctypes.c_int]
         L.orc_argmax.argtypes = [_P, ctypes.c_int]
         L.orc_argmax.restype = ctypes.c_int
         _lib = L
@@ -118,6 +119,15 @@ def gemv_fp8(W_bits, x, nthreads: int = 1) -> np.ndarray:
     return y
 
 
+def gemv_fp8_rows(W_bits, x, nthreads: int = 1) -> np.ndarray:
+    """FP8 (E4M3) GEMV with one scale per row (the row's largest magnitude / 448)."""
+    W, x = _u16(W_bits), _f64(x)
+    rows, cols = W.shape
+    y = np.empty(rows, dtype=np.float64)
+    lib().orc_gemv_fp8_rows(W.ctypes.data, rows, cols, x.ctypes.data, y.ctypes.data, nthreads)
+    return y
+
+
 def rope(v, pos: int, theta: float) -> np.ndarray:
     v = _f64(v).copy()
     lib().orc_rope(v.ctypes.data, v.size, pos, theta)
@@ -139,11 +149,14 @@ def silu(z: float) -> float:
 class Oracle:
     """Holds weight pointers (the numpy arrays stay referenced) for repeated steps."""
 
-    def __init__(self, shape, weights: Dict[str, object], batch: int, max_seq: int, fp8: bool = False):
+    def __init__(self, shape, weights: Dict[str, object], batch: int, max_seq: int, fp8=False):
+        """fp8: False (bf16 weights), True or "matrix" (FP8, one scale per matrix), "row" (FP8, one
+        scale per output row)."""
         self.shape = shape
+        mode = 0 if not fp8 else 2 if fp8 == "row" else 1
         self.cfg = OrcConfig(shape.n_layers, shape.hidden, shape.n_q_heads, shape.n_kv_heads,
                              shape.head_dim, shape.ffn, shape.vocab, batch, max_seq,
-                             1 if shape.tied else 0, shape.rms_eps, shape.rope_theta, 1 if fp8 else 0)
+                             1 if shape.tied else 0, shape.rms_eps, shape.rope_theta, mode)
         self._keep = weights
         L = shape.n_layers
         w = OrcWeights()

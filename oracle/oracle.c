@@ -120,9 +120,11 @@ static void *gemv_rows(void *p) {
         const uint16_t *row = j->W + (size_t)r * j->cols;
         double acc = 0.0;
         if (j->fp8) {
+            /* fp8 == 2: every row has its own scale, from its own largest magnitude */
+            const float scale = j->fp8 == 2 ? orc_fp8_scale(row, (size_t)j->cols) : j->scale;
             for (int c = 0; c < j->cols; ++c) {
-                const float q = (float)orc_bf16_to_double(row[c]) / j->scale;
-                acc += (double)j->scale * orc_e4m3_to_double(orc_e4m3_round(q)) * j->x[c];
+                const float q = (float)orc_bf16_to_double(row[c]) / scale;
+                acc += (double)scale * orc_e4m3_to_double(orc_e4m3_round(q)) * j->x[c];
             }
         } else {
             for (int c = 0; c < j->cols; ++c) acc += orc_bf16_to_double(row[c]) * j->x[c];
@@ -143,8 +145,12 @@ void orc_gemv_fp8(const uint16_t *W, int rows, int cols, const double *x, double
     gemv_any(W, rows, cols, x, y, nthreads, 1);
 }
 
+void orc_gemv_fp8_rows(const uint16_t *W, int rows, int cols, const double *x, double *y, int nthreads) {
+    gemv_any(W, rows, cols, x, y, nthreads, 2);
+}
+
 static void gemv_any(const uint16_t *W, int rows, int cols, const double *x, double *y, int nthreads, int fp8) {
-    const float scale = fp8 ? orc_fp8_scale(W, (size_t)rows * cols) : 1.0f;
+    const float scale = fp8 == 1 ? orc_fp8_scale(W, (size_t)rows * cols) : 1.0f;
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;
     if (nthreads > rows / 64 + 1) nthreads = rows / 64 + 1;

@@ -35,7 +35,8 @@ typedef struct {
     int tied;      /* 1: LM head weight is the embedding matrix */
     double rms_eps, rope_theta;
     int fp8;       /* 1: every projection matrix and the LM head are used as their FP8
-                      quantisation (orc_gemv_fp8); the embedding lookup stays bf16 */
+                      quantisation with one scale per matrix (orc_gemv_fp8); 2: with one
+                      scale per output row (orc_gemv_fp8_rows); the embedding lookup stays bf16 */
 } orc_config;
 
 /* Host pointers, bf16 bit patterns, row-major nn.Linear layout [out][in]. */
@@ -78,6 +79,8 @@ float orc_fp8_scale(const uint16_t *W, size_t n);
  * the product with the matrix's FP8 quantisation (fp32 division, as the
  * quantiser computes it).  Same threading and summation order as orc_gemv. */
 void orc_gemv_fp8(const uint16_t *W, int rows, int cols, const double *x, double *y, int nthreads);
+/* The same with one scale per row: s_r = orc_fp8_scale(W[r], cols). */
+void orc_gemv_fp8_rows(const uint16_t *W, int rows, int cols, const double *x, double *y, int nthreads);
 /* Rotate-half RoPE of one head vector at position `pos`. */
 void orc_rope(double *v, int head_dim, int pos, double theta);
 /* Softmax attention of one query over n_keys bf16 K/V rows (row stride head_dim). */

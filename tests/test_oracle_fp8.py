@@ -156,3 +156,61 @@ def test_each_matrix_goes_through_the_quantiser(lossy):
         orc.decode_step(kv, [7], [0])
         lg.append(orc.decode_step(kv, [11], [1]))
     assert np.abs(lg[0] - lg[1]).max() > 1e-7
+
+
+def test_per_row_scale_is_lossless_on_scaled_e4m3_rows():
+    """Rows a_r * e_k with e_k E4M3 values (largest 448) and a_r powers of two from 1 to 2^-12: with
+    its own scale s_r = a_r every row quantises exactly, so the per-row GEMV equals the bf16 GEMV;
+    one scale for the whole matrix pushes the small rows into subnormals and loses them."""
+    codes, values = finite_table()
+    rng = np.random.default_rng(11)
+    fin = values[np.isfinite(values) & (np.abs(values) >= 2.0 ** -6)]  # normal E4M3 values
+    rows, cols = 13, 96
+    e = rng.choice(fin, size=(rows, cols))
+    e[:, 0] = 448.0  # every row's largest magnitude is 448
+    a = 2.0 ** -np.arange(rows)
+    Wf = (a[:, None] * e).astype(np.float32)
+    W = (Wf.view(np.uint32) >> 16).astype(np.uint16)  # exact in bf16: E4M3 values have 4 significant bits
+    assert np.array_equal((W.astype(np.uint32) << 16).view(np.float32), Wf)
+    x = rng.standard_normal(cols)
+    exact = oracle.gemv(W, x)
+    per_row = oracle.gemv_fp8_rows(W, x)
+    assert np.allclose(per_row, exact, rtol=0, atol=1e-12 * np.max(np.abs(exact)))
+    per_mat = oracle.gemv_fp8(W, x)
+    assert np.max(np.abs(per_mat[-3:] - exact[-3:])) > 1e-3 * np.max(np.abs(exact[-3:]))
+
+
+def test_per_row_scale_error_bound():
+    """|y_r - exact_r| <= s_r * sum_k |x_k| * (half the E4M3 spacing at |w_rk| / s_r)."""
+    w = synth.make_weights(synth.TINY)["layers"][0]["w_gate"][:40]
+    x = np.random.default_rng(3).standard_normal(w.shape[1])
+    exact = oracle.gemv(w, x)
+    got = oracle.gemv_fp8_rows(w, x)
+    wf = (w.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for r in range(w.shape[0]):
+        s = oracle.fp8_scale(w[r:r + 1])
+        q = np.abs(np.float32(wf[r]) / np.float32(s)).astype(np.float64)
+        e = np.where(q >= 2.0 ** -6, np.floor(np.log2(np.maximum(q, 2.0 ** -6))), -6)
+        half = np.ldexp(1.0, (e - 3).astype(int)) / 2
+        bound = s * np.sum(np.abs(x) * half) * (1 + 1e-6) + 1e-12
+        assert abs(got[r] - exact[r]) <= bound, (r, got[r] - exact[r], bound)
+
+
+@pytest.mark.parametrize("mb,wb", [(0x3D98, 0x3BE4), (0x3E5C, 0x365C), (0x3EA2, 0x38F3)])
+def test_quotient_is_taken_in_fp32(mb, wb):
+    """The quantiser divides in fp32 (w / s with s an fp32 value).  These bf16 pairs (found by a
+    search over random pairs) are ones where the fp32 quotient lands on a rounding midpoint
+    that the exact quotient misses, so the two give neighbouring E4M3 codes: a quantiser that
+    divided in double would fail here."""
+    codes, values = finite_table()
+    W = np.array([[mb, wb]], dtype=np.uint16)
+    m, w = (W.astype(np.uint32) << 16).view(np.float32)[0]
+    s = np.float32(m) / np.float32(448.0)
+    assert oracle.fp8_scale(W) == s
+    q32 = float(np.float32(w) / s)
+    q64 = float(w) / float(s)
+    c32, c64 = brute_round(q32, codes, values), brute_round(q64, codes, values)
+    assert c32 != c64
+    x = np.array([0.0, 1.0])
+    for y in (oracle.gemv_fp8(W, x), oracle.gemv_fp8_rows(W, x)):
+        assert y[0] == float(s) * oracle.e4m3_to_double(int(c32))
