@@ -20,7 +20,7 @@ hipError_t launch_step(const Params* dev_params, int head_dim, int ncu, size_t l
 hipError_t set_step_kernel_lds(size_t lds_bytes);
 hipError_t launch_pack(const void* rows, uint32_t n, const uint16_t* const* mats, uint8_t* dst, int fp8,
                        const float* scales, hipStream_t stream);
-hipError_t launch_amax(const uint16_t* w, size_t n, uint32_t* out, hipStream_t stream);
+hipError_t launch_row_amax(const uint16_t* w, uint32_t rows, uint32_t cols, uint16_t* out, hipStream_t stream);
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int ncu, hipStream_t stream);
 hipError_t launch_empty(int n_blocks, int n_threads, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
@@ -44,7 +44,8 @@ struct mk_handle {
     std::string last_error;
     uint64_t* greedy_part = nullptr;  // [B][GREEDY_BLOCKS] per-slice (value, index) pairs
     uint32_t* greedy_cnt = nullptr;   // [B] finished slices of the current call (zero between calls)
-    uint32_t* amax_bits = nullptr;    // FP8: [n_mats] largest |w| per matrix (bf16 bits), at load time
+    uint16_t* row_amax = nullptr;     // FP8: [rows of all matrices] largest |w| per row (bf16 bits)
+    float* row_scale = nullptr;       // FP8: [rows of all matrices] scale of each row (pack input)
     void* prefill_ws = nullptr;       // mk_prefill's workspace, kept between calls
     size_t prefill_ws_bytes = 0;
     void* prefill_scratch = nullptr;  // device address of this device's static prefill scratch
@@ -259,8 +260,12 @@ int mk_create(const mk_config* cfg, mk_handle** out) {
         hp.n_stages = p.n_stages;
         hp.fp8 = p.fp8 ? 1 : 0;
         if (p.fp8) {
-            hp.wscale = dalloc<float>(h, (size_t)p.n_mats());
-            h->amax_bits = dalloc<uint32_t>(h, (size_t)p.n_mats());
+            const size_t nrows = p.mat_row_off[(size_t)p.n_mats()];
+            hp.rgscale = dalloc<float>(h, ((size_t)p.rgs_stride * p.L + p.V) * 2);
+            for (int i = 0; i < 4; ++i) hp.rgs_off[i] = p.rgs_off[i];
+            hp.rgs_stride = p.rgs_stride;
+            h->row_amax = dalloc<uint16_t>(h, nrows);
+            h->row_scale = dalloc<float>(h, nrows);
         }
 
         hp.wstream = dalloc<uint8_t>(h, (size_t)p.total_units * UNIT_BYTES);
@@ -373,30 +378,32 @@ int mk_load_weights(mk_handle* h, const mk_weights* w, void* stream) {
         HIPCHK(hipMemcpyAsync(d_rows, p.pack.data(), p.pack.size() * sizeof(PackRow), hipMemcpyHostToDevice, s));
         HIPCHK(hipMemcpyAsync(d_mats, mats.data(), mats.size() * sizeof(void*), hipMemcpyHostToDevice, s));
         if (p.fp8) {
-            // per-matrix scale fp32(max|w| / 448): the largest magnitude as bf16 bits (magnitudes of
-            // finite bf16 values order like their bits with the sign cleared), then on the host
-            const int nm = p.n_mats();
-            HIPCHK(hipMemsetAsync(h->amax_bits, 0, (size_t)nm * 4, s));
-            for (int m = 0; m < nm; ++m) {
+            // one scale per row, fp32(max|w_row| / 448) (1 for a zero row): the largest magnitude of
+            // every row as bf16 bits on the device, the quotient on the host
+            const size_t nrows = p.mat_row_off[(size_t)p.n_mats()];
+            for (int m = 0; m < p.n_mats(); ++m) {
                 uint32_t rows = 0, cols = 0;
                 p.mat_shape((uint32_t)m, rows, cols);
-                HIPCHK(launch_amax(mats[(size_t)m], (size_t)rows * cols, h->amax_bits + m, s));
+                HIPCHK(launch_row_amax(mats[(size_t)m], rows, cols, h->row_amax + p.mat_row_off[(size_t)m], s));
             }
-            std::vector<uint32_t> bits((size_t)nm);
-            HIPCHK(hipMemcpyAsync(bits.data(), h->amax_bits, (size_t)nm * 4, hipMemcpyDeviceToHost, s));
+            std::vector<uint16_t> bits(nrows);
+            HIPCHK(hipMemcpyAsync(bits.data(), h->row_amax, nrows * 2, hipMemcpyDeviceToHost, s));
             HIPCHK(hipStreamSynchronize(s));
-            std::vector<float> scale((size_t)nm);
-            for (int m = 0; m < nm; ++m) {
-                uint32_t f = bits[(size_t)m] << 16;
+            std::vector<float> scale(nrows);
+            for (size_t r = 0; r < nrows; ++r) {
+                const uint32_t f = (uint32_t)bits[r] << 16;
                 float amax;
                 std::memcpy(&amax, &f, 4);
-                scale[(size_t)m] = amax == 0.0f ? 1.0f : amax / 448.0f;
+                scale[r] = amax == 0.0f ? 1.0f : amax / 448.0f;
             }
-            HIPCHK(hipMemcpyAsync((void*)h->hp.wscale, scale.data(), (size_t)nm * 4, hipMemcpyHostToDevice, s));
-            HIPCHK(hipStreamSynchronize(s));  // the host vector goes out of scope
+            std::vector<float> rgs;
+            build_rg_scales(p, scale, rgs);
+            HIPCHK(hipMemcpyAsync(h->row_scale, scale.data(), nrows * 4, hipMemcpyHostToDevice, s));
+            HIPCHK(hipMemcpyAsync((void*)h->hp.rgscale, rgs.data(), rgs.size() * 4, hipMemcpyHostToDevice, s));
+            HIPCHK(hipStreamSynchronize(s));  // the host vectors go out of scope
         }
         HIPCHK(launch_pack(d_rows, (uint32_t)p.pack.size(), (const uint16_t* const*)d_mats, (uint8_t*)h->hp.wstream,
-                           p.fp8 ? 1 : 0, h->hp.wscale, s));
+                           p.fp8 ? 1 : 0, h->row_scale, s));
         const size_t HB = (size_t)p.H * 2;
         HIPCHK(hipMemcpyAsync((void*)h->hp.embed, w->embed, (size_t)p.V * HB, hipMemcpyDeviceToDevice, s));
         for (int l = 0; l < p.L; ++l) {

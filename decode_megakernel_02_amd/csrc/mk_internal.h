@@ -120,7 +120,13 @@ struct Params {
     uint32_t* epoch;  // [ncu] per-workgroup step counter
     uint32_t* error;  // [8] device error record (code, wg, pc, op, wave, detail), abort flag at [7]
 
-    const float* wscale;  // FP8 weights: [L * MATS_PER_LAYER + 1] per-matrix scales (LM head last)
+    // FP8 weights: the scales of the two rows of every row-group, {row 0, row 1} pairs (1 for a
+    // row-group of one row), in row-group order: layer l's QKV pairs at l * rgs_stride +
+    // rgs_off[0], its O rows at + rgs_off[1], gate/up rows at + rgs_off[2], down rows at +
+    // rgs_off[3]; the LM head's rows at L * rgs_stride
+    const float* rgscale;
+    uint32_t rgs_off[4];
+    uint32_t rgs_stride;
     int32_t fp8;          // weights packed as FP8 codes (units of 1024 elements)
 };
 

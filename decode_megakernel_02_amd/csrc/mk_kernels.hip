@@ -1132,6 +1132,22 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
     const int B = p.B, H = p.H, l = in.layer;
     const int ku = in.op == OP_O_PROJ_RES ? p.ku_q : in.op == OP_DOWN_RES ? p.ku_f : p.ku_h;
     const uint32_t row_end = st.unit + in.b;  // the instruction's unit-rows end here in every ring
+    // FP8 weights: each row sum times its row's scale; lane j holds the pair of row-group
+    // cx.wave + (j0 + j) * NW, loaded once per 64 row-groups of the wave before the inputs are
+    // awaited, and row-group ri's pair is read out with readlane
+    float2 rsc = make_float2(1.f, 1.f);
+    const float* rgs = nullptr;
+    auto load_rsc = [&](uint32_t j0) {
+        const uint32_t i = cx.wave + (j0 + cx.lane) * NW;
+        rsc = i < in.nrg ? *(const float2*)(rgs + 2 * (size_t)i) : make_float2(1.f, 1.f);
+    };
+    if constexpr (FP8) {
+        const int k = in.op == OP_RMS_QKV_ROPE ? 0 : in.op == OP_O_PROJ_RES ? 1 : in.op == OP_RMS_UP_GATE ? 2 : 3;
+        const size_t base = in.op == OP_RMS_LM_HEAD ? (size_t)p.L * p.rgs_stride
+                                                    : (size_t)l * p.rgs_stride + p.rgs_off[k];
+        rgs = p.rgscale + 2 * (base + in.rg0);
+        load_rsc(0);
+    }
     // x = raw input * gain, staged by the gather wave; lane b: RMSNorm scale of batch row b
     wait_inputs(cx, s, r);
     if (cx.aborted) return;
@@ -1150,11 +1166,10 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
         if constexpr (KU > 0) rowgroup_dot_b1<KU, 2, FP8>(cx, s, st, xs, ru, o);
         else rowgroup_dot_batch<2, FP8>(cx, s, st, xb, ku, o);
     };
-    // FP8 weights: each row sum times the scale of the row's matrix
-    auto fp8_scale = [&](RowOut& o, uint32_t kind0, uint32_t kind1) {
-        const float* wsc = p.wscale + (size_t)l * MATS_PER_LAYER;
-        o.mine[0] *= wsc[kind0];
-        o.mine[1] *= wsc[kind1];
+    float2 sc = make_float2(1.f, 1.f);
+    auto fp8_scale = [&](RowOut& o) {
+        o.mine[0] *= sc.x;
+        o.mine[1] *= sc.y;
     };
 
     // ---- this wave's row-groups; lane b < B finishes batch row b
@@ -1167,15 +1182,16 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
         const uint32_t i = cx.wave + ri * NW;
         if (i >= in.nrg) break;
         const uint32_t rg = in.rg0 + i;
+        if constexpr (FP8) {
+            if (ri > 0 && (ri & 63) == 0) load_rsc(ri);
+            sc.x = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rsc.x), (int)(ri & 63)));
+            sc.y = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rsc.y), (int)(ri & 63)));
+        }
         RowOut o;
         switch (in.op) {
         case OP_RMS_QKV_ROPE: {
             dot2(o);
-            if constexpr (FP8) {  // the pair's matrix: q, k or v rows of its KV group
-                const int PGf = (p.G + 2) * half, tf = rg % PGf;
-                const uint32_t kind = tf < p.G * half ? MAT_WQ : tf < (p.G + 1) * half ? MAT_WK : MAT_WV;
-                fp8_scale(o, kind, kind);
-            }
+            if constexpr (FP8) fp8_scale(o);
             if (lane_row) {
                 const int pos = sp.pos;
                 const float y1 = o.mine[0] * scale, y2 = o.mine[1] * scale;
@@ -1223,7 +1239,7 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
                 else hin = wait_word(cx, p.hout + ((size_t)(l - 1) * B + b) * H + rg);
             }
             dot1(o);
-            if constexpr (FP8) fp8_scale(o, MAT_WO, MAT_WO);
+            if constexpr (FP8) fp8_scale(o);
             if (lane_row) {
                 const float hm = hin + o.mine[0];
                 st_tag(p.hmid + ((size_t)l * B + b) * H + rg, hm, cx.epoch);
@@ -1233,7 +1249,7 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
         }
         case OP_RMS_UP_GATE: {
             dot2(o);
-            if constexpr (FP8) fp8_scale(o, MAT_GATE, MAT_UP);
+            if constexpr (FP8) fp8_scale(o);
             if (lane_row) {
                 const float gt = o.mine[0] * scale, up = o.mine[1] * scale;
                 const float a = gt / (1.0f + __expf(-gt)) * up;  // silu(gate) * up
@@ -1256,7 +1272,7 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
                     prev = gld_now(acc);
             }
             dot1(o);
-            if constexpr (FP8) fp8_scale(o, MAT_DOWN, MAT_DOWN);
+            if constexpr (FP8) fp8_scale(o);
             const float v = o.mine[0] + prev;
             if (last) {
                 if (lane_row) {
@@ -1273,9 +1289,9 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
             }
             break;
         }
-        default: {  // OP_RMS_LM_HEAD (its scale follows the last layer's matrices)
+        default: {  // OP_RMS_LM_HEAD
             dot1(o);
-            if constexpr (FP8) fp8_scale(o, (uint32_t)(p.L - l) * MATS_PER_LAYER, 0u);
+            if constexpr (FP8) fp8_scale(o);
             if (lane_row) gst(sp.logits + (size_t)b * p.V + rg, o.mine[0] * scale);
             break;
         }
@@ -1671,7 +1687,7 @@ mk_stage_kernel(const Params* __restrict__ pp, const int32_t* tokens, const int3
 // ------------------------------------------------------------ pack kernel --
 
 struct PackRowDev {
-    uint32_t mat, row, k0, klen, src_cols, kunits, ustride, reserved;
+    uint32_t mat, row, k0, klen, src_cols, kunits, ustride, grow;
     uint64_t dst_unit;
 };
 
@@ -1697,30 +1713,35 @@ __device__ __forceinline__ uint32_t e4m3_code(float x) {
     return sign | ((uint32_t)(e + 7) << 3) | q;
 }
 
-// Largest |w| of n bf16 weights as bf16 bits (sign cleared: finite bf16
-// magnitudes order like their bits), folded into *out with an atomic max.
-__global__ void __launch_bounds__(256) mk_amax_kernel(const uint16_t* w, size_t n, uint32_t* out) {
-    uint32_t m = 0;
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
-        const uint32_t v = w[i] & 0x7fffu;
-        m = v > m ? v : m;
+// Largest |w| of each row of a [rows][cols] bf16 matrix, as bf16 bits (sign
+// cleared: finite bf16 magnitudes order like their bits): one wave per row.
+__global__ void __launch_bounds__(256) mk_row_amax_kernel(const uint16_t* w, uint32_t rows, uint32_t cols,
+                                                          uint16_t* out) {
+    const uint32_t lane = threadIdx.x & 63, nw = gridDim.x * (blockDim.x >> 6);
+    for (uint32_t r = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); r < rows; r += nw) {
+        const uint16_t* row = w + (size_t)r * cols;
+        uint32_t m = 0;
+        for (uint32_t c = lane; c < cols; c += 64) {
+            const uint32_t v = row[c] & 0x7fffu;
+            m = v > m ? v : m;
+        }
+        for (int d = 32; d >= 1; d >>= 1) {
+            const uint32_t o = (uint32_t)__shfl_xor((int)m, d);
+            m = o > m ? o : m;
+        }
+        if (lane == 0) out[r] = (uint16_t)m;
     }
-    for (int d = 32; d >= 1; d >>= 1) {
-        const uint32_t o = (uint32_t)__shfl_xor((int)m, d);
-        m = o > m ? o : m;
-    }
-    if ((threadIdx.x & 63) == 0) atomicMax(out, m);
 }
 
 // One workgroup per stream row: dst[unit .. unit + kunits) = src row slice, zero padded;
-// with fp8, the codes of fp32(w / scale[mat]) (1024 per unit) instead of the bf16 values.
+// with fp8, the codes of fp32(w / scale[row]) (1024 per unit) instead of the bf16 values.
 __global__ void __launch_bounds__(256) mk_pack_kernel(const PackRowDev* rows, uint32_t n, const uint16_t* const* mats,
                                                       uint8_t* dst, int fp8, const float* scales) {
     for (uint32_t r = blockIdx.x; r < n; r += gridDim.x) {
         const PackRowDev pr = rows[r];
         if (fp8) {
             const uint16_t* src = mats[pr.mat] + (size_t)pr.row * pr.src_cols + pr.k0;
-            const float sc = scales[pr.mat];
+            const float sc = scales[pr.grow];
             const uint32_t n_el = pr.kunits * FP8_UNIT_ELEMS;
             for (uint32_t e = threadIdx.x; e < n_el; e += blockDim.x) {
                 uint8_t* out = dst + (pr.dst_unit + (uint64_t)(e / FP8_UNIT_ELEMS) * NW * pr.ustride) * UNIT_BYTES;
@@ -2003,10 +2024,11 @@ hipError_t launch_pack(const void* rows, uint32_t n, const uint16_t* const* mats
     return hipGetLastError();
 }
 
-hipError_t launch_amax(const uint16_t* w, size_t n, uint32_t* out, hipStream_t stream) {
-    if (n == 0) return hipSuccess;
-    const size_t blocks = (n + 255) / 256;
-    hipLaunchKernelGGL(mk_amax_kernel, dim3(blocks < 4096 ? (uint32_t)blocks : 4096u), dim3(256), 0, stream, w, n, out);
+hipError_t launch_row_amax(const uint16_t* w, uint32_t rows, uint32_t cols, uint16_t* out, hipStream_t stream) {
+    if (rows == 0) return hipSuccess;
+    const uint32_t blocks = (rows + 3) / 4;
+    hipLaunchKernelGGL(mk_row_amax_kernel, dim3(blocks < 8192 ? blocks : 8192u), dim3(256), 0, stream, w, rows, cols,
+                       out);
     return hipGetLastError();
 }
 

@@ -167,6 +167,32 @@ int build_plan(const mk_config& c, int ncu, Plan& p, std::string& err) {
     }
     p.ku_f = ceil_div(maxc, p.epu);
     p.n_stages = p.L * STAGES_PER_LAYER + 1;
+    // global row indices (per-row FP8 scales) and the row-group scale table layout
+    {
+        uint64_t acc = 0;
+        p.mat_row_off.assign((size_t)p.n_mats() + 1, 0);
+        for (int m = 0; m < p.n_mats(); ++m) {
+            uint32_t rows = 0, cols = 0;
+            p.mat_shape((uint32_t)m, rows, cols);
+            p.mat_row_off[(size_t)m] = (uint32_t)acc;
+            acc += rows;
+            if (acc > 0xffffffffull) {
+                err = "more than 2^32 weight rows";
+                return MK_ERR_UNSUPPORTED_SHAPE;
+            }
+        }
+        p.mat_row_off[(size_t)p.n_mats()] = (uint32_t)acc;
+        const uint64_t n_pairs = (uint64_t)(p.Hq + 2 * p.Hkv) * p.D / 2;
+        p.rgs_off[0] = 0;
+        p.rgs_off[1] = (uint32_t)n_pairs;
+        p.rgs_off[2] = (uint32_t)(n_pairs + p.H);
+        p.rgs_off[3] = (uint32_t)(n_pairs + p.H + p.F);
+        p.rgs_stride = (uint32_t)(n_pairs + 2 * (uint64_t)p.H + p.F);
+        if ((uint64_t)p.rgs_stride * p.L + p.V > 0x7fffffffull) {
+            err = "the row-group scale table exceeds 2^31 entries";
+            return MK_ERR_UNSUPPORTED_SHAPE;
+        }
+    }
 
     Builder b(p);
     std::vector<std::vector<uint32_t>> stage_pc(ncu, std::vector<uint32_t>(p.n_stages + 1, 0));
@@ -307,7 +333,7 @@ int build_plan(const mk_config& c, int ncu, Plan& p, std::string& err) {
                 for (int k = 0; k < nrows; ++k) {
                     const uint64_t first = inter ? cur + k : cur;
                     p.pack.push_back(PackRow{rr[k].mat, rr[k].row, rr[k].k0, rr[k].klen, rr[k].cols, ku,
-                                             inter ? 2u : 1u, 0u,
+                                             inter ? 2u : 1u, p.mat_row_off[rr[k].mat] + rr[k].row,
                                              p.stream_base[(size_t)cu * NW + i % NW] + first * NW});
                     if (!inter) cur += ku;
                 }
@@ -316,6 +342,25 @@ int build_plan(const mk_config& c, int ncu, Plan& p, std::string& err) {
         }
     }
     return MK_OK;
+}
+
+void build_rg_scales(const Plan& p, const std::vector<float>& row_scale, std::vector<float>& out) {
+    Builder b(const_cast<Plan&>(p));  // rows_of only reads the plan
+    out.assign(((size_t)p.rgs_stride * p.L + p.V) * 2, 1.0f);
+    const uint16_t ops[4] = {OP_RMS_QKV_ROPE, OP_O_PROJ_RES, OP_RMS_UP_GATE, OP_DOWN_RES};
+    const uint32_t counts[4] = {p.rgs_off[1], (uint32_t)p.H, (uint32_t)p.F, (uint32_t)p.H};
+    auto fill = [&](const Inst& in, size_t base, uint32_t n) {
+        RowRef rr[2];
+        for (uint32_t rg = 0; rg < n; ++rg) {
+            const int nr = b.rows_of(in, rg, rr);
+            for (int k = 0; k < nr; ++k)
+                out[(base + rg) * 2 + k] = row_scale[(size_t)p.mat_row_off[rr[k].mat] + rr[k].row];
+        }
+    };
+    for (int l = 0; l < p.L; ++l)
+        for (int o = 0; o < 4; ++o)
+            fill(Inst{ops[o], (uint16_t)l, 0, 0, 0, 0}, (size_t)l * p.rgs_stride + p.rgs_off[o], counts[o]);
+    fill(Inst{OP_RMS_LM_HEAD, 0, 0, 0, 0, 0}, (size_t)p.L * p.rgs_stride, (uint32_t)p.V);
 }
 
 // ---------------------------------------------------------------- checking --

@@ -23,7 +23,7 @@ struct PackRow {
     uint32_t kunits;
     uint32_t ustride;    // stream units from one of the row's units to the next (2: interleaved with
                          // the other row of its row-group)
-    uint32_t reserved;
+    uint32_t grow;       // global row index: mat_row_off[mat] + row (FP8: the row's scale)
     uint64_t dst_unit;   // absolute unit index in the packed buffer (first unit; later units every
                          // ustride * NW)
 };
@@ -50,6 +50,9 @@ struct Plan {
     std::vector<uint64_t> stream_len;    // [ncu * NW]
     uint64_t total_units = 0;
     std::vector<PackRow> pack;
+    std::vector<uint32_t> mat_row_off;   // [n_mats + 1] global index of each matrix's row 0
+    uint32_t rgs_off[4] = {0, 0, 0, 0};  // row-group scale table layout (Params::rgscale)
+    uint32_t rgs_stride = 0;
 
     int lm_mat() const { return L * MATS_PER_LAYER; }
     // rows and columns of source matrix `mat`; false for an index past the LM head
@@ -72,6 +75,9 @@ struct Plan {
     }
     int n_mats() const { return L * MATS_PER_LAYER + 1; }
 };
+
+// FP8 row-group scale table (Params::rgscale) from per-row scales indexed by global row.
+void build_rg_scales(const Plan& p, const std::vector<float>& row_scale, std::vector<float>& out);
 
 // Checks the config against the kernels' limits; fills `err` on failure.
 int validate_config(const mk_config& cfg, std::string& err);

@@ -70,9 +70,10 @@ typedef struct {
 #define MK_FLAG_PROFILE 1u  /* per-wave cycle counters, read with mk_get_profile */
 #define MK_FLAG_TRACE 2u    /* per-instruction timeline, read with mk_get_trace */
 #define MK_FLAG_FP8_WEIGHTS 4u /* every projection matrix and the LM head are packed as OCP FP8
-                                  E4M3 codes with one fp32 scale per matrix (fp32(max|w| / 448);
-                                  code = E4M3 value nearest to fp32(w / scale), ties to even), half
-                                  the bytes of bf16; the embedding lookup stays bf16.  Not
+                                  E4M3 codes with one fp32 scale per output row (fp32(max|w_row| /
+                                  448), 1 for a zero row; code = E4M3 value nearest to
+                                  fp32(w / scale), ties to even), half the bytes of bf16 plus 4
+                                  bytes per row; the embedding lookup stays bf16.  Not
                                   combinable with MK_FLAG_PROFILE / MK_FLAG_TRACE. */
 
 /* Per-layer weight pointers: arrays of n_layers DEVICE pointers held in HOST

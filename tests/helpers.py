@@ -107,8 +107,8 @@ class GpuDecoder:
 
 
 def oracle_replay(shape, weights, batch, max_seq, run: Run, kv_init: Optional[np.ndarray] = None,
-                  nthreads: int = 8, fp8: bool = False) -> List[np.ndarray]:
-    """Teacher-forced oracle logits for the exact inputs the GPU saw."""
+                  nthreads: int = 8, fp8=False) -> List[np.ndarray]:
+    """Teacher-forced oracle logits for the exact inputs the GPU saw (fp8: as oracle.Oracle)."""
     import oracle
     orc = oracle.Oracle(shape, weights, batch, max_seq, fp8=fp8)
     cache = (np.zeros(synth.kv_cache_shape(shape, batch, max_seq), dtype=np.uint16) if kv_init is None

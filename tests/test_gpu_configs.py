@@ -21,19 +21,28 @@ pytestmark = pytest.mark.gpu
 THREADS = min(32, os.cpu_count() or 1)
 
 
-def run_and_compare(shape, weights, batch, prompt_lens, steps, label, multikernel=False, n_chunks=0):
+FP8 = 4  # MK_FLAG_FP8_WEIGHTS
+
+
+def run_and_compare(shape, weights, batch, prompt_lens, steps, label, multikernel=False, n_chunks=0, flags=0,
+                    to_the_end=False):
+    """to_the_end: the cache holds exactly max(prompt) + steps positions, so the last step of the
+    longest row writes and attends to position max_seq - 1."""
     P = np.asarray(prompt_lens, dtype=np.int32)
-    max_seq = int(P.max()) + steps + 1
+    max_seq = int(P.max()) + steps + (0 if to_the_end else 1)
     kv = synth.make_kv_cache(shape, batch, max_seq, int(P.max()))
     # rows with shorter prompts: slots [P_b, max) stay unused (the step writes slot P_b and
     # attends to 0..P_b), so the extra filled slots of those rows are never read
     first = synth.make_first_tokens(shape.vocab, batch)
-    dec = H.GpuDecoder(shape, weights, batch, max_seq, n_chunks=n_chunks, kv_init=kv)
+    dec = H.GpuDecoder(shape, weights, batch, max_seq, n_chunks=n_chunks, kv_init=kv, flags=flags)
     try:
         run = dec.greedy(first, P, steps, multikernel)
     finally:
         dec.close()
-    ref = H.oracle_replay(shape, weights, batch, max_seq, run, kv_init=kv, nthreads=THREADS)
+    if to_the_end:
+        assert int(run.positions[-1].max()) == max_seq - 1
+    ref = H.oracle_replay(shape, weights, batch, max_seq, run, kv_init=kv, nthreads=THREADS,
+                          fp8="row" if flags & FP8 else False)
     stats = H.compare(run, ref, label)
     print(label, stats, flush=True)
     return stats
@@ -45,9 +54,37 @@ def test_llama1b_batch_shared_position(llama1b, batch):
     run_and_compare(shape, weights, batch, [1024] * batch, 2, f"llama1b b{batch}")
 
 
-def test_llama1b_batch8_staggered_positions_multikernel(llama1b):
+@pytest.mark.parametrize("multikernel", [False, True], ids=["single-launch", "per-op"])
+def test_llama1b_batch8_staggered_positions(llama1b, multikernel):
     shape, weights = llama1b
-    run_and_compare(shape, weights, 8, [1024 - 37 * b for b in range(8)], 2, "llama1b b8 staggered", True)
+    run_and_compare(shape, weights, 8, [1024 - 37 * b for b in range(8)], 2, "llama1b b8 staggered", multikernel)
+
+
+@pytest.mark.parametrize("batch", [1, 4])
+def test_llama1b_step_at_last_cache_position(llama1b, batch):
+    """The last step writes the cache's final slot (position max_seq - 1) and attends to every
+    slot; rows of a batch stop one or more positions short of it."""
+    shape, weights = llama1b
+    run_and_compare(shape, weights, batch, [1022 - 3 * b for b in range(batch)], 2,
+                    f"llama1b b{batch} to max_seq - 1", to_the_end=True)
+
+
+@pytest.mark.parametrize("batch,multikernel", [(1, False), (4, False), (1, True)])
+def test_llama1b_fp8_full_shape(llama1b, batch, multikernel):
+    """FP8 weights (one scale per output row) at the full 1B shape: 16 layers, the 128256-row
+    tied LM head, 1024 tokens in the cache; the oracle quantises the same way."""
+    shape, weights = llama1b
+    stats = run_and_compare(shape, weights, batch, [1024 - 5 * b for b in range(batch)], 2,
+                            f"llama1b fp8 b{batch}" + (" per-op" if multikernel else ""), multikernel, flags=FP8)
+    assert stats["max_abs"] < 2e-3
+
+
+@pytest.mark.timeout(900)
+def test_llama8b_fp8():
+    shape = synth.LLAMA_8B
+    weights = synth.make_weights(shape)
+    stats = run_and_compare(shape, weights, 1, [1024], 2, "llama8b fp8", flags=FP8)
+    assert stats["max_abs"] < 2e-3
 
 
 @pytest.mark.parametrize("prompt", [8192, 32768])

@@ -64,6 +64,17 @@ def test_graph_replays_match_eager_steps(multikernel, steps_per_graph):
         if g is not None:
             mk.mk_graph_destroy(g)
         dec.close()
+    if steps_per_graph == 1:
+        # teacher-forced against the oracle: replay r saw the tokens replay r - 1 wrote
+        run = H.Run([], [], [])
+        toks, pos = np.asarray(first, dtype=np.int32), np.full(B, P, dtype=np.int32)
+        for lg, tok, npos in ref:
+            run.tokens.append(toks)
+            run.positions.append(pos)
+            run.logits.append(lg)
+            toks, pos = tok, npos
+        stats = H.compare(run, H.oracle_replay(shape, synth.make_weights(shape), B, P + n_total + 2, run), "graph")
+        print("graph replays vs oracle", stats)
 
 
 def test_empty_launch_graph_and_eager_empty_launches_touch_nothing():
