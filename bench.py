@@ -3,10 +3,11 @@
 
 Workload (default): Llama-3.2-1B-shaped decoder with random bf16 weights
 N(0, 0.02), batch 1, a 1024-token context pre-filled in the KV cache with
-seeded N(0,1) bf16 rows, greedy decode.  One timed step = one mk_decode_step
-launch (the whole forward pass) + one mk_greedy_advance launch (argmax into
-the next step's tokens, positions + 1), all on one stream with no host
-synchronisation inside the timed region.
+seeded N(0,1) bf16 rows, greedy decode.  One timed step = one
+mk_decode_step_greedy launch: the whole forward pass and the argmax into the
+next step's tokens (positions + 1) in a single kernel, on one stream with no
+host synchronisation inside the timed region.  The two-launch form (the step,
+then mk_greedy_advance) is timed beside it.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -194,7 +195,7 @@ def main():
                          "--kernel-trace run and exit")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: every core, at most 64)")
     ap.add_argument("--fp8", action="store_true",
-                    help="FP8 (E4M3, per-matrix scale) weights instead of bf16 (a variant, not the headline)")
+                    help="FP8 (E4M3, one scale per output row) weights instead of bf16 (a variant, not the headline)")
     ap.add_argument("--cpu-only", action="store_true",
                     help="time only the CPU oracle on the workload and print it as one JSON line")
     ap.add_argument("--prefill", action="store_true",
@@ -306,22 +307,26 @@ def main():
             fn(h, tokens, positions, kv, logits, stream)
             mk.mk_greedy_advance(h, logits, tokens, positions, stream)  # argmax -> tokens, positions += 1
 
+    def fused(n):  # one launch per step: the step advances tokens and positions itself
+        for _ in range(n):
+            mk.mk_decode_step_greedy(h, tokens, positions, kv, logits, stream)
+
     def check_device():
         err = mk.mk_get_device_error(h)
         if err is not None:
             raise RuntimeError(f"device error record: code {err.code} wg {err.workgroup} pc {err.pc} "
                                f"op {err.opcode} detail {err.detail:#x}")
 
-    # ---- megakernel: warm-up, then K timed greedy steps
-    greedy(W, mk.mk_decode_step)
+    # ---- megakernel with greedy selection fused in: warm-up, then K timed steps
+    fused(W)
     torch.cuda.synchronize()
     check_device()
     t0 = time.perf_counter()
-    greedy(K, mk.mk_decode_step)
+    fused(K)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     check_device()
-    log(f"megakernel: {K} steps in {wall * 1e3:.1f} ms")
+    log(f"megakernel (fused greedy): {K} steps in {wall * 1e3:.1f} ms")
 
     # ---- per-launch kernel time (events on the launch stream), same positions
     positions.fill_(P + W)
@@ -329,13 +334,23 @@ def main():
     cur = torch.cuda.current_stream()  # the stream mk_decode_step launches on
     for i in range(K):
         ev[i][0].record(cur)
-        mk.mk_decode_step(h, tokens, positions, kv, logits, stream)
+        mk.mk_decode_step_greedy(h, tokens, positions, kv, logits, stream)
         ev[i][1].record(cur)
-        mk.mk_greedy_advance(h, logits, tokens, positions, stream)
     torch.cuda.synchronize()
     check_device()
     kern_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
     kern_mean = statistics.mean(kern_us)
+
+    # ---- the two-launch form: the step, then the argmax kernel
+    positions.fill_(P)
+    greedy(3, mk.mk_decode_step)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    greedy(K, mk.mk_decode_step)
+    torch.cuda.synchronize()
+    wall_two = time.perf_counter() - t0
+    check_device()
+    log(f"megakernel + argmax launch: {K} steps in {wall_two * 1e3:.1f} ms")
 
     # ---- per-op launches (same op bodies, 6L+1 launches per step)
     KM = args.mk_steps
@@ -383,7 +398,7 @@ def main():
     graph_mk = graph_us(mk.MK_GRAPH_MULTIKERNEL, KM)
     check_device()
     try:
-        graph_mega = graph_us(0, KM)
+        graph_mega = graph_us(mk.MK_GRAPH_FUSED_GREEDY, KM)
         check_device()
     except mk.MkError as e:  # the runtime may refuse to capture a cooperative launch
         graph_mega = None
@@ -440,7 +455,7 @@ def main():
         "config": {"workload": f"{shape.name}, batch {B}, {P}-token synthetic KV prefill, greedy decode",
                    "batch": B, "prompt_tokens": P, "decode_steps": K, "kv_prefill": "seeded N(0,1) bf16 rows",
                    "weights": "seeded N(0,0.02) bf16, norm gains 1.0" + (
-                       ", projections and LM head quantised to FP8 E4M3 with one scale per matrix" if args.fp8 else ""),
+                       ", projections and LM head quantised to FP8 E4M3 with one scale per output row" if args.fp8 else ""),
                    "accumulate": "fp32",
                    "kernel_launches_per_step": 1},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": peak, "unit": "GB/s", "frac": achieved / peak,
@@ -448,6 +463,7 @@ def main():
         "hbm_read_probe_GBps": probe_gbps,
         "achieved_frac_of_read_probe": achieved / probe_gbps,
         "kernel_us_per_step": kern_mean,
+        "two_launch_ms_per_step": wall_two / K * 1e3,
         "kernel_us_median": statistics.median(kern_us),
         "bytes_per_step": bytes_step,
         "floor_us_per_step": R.floor_us(bytes_step),
@@ -456,7 +472,8 @@ def main():
                         "megakernel_speedup": kern_mk / kern_mean,
                         "graph_us_per_step": graph_mk, "megakernel_speedup_vs_graph": graph_mk / (wall / K * 1e6)},
         "graph": {"megakernel_us_per_step": graph_mega, "per_op_us_per_step": graph_mk,
-                  "note": "one replay = one decode step + the argmax launch, captured once, replayed back to back"},
+                  "note": "one replay = one step: the per-op launches + the argmax launch, or the single fused "
+                          "launch; captured once, replayed back to back"},
         "launch_overhead": {"launches": n_launch, "blocks": ncu, "threads": 768, "eager_empty_us": eager_empty,
                             "graph_empty_us": graph_empty},
         "kernel_source_hash": kernel_source_hash(),
@@ -464,7 +481,13 @@ def main():
     if args.cpu_steps > 0:
         log("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(shape, weights, kv_host, first, P, args.cpu_steps, args.cpu_threads)
+    # release everything device-side before returning (graphs were destroyed above), so that
+    # nothing of the library or torch's caching allocator is left for exit-time teardown
+    torch.cuda.synchronize()
     mk.mk_destroy(h)
+    del kv, tokens, positions, logits
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
 
 

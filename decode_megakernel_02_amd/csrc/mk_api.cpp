@@ -324,6 +324,11 @@ int mk_create(const mk_config* cfg, mk_handle** out) {
         HIPCHK(hipMemset(hp.epoch, 0, (size_t)ncu * 4));
         hp.error = dalloc<uint32_t>(h, 8);
         HIPCHK(hipMemset(hp.error, 0, 32));
+        // fused greedy decoding: the CUs' arrival counter and their (max, index) pairs
+        hp.greedy_cnt = dalloc<uint32_t>(h, 1);
+        HIPCHK(hipMemset(hp.greedy_cnt, 0, 4));
+        hp.greedy_pair = dalloc<uint64_t>(h, (size_t)ncu * MAX_BATCH * 2);
+        HIPCHK(hipMemset(hp.greedy_pair, 0, (size_t)ncu * MAX_BATCH * 2 * 8));
         h->greedy_part = dalloc<uint64_t>(h, (size_t)B * GREEDY_BLOCKS);
         h->greedy_cnt = dalloc<uint32_t>(h, (size_t)B);
         HIPCHK(hipMemset(h->greedy_cnt, 0, (size_t)B * 4));
@@ -449,6 +454,18 @@ int mk_decode_step(mk_handle* h, const int32_t* tokens, const int32_t* positions
     return MK_OK;
 }
 
+int mk_decode_step_greedy(mk_handle* h, int32_t* tokens, int32_t* positions, void* kv_cache, float* logits,
+                          void* stream) {
+    int rc = step_args_ok(h, tokens, positions, kv_cache, logits);
+    if (rc != MK_OK) return rc;
+    if (instr_flag(h) & KF_INSTRUMENTED)
+        return fail(h, MK_ERR_STATE, "the fused greedy step has no profiling or tracing build");
+    hipError_t e = launch_step(h->dparams, h->hp.D, h->hp.ncu, h->lds_bytes, tokens, positions, kv_cache, logits, -1,
+                               KF_BUMP_EPOCH | KF_GREEDY | instr_flag(h), (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(h, HipError{e, "mk_step_kernel launch (fused greedy)"});
+    return MK_OK;
+}
+
 int mk_decode_step_multikernel(mk_handle* h, const int32_t* tokens, const int32_t* positions, void* kv_cache,
                                float* logits, void* stream) {
     int rc = step_args_ok(h, tokens, positions, kv_cache, logits);
@@ -564,7 +581,11 @@ int mk_graph_create(mk_handle* h, int32_t* tokens, int32_t* positions, void* kv_
     int rc = step_args_ok(h, tokens, positions, kv_cache, logits);
     if (rc != MK_OK) return rc;
     if (n_steps < 1 || n_steps > 4096) return fail(h, MK_ERR_INVALID_ARG, "n_steps outside 1..4096");
-    if (flags & ~(MK_GRAPH_MULTIKERNEL | MK_GRAPH_EMPTY)) return fail(h, MK_ERR_INVALID_ARG, "unknown graph flag");
+    if (flags & ~(MK_GRAPH_MULTIKERNEL | MK_GRAPH_EMPTY | MK_GRAPH_FUSED_GREEDY))
+        return fail(h, MK_ERR_INVALID_ARG, "unknown graph flag");
+    if ((flags & MK_GRAPH_FUSED_GREEDY) && ((flags & (MK_GRAPH_MULTIKERNEL | MK_GRAPH_EMPTY)) ||
+                                            (instr_flag(h) & KF_INSTRUMENTED)))
+        return fail(h, MK_ERR_INVALID_ARG, "MK_GRAPH_FUSED_GREEDY takes the plain single-launch step only");
     mk_graph* g = new (std::nothrow) mk_graph;
     if (!g) return fail(h, MK_ERR_OOM, "host allocation failed");
     hipStream_t cs = nullptr;
@@ -586,6 +607,11 @@ int mk_graph_create(mk_handle* h, int32_t* tokens, int32_t* positions, void* kv_
                                                  kv_cache, logits, st,
                                                  (st == ns - 1 ? KF_BUMP_EPOCH : 0u) | instr_flag(h), cs),
                                      "mk_step_kernel stage launch"};
+            } else if (flags & MK_GRAPH_FUSED_GREEDY) {
+                first = HipError{launch_step(h->dparams, h->hp.D, h->hp.ncu, h->lds_bytes, tokens, positions, kv_cache,
+                                             logits, -1, KF_BUMP_EPOCH | KF_GREEDY | instr_flag(h), cs),
+                                 "mk_step_kernel launch (fused greedy)"};
+                continue;  // the step itself advanced the tokens and positions
             } else {
                 first = HipError{launch_step(h->dparams, h->hp.D, h->hp.ncu, h->lds_bytes, tokens, positions, kv_cache,
                                              logits, -1, KF_BUMP_EPOCH | instr_flag(h), cs),
@@ -633,7 +659,11 @@ int mk_get_device_error(mk_handle* h, mk_device_error* out) {
         HIPCHK(hipSetDevice(h->cfg.device));
         HIPCHK(hipDeviceSynchronize());
         HIPCHK(hipMemcpy(rec, h->hp.error, sizeof rec, hipMemcpyDeviceToHost));
-        if (rec[0] || rec[7]) HIPCHK(hipMemset(h->hp.error, 0, sizeof rec));
+        if (rec[0] || rec[7]) {
+            HIPCHK(hipMemset(h->hp.error, 0, sizeof rec));
+            // an aborted fused-greedy step may have left CUs counted in: start the count afresh
+            HIPCHK(hipMemset(h->hp.greedy_cnt, 0, 4));
+        }
     } catch (const HipError& e) {
         return hip_fail(h, e);
     }

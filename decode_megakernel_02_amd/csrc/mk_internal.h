@@ -128,12 +128,18 @@ struct Params {
     uint32_t rgs_off[4];
     uint32_t rgs_stride;
     int32_t fp8;          // weights packed as FP8 codes (units of 1024 elements)
+
+    // fused greedy decoding (mk_decode_step_greedy): arrival counter of the CUs (0 between
+    // steps) and each CU's (max logit, lowest index) per batch row as two tagged words
+    uint32_t* greedy_cnt;      // [1]
+    uint64_t* greedy_pair;     // [ncu][MAX_BATCH][2]
 };
 
 // Kernel launch flags.
 constexpr uint32_t KF_BUMP_EPOCH = 1u;  // last launch of a step: advance the per-workgroup epoch
 constexpr uint32_t KF_INSTRUMENTED = 2u;  // run the kernel build that records profile counters / timelines
 constexpr uint32_t KF_FP8 = 4u;           // run the kernel build for FP8 weights
+constexpr uint32_t KF_GREEDY = 8u;        // single launch only: the build that also takes the argmax
 constexpr int PROF_SLOTS = 8;          // counters per wave
 // Timeline record per instruction (100 MHz real-time clock): [0] op | layer << 8 |
 // a << 16 | b << 32 | cu << 48, then per compute wave w at [1 + 6w]: start,

@@ -170,6 +170,17 @@ __device__ __forceinline__ void asm_lds_st(uint32_t a, uint32_t v) {
     asm volatile("ds_write_b32 %0, %1" ::"v"(a), "v"(v) : "memory");
 }
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Smallest of the 8 words at a (16-byte aligned): two 16-byte reads and one wait, inside the
+// block (the outputs are early-clobber: the second read still needs the address register)
+__device__ __forceinline__ uint32_t asm_lds_min8(uint32_t a) {
+    u32x4 v0, v1;
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(v0), "=&v"(v1)
+                 : "v"(a)
+                 : "memory");
+    const uint32_t m0 = min(min(v0.x, v0.y), min(v0.z, v0.w)), m1 = min(min(v1.x, v1.y), min(v1.z, v1.w));
+    return min(m0, m1);
+}
 
 // ------------------------------------------------------------ wave context --
 
@@ -189,7 +200,10 @@ struct Ctx {
     uint64_t t_mid;    // real time at which the main loop ended
     uint64_t t_ring;   // real-time ticks spent waiting for weight units in the current instruction
     uint64_t cnt[8];   // see mk_get_profile
+    float gv;          // fused greedy: largest logit of this wave's LM-head rows for batch row `lane`
+    uint32_t gi;       // and its lowest index (GREEDY_NONE: no row, or only NaN)
 };
+constexpr uint32_t GREEDY_NONE = 0xffffffffu;
 
 __device__ __forceinline__ uint64_t cycles() { return __builtin_readcyclecounter(); }
 // constant-rate (100 MHz) clock shared by all CUs
@@ -360,7 +374,11 @@ constexpr int CPOL_NT = 2;
 constexpr int vmcnt_imm(int n) { return ((n >> 4) << 14) | 0xF00 | 0x70 | (n & 15); }
 static_assert(vmcnt_imm(0) == 0x0F70, "matches the encoding of vm_drain");
 
-__device__ __forceinline__ void loader(Ctx& cx, const Lds& s, const uint32_t* uoff, uint32_t pc0, uint32_t pc1) {
+// uoff: the instruction boundaries' unit offsets, read through the constant address space: as
+// scalar loads they are waited for with the LDS/scalar counter, where a vector load would wait
+// for every DMA in flight (the vector-memory counter covers them all).
+__device__ __forceinline__ void loader(Ctx& cx, const Lds& s, const CONST_AS uint32_t* uoff, uint32_t pc0,
+                                       uint32_t pc1) {
     __builtin_amdgcn_s_setprio(MK_LOADER_PRIO);
     CParams& p = *cx.p;
     const uint32_t ru = uni((uint32_t)p.ring_units);
@@ -395,13 +413,8 @@ __device__ __forceinline__ void loader(Ctx& cx, const Lds& s, const uint32_t* uo
         }
         for (uint32_t j = 0; j < rows;) {
             if (u >= room) {
-                uint32_t m = 0xffffffffu;
-#pragma unroll
-                for (int w = 0; w < NW; ++w) {
-                    const uint32_t c = uni(asm_lds_ld(lds_addr(&s.consumed[w])));
-                    m = c < m ? c : m;
-                }
-                room = m + ru;
+                static_assert(NW == 8, "eight consumed counters, read as two 16-byte words");
+                room = uni(asm_lds_min8(lds_addr(&s.consumed[0]))) + ru;
                 if (u >= room) {
                     const uint64_t t0 = cx.prof ? cycles() : 0;
                     if (published < u) {  // hand over what is in flight before waiting on the consumers
@@ -507,7 +520,7 @@ __device__ __forceinline__ float dot8(const uint4 w, const float4 a, const float
 // One unit of FP8 codes: lane c holds the 16 codes of elements 16c .. 16c+15 of
 // the unit, i.e. x chunks 2c (a0: elements 0-3, b0: 4-7) and 2c+1 (a1, b1).
 // The conversion instruction decodes OCP E4M3 (checked against the format
-// table on this device); the per-matrix scale is applied to the row sum.
+// table on this device); the row scale is applied to the row sum.
 __device__ __forceinline__ float dot16_fp8(const uint4 w, const float4 a0, const float4 b0, const float4 a1,
                                            const float4 b1) {
     const auto c0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false), c1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
@@ -1123,9 +1136,19 @@ struct DownAcc {
     float r[DREG];
 };
 
+// Up/gate instructions: one per CU and layer, its share of every down-projection chunk, chunk
+// after chunk.  CU slot t's share of chunk c is rows [r0, r0 + n) (the schedule builder splits
+// the same way); values below 2^24, so the products stay in 32 bits.
+__device__ __forceinline__ uint32_t ug_share(CParams& p, uint32_t t, int c, uint32_t& r0) {
+    const uint32_t c0 = (uint32_t)p.chunk_begin[c], len = (uint32_t)p.chunk_begin[c + 1] - c0;
+    const uint32_t ncu = (uint32_t)p.ncu;
+    r0 = c0 + len * t / ncu;
+    return c0 + len * (t + 1) / ncu - r0;
+}
+
 // KU > 0: batch-1 path with KU units per row (x slice in registers);
 // KU == 0: general path.
-template <int KU, bool FP8>
+template <int KU, bool FP8, bool GREEDY>
 __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint32_t r, uint32_t slot, const Inst& in,
                                         LDS float* xb, const Step& sp, DownAcc& da) {
     CParams& p = *cx.p;
@@ -1139,13 +1162,23 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
     const float* rgs = nullptr;
     auto load_rsc = [&](uint32_t j0) {
         const uint32_t i = cx.wave + (j0 + cx.lane) * NW;
-        rsc = i < in.nrg ? *(const float2*)(rgs + 2 * (size_t)i) : make_float2(1.f, 1.f);
+        uint32_t row = i;
+        if (in.op == OP_RMS_UP_GATE) {  // the table is indexed by row: find row-group i's
+            uint32_t base = 0;
+            for (int c = 0; c < p.n_chunk; ++c) {
+                uint32_t r0;
+                const uint32_t n = ug_share(p, in.rg0, c, r0);
+                if (i >= base && i < base + n) row = r0 + (i - base);
+                base += n;
+            }
+        }
+        rsc = i < in.nrg ? *(const float2*)(rgs + 2 * (size_t)row) : make_float2(1.f, 1.f);
     };
     if constexpr (FP8) {
         const int k = in.op == OP_RMS_QKV_ROPE ? 0 : in.op == OP_O_PROJ_RES ? 1 : in.op == OP_RMS_UP_GATE ? 2 : 3;
         const size_t base = in.op == OP_RMS_LM_HEAD ? (size_t)p.L * p.rgs_stride
                                                     : (size_t)l * p.rgs_stride + p.rgs_off[k];
-        rgs = p.rgscale + 2 * (base + in.rg0);
+        rgs = p.rgscale + 2 * (base + (in.op == OP_RMS_UP_GATE ? 0u : in.rg0));
         load_rsc(0);
     }
     // x = raw input * gain, staged by the gather wave; lane b: RMSNorm scale of batch row b
@@ -1178,10 +1211,21 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
     const int b = lane_row ? cx.lane : 0;
     const int nrg = (int)in.nrg;
     const LDS float* sd = p.side_floats ? sslot(s, p, slot) : nullptr;  // staged epilogue inputs
+    // up/gate: chunk ug_c of the current row-group, whose rows [ug_r0, ug_r0 + ug_n) are the
+    // instruction's row-groups [ug_base, ug_base + ug_n)
+    uint32_t ug_c = 0, ug_base = 0, ug_r0 = 0, ug_n = 0;
+    if (in.op == OP_RMS_UP_GATE) ug_n = ug_share(p, in.rg0, 0, ug_r0);
     for (uint32_t ri = 0;; ++ri) {
         const uint32_t i = cx.wave + ri * NW;
         if (i >= in.nrg) break;
-        const uint32_t rg = in.rg0 + i;
+        uint32_t rg = in.rg0 + i;
+        if (in.op == OP_RMS_UP_GATE) {
+            while (i >= ug_base + ug_n) {  // i < nrg: a later chunk holds it
+                ug_base += ug_n;
+                ug_n = ug_share(p, in.rg0, ++ug_c, ug_r0);
+            }
+            rg = ug_r0 + (i - ug_base);
+        }
         if constexpr (FP8) {
             if (ri > 0 && (ri & 63) == 0) load_rsc(ri);
             sc.x = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rsc.x), (int)(ri & 63)));
@@ -1292,7 +1336,16 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
         default: {  // OP_RMS_LM_HEAD
             dot1(o);
             if constexpr (FP8) fp8_scale(o);
-            if (lane_row) gst(sp.logits + (size_t)b * p.V + rg, o.mine[0] * scale);
+            if (lane_row) {
+                const float v = o.mine[0] * scale;
+                gst(sp.logits + (size_t)b * p.V + rg, v);
+                // running (max, lowest index) of the rows: NaN never compares greater or equal
+                if constexpr (GREEDY)
+                    if (v > cx.gv || (v == cx.gv && rg < cx.gi)) {
+                        cx.gv = v;
+                        cx.gi = rg;
+                    }
+            }
             break;
         }
         }
@@ -1515,6 +1568,76 @@ __device__ __forceinline__ void op_reduce(Ctx& cx, const Lds& s, uint32_t r, con
     if (nh == 2) st_tag(out + 64 + cx.lane, O1 * inv, cx.epoch);
 }
 
+// ---------------------------------------------------------- fused greedy --
+
+__device__ __forceinline__ void argmax_pair(float& v, uint32_t& i, float ov, uint32_t oi) {
+    if (ov > v || (ov == v && oi < i)) {
+        v = ov;
+        i = oi;
+    }
+}
+
+// Greedy decoding inside the step (the single-launch GREEDY build): after its queue, every
+// CU merges its compute waves' (max, lowest index) pairs and publishes them as tagged words;
+// the last CU to count itself in (every other CU has then finished its queue, so none reads
+// the tokens or positions any more) merges all pairs, writes next token = argmax of each
+// logits row (lowest index among equal maxima, NaN never wins, 0 for a row without a number)
+// and advances the positions, then resets the counter for the next launch.
+__device__ __forceinline__ void greedy_finish(Ctx& cx, const Lds& s, const Step& sp, uint32_t& seq) {
+    CParams& p = *cx.p;
+    const int B = p.B;
+    if (cx.aborted) return;
+    cbar(cx, s, seq);  // every wave is past its last instruction: buffer set 0 is free
+    LDS uint32_t* gs = (LDS uint32_t*)xslot(s, p, 0);  // [NW][MAX_BATCH] (value, index)
+    if (cx.lane < B) {
+        gs[(cx.wave * MAX_BATCH + cx.lane) * 2] = __float_as_uint(cx.gv);
+        gs[(cx.wave * MAX_BATCH + cx.lane) * 2 + 1] = cx.gi;
+    }
+    cbar(cx, s, seq);
+    if (cx.wave != 0 || cx.aborted) return;
+    const float ninf = -__builtin_inff();
+    float v = ninf;
+    uint32_t i = GREEDY_NONE;
+    if (cx.lane < B)
+        for (int w = 0; w < NW; ++w)
+            argmax_pair(v, i, __uint_as_float(gs[(w * MAX_BATCH + cx.lane) * 2]), gs[(w * MAX_BATCH + cx.lane) * 2 + 1]);
+    if (cx.lane < B) {
+        uint64_t* q = p.greedy_pair + ((size_t)cx.cu * MAX_BATCH + cx.lane) * 2;
+        st_tag(q, v, cx.epoch);
+        st_tag(q + 1, __uint_as_float(i), cx.epoch);
+    }
+    uint32_t old = 0;
+    if (cx.lane == 0) old = __hip_atomic_fetch_add(p.greedy_cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (uni(old) != (uint32_t)p.ncu - 1) return;
+    if (cx.lane == 0) __hip_atomic_store(p.greedy_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int ncu = p.ncu;
+    for (int bb = 0; bb < B; ++bb) {
+        float bv = ninf;
+        uint32_t bi = GREEDY_NONE;
+        for (int c0 = 0; c0 < ncu; c0 += 64) {
+            const int c = c0 + cx.lane;
+            const uint64_t* q = p.greedy_pair + ((size_t)(c < ncu ? c : 0) * MAX_BATCH + bb) * 2;
+            uint64_t wv = ld_tag(q), wi = ld_tag(q + 1);
+            uint32_t spins = 0;
+            while (any_lane(c < ncu && (tag_of(wv) != cx.epoch || tag_of(wi) != cx.epoch))) {
+                if (!keep_waiting(cx, spins, 0x60000000u | (uint32_t)c0)) return;
+                if (tag_of(wv) != cx.epoch) wv = ld_tag(q);
+                if (tag_of(wi) != cx.epoch) wi = ld_tag(q + 1);
+            }
+            if (c < ncu) argmax_pair(bv, bi, val_of(wv), __float_as_uint(val_of(wi)));
+        }
+        for (int d = 32; d >= 1; d >>= 1) {
+            const float ov = __shfl_xor(bv, d);
+            const uint32_t oi = (uint32_t)__shfl_xor((int)bi, d);
+            argmax_pair(bv, bi, ov, oi);
+        }
+        if (cx.lane == 0) {
+            gst((int32_t*)sp.tokens + bb, bi == GREEDY_NONE ? 0 : (int32_t)bi);
+            gst((int32_t*)sp.positions + bb, __builtin_amdgcn_readlane(sp.pos, bb) + 1);
+        }
+    }
+}
+
 // --------------------------------------------------------------- the kernel --
 
 // stage < 0: run the whole queue (one launch per step); stage >= 0: only that
@@ -1522,7 +1645,7 @@ __device__ __forceinline__ void op_reduce(Ctx& cx, const Lds& s, uint32_t r, con
 // head size, each with and without the profile/timeline instrumentation (its
 // bookkeeping costs registers and scalar work on every instruction, so the
 // plain build leaves it out entirely).
-template <int HEAD_DIM, bool INSTR, bool FP8>
+template <int HEAD_DIM, bool INSTR, bool FP8, bool GREEDY>
 __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const int32_t* tokens,
                                           const int32_t* positions, uint16_t* kv, float* logits, int stage,
                                           uint32_t flags) {
@@ -1542,6 +1665,8 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
     cx.trace = INSTR && p.trace != nullptr;
     cx.t_in = cx.t_acq = cx.t_mid = cx.t_ring = 0;
     for (int k = 0; k < 8; ++k) cx.cnt[k] = 0;
+    cx.gv = -__builtin_inff();
+    cx.gi = GREEDY_NONE;
     const uint64_t t_kernel = cx.prof ? cycles() : 0;
     auto flush_prof = [&](int wave_slot) {
         if (cx.prof && cx.lane == 0) {
@@ -1591,7 +1716,7 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
     if (threadIdx.x < SYNC_WORDS) s.landed[threadIdx.x] = 0;
     __syncthreads();
 
-    const uint32_t* uoff = p.unit_off + ((size_t)qb + cx.cu) * NW;
+    const CONST_AS uint32_t* uoff = (const CONST_AS uint32_t*)(p.unit_off + ((size_t)qb + cx.cu) * NW);
     if (wave >= NW + NWL) {  // gather waves
         cx.wave = wave;
         gatherer<FP8>(cx, s, sp, qb, pc0, pc1, wave - NW - NWL);
@@ -1641,9 +1766,9 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
         case OP_ATTN_REDUCE: op_reduce(cx, s, r, in, xb); break;
         default: {
             const int ku = in.op == OP_O_PROJ_RES ? p.ku_q : in.op == OP_DOWN_RES ? p.ku_f : p.ku_h;
-            if (!batch1_path(p.B, ku, FP8)) op_gemv<0, FP8>(cx, s, st, r, slot, in, xb, sp, da);
-            else if (!FP8 && ku == 4) op_gemv<FP8 ? 2 : 4, FP8>(cx, s, st, r, slot, in, xb, sp, da);
-            else op_gemv<2, FP8>(cx, s, st, r, slot, in, xb, sp, da);
+            if (!batch1_path(p.B, ku, FP8)) op_gemv<0, FP8, GREEDY>(cx, s, st, r, slot, in, xb, sp, da);
+            else if (!FP8 && ku == 4) op_gemv<FP8 ? 2 : 4, FP8, GREEDY>(cx, s, st, r, slot, in, xb, sp, da);
+            else op_gemv<2, FP8, GREEDY>(cx, s, st, r, slot, in, xb, sp, da);
             break;
         }
         }
@@ -1664,16 +1789,18 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
             rw[5] = cx.t_ring;
         }
     }
+    if constexpr (GREEDY) greedy_finish(cx, s, sp, seq);
     flush_prof(wave);
     if ((flags & KF_BUMP_EPOCH) && wave == 0 && cx.lane == 0) p.epoch[cx.cu] = cx.epoch;
 }
 
-// The whole step in one launch (every workgroup runs its full queue).
-template <int HEAD_DIM, bool INSTR, bool FP8 = false>
+// The whole step in one launch (every workgroup runs its full queue); GREEDY: the build that
+// also writes the argmax tokens and advances the positions.
+template <int HEAD_DIM, bool INSTR, bool FP8 = false, bool GREEDY = false>
 __global__ void __launch_bounds__(WG_THREADS, 1)
 mk_decode_kernel(const Params* __restrict__ pp, const int32_t* tokens, const int32_t* positions, uint16_t* kv,
                  float* logits, int stage, uint32_t flags) {
-    step_body<HEAD_DIM, INSTR, FP8>(pp, tokens, positions, kv, logits, -1, flags);
+    step_body<HEAD_DIM, INSTR, FP8, GREEDY>(pp, tokens, positions, kv, logits, -1, flags);
 }
 
 // One stage of the step (one op of one layer) per launch.
@@ -1681,7 +1808,7 @@ template <int HEAD_DIM, bool INSTR, bool FP8 = false>
 __global__ void __launch_bounds__(WG_THREADS, 1)
 mk_stage_kernel(const Params* __restrict__ pp, const int32_t* tokens, const int32_t* positions, uint16_t* kv,
                 float* logits, int stage, uint32_t flags) {
-    step_body<HEAD_DIM, INSTR, FP8>(pp, tokens, positions, kv, logits, stage, flags);
+    step_body<HEAD_DIM, INSTR, FP8, false>(pp, tokens, positions, kv, logits, stage, flags);
 }
 
 // ------------------------------------------------------------ pack kernel --
@@ -1987,6 +2114,14 @@ hipError_t launch_step(const Params* dev_params, int head_dim, int ncu, size_t l
                     (void*)&stage, (void*)&flags};
     const bool instr = (flags & KF_INSTRUMENTED) != 0, fp8 = (flags & KF_FP8) != 0;
     if (fp8 && instr) return hipErrorInvalidValue;  // no instrumented FP8 build
+    if (flags & KF_GREEDY) {  // single launch, plain builds only
+        if (stage >= 0 || instr) return hipErrorInvalidValue;
+        const void* fn = fp8 ? (head_dim == 64 ? (const void*)mk_decode_kernel<64, false, true, true>
+                                               : (const void*)mk_decode_kernel<128, false, true, true>)
+                             : (head_dim == 64 ? (const void*)mk_decode_kernel<64, false, false, true>
+                                               : (const void*)mk_decode_kernel<128, false, false, true>);
+        return hipLaunchCooperativeKernel(fn, dim3(ncu), dim3(WG_THREADS), args, (unsigned)lds_bytes, stream);
+    }
     if (stage < 0) {
         const void* fn =
             fp8 ? (head_dim == 64 ? (const void*)mk_decode_kernel<64, false, true> : (const void*)mk_decode_kernel<128, false, true>)
@@ -2007,7 +2142,9 @@ hipError_t set_step_kernel_lds(size_t lds_bytes) {
                          (const void*)mk_decode_kernel<64, true>,  (const void*)mk_decode_kernel<128, true>,
                          (const void*)mk_stage_kernel<64, true>,   (const void*)mk_stage_kernel<128, true>,
                          (const void*)mk_decode_kernel<64, false, true>, (const void*)mk_decode_kernel<128, false, true>,
-                         (const void*)mk_stage_kernel<64, false, true>,  (const void*)mk_stage_kernel<128, false, true>};
+                         (const void*)mk_stage_kernel<64, false, true>,  (const void*)mk_stage_kernel<128, false, true>,
+                         (const void*)mk_decode_kernel<64, false, false, true>, (const void*)mk_decode_kernel<128, false, false, true>,
+                         (const void*)mk_decode_kernel<64, false, true, true>, (const void*)mk_decode_kernel<128, false, true, true>};
     for (const void* fn : fns) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
         if (e != hipSuccess) return e;

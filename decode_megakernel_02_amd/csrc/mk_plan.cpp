@@ -89,10 +89,12 @@ struct Builder {
         case OP_O_PROJ_RES:
             out[0] = {base + MAT_WO, rg, 0, (uint32_t)(p.Hq * D), (uint32_t)(p.Hq * D)};
             return 1;
-        case OP_RMS_UP_GATE:
-            out[0] = {base + MAT_GATE, rg, 0, (uint32_t)p.H, (uint32_t)p.H};
-            out[1] = {base + MAT_UP, rg, 0, (uint32_t)p.H, (uint32_t)p.H};
+        case OP_RMS_UP_GATE: {  // rg0 = CU slot, rg - rg0 = row-group within its share
+            const uint32_t r = p.ug_row((int)in.rg0, rg - in.rg0);
+            out[0] = {base + MAT_GATE, r, 0, (uint32_t)p.H, (uint32_t)p.H};
+            out[1] = {base + MAT_UP, r, 0, (uint32_t)p.H, (uint32_t)p.H};
             return 2;
+        }
         case OP_DOWN_RES: {
             int c = in.a;
             uint32_t k0 = p.chunk_begin[c], k1 = p.chunk_begin[c + 1];
@@ -225,14 +227,12 @@ int build_plan(const mk_config& c, int ncu, Plan& p, std::string& err) {
         // K-chunk 0 of the down projection first, then of chunk 1, ..., so a
         // chunk is complete after the matching fraction of the stage instead
         // of after the whole stage, and the down instructions of the early
-        // chunks find their inputs ready
-        for (int cch = 0; cch < p.n_chunk; ++cch) {
-            const int c0 = p.chunk_begin[cch], len = p.chunk_begin[cch + 1] - c0;
-            for (int t = 0; t < ncu; ++t) {
-                int r0 = (int)((long long)len * t / ncu), r1 = (int)((long long)len * (t + 1) / ncu);
-                if (r1 > r0)
-                    b.q[t].push_back(Inst{OP_RMS_UP_GATE, (uint16_t)l, (uint32_t)(c0 + r0), (uint32_t)(r1 - r0), 0, 0});
-            }
+        // chunks find their inputs ready.  One instruction per CU holds all
+        // its shares in that order (every output word carries its own tag,
+        // so no instruction boundary is needed between chunks)
+        for (int t = 0; t < ncu; ++t) {
+            const uint32_t n = p.ug_count(t);
+            if (n) b.q[t].push_back(Inst{OP_RMS_UP_GATE, (uint16_t)l, (uint32_t)t, n, 0, 0});
         }
         mark(st + 5);
         // down projection: a CU owns rows [r0, r1) for every K-chunk, one
@@ -358,8 +358,17 @@ void build_rg_scales(const Plan& p, const std::vector<float>& row_scale, std::ve
         }
     };
     for (int l = 0; l < p.L; ++l)
-        for (int o = 0; o < 4; ++o)
+        for (int o = 0; o < 4; ++o) {
+            if (ops[o] == OP_RMS_UP_GATE) {  // indexed by row (the instruction's row-groups are not contiguous)
+                const size_t base = (size_t)l * p.rgs_stride + p.rgs_off[o];
+                for (int r = 0; r < p.F; ++r) {
+                    out[(base + r) * 2] = row_scale[(size_t)p.mat_row_off[(size_t)l * MATS_PER_LAYER + MAT_GATE] + r];
+                    out[(base + r) * 2 + 1] = row_scale[(size_t)p.mat_row_off[(size_t)l * MATS_PER_LAYER + MAT_UP] + r];
+                }
+                continue;
+            }
             fill(Inst{ops[o], (uint16_t)l, 0, 0, 0, 0}, (size_t)l * p.rgs_stride + p.rgs_off[o], counts[o]);
+        }
     fill(Inst{OP_RMS_LM_HEAD, 0, 0, 0, 0, 0}, (size_t)p.L * p.rgs_stride, (uint32_t)p.V);
 }
 
@@ -392,7 +401,12 @@ bool check_plan(const Plan& p, std::string& err, bool check_order) {
                 for (uint32_t r = 0; r < in.nrg; ++r) o[(size_t)in.layer * p.H + in.rg0 + r]++;
                 break;
             case OP_RMS_UP_GATE: stage = in.layer * STAGES_PER_LAYER + 4;
-                for (uint32_t r = 0; r < in.nrg; ++r) ug[(size_t)in.layer * p.F + in.rg0 + r]++;
+                if (in.rg0 >= (uint32_t)ncu || in.nrg > p.ug_count((int)in.rg0)) {
+                    snprintf(buf, sizeof buf, "CU %d: up/gate instruction beyond its CU share", cu);
+                    err = buf;
+                    return false;
+                }
+                for (uint32_t r = 0; r < in.nrg; ++r) ug[(size_t)in.layer * p.F + p.ug_row((int)in.rg0, r)]++;
                 break;
             case OP_DOWN_RES: stage = in.layer * STAGES_PER_LAYER + 5;
                 for (uint32_t r = 0; r < in.nrg; ++r) dn[((size_t)in.layer * p.n_chunk + in.a) * p.H + in.rg0 + r]++;
@@ -471,7 +485,8 @@ bool check_plan(const Plan& p, std::string& err, bool check_order) {
             for (uint32_t r = 0; r < in.nrg; ++r) o_row[(size_t)l * p.H + in.rg0 + r] = 1;
             break;
         case OP_RMS_UP_GATE:
-            for (uint32_t r = 0; r < in.nrg; ++r) ug_chunk[(size_t)l * p.n_chunk + chunk_of(in.rg0 + r)]++;
+            for (uint32_t r = 0; r < in.nrg; ++r)
+                ug_chunk[(size_t)l * p.n_chunk + chunk_of((int)p.ug_row((int)in.rg0, r))]++;
             break;
         case OP_DOWN_RES:
             dn_cnt[l] += in.nrg;

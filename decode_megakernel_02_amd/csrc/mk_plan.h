@@ -74,6 +74,27 @@ struct Plan {
         return true;
     }
     int n_mats() const { return L * MATS_PER_LAYER + 1; }
+    // Up/gate rows of CU slot t: its share of every down-projection chunk, chunk after chunk
+    // (one instruction per CU and layer; row-group i of it is row ug_row(t, i))
+    uint32_t ug_share(int t, int c, uint32_t& r0) const {
+        const int c0 = chunk_begin[c], len = chunk_begin[c + 1] - c0;
+        r0 = (uint32_t)(c0 + (int)((long long)len * t / ncu));
+        return (uint32_t)(c0 + (int)((long long)len * (t + 1) / ncu)) - r0;
+    }
+    uint32_t ug_count(int t) const {
+        uint32_t n = 0, r0;
+        for (int c = 0; c < n_chunk; ++c) n += ug_share(t, c, r0);
+        return n;
+    }
+    uint32_t ug_row(int t, uint32_t i) const {
+        uint32_t r0 = 0;
+        for (int c = 0; c < n_chunk; ++c) {
+            const uint32_t n = ug_share(t, c, r0);
+            if (i < n) return r0 + i;
+            i -= n;
+        }
+        return 0xffffffffu;  // past the CU's rows
+    }
 };
 
 // FP8 row-group scale table (Params::rgscale) from per-row scales indexed by global row.

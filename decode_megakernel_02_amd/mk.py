@@ -53,6 +53,7 @@ class MkScheduleInfo(ctypes.Structure):
 
 
 EXPORTS = ["mk_create", "mk_load_weights", "mk_kv_cache_bytes", "mk_decode_step", "mk_decode_step_multikernel",
+           "mk_decode_step_greedy",
            "mk_destroy", "mk_status_string", "mk_last_error", "mk_get_device_error", "mk_get_profile",
            "mk_schedule_inspect", "mk_get_trace", "mk_greedy_advance", "mk_read_probe", "mk_empty_launches",
            "mk_graph_create", "mk_graph_launch", "mk_graph_destroy", "mk_prefill", "mk_schedule_selftest", "mk_litmus", "mk_set_spin_limit",
@@ -62,6 +63,7 @@ MK_FLAG_TRACE = 2
 MK_FLAG_FP8_WEIGHTS = 4
 MK_GRAPH_MULTIKERNEL = 1
 MK_GRAPH_EMPTY = 2
+MK_GRAPH_FUSED_GREEDY = 4
 TRACE_SLOTS = 52
 PROF_WAVES = 10  # 8 compute waves, the loader and the gather wave per workgroup
 PROF_SLOTS = 8
@@ -83,6 +85,7 @@ def lib():
         L.mk_kv_cache_bytes.restype = ctypes.c_size_t
         L.mk_decode_step.argtypes = [H, _P, _P, _P, _P, _P]
         L.mk_decode_step_multikernel.argtypes = [H, _P, _P, _P, _P, _P]
+        L.mk_decode_step_greedy.argtypes = [H, _P, _P, _P, _P, _P]
         L.mk_read_probe.argtypes = [_P, ctypes.c_size_t, _P, ctypes.c_int, _P]
         L.mk_destroy.argtypes = [H]
         L.mk_status_string.argtypes = [ctypes.c_int]
@@ -104,7 +107,8 @@ def lib():
         L.mk_graph_destroy.argtypes = [ctypes.c_void_p]
         L.mk_prefill.argtypes = [H, ctypes.POINTER(MkWeights), _P, ctypes.c_int32, _P, _P, _P]
         L.mk_prefill_static.argtypes = [H, ctypes.POINTER(MkWeights), _P, ctypes.c_int32, _P, _P, _P]
-        for name in ["mk_create", "mk_load_weights", "mk_decode_step", "mk_decode_step_multikernel", "mk_destroy",
+        for name in ["mk_create", "mk_load_weights", "mk_decode_step", "mk_decode_step_multikernel",
+                     "mk_decode_step_greedy", "mk_destroy",
                      "mk_get_device_error", "mk_schedule_inspect", "mk_get_profile", "mk_get_trace",
                      "mk_greedy_advance", "mk_read_probe", "mk_empty_launches", "mk_graph_create",
                      "mk_graph_launch", "mk_graph_destroy", "mk_prefill", "mk_schedule_selftest", "mk_litmus", "mk_set_spin_limit", "mk_debug_stage", "mk_prefill_static"]:
@@ -253,6 +257,12 @@ def mk_graph_launch(graph, stream: Optional[int] = None):
 
 def mk_graph_destroy(graph):
     _check(lib().mk_graph_destroy(graph))
+
+
+def mk_decode_step_greedy(handle, tokens, positions, kv_cache, logits, stream: Optional[int] = None):
+    """mk_decode_step plus greedy selection in one launch: tokens <- argmax(logits), positions += 1."""
+    _check(lib().mk_decode_step_greedy(handle, _ptr(tokens), _ptr(positions), _ptr(kv_cache), _ptr(logits),
+                                       stream), handle)
 
 
 def mk_decode_step_multikernel(handle, tokens, positions, kv_cache, logits, stream: Optional[int] = None):

@@ -129,6 +129,19 @@ size_t mk_kv_cache_bytes(const mk_config* cfg);
 int mk_decode_step(mk_handle* h, const int32_t* tokens, const int32_t* positions,
                    void* kv_cache, float* logits, void* stream);
 
+/* mk_decode_step followed by greedy selection, in the same ONE launch:
+ * the next token of each row is argmax_v logits[b][v] (the lowest index among
+ * equal maxima; NaN never wins; a row without a number gives 0), written to
+ * tokens[b], and positions[b] advances by one -- the loop of greedy
+ * decoding (pages "Megakernels for Gemma 4" and "Why it only works at low
+ * concurrency": the per-token interval of an agent loop).  Each CU reduces
+ * its LM-head rows; the last CU to finish merges the per-CU results.  The
+ * logits are written as by mk_decode_step.  Not for handles created with
+ * MK_FLAG_PROFILE or MK_FLAG_TRACE (MK_ERR_STATE).  After a device error,
+ * mk_get_device_error also resets the merge counter.                      */
+int mk_decode_step_greedy(mk_handle* h, int32_t* tokens, int32_t* positions,
+                          void* kv_cache, float* logits, void* stream);
+
 /* Same arguments, results and ordering rules; the same op bodies launched
  * once per op and layer (6 * n_layers + 1 launches), ordered only by the
  * kernel boundaries.  For A/B comparison with mk_decode_step.             */
@@ -180,13 +193,16 @@ int mk_empty_launches(int n_launches, int n_blocks, int n_threads, void* stream)
  * launch path, the replay point next to "one launch, one interpreter" of the
  * megakernel page); MK_GRAPH_EMPTY = as many empty-kernel launches as the
  * per-op step has, with the step's grid shape, and no greedy kernel (the
- * graph launch overhead alone; the buffers are not touched).  The graph
+ * graph launch overhead alone; the buffers are not touched);
+ * MK_GRAPH_FUSED_GREEDY = each step one mk_decode_step_greedy launch (no
+ * separate greedy kernel; not combinable with the other flags).  The graph
  * holds no memset nodes.  Replays on one handle must be ordered on one
  * stream, like steps.  *out is NULL on error.  MK_ERR_HIP when the runtime
  * refuses the capture (for instance of the cooperative single-launch step);
  * the handle stays usable.  The graph must be destroyed before its handle. */
 #define MK_GRAPH_MULTIKERNEL 1u
 #define MK_GRAPH_EMPTY 2u
+#define MK_GRAPH_FUSED_GREEDY 4u /* each step is one mk_decode_step_greedy launch */
 typedef struct mk_graph mk_graph;
 int mk_graph_create(mk_handle* h, int32_t* tokens, int32_t* positions, void* kv_cache,
                     float* logits, int n_steps, uint32_t flags, mk_graph** out);
