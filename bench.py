@@ -178,6 +178,51 @@ def write_stage_summary(trace_csv, workload, command):
     return path
 
 
+OPCODES = ["RMS_QKV_ROPE", "ATTENTION", "ATTN_REDUCE", "O_PROJ_RES", "RMS_UP_GATE", "DOWN_RES", "RMS_LM_HEAD"]
+
+
+def ablation_table(mk, h, tokens, positions, kv, logits, stream, P, K, W, args):
+    """Single-launch step time (CUDA-event mean over K launches, median of 5 interleaved rounds)
+    with no opcode and with each opcode's arithmetic switched off; Markdown."""
+    import torch
+    cur = torch.cuda.current_stream()
+    rounds = {op: [] for op in range(8)}
+    for _ in range(5):
+        for op in range(8):
+            mk.mk_set_ablation(h, op)
+            positions.fill_(P)
+            for _ in range(W):
+                mk.mk_decode_step(h, tokens, positions, kv, logits, stream)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+            for a, b in ev:
+                a.record(cur)
+                mk.mk_decode_step(h, tokens, positions, kv, logits, stream)
+                b.record(cur)
+            torch.cuda.synchronize()
+            err = mk.mk_get_device_error(h)
+            if err is not None:
+                raise RuntimeError(f"device error with opcode {op} switched off: code {err.code}")
+            rounds[op].append(statistics.mean(a.elapsed_time(b) * 1e3 for a, b in ev))
+    mk.mk_set_ablation(h, 0)
+    base = statistics.median(rounds[0])
+    lines = [f"# Single-launch step with one opcode's arithmetic switched off, workload {args.workload}",
+             "",
+             "The ablation build (mk_set_ablation) keeps every dependency: the switched-off opcode's weight "
+             "units still stream through the rings unread, its inputs are still awaited and its tagged "
+             "outputs still written. Kernel time per step: CUDA events around each launch, mean over "
+             f"{K} launches, median of 5 interleaved rounds.",
+             "",
+             f"Command: `python bench.py --ablation --workload {args.workload} --steps {K} --warmup {W}`",
+             "",
+             "| switched off | us per step | shrink us | shrink % |",
+             "|---|---|---|---|",
+             f"| nothing | {base:.1f} | | |"]
+    for op in range(1, 8):
+        t = statistics.median(rounds[op])
+        lines.append(f"| {OPCODES[op - 1]} | {t:.1f} | {base - t:.1f} | {100 * (base - t) / base:.1f} |")
+    return "\n".join(lines)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -200,6 +245,9 @@ def main():
                     help="time only the CPU oracle on the workload and print it as one JSON line")
     ap.add_argument("--prefill", action="store_true",
                     help="time batched prefill (mk_prefill) of the workload's prompt instead of decode; one JSON line")
+    ap.add_argument("--ablation", action="store_true",
+                    help="print the table of the single-launch step time with each opcode's arithmetic "
+                         "switched off (mk_set_ablation) instead of the JSON line")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (3 launches), the reference "
                          "kernel for scaling HBM byte counters")
@@ -301,6 +349,12 @@ def main():
     positions = torch.full((B,), P, dtype=torch.int32, device="cuda")
     logits = torch.empty(B, shape.vocab, dtype=torch.float32, device="cuda")
     log(f"handle ready; schedule: {mk.mk_schedule_inspect(cfg, torch.cuda.get_device_properties(0).multi_processor_count).total_insts} instructions")
+
+    if args.ablation:
+        print(ablation_table(mk, h, tokens, positions, kv, logits, stream, P, K, W, args), flush=True)
+        torch.cuda.synchronize()
+        mk.mk_destroy(h)
+        return
 
     def greedy(n, fn):
         for _ in range(n):

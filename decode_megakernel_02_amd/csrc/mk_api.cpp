@@ -44,6 +44,7 @@ struct mk_handle {
     std::string last_error;
     uint64_t* greedy_part = nullptr;  // [B][GREEDY_BLOCKS] per-slice (value, index) pairs
     uint32_t* greedy_cnt = nullptr;   // [B] finished slices of the current call (zero between calls)
+    uint32_t ablate = 0;              // mk_set_ablation: opcode switched off in mk_decode_step (0: none)
     uint16_t* row_amax = nullptr;     // FP8: [rows of all matrices] largest |w| per row (bf16 bits)
     float* row_scale = nullptr;       // FP8: [rows of all matrices] scale of each row (pack input)
     void* prefill_ws = nullptr;       // mk_prefill's workspace, kept between calls
@@ -449,7 +450,7 @@ int mk_decode_step(mk_handle* h, const int32_t* tokens, const int32_t* positions
     int rc = step_args_ok(h, tokens, positions, kv_cache, logits);
     if (rc != MK_OK) return rc;
     hipError_t e = launch_step(h->dparams, h->hp.D, h->hp.ncu, h->lds_bytes, tokens, positions, kv_cache, logits, -1,
-                               KF_BUMP_EPOCH | instr_flag(h), (hipStream_t)stream);
+                               KF_BUMP_EPOCH | instr_flag(h) | (h->ablate ? KF_ABLATE : 0u), (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(h, HipError{e, "mk_step_kernel launch"});
     return MK_OK;
 }
@@ -458,6 +459,7 @@ int mk_decode_step_greedy(mk_handle* h, int32_t* tokens, int32_t* positions, voi
                           void* stream) {
     int rc = step_args_ok(h, tokens, positions, kv_cache, logits);
     if (rc != MK_OK) return rc;
+    if (h->ablate) return fail(h, MK_ERR_STATE, "an ablation is set: use mk_decode_step");
     if (instr_flag(h) & KF_INSTRUMENTED)
         return fail(h, MK_ERR_STATE, "the fused greedy step has no profiling or tracing build");
     hipError_t e = launch_step(h->dparams, h->hp.D, h->hp.ncu, h->lds_bytes, tokens, positions, kv_cache, logits, -1,
@@ -476,6 +478,24 @@ int mk_decode_step_multikernel(mk_handle* h, const int32_t* tokens, const int32_
                                    (st == ns - 1 ? KF_BUMP_EPOCH : 0u) | instr_flag(h), (hipStream_t)stream);
         if (e != hipSuccess) return hip_fail(h, HipError{e, "mk_step_kernel stage launch"});
     }
+    return MK_OK;
+}
+
+int mk_set_ablation(mk_handle* h, int32_t opcode) {
+    if (!h) return fail(nullptr, MK_ERR_INVALID_ARG, "handle is NULL");
+    if (opcode < 0 || opcode > (int32_t)OP_RMS_LM_HEAD) return fail(h, MK_ERR_INVALID_ARG, "opcode outside 0..7");
+    if (opcode && (instr_flag(h) & (KF_INSTRUMENTED | KF_FP8)))
+        return fail(h, MK_ERR_STATE, "the ablation build has no FP8, profiling or tracing form");
+    const uint32_t v = (uint32_t)opcode;
+    try {
+        HIPCHK(hipSetDevice(h->cfg.device));
+        HIPCHK(hipDeviceSynchronize());  // no step may be reading the parameter block
+        HIPCHK(hipMemcpy(&h->dparams->ablate_op, &v, sizeof v, hipMemcpyHostToDevice));
+    } catch (const HipError& e) {
+        return hip_fail(h, e);
+    }
+    h->ablate = v;
+    h->hp.ablate_op = v;
     return MK_OK;
 }
 

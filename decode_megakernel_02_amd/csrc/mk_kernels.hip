@@ -575,6 +575,22 @@ __device__ __forceinline__ void ring_wait(Ctx& cx, const Lds& s, Stream& st, uin
     if (cx.trace) cx.t_ring += rtime() - r0;
 }
 
+// Ablation build: pass over n units of this wave's stream without reading them, a quarter
+// ring at a time (the granularity of the dot products, so the loader keeps streaming instead
+// of refilling an emptied ring; everything read is released before each wait); the loader
+// still streams them.
+__device__ __forceinline__ void ring_skip(Ctx& cx, const Lds& s, Stream& st, uint32_t n) {
+    const uint32_t ru = uni((uint32_t)cx.p->ring_units), q = ru / 4 > 0 ? ru / 4 : 1;
+    while (n > 0 && !cx.aborted) {
+        const uint32_t c = n < q ? n : q;
+        ring_wait(cx, s, st, st.unit + c);
+        st.unit += c;
+        st.slot = (st.slot + c) % ru;
+        ring_release(cx, s, st);
+        n -= c;
+    }
+}
+
 // Batch-1 row dot products with this wave's x slice in registers: the KU
 // units of a row are read from the ring together and accumulated in KU
 // independent chains.
@@ -1148,7 +1164,7 @@ __device__ __forceinline__ uint32_t ug_share(CParams& p, uint32_t t, int c, uint
 
 // KU > 0: batch-1 path with KU units per row (x slice in registers);
 // KU == 0: general path.
-template <int KU, bool FP8, bool GREEDY>
+template <int KU, bool FP8, bool GREEDY, bool ABLATE>
 __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint32_t r, uint32_t slot, const Inst& in,
                                         LDS float* xb, const Step& sp, DownAcc& da) {
     CParams& p = *cx.p;
@@ -1191,11 +1207,23 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
     XSlice<KU == 0 ? 1 : (FP8 ? 2 * KU : KU)> xs;
     const uint32_t ru = __builtin_amdgcn_readfirstlane((uint32_t)p.ring_units);
     if constexpr (KU > 0) load_xslice<KU, FP8>(cx, xb, __builtin_amdgcn_readfirstlane(p.xstride), xs);
+    // ablation build, this opcode switched off: the row sums are 0 (units passed over unread)
+    const bool off = ABLATE && in.op == p.ablate_op;
     auto dot1 = [&](RowOut& o) {
+        if (ABLATE && off) {
+            ring_skip(cx, s, st, (uint32_t)ku);
+            o.mine[0] = o.mine[1] = 0.f;
+            return;
+        }
         if constexpr (KU > 0) rowgroup_dot_b1<KU, 1, FP8>(cx, s, st, xs, ru, o);
         else rowgroup_dot_batch<1, FP8>(cx, s, st, xb, ku, o);
     };
     auto dot2 = [&](RowOut& o) {
+        if (ABLATE && off) {
+            ring_skip(cx, s, st, 2u * (uint32_t)ku);
+            o.mine[0] = o.mine[1] = 0.f;
+            return;
+        }
         if constexpr (KU > 0) rowgroup_dot_b1<KU, 2, FP8>(cx, s, st, xs, ru, o);
         else rowgroup_dot_batch<2, FP8>(cx, s, st, xb, ku, o);
     };
@@ -1407,7 +1435,7 @@ __device__ __forceinline__ float pv_reduce_scatter64(const uint4 (&row)[8], floa
 // Waves split the group's heads and 64-key blocks; in a block lane j owns key
 // j (its K and V rows, loaded with independent 16-byte loads), and the PV
 // product is reduce-scattered so lane d ends with dims d (and d + 64).
-template <int D>
+template <int D, bool ABLATE>
 __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& seq, uint32_t r, const Inst& in,
                                                LDS float* xb,
                                                const Step& sp) {
@@ -1457,6 +1485,17 @@ __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& 
     // q of the group's heads (pre-scaled), then the new K and V rows, staged by the gather wave
     wait_inputs(cx, s, r);
     if (cx.aborted) return;
+    if (ABLATE && p.ablate_op == OP_ATTENTION) {  // switched off: the partial of an all-zero output
+        if (sub != 0) return;
+        uint64_t* out = p.part + ((((size_t)l * B + b) * p.Hq + g * G + gi) * p.n_split + split) * (D + 2);
+        if (cx.lane == 0) {
+            st_tag(out + 0, 0.f, cx.epoch);
+            st_tag(out + 1, 1.f, cx.epoch);
+        }
+#pragma unroll
+        for (int h = 0; h < NH; ++h) st_tag(out + 2 + h * 64 + cx.lane, 0.f, cx.epoch);
+        return;
+    }
 
     const LDS float* qh = qs + gi * D;
     const float ninf = -__builtin_inff();
@@ -1544,11 +1583,17 @@ __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& 
 
 // Log-sum-exp merge of the n_split partials of (row b, head):
 // out = sum_s o_s e^(m_s - M) / sum_s l_s e^(m_s - M), M = max_s m_s.
+template <bool ABLATE>
 __device__ __forceinline__ void op_reduce(Ctx& cx, const Lds& s, uint32_t r, const Inst& in, LDS float* xb) {
     CParams& p = *cx.p;
     const int B = p.B, D = p.D, l = in.layer, b = in.a, head = in.b, ns = p.n_split, W = D + 2;
     wait_inputs(cx, s, r);  // xb = the n_split partials, staged by the gather wave
     if (cx.wave != 0 || cx.aborted) return;
+    if (ABLATE && p.ablate_op == OP_ATTN_REDUCE) {  // switched off: a zero output
+        uint64_t* out = p.attn + ((size_t)l * B + b) * p.Hq * D + (size_t)head * D;
+        for (int d = cx.lane; d < D; d += 64) st_tag(out + d, 0.f, cx.epoch);
+        return;
+    }
     const float ninf = -__builtin_inff();
     float M = ninf;
     for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, xb[sp * W]);
@@ -1645,7 +1690,7 @@ __device__ __forceinline__ void greedy_finish(Ctx& cx, const Lds& s, const Step&
 // head size, each with and without the profile/timeline instrumentation (its
 // bookkeeping costs registers and scalar work on every instruction, so the
 // plain build leaves it out entirely).
-template <int HEAD_DIM, bool INSTR, bool FP8, bool GREEDY>
+template <int HEAD_DIM, bool INSTR, bool FP8, bool GREEDY, bool ABLATE>
 __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const int32_t* tokens,
                                           const int32_t* positions, uint16_t* kv, float* logits, int stage,
                                           uint32_t flags) {
@@ -1760,15 +1805,15 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
         LDS float* xb = xslot(s, p, slot);
         switch (in.op) {
         case OP_ATTENTION:
-            op_attention_t<HEAD_DIM>(cx, s, seq, r, in, xb, sp);
+            op_attention_t<HEAD_DIM, ABLATE>(cx, s, seq, r, in, xb, sp);
             vm_drain();  // no load of the attention body stays tracked into the next instruction
             break;
-        case OP_ATTN_REDUCE: op_reduce(cx, s, r, in, xb); break;
+        case OP_ATTN_REDUCE: op_reduce<ABLATE>(cx, s, r, in, xb); break;
         default: {
             const int ku = in.op == OP_O_PROJ_RES ? p.ku_q : in.op == OP_DOWN_RES ? p.ku_f : p.ku_h;
-            if (!batch1_path(p.B, ku, FP8)) op_gemv<0, FP8, GREEDY>(cx, s, st, r, slot, in, xb, sp, da);
-            else if (!FP8 && ku == 4) op_gemv<FP8 ? 2 : 4, FP8, GREEDY>(cx, s, st, r, slot, in, xb, sp, da);
-            else op_gemv<2, FP8, GREEDY>(cx, s, st, r, slot, in, xb, sp, da);
+            if (!batch1_path(p.B, ku, FP8)) op_gemv<0, FP8, GREEDY, ABLATE>(cx, s, st, r, slot, in, xb, sp, da);
+            else if (!FP8 && ku == 4) op_gemv<FP8 ? 2 : 4, FP8, GREEDY, ABLATE>(cx, s, st, r, slot, in, xb, sp, da);
+            else op_gemv<2, FP8, GREEDY, ABLATE>(cx, s, st, r, slot, in, xb, sp, da);
             break;
         }
         }
@@ -1795,12 +1840,13 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
 }
 
 // The whole step in one launch (every workgroup runs its full queue); GREEDY: the build that
-// also writes the argmax tokens and advances the positions.
-template <int HEAD_DIM, bool INSTR, bool FP8 = false, bool GREEDY = false>
+// also writes the argmax tokens and advances the positions; ABLATE: the build that can skip
+// the arithmetic of one opcode (Params::ablate_op) while keeping its data flow.
+template <int HEAD_DIM, bool INSTR, bool FP8 = false, bool GREEDY = false, bool ABLATE = false>
 __global__ void __launch_bounds__(WG_THREADS, 1)
 mk_decode_kernel(const Params* __restrict__ pp, const int32_t* tokens, const int32_t* positions, uint16_t* kv,
                  float* logits, int stage, uint32_t flags) {
-    step_body<HEAD_DIM, INSTR, FP8, GREEDY>(pp, tokens, positions, kv, logits, -1, flags);
+    step_body<HEAD_DIM, INSTR, FP8, GREEDY, ABLATE>(pp, tokens, positions, kv, logits, -1, flags);
 }
 
 // One stage of the step (one op of one layer) per launch.
@@ -1808,7 +1854,7 @@ template <int HEAD_DIM, bool INSTR, bool FP8 = false>
 __global__ void __launch_bounds__(WG_THREADS, 1)
 mk_stage_kernel(const Params* __restrict__ pp, const int32_t* tokens, const int32_t* positions, uint16_t* kv,
                 float* logits, int stage, uint32_t flags) {
-    step_body<HEAD_DIM, INSTR, FP8, false>(pp, tokens, positions, kv, logits, stage, flags);
+    step_body<HEAD_DIM, INSTR, FP8, false, false>(pp, tokens, positions, kv, logits, stage, flags);
 }
 
 // ------------------------------------------------------------ pack kernel --
@@ -2114,6 +2160,12 @@ hipError_t launch_step(const Params* dev_params, int head_dim, int ncu, size_t l
                     (void*)&stage, (void*)&flags};
     const bool instr = (flags & KF_INSTRUMENTED) != 0, fp8 = (flags & KF_FP8) != 0;
     if (fp8 && instr) return hipErrorInvalidValue;  // no instrumented FP8 build
+    if (flags & KF_ABLATE) {  // single launch, bf16 plain builds only
+        if (stage >= 0 || instr || fp8 || (flags & KF_GREEDY)) return hipErrorInvalidValue;
+        const void* fn = head_dim == 64 ? (const void*)mk_decode_kernel<64, false, false, false, true>
+                                        : (const void*)mk_decode_kernel<128, false, false, false, true>;
+        return hipLaunchCooperativeKernel(fn, dim3(ncu), dim3(WG_THREADS), args, (unsigned)lds_bytes, stream);
+    }
     if (flags & KF_GREEDY) {  // single launch, plain builds only
         if (stage >= 0 || instr) return hipErrorInvalidValue;
         const void* fn = fp8 ? (head_dim == 64 ? (const void*)mk_decode_kernel<64, false, true, true>
@@ -2144,7 +2196,9 @@ hipError_t set_step_kernel_lds(size_t lds_bytes) {
                          (const void*)mk_decode_kernel<64, false, true>, (const void*)mk_decode_kernel<128, false, true>,
                          (const void*)mk_stage_kernel<64, false, true>,  (const void*)mk_stage_kernel<128, false, true>,
                          (const void*)mk_decode_kernel<64, false, false, true>, (const void*)mk_decode_kernel<128, false, false, true>,
-                         (const void*)mk_decode_kernel<64, false, true, true>, (const void*)mk_decode_kernel<128, false, true, true>};
+                         (const void*)mk_decode_kernel<64, false, true, true>, (const void*)mk_decode_kernel<128, false, true, true>,
+                         (const void*)mk_decode_kernel<64, false, false, false, true>,
+                         (const void*)mk_decode_kernel<128, false, false, false, true>};
     for (const void* fn : fns) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
         if (e != hipSuccess) return e;

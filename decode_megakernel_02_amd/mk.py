@@ -53,7 +53,7 @@ class MkScheduleInfo(ctypes.Structure):
 
 
 EXPORTS = ["mk_create", "mk_load_weights", "mk_kv_cache_bytes", "mk_decode_step", "mk_decode_step_multikernel",
-           "mk_decode_step_greedy",
+           "mk_decode_step_greedy", "mk_set_ablation",
            "mk_destroy", "mk_status_string", "mk_last_error", "mk_get_device_error", "mk_get_profile",
            "mk_schedule_inspect", "mk_get_trace", "mk_greedy_advance", "mk_read_probe", "mk_empty_launches",
            "mk_graph_create", "mk_graph_launch", "mk_graph_destroy", "mk_prefill", "mk_schedule_selftest", "mk_litmus", "mk_set_spin_limit",
@@ -86,6 +86,7 @@ def lib():
         L.mk_decode_step.argtypes = [H, _P, _P, _P, _P, _P]
         L.mk_decode_step_multikernel.argtypes = [H, _P, _P, _P, _P, _P]
         L.mk_decode_step_greedy.argtypes = [H, _P, _P, _P, _P, _P]
+        L.mk_set_ablation.argtypes = [H, ctypes.c_int32]
         L.mk_read_probe.argtypes = [_P, ctypes.c_size_t, _P, ctypes.c_int, _P]
         L.mk_destroy.argtypes = [H]
         L.mk_status_string.argtypes = [ctypes.c_int]
@@ -108,7 +109,7 @@ def lib():
         L.mk_prefill.argtypes = [H, ctypes.POINTER(MkWeights), _P, ctypes.c_int32, _P, _P, _P]
         L.mk_prefill_static.argtypes = [H, ctypes.POINTER(MkWeights), _P, ctypes.c_int32, _P, _P, _P]
         for name in ["mk_create", "mk_load_weights", "mk_decode_step", "mk_decode_step_multikernel",
-                     "mk_decode_step_greedy", "mk_destroy",
+                     "mk_decode_step_greedy", "mk_set_ablation", "mk_destroy",
                      "mk_get_device_error", "mk_schedule_inspect", "mk_get_profile", "mk_get_trace",
                      "mk_greedy_advance", "mk_read_probe", "mk_empty_launches", "mk_graph_create",
                      "mk_graph_launch", "mk_graph_destroy", "mk_prefill", "mk_schedule_selftest", "mk_litmus", "mk_set_spin_limit", "mk_debug_stage", "mk_prefill_static"]:
@@ -263,6 +264,11 @@ def mk_decode_step_greedy(handle, tokens, positions, kv_cache, logits, stream: O
     """mk_decode_step plus greedy selection in one launch: tokens <- argmax(logits), positions += 1."""
     _check(lib().mk_decode_step_greedy(handle, _ptr(tokens), _ptr(positions), _ptr(kv_cache), _ptr(logits),
                                        stream), handle)
+
+
+def mk_set_ablation(handle, opcode: int):
+    """Switch off one opcode's arithmetic in mk_decode_step (0: none); measurement only."""
+    _check(lib().mk_set_ablation(handle, opcode), handle)
 
 
 def mk_decode_step_multikernel(handle, tokens, positions, kv_cache, logits, stream: Optional[int] = None):

@@ -273,6 +273,21 @@ typedef struct {
  * clears it.  Returns MK_OK, or MK_ERR_DEVICE when a record was present.  */
 int mk_get_device_error(mk_handle* h, mk_device_error* out);
 
+/* Ablation (measurement only): from the next mk_decode_step on, the
+ * single-launch step runs a kernel build in which the arithmetic of one
+ * opcode is switched off -- its weight units still stream through the rings
+ * and unread, its inputs are still awaited and its tagged outputs still
+ * written (zeros; the O and down projections pass the residual through), so
+ * every dependency stays in place and the step time shows what that
+ * component costs (page "Megakernels for Gemma 4": how much the step
+ * shrinks when a component is switched off).  opcode: 0 = none (the normal
+ * build again), 1 RMS+QKV+RoPE, 2 attention, 3 attention reduce, 4 O
+ * projection, 5 RMS+up/gate, 6 down projection, 7 RMS+LM head.  The logits
+ * are then not the model's.  bf16 handles without profiling or tracing only
+ * (MK_ERR_STATE); mk_decode_step_greedy refuses to run while one is set.
+ * Synchronises the device.                                                 */
+int mk_set_ablation(mk_handle* h, int32_t opcode);
+
 /* Watchdog of the bounded waits ("Megakernels: Deleting the Kernel Boundary
  * to Win Back Microseconds", section "The catch": a hand-rolled dependency
  * graph that is wrong hangs instead of failing).  Every wait in the step
