@@ -8,8 +8,8 @@
 //
 // Rows are (batch row, position) pairs, so every projection is a dense
 // contraction C[M][N] = A[M][K] * W[N][K]^T with M = B * P: those run on the
-// fp32 matrix cores (v_mfma_f32_16x16x4f32, fp32 activations against bf16
-// weights widened in LDS).  RMSNorm, RoPE + cache append, causal attention and
+// bf16 matrix cores (fp32 activations as two bf16 terms against the bf16
+// weights, fp32 sums; see gemm).  RMSNorm, RoPE + cache append, causal attention and
 // SwiGLU are small vector kernels between them, all on the caller's stream.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -83,63 +83,84 @@ __global__ void __launch_bounds__(256) rmsnorm(const float* X, size_t ldx, int H
 
 // C[M][N] (row stride ldc) = or += A[M][K] (stride lda) * W[N][K]^T.
 // 64 x 64 tile per block of 4 waves, each wave a 32 x 32 quarter as 2 x 2
-// MFMA 16x16 tiles; K in steps of 32 staged through LDS.  K, lda and the
-// pointers are multiples of 8 elements (the config guarantees it), so the
-// staging loads are whole float4 / 8 x bf16 vectors, inside or outside K.
-constexpr int TM = 64, TN = 64, TK = 32;
+// C[M][N] (=, or += with accumulate) A[M][K] * W[N][K]^T on the bf16 matrix cores
+// (v_mfma_f32_16x16x32_bf16).  The fp32 activations go in as two bf16 terms,
+// a = hi + lo with hi = bf16(a) and lo = bf16(a - hi) (16 significant bits), so
+// every product with the bf16 weights is exact and the sums are fp32: two
+// MFMAs per step.  Block tile 128 x 128 (four waves of 64 x 64, i.e. 4 x 4
+// MFMA tiles each), K in steps of 32 staged through double-buffered LDS; the
+// next step's global loads are in flight during the current step's MFMAs.
+// K, lda and the pointers are multiples of 8 elements (the config guarantees
+// it), so the staging loads are whole float4 / 8 x bf16 vectors, inside or
+// outside K.  Operand layout (16x16x32): lane l holds A[l % 16][8 (l / 16) + j]
+// and B[8 (l / 16) + j][l % 16], j < 8; the result's lane l holds rows
+// 4 (l / 16) + i of column l % 16, i < 4.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+constexpr int BM = 128, BN = 128, BK = 32, LDK = BK + 8;  // LDS rows of 80 bytes: 16-byte aligned, banks staggered
 __global__ void __launch_bounds__(256) gemm(const float* A, int lda, const uint16_t* W, int K, float* C, int ldc,
                                             int M, int N, int accumulate) {
-    __shared__ float As[TM][TK + 1];
-    __shared__ float Ws[TN][TK + 1];
-    const int m0 = blockIdx.y * TM, n0 = blockIdx.x * TN;
+    __shared__ __attribute__((aligned(16))) __bf16 Ah[2][BM * LDK];
+    __shared__ __attribute__((aligned(16))) __bf16 Al[2][BM * LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t Ws[2][BN * LDK];
+    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
-    f32x4 acc[2][2];
-    for (int i = 0; i < 2; ++i)
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < K; k0 += TK) {
-        // A: 64 rows x 32 floats = 512 float4, two per thread
-        for (int e = tid; e < TM * TK / 4; e += 256) {
-            const int r = e / (TK / 4), c = (e % (TK / 4)) * 4;
-            const int gm = m0 + r, gk = k0 + c;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (gm < M && gk < K) v = *(const float4*)(A + (size_t)gm * lda + gk);
-            As[r][c] = v.x;
-            As[r][c + 1] = v.y;
-            As[r][c + 2] = v.z;
-            As[r][c + 3] = v.w;
+    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+    const int lr = lane & 15, lk = 8 * (lane >> 4);
+    f32x4 acc[4][4];
+    for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // staging: A is 128 rows x 8 float4 (four per thread), W 128 rows x 4 vectors of 8 bf16 (two)
+    float4 ra[4];
+    uint4 rw[2];
+    auto gload = [&](int k0) {
+        for (int i = 0; i < 4; ++i) {
+            const int e = tid + i * 256, r = e >> 3, c = (e & 7) * 4, gm = m0 + r, gk = k0 + c;
+            ra[i] = gm < M && gk < K ? *(const float4*)(A + (size_t)gm * lda + gk) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        // W: 64 rows x 32 bf16 = 256 vectors of 8, one per thread
-        {
-            const int r = tid / (TK / 8), c = (tid % (TK / 8)) * 8;
-            const int gn = n0 + r, gk = k0 + c;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (gn < N && gk < K) v = *(const uint4*)(W + (size_t)gn * K + gk);
-            const uint32_t q[4] = {v.x, v.y, v.z, v.w};
-            for (int i = 0; i < 4; ++i) {
-                Ws[r][c + 2 * i] = __uint_as_float(q[i] << 16);
-                Ws[r][c + 2 * i + 1] = __uint_as_float(q[i] & 0xffff0000u);
+        for (int i = 0; i < 2; ++i) {
+            const int e = tid + i * 256, r = e >> 2, c = (e & 3) * 8, gn = n0 + r, gk = k0 + c;
+            rw[i] = gn < N && gk < K ? *(const uint4*)(W + (size_t)gn * K + gk) : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    auto sstore = [&](int buf) {
+        for (int i = 0; i < 4; ++i) {
+            const int e = tid + i * 256, r = e >> 3, c = (e & 7) * 4;
+            const f32x4v x = {ra[i].x, ra[i].y, ra[i].z, ra[i].w};
+            const bf16x4 hi = __builtin_convertvector(x, bf16x4);  // round to nearest even
+            const bf16x4 lo = __builtin_convertvector(x - __builtin_convertvector(hi, f32x4v), bf16x4);
+            *(bf16x4*)&Ah[buf][r * LDK + c] = hi;
+            *(bf16x4*)&Al[buf][r * LDK + c] = lo;
+        }
+        for (int i = 0; i < 2; ++i) {
+            const int e = tid + i * 256, r = e >> 2, c = (e & 3) * 8;
+            *(uint4*)&Ws[buf][r * LDK + c] = rw[i];
+        }
+    };
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int k0 = 0, buf = 0; k0 < K; k0 += BK, buf ^= 1) {
+        const bool more = k0 + BK < K;
+        if (more) gload(k0 + BK);
+        bf16x8 b[4];
+        for (int tj = 0; tj < 4; ++tj) b[tj] = *(const bf16x8*)&Ws[buf][(wn + tj * 16 + lr) * LDK + lk];
+        for (int ti = 0; ti < 4; ++ti) {
+            const bf16x8 ah = *(const bf16x8*)&Ah[buf][(wm + ti * 16 + lr) * LDK + lk];
+            const bf16x8 al = *(const bf16x8*)&Al[buf][(wm + ti * 16 + lr) * LDK + lk];
+            for (int tj = 0; tj < 4; ++tj) {
+                acc[ti][tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b[tj], acc[ti][tj], 0, 0, 0);
+                acc[ti][tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b[tj], acc[ti][tj], 0, 0, 0);
             }
         }
-        __syncthreads();
-        // 16x16x4 operands: lane l holds A[row l % 16][k l / 16] and
-        // B[k l / 16][col l % 16]; the result's lane l holds rows 4 (l / 16) + j
-        // of column l % 16
-        for (int kk = 0; kk < TK; kk += 4) {
-            const int kr = kk + (lane >> 4);
-            const float a0 = As[wm + (lane & 15)][kr], a1 = As[wm + 16 + (lane & 15)][kr];
-            const float b0 = Ws[wn + (lane & 15)][kr], b1 = Ws[wn + 16 + (lane & 15)][kr];
-            acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc[0][0], 0, 0, 0);
-            acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc[0][1], 0, 0, 0);
-            acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b0, acc[1][0], 0, 0, 0);
-            acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc[1][1], 0, 0, 0);
-        }
+        if (more) sstore(buf ^ 1);  // the other buffer was last read before the previous barrier
         __syncthreads();
     }
-    for (int ti = 0; ti < 2; ++ti)
-        for (int tj = 0; tj < 2; ++tj)
+    for (int ti = 0; ti < 4; ++ti)
+        for (int tj = 0; tj < 4; ++tj)
             for (int j = 0; j < 4; ++j) {
-                const int r = m0 + wm + ti * 16 + 4 * (lane >> 4) + j, c = n0 + wn + tj * 16 + (lane & 15);
+                const int r = m0 + wm + ti * 16 + 4 * (lane >> 4) + j, c = n0 + wn + tj * 16 + lr;
                 if (r < M && c < N) {
                     float* p = C + (size_t)r * ldc + c;
                     *p = accumulate ? *p + acc[ti][tj][j] : acc[ti][tj][j];
@@ -242,7 +263,7 @@ __global__ void __launch_bounds__(256) swiglu(float* G, const float* U, size_t n
 
 void run_gemm(const float* A, int lda, const uint16_t* W, int K, float* C, int ldc, int M, int N, int acc,
               hipStream_t s) {
-    const dim3 grid((unsigned)((N + TN - 1) / TN), (unsigned)((M + TM - 1) / TM));
+    const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
     hipLaunchKernelGGL(gemm, grid, dim3(256), 0, s, A, lda, W, K, C, ldc, M, N, acc);
 }
 
