@@ -9,8 +9,9 @@
 // Rows are (batch row, position) pairs, so every projection is a dense
 // contraction C[M][N] = A[M][K] * W[N][K]^T with M = B * P: those run on the
 // bf16 matrix cores (fp32 activations as two bf16 terms against the bf16
-// weights, fp32 sums; see gemm).  RMSNorm, RoPE + cache append, causal attention and
-// SwiGLU are small vector kernels between them, all on the caller's stream.
+// weights, fp32 sums; see gemm).  Causal attention is a tiled online-softmax
+// kernel on the same matrix cores; RMSNorm, RoPE + cache append and SwiGLU are
+// small vector kernels between them; all on the caller's stream.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <algorithm>
@@ -194,63 +195,115 @@ __global__ void __launch_bounds__(256) rope_kv(float* QKV, int ld, int B, int t0
     }
 }
 
-// Causal attention of query (row m of the chunk, head h) over cache slots
-// 0 .. t of its KV group (earlier chunks' slots were written by their passes): one wave each, keys in blocks of 64 (lane j scores key j of the
-// block), online softmax across blocks, lane d accumulating output dims
-// d, d + 64.  O[m][h * D + d] = sum_j softmax(q . k_j / sqrt(D))_j v_j[d].
+// Causal attention of every query of the chunk (row m, head h at position t) over cache slots
+// 0 .. t of its KV group (earlier chunks' slots were written by their passes), in the tiled
+// online-softmax form on the bf16 matrix cores:
+//   O[m][h D + d] = sum_j softmax_j(q . k_j / sqrt(D)) v_j[d].
+// A block takes 64 queries of one head (a wave per 16) and walks the keys in tiles of 32,
+// staged in LDS (K as rows, V transposed).  Per tile a wave computes S^T = K Q^T (q in two
+// bf16 terms, K exact in bf16: lane l ends with keys 4 (l/16) + i and 16 + 4 (l/16) + i of
+// query l % 16), updates the running max and sum of its query, and adds V^T P^T to O^T with
+// those eight probabilities (two bf16 terms) as the B operand: the contraction's key order is
+// permuted the same way in both operands, which leaves the sum unchanged.  The products are
+// exact and every sum is fp32, as in the per-position form.
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 template <int D>
 __global__ void __launch_bounds__(256) attention(const float* QKV, int ld, const uint16_t* kv, int B, int t0, int Pc,
                                                  int Hq, int Hkv, int layer, int max_seq, float* O, int ldo) {
-    constexpr int NC = D / 64;
-    __shared__ float qs[4][D];
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int wid = blockIdx.x * 4 + w;
-    if (wid >= B * Pc * Hq) return;  // the whole wave leaves; no block barrier follows
-    const int head = wid % Hq, m = wid / Hq, b = m / Pc, t = t0 + m % Pc, g = head / (Hq / Hkv);
-    const float* q = QKV + (size_t)m * ld + (size_t)head * D;
-    for (int d = lane; d < D; d += 64) qs[w][d] = q[d];
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    constexpr int KT = 32, KS = D / 32, DT = D / 16, LDKS = D + 8, LDV = KT + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * LDKS];
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * LDV];
+    const int head = blockIdx.y, b = blockIdx.z, g = head / (Hq / Hkv);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lq = lane & 15, lg = lane >> 4;
+    const int qb0 = blockIdx.x * 64;             // the block's first query (row of the chunk)
+    const int qi = qb0 + wave * 16 + lq;         // this lane's query
+    const bool qvalid = qi < Pc;
+    const int qr = qvalid ? qi : Pc - 1;         // rows past the chunk repeat its last (not written)
+    const int t = t0 + qr;                       // its position
+    const int t_blk = t0 + min(qb0 + 63, Pc - 1), t_wave = t0 + min(qb0 + wave * 16 + 15, Pc - 1);
+    // q of this lane's query, dims ks * 32 + 8 (l / 16) + j: the B operand of S^T = K Q^T
+    const float* qrow = QKV + (size_t)(b * Pc + qr) * ld + (size_t)head * D;
+    bf16x8 qh[KS], ql[KS];
+    for (int ks = 0; ks < KS; ++ks) {
+        const float4 u = *(const float4*)(qrow + ks * 32 + 8 * lg), w = *(const float4*)(qrow + ks * 32 + 8 * lg + 4);
+        const f32x8 x = {u.x, u.y, u.z, u.w, w.x, w.y, w.z, w.w};
+        qh[ks] = __builtin_convertvector(x, bf16x8);
+        ql[ks] = __builtin_convertvector(x - __builtin_convertvector(qh[ks], f32x8), bf16x8);
+    }
     const uint16_t* Kb = kv + ((((size_t)layer * 2 + 0) * B + b) * Hkv + g) * (size_t)max_seq * D;
     const uint16_t* Vb = kv + ((((size_t)layer * 2 + 1) * B + b) * Hkv + g) * (size_t)max_seq * D;
-    const float scale = rsqrtf((float)D);
-    float mx = -__builtin_inff(), l = 0.f, o[NC];
-    for (int c = 0; c < NC; ++c) o[c] = 0.f;
-    for (int j0 = 0; j0 <= t; j0 += 64) {
-        const int j = j0 + lane;
-        float s = -__builtin_inff();
-        if (j <= t) {
-            const uint4* kr = (const uint4*)(Kb + (size_t)j * D);
-            float acc = 0.f;
-            for (int u = 0; u < D / 8; ++u) {
-                const uint4 v = kr[u];
-                const float* qq = &qs[w][u * 8];
-                acc = fmaf(__uint_as_float(v.x << 16), qq[0], acc);
-                acc = fmaf(__uint_as_float(v.x & 0xffff0000u), qq[1], acc);
-                acc = fmaf(__uint_as_float(v.y << 16), qq[2], acc);
-                acc = fmaf(__uint_as_float(v.y & 0xffff0000u), qq[3], acc);
-                acc = fmaf(__uint_as_float(v.z << 16), qq[4], acc);
-                acc = fmaf(__uint_as_float(v.z & 0xffff0000u), qq[5], acc);
-                acc = fmaf(__uint_as_float(v.w << 16), qq[6], acc);
-                acc = fmaf(__uint_as_float(v.w & 0xffff0000u), qq[7], acc);
+    const float scale = rsqrtf((float)D), ninf = -__builtin_inff();
+    f32x4 o[DT];
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = ninf, lsum = 0.f;
+    for (int j0 = 0; j0 <= t_blk; j0 += KT) {
+        __syncthreads();  // every wave is done with the previous tile
+        for (int e = threadIdx.x; e < KT * D / 8; e += 256) {
+            const int r = e / (D / 8), c = (e % (D / 8)) * 8, j = j0 + r;
+            uint4 kk = make_uint4(0u, 0u, 0u, 0u), vv = make_uint4(0u, 0u, 0u, 0u);
+            if (j <= t_blk) {
+                kk = *(const uint4*)(Kb + (size_t)j * D + c);
+                vv = *(const uint4*)(Vb + (size_t)j * D + c);
             }
-            s = acc * scale;
+            *(uint4*)&Ks[r * LDKS + c] = kk;
+            const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+            for (int k = 0; k < 4; ++k) {
+                Vt[(c + 2 * k) * LDV + r] = (uint16_t)(vw[k] & 0xffffu);
+                Vt[(c + 2 * k + 1) * LDV + r] = (uint16_t)(vw[k] >> 16);
+            }
         }
-        const float nm = fmaxf(mx, wmax(s));  // lane 0's key j0 <= t, so nm is finite
-        const float p = j <= t ? __expf(s - nm) : 0.f;
-        const float corr = __expf(mx - nm);
-        l = l * corr + wsum(p);
-        for (int c = 0; c < NC; ++c) o[c] *= corr;
-        const int nk = t - j0 + 1 < 64 ? t - j0 + 1 : 64;
-        for (int jj = 0; jj < nk; ++jj) {
-            const float pj = __shfl(p, jj);
-            const uint16_t* vr = Vb + (size_t)(j0 + jj) * D;
-            for (int c = 0; c < NC; ++c) o[c] = fmaf(pj, bf(vr[lane + 64 * c]), o[c]);
+        __syncthreads();
+        if (j0 > t_wave) continue;  // every query of this wave precedes the tile
+        f32x4 st[2];
+        for (int kt = 0; kt < 2; ++kt) {
+            st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 a = *(const bf16x8*)&Ks[(kt * 16 + lq) * LDKS + ks * 32 + 8 * lg];
+                st[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[ks], st[kt], 0, 0, 0);
+                st[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[ks], st[kt], 0, 0, 0);
+            }
         }
-        mx = nm;
+        // lane l: query l % 16, keys j0 + kt 16 + 4 (l / 16) + i
+        float sc[8], mx = m;
+        for (int kt = 0; kt < 2; ++kt)
+            for (int i = 0; i < 4; ++i) {
+                const int j = j0 + kt * 16 + 4 * lg + i;
+                const float v = j <= t ? st[kt][i] * scale : ninf;
+                sc[kt * 4 + i] = v;
+                mx = fmaxf(mx, v);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));  // finite: key 0 of the first tile precedes every query
+        const float corr = __expf(m - mx);
+        float ps = 0.f;
+        f32x8 pv;
+        for (int k = 0; k < 8; ++k) {
+            pv[k] = __expf(sc[k] - mx);
+            ps += pv[k];
+        }
+        ps += __shfl_xor(ps, 16);
+        ps += __shfl_xor(ps, 32);
+        lsum = lsum * corr + ps;
+        m = mx;
+        const bf16x8 ph = __builtin_convertvector(pv, bf16x8);
+        const bf16x8 pl = __builtin_convertvector(pv - __builtin_convertvector(ph, f32x8), bf16x8);
+        for (int dt = 0; dt < DT; ++dt) {
+            o[dt] *= corr;
+            // V^T rows dt 16 + l % 16, keys 4 (l / 16) .. +3 and 16 + 4 (l / 16) .. +3
+            const uint16_t* vr = &Vt[(dt * 16 + lq) * LDV];
+            const uint2 v0 = *(const uint2*)(vr + 4 * lg), v1 = *(const uint2*)(vr + 16 + 4 * lg);
+            const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ph, o[dt], 0, 0, 0);
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl, o[dt], 0, 0, 0);
+        }
     }
-    const float inv = 1.0f / l;
-    for (int c = 0; c < NC; ++c) O[(size_t)m * ldo + (size_t)head * D + lane + 64 * c] = o[c] * inv;
+    // lane l holds O^T[dt 16 + 4 (l / 16) + i][query l % 16]
+    if (qvalid) {
+        const float inv = 1.0f / lsum;
+        float* out = O + (size_t)(b * Pc + qi) * ldo + (size_t)head * D;
+        for (int dt = 0; dt < DT; ++dt)
+            for (int i = 0; i < 4; ++i) out[dt * 16 + 4 * lg + i] = o[dt][i] * inv;
+    }
 }
 
 // G[i] = silu(G[i]) * U[i]
@@ -287,13 +340,13 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
             run_gemm(a.A, H, bf16(a.wv[l]), H, a.QKV + QD + KD, NQKV, M, KD, 0, s);
             hipLaunchKernelGGL(rope_kv, dim3(M), dim3(256), 0, s, a.QKV, NQKV, B, t0, Pc, a.Hq, a.Hkv, D, a.rope, a.kv,
                                l, a.max_seq);
-            const unsigned nat = (unsigned)(((size_t)M * a.Hq + 3) / 4);
+            const dim3 agrid((unsigned)((Pc + 63) / 64), (unsigned)a.Hq, (unsigned)B);
             if (D == 64)
-                hipLaunchKernelGGL(attention<64>, dim3(nat), dim3(256), 0, s, a.QKV, NQKV, a.kv, B, t0, Pc, a.Hq, a.Hkv,
-                                   l, a.max_seq, a.O, QD);
+                hipLaunchKernelGGL(attention<64>, agrid, dim3(256), 0, s, a.QKV, NQKV, a.kv, B, t0, Pc, a.Hq, a.Hkv, l,
+                                   a.max_seq, a.O, QD);
             else
-                hipLaunchKernelGGL(attention<128>, dim3(nat), dim3(256), 0, s, a.QKV, NQKV, a.kv, B, t0, Pc, a.Hq,
-                                   a.Hkv, l, a.max_seq, a.O, QD);
+                hipLaunchKernelGGL(attention<128>, agrid, dim3(256), 0, s, a.QKV, NQKV, a.kv, B, t0, Pc, a.Hq, a.Hkv,
+                                   l, a.max_seq, a.O, QD);
             run_gemm(a.O, QD, bf16(a.wo[l]), QD, a.X, H, M, H, 1, s);  // h += W_o attn
             hipLaunchKernelGGL(rmsnorm, dim3(M), dim3(256), 0, s, a.X, (size_t)H, H, bf16(a.mlp_norm[l]), a.eps, a.A,
                                (size_t)H);
