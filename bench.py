@@ -465,10 +465,10 @@ def main():
         log(f"single-launch step not capturable: {e}")
     graph_empty = graph_us(mk.MK_GRAPH_EMPTY, 20)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    mk.mk_empty_launches(n_launch, ncu, 768, stream)
+    mk.mk_empty_launches(n_launch, ncu, mk.MK_STEP_THREADS, stream)
     e0.record(cur)
     for _ in range(20):
-        mk.mk_empty_launches(n_launch, ncu, 768, stream)
+        mk.mk_empty_launches(n_launch, ncu, mk.MK_STEP_THREADS, stream)
     e1.record(cur)
     torch.cuda.synchronize()
     eager_empty = e0.elapsed_time(e1) * 1e3 / 20
@@ -534,7 +534,7 @@ def main():
         "graph": {"megakernel_us_per_step": graph_mega, "per_op_us_per_step": graph_mk,
                   "note": "one replay = one step: the per-op launches + the argmax launch, or the single fused "
                           "launch; captured once, replayed back to back"},
-        "launch_overhead": {"launches": n_launch, "blocks": ncu, "threads": 768, "eager_empty_us": eager_empty,
+        "launch_overhead": {"launches": n_launch, "blocks": ncu, "threads": mk.MK_STEP_THREADS, "eager_empty_us": eager_empty,
                             "graph_empty_us": graph_empty},
         "kernel_source_hash": kernel_source_hash(),
     }

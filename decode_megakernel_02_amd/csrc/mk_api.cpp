@@ -13,6 +13,8 @@
 #include "mk_internal.h"
 #include "mk_plan.h"
 
+static_assert(MK_STEP_THREADS == mk::WG_THREADS, "public workgroup size matches the kernels");
+
 namespace mk {
 hipError_t launch_step(const Params* dev_params, int head_dim, int ncu, size_t lds_bytes, const int32_t* tokens,
                        const int32_t* positions, void* kv, float* logits, int stage, uint32_t flags,

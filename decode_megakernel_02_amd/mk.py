@@ -64,6 +64,7 @@ MK_FLAG_FP8_WEIGHTS = 4
 MK_GRAPH_MULTIKERNEL = 1
 MK_GRAPH_EMPTY = 2
 MK_GRAPH_FUSED_GREEDY = 4
+MK_STEP_THREADS = 640  # threads per workgroup of the step kernels (include/mk.h)
 TRACE_SLOTS = 52
 PROF_WAVES = 10  # 8 compute waves, the loader and the gather wave per workgroup
 PROF_SLOTS = 8

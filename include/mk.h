@@ -66,6 +66,10 @@ typedef struct {
     uint32_t flags;          /* MK_FLAG_* */
 } mk_config;
 
+/* Threads per workgroup of the step kernels (one workgroup per CU): 8 compute
+ * waves, 1 weight-loader wave, 1 gather wave.                             */
+#define MK_STEP_THREADS 640
+
 #define MK_FLAG_NONE 0u
 #define MK_FLAG_PROFILE 1u  /* per-wave cycle counters, read with mk_get_profile */
 #define MK_FLAG_TRACE 2u    /* per-instruction timeline, read with mk_get_trace */

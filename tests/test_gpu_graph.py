@@ -92,7 +92,7 @@ def test_empty_launch_graph_and_eager_empty_launches_touch_nothing():
         for _ in range(3):
             mk.mk_graph_launch(g, s)
         ncu = torch.cuda.get_device_properties(0).multi_processor_count
-        mk.mk_empty_launches(97, ncu, 768, s)
+        mk.mk_empty_launches(97, ncu, mk.MK_STEP_THREADS, s)
         torch.cuda.synchronize()
         assert torch.all(dec.logits == 3.0) and torch.all(dec.tokens == 5) and torch.all(dec.positions == 7)
         assert torch.all(dec.kv == 0)
