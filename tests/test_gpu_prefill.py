@@ -131,3 +131,47 @@ def test_full_llama1b_p1024(llama1b):
     ref = orc.decode_step(cache, prompts[:, P - 1].astype(np.int32), np.full(B, P - 1, dtype=np.int32), 16)
     stats = H.compare(H.Run([prompts[:, -1]], [np.full(B, P - 1)], [pf_logits]), [ref], "1B P1024 prefill")
     print("1B P1024 prefill: vs decode max|d|", d, "vs oracle", stats, flush=True)
+
+
+@pytest.mark.timeout(600)
+def test_full_llama1b_p8192(llama1b):
+    """The long-prompt benchmark shape (full 1B, one 8192-token prompt: 128 query blocks and up
+    to 256 key tiles per head in the prefill's attention, the chunked pass when the workspace
+    cap applies): logits and cache against the decode step run token by token on the GPU, and the
+    last-position logits against one oracle step on the prefilled cache."""
+    import torch
+    import oracle
+    from decode_megakernel_02_amd import mk
+    shape, weights = llama1b
+    B, P = 1, 8192
+    max_seq = P + 2
+    prompts = synth.make_prompts(shape.vocab, B, P)
+    dec = H.GpuDecoder(shape, weights, B, max_seq)
+    try:
+        toks = torch.as_tensor(np.ascontiguousarray(prompts, dtype=np.int32)).cuda()
+        mk.mk_prefill(dec.h, dec.dw, toks, P, dec.kv, dec.logits, mk.current_stream())
+        torch.cuda.synchronize()
+        pf_logits = dec.logits.cpu().numpy().copy()
+        pf_kv = dec.kv_host().copy()
+        dec.kv.zero_()
+        s = mk.current_stream()
+        dtok = torch.as_tensor(np.ascontiguousarray(prompts[0], dtype=np.int32)).cuda()  # B = 1
+        dpos = torch.arange(P, dtype=torch.int32, device="cuda")
+        for t in range(P):  # the decode step, token by token, with no host round trip per step
+            mk.mk_decode_step(dec.h, dtok[t:t + 1], dpos[t:t + 1], dec.kv, dec.logits, s)
+        torch.cuda.synchronize()
+        assert mk.mk_get_device_error(dec.h) is None
+        lg = dec.logits.cpu().numpy().copy()
+        dk_kv = dec.kv_host().copy()
+    finally:
+        dec.close()
+    d = float(np.max(np.abs(pf_logits - lg)))
+    assert d <= 1e-2, f"prefill vs token-by-token decode: max|d| {d}"
+    g, o = bf16_to_f32(pf_kv[..., :P, :]), bf16_to_f32(dk_kv[..., :P, :])
+    assert float(np.max(np.abs(g - o))) <= 2e-2 * max(1.0, float(np.max(np.abs(o))))
+    assert float(np.mean(pf_kv[..., :P, :] == dk_kv[..., :P, :])) > 0.8
+    orc = oracle.Oracle(shape, weights, B, max_seq)
+    cache = pf_kv.copy()
+    ref = orc.decode_step(cache, prompts[:, P - 1].astype(np.int32), np.full(B, P - 1, dtype=np.int32), 16)
+    stats = H.compare(H.Run([prompts[:, -1]], [np.full(B, P - 1)], [pf_logits]), [ref], "1B P8192 prefill")
+    print("1B P8192 prefill: vs decode max|d|", d, "vs oracle", stats, flush=True)
