@@ -22,6 +22,8 @@ hipError_t launch_step(const Params* dev_params, int head_dim, int ncu, size_t l
 hipError_t set_step_kernel_lds(size_t lds_bytes);
 hipError_t launch_pack(const void* rows, uint32_t n, const uint16_t* const* mats, uint8_t* dst, int fp8,
                        const float* scales, hipStream_t stream);
+hipError_t launch_poison(uint64_t* arena, size_t words, float* f0, size_t n0, float* f1, size_t n1,
+                         hipStream_t stream);
 hipError_t launch_row_amax(const uint16_t* w, uint32_t rows, uint32_t cols, uint16_t* out, hipStream_t stream);
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int ncu, hipStream_t stream);
 hipError_t launch_empty(int n_blocks, int n_threads, hipStream_t stream);
@@ -47,6 +49,8 @@ struct mk_handle {
     uint64_t* greedy_part = nullptr;  // [B][GREEDY_BLOCKS] per-slice (value, index) pairs
     uint32_t* greedy_cnt = nullptr;   // [B] finished slices of the current call (zero between calls)
     uint32_t ablate = 0;              // mk_set_ablation: opcode switched off in mk_decode_step (0: none)
+    uint64_t* arena = nullptr;        // the tagged activation words (the debug NaN fill)
+    size_t arena_words = 0;
     uint16_t* row_amax = nullptr;     // FP8: [rows of all matrices] largest |w| per row (bf16 bits)
     float* row_scale = nullptr;       // FP8: [rows of all matrices] scale of each row (pack input)
     void* prefill_ws = nullptr;       // mk_prefill's workspace, kept between calls
@@ -247,6 +251,7 @@ int mk_create(const mk_config* cfg, mk_handle** out) {
             return fail(nullptr, MK_ERR_UNSUPPORTED_SHAPE, "batch x hidden too large for the LDS budget");
         }
         h->lds_bytes = (size_t)NW * ring_units * UNIT_BYTES + nslot * (xb + side_bytes) + sync_bytes + keep_bytes;
+        h->hp.lds_bytes = (uint32_t)h->lds_bytes;
 
         Params& hp = h->hp;
         hp.L = p.L; hp.H = p.H; hp.Hq = p.Hq; hp.Hkv = p.Hkv; hp.D = p.D; hp.F = p.F; hp.V = p.V; hp.B = p.B;
@@ -302,6 +307,8 @@ int mk_create(const mk_config* cfg, mk_handle** out) {
         const size_t words = n_qkv + n_part + n_attn + 2 * n_h + n_act;
         uint64_t* arena = dalloc<uint64_t>(h, words);
         HIPCHK(hipMemset(arena, 0, words * 8));
+        h->arena = arena;
+        h->arena_words = words;
         uint64_t* cur = arena;
         hp.qkv = cur; cur += n_qkv;
         hp.part = cur; cur += n_part;
@@ -444,15 +451,25 @@ static int step_args_ok(mk_handle* h, const int32_t* tokens, const int32_t* posi
 
 // handles created with profiling or tracing run the instrumented kernel build, FP8 handles the FP8 one
 static uint32_t instr_flag(const mk_handle* h) {
-    return ((h->hp.prof || h->hp.trace) ? KF_INSTRUMENTED : 0u) | (h->hp.fp8 ? KF_FP8 : 0u);
+    return ((h->hp.prof || h->hp.trace) ? KF_INSTRUMENTED : 0u) | (h->hp.fp8 ? KF_FP8 : 0u) |
+           ((h->cfg.flags & MK_FLAG_DEBUG_NAN) ? KF_POISON : 0u);
+}
+
+// MK_FLAG_DEBUG_NAN: NaN into the step's scratch before its first launch
+static hipError_t poison_before_step(mk_handle* h, float* logits, hipStream_t s) {
+    if (!(h->cfg.flags & MK_FLAG_DEBUG_NAN)) return hipSuccess;
+    return launch_poison(h->arena, h->arena_words, h->hp.dacc, (size_t)h->hp.B * h->hp.H, logits,
+                         (size_t)h->hp.B * h->hp.V, s);
 }
 
 int mk_decode_step(mk_handle* h, const int32_t* tokens, const int32_t* positions, void* kv_cache, float* logits,
                    void* stream) {
     int rc = step_args_ok(h, tokens, positions, kv_cache, logits);
     if (rc != MK_OK) return rc;
-    hipError_t e = launch_step(h->dparams, h->hp.D, h->hp.ncu, h->lds_bytes, tokens, positions, kv_cache, logits, -1,
-                               KF_BUMP_EPOCH | instr_flag(h) | (h->ablate ? KF_ABLATE : 0u), (hipStream_t)stream);
+    hipError_t e = poison_before_step(h, logits, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(h, HipError{e, "mk_poison_kernel launch"});
+    e = launch_step(h->dparams, h->hp.D, h->hp.ncu, h->lds_bytes, tokens, positions, kv_cache, logits, -1,
+                    KF_BUMP_EPOCH | instr_flag(h) | (h->ablate ? KF_ABLATE : 0u), (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(h, HipError{e, "mk_step_kernel launch"});
     return MK_OK;
 }
@@ -464,7 +481,9 @@ int mk_decode_step_greedy(mk_handle* h, int32_t* tokens, int32_t* positions, voi
     if (h->ablate) return fail(h, MK_ERR_STATE, "an ablation is set: use mk_decode_step");
     if (instr_flag(h) & KF_INSTRUMENTED)
         return fail(h, MK_ERR_STATE, "the fused greedy step has no profiling or tracing build");
-    hipError_t e = launch_step(h->dparams, h->hp.D, h->hp.ncu, h->lds_bytes, tokens, positions, kv_cache, logits, -1,
+    hipError_t e = poison_before_step(h, logits, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(h, HipError{e, "mk_poison_kernel launch"});
+    e = launch_step(h->dparams, h->hp.D, h->hp.ncu, h->lds_bytes, tokens, positions, kv_cache, logits, -1,
                                KF_BUMP_EPOCH | KF_GREEDY | instr_flag(h), (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(h, HipError{e, "mk_step_kernel launch (fused greedy)"});
     return MK_OK;
@@ -475,6 +494,8 @@ int mk_decode_step_multikernel(mk_handle* h, const int32_t* tokens, const int32_
     int rc = step_args_ok(h, tokens, positions, kv_cache, logits);
     if (rc != MK_OK) return rc;
     const int ns = h->hp.n_stages;
+    hipError_t e0 = poison_before_step(h, logits, (hipStream_t)stream);
+    if (e0 != hipSuccess) return hip_fail(h, HipError{e0, "mk_poison_kernel launch"});
     for (int st = 0; st < ns; ++st) {
         hipError_t e = launch_step(h->dparams, h->hp.D, h->hp.ncu, h->lds_bytes, tokens, positions, kv_cache, logits, st,
                                    (st == ns - 1 ? KF_BUMP_EPOCH : 0u) | instr_flag(h), (hipStream_t)stream);
@@ -618,6 +639,10 @@ int mk_graph_create(mk_handle* h, int32_t* tokens, int32_t* positions, void* kv_
         const int ns = h->hp.n_stages;
         HipError first{hipSuccess, ""};
         for (int i = 0; i < n_steps && first.e == hipSuccess; ++i) {
+            if (!(flags & MK_GRAPH_EMPTY)) {
+                first = HipError{poison_before_step(h, logits, cs), "mk_poison_kernel launch"};
+                if (first.e != hipSuccess) break;
+            }
             if (flags & MK_GRAPH_EMPTY) {
                 for (int st = 0; st < ns && first.e == hipSuccess; ++st)
                     first = HipError{launch_empty(h->hp.ncu, WG_THREADS, cs), "mk_empty_kernel launch"};

@@ -87,6 +87,7 @@ struct Params {
     float inv_sqrt_d;
     uint32_t spin_limit;    // bounded waits (watchdog)
     uint32_t ablate_op;     // ablation build: the opcode whose arithmetic is skipped (0: none)
+    uint32_t lds_bytes;     // dynamic LDS of the step kernels (the NaN fill of the debug mode)
     int32_t chunk_begin[17];// down-proj chunk boundaries in [0, F], n_chunk + 1 entries
 
     // packed weights: per (cu, wave) stream of units
@@ -142,6 +143,7 @@ constexpr uint32_t KF_INSTRUMENTED = 2u;  // run the kernel build that records p
 constexpr uint32_t KF_FP8 = 4u;           // run the kernel build for FP8 weights
 constexpr uint32_t KF_GREEDY = 8u;        // single launch only: the build that also takes the argmax
 constexpr uint32_t KF_ABLATE = 16u;       // single launch only: the build that can skip one opcode's math
+constexpr uint32_t KF_POISON = 32u;       // debugging: fill the workgroup's LDS with NaN at launch
 constexpr int PROF_SLOTS = 8;          // counters per wave
 // Timeline record per instruction (100 MHz real-time clock): [0] op | layer << 8 |
 // a << 16 | b << 32 | cu << 48, then per compute wave w at [1 + 6w]: start,

@@ -1758,6 +1758,10 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
         pc0 = p.stage_pc[(size_t)cx.cu * (p.n_stages + 1) + stage];
         pc1 = p.stage_pc[(size_t)cx.cu * (p.n_stages + 1) + stage + 1];
     }
+    if (flags & KF_POISON) {  // debugging: every LDS word NaN until something writes it
+        for (uint32_t i = threadIdx.x; i < p.lds_bytes / 4; i += WG_THREADS) ((LDS uint32_t*)smem)[i] = 0xffffffffu;
+        __syncthreads();
+    }
     if (threadIdx.x < SYNC_WORDS) s.landed[threadIdx.x] = 0;
     __syncthreads();
 
@@ -1855,6 +1859,25 @@ __global__ void __launch_bounds__(WG_THREADS, 1)
 mk_stage_kernel(const Params* __restrict__ pp, const int32_t* tokens, const int32_t* positions, uint16_t* kv,
                 float* logits, int stage, uint32_t flags) {
     step_body<HEAD_DIM, INSTR, FP8, false, false>(pp, tokens, positions, kv, logits, stage, flags);
+}
+
+// ----------------------------------------------------------- debug fill --
+
+// The NaN fill of MK_FLAG_DEBUG_NAN before a step: the value half of every tagged word (its tag,
+// a previous step's, stays), the down-projection accumulators and the logits.
+__global__ void __launch_bounds__(256) mk_poison_kernel(uint64_t* arena, size_t words, float* f0, size_t n0,
+                                                        float* f1, size_t n1) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += stride)
+        arena[i] = (arena[i] & 0xffffffff00000000ull) | 0xffffffffull;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n0; i += stride) f0[i] = __int_as_float(-1);
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n1; i += stride) f1[i] = __int_as_float(-1);
+}
+
+hipError_t launch_poison(uint64_t* arena, size_t words, float* f0, size_t n0, float* f1, size_t n1,
+                         hipStream_t stream) {
+    hipLaunchKernelGGL(mk_poison_kernel, dim3(1024), dim3(256), 0, stream, arena, words, f0, n0, f1, n1);
+    return hipGetLastError();
 }
 
 // ------------------------------------------------------------ pack kernel --

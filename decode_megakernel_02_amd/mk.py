@@ -61,6 +61,7 @@ EXPORTS = ["mk_create", "mk_load_weights", "mk_kv_cache_bytes", "mk_decode_step"
 MK_FLAG_PROFILE = 1
 MK_FLAG_TRACE = 2
 MK_FLAG_FP8_WEIGHTS = 4
+MK_FLAG_DEBUG_NAN = 8
 MK_GRAPH_MULTIKERNEL = 1
 MK_GRAPH_EMPTY = 2
 MK_GRAPH_FUSED_GREEDY = 4

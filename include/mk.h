@@ -79,6 +79,14 @@ typedef struct {
                                   fp32(w / scale), ties to even), half the bytes of bf16 plus 4
                                   bytes per row; the embedding lookup stays bf16.  Not
                                   combinable with MK_FLAG_PROFILE / MK_FLAG_TRACE. */
+#define MK_FLAG_DEBUG_NAN 8u   /* debugging: before every step (mk_decode_step, _greedy,
+                                  _multikernel, graph replays) the library overwrites the values
+                                  of the step's activation scratch with NaN (the tagged words keep
+                                  their previous step's tags, so waits are unchanged), the
+                                  down-projection accumulators and the logits, and each
+                                  workgroup fills its LDS with NaN at launch: a read of any of
+                                  them before its write shows up as NaN logits.  One extra
+                                  launch per step.                                         */
 
 /* Per-layer weight pointers: arrays of n_layers DEVICE pointers held in HOST
  * memory.  Every tensor is bf16, row-major in the nn.Linear layout [out][in]:
