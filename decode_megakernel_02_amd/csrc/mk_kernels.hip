@@ -1401,40 +1401,61 @@ __device__ __forceinline__ float bf_elem(const uint4 (&r)[8], int i) {
 // Wave64 reduce-scatter of e * row[d] (d < 64) by recursive halving: afterwards
 // lane d holds the sum over lanes of e * row[d].  The first halving step is
 // fused with the products so at most 32 values are live; 63 lane exchanges.
+// One butterfly stage across lanes L and its partner L ^ stride: a lane whose stride bit is clear
+// keeps the lower-destined value a plus its partner's a, the other keeps b plus the partner's
+// b.  The exchanges are VALU lane permutations (gfx950's permlane swaps for strides 32 and 16,
+// DPP within rows of 16 lanes below), not trips through the LDS crossbar.
+template <int STRIDE>
+__device__ __forceinline__ float bfly(float a, float b, int lane) {
+    if constexpr (STRIDE == 32 || STRIDE == 16) {
+        // swap(a, b) leaves lane L with (a of L, a of L + stride) when the bit is clear and
+        // (b of L - stride, b of L) when it is set
+        const auto r = STRIDE == 32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false)
+                                    : __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    } else {
+        const bool upper = (lane & STRIDE) != 0;
+        const int x = __float_as_int(upper ? a : b);  // what the partner needs
+        int y;
+        if constexpr (STRIDE == 8) {
+            y = __builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false);  // row_ror:8 = lane ^ 8
+        } else if constexpr (STRIDE == 4) {
+            const int up = __builtin_amdgcn_update_dpp(0, x, 0x12C, 0xF, 0xF, false);  // from lane + 4
+            const int dn = __builtin_amdgcn_update_dpp(0, x, 0x124, 0xF, 0xF, false);  // from lane - 4
+            y = upper ? dn : up;
+        } else if constexpr (STRIDE == 2) {
+            y = __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+        } else {
+            y = __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+        }
+        return (upper ? b : a) + __int_as_float(y);
+    }
+}
+
 __device__ __forceinline__ float pv_reduce_scatter64(const uint4 (&row)[8], float e, int lane) {
     float v[32];
-    {
-        const bool upper = (lane & 32) != 0;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-            for (int i = h * 16; i < h * 16 + 16; ++i) {
-                const float a = e * bf_elem(row, i), b = e * bf_elem(row, i + 32);
-                v[i] = (upper ? b : a) + __shfl_xor(upper ? a : b, 32);
-            }
-            CBAR();
-        }
+        for (int i = h * 16; i < h * 16 + 16; ++i) v[i] = bfly<32>(e * bf_elem(row, i), e * bf_elem(row, i + 32), lane);
+        CBAR();
     }
 #pragma unroll
-    for (int d = 16, m = 32; d >= 1; d >>= 1, m >>= 1) {
-        const bool upper = (lane & d) != 0;
+    for (int i = 0; i < 16; ++i) v[i] = bfly<16>(v[i], v[i + 16], lane);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            if (i < m / 2) {
-                const float a = v[i], b = v[i + m / 2];
-                v[i] = (upper ? b : a) + __shfl_xor(upper ? a : b, d);
-            }
-        }
-    }
-    return v[0];
+    for (int i = 0; i < 8; ++i) v[i] = bfly<8>(v[i], v[i + 8], lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = bfly<4>(v[i], v[i + 4], lane);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) v[i] = bfly<2>(v[i], v[i + 2], lane);
+    return bfly<1>(v[0], v[1], lane);
 }
 
 // Split-KV partial attention of query heads g*G .. g*G+G-1 of batch row b over
 // keys [j0, j1) of split s: writes (m, l, o[D]) with m the max score, l the
 // sum of exp(score - m) and o the exp-weighted sum of V rows (unnormalised).
-// Waves split the group's heads and 64-key blocks; in a block lane j owns key
-// j (its K and V rows, loaded with independent 16-byte loads), and the PV
-// product is reduce-scattered so lane d ends with dims d (and d + 64).
+// Waves split the group's heads and 64-key blocks (the lane layouts within a
+// block are described at the loads below).
 template <int D, bool ABLATE>
 __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& seq, uint32_t r, const Inst& in,
                                                LDS float* xb,
@@ -1448,16 +1469,38 @@ __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& 
     LDS float* qs = xb;              // [G][D], pre-scaled by 1/sqrt(D)
     LDS float* kn = qs + G * D;      // [D] new K row (bf16 values)
     LDS float* vn = kn + D;          // [D] new V row
-    LDS float* stt = vn + D;         // [NW][D + 2] per-wave (m, l, o)
+    LDS float* stt = vn + D;         // [NW][D + 2] per-wave (m, l, o), then [NW][64] weights
     const int gi = cx.wave % G, wph = NW / G, sub = cx.wave / G;
     const uint16_t* Kc = sp.kv + ((((size_t)l * 2 + 0) * B + b) * p.Hkv + g) * (size_t)p.max_seq * D;
     const uint16_t* Vc = sp.kv + ((((size_t)l * 2 + 1) * B + b) * p.Hkv + g) * (size_t)p.max_seq * D;
     const int nkeys = j1 - j0;
 
-    // K and V rows written by earlier steps do not depend on this step: load
-    // the first block's first 64 dims before waiting for q.  Rows are handled in
-    // 64-dim halves (eight 16-byte chunks) to bound register use.
+    // K and V rows written by earlier steps do not depend on this step: the first block's are
+    // loaded before the wait for q.
+    //
+    // 64-dim heads (NH == 1) use a coalesced layout: in a block of 64 keys, load c (0..7) has
+    // lane L read dims 8(L%8) .. 8(L%8)+7 of key 8c + L/8, so one load instruction covers 1 KiB
+    // of consecutive cache rows.  A lane then holds eight partial scores (one per key it
+    // touched, over its eight dims); a reduce-scatter over the eight lanes of its group leaves
+    // it with the whole score of key 8(L%8) + L/8.  After the softmax the group's eight
+    // weights are shared through LDS, the lane accumulates its eight keys into its eight dims,
+    // and a reduce-scatter over the eight groups leaves it with output dim 8(L%8) + L/8.  A
+    // block's K and V are loaded together (the next block's at the end of the current one).
+    //
+    // 128-dim heads keep one key per lane (eight 16-byte loads of a 64-dim half of its row,
+    // halves loaded on demand for the register budget) and reduce-scatter the PV product over
+    // the whole wave.
     uint4 kr[8], vr[8];
+    const int ch = cx.lane & 7, grp = cx.lane >> 3;
+    auto load_blk = [&](uint4 (&r)[8], const uint16_t* base, int kb) {
+        const int jb = j0 + kb * 64 + grp;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int j = jb + c * 8;
+            const bool old = j < j1 && j < pos;
+            r[c] = old ? gld_u4(base + (size_t)(old ? j : 0) * 64 + ch * 8) : make_uint4(0, 0, 0, 0);
+        }
+    };
     auto load_half = [&](uint4 (&r)[8], const uint16_t* base, int kb, int h) {
         const int j = j0 + kb * 64 + cx.lane;
         const bool old = j < j1 && j < pos;
@@ -1465,21 +1508,23 @@ __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& 
 #pragma unroll
         for (int c = 0; c < 8; ++c) r[c] = old ? gld_u4(src + c) : make_uint4(0, 0, 0, 0);
     };
-    // the new row's values are bf16 numbers held as fp32: their upper halves
-    // are the bf16 bits
+    // the new row's values are bf16 numbers held as fp32: their upper halves are the bf16 bits
+    auto pack8 = [&](const LDS float* row) {
+        const uint4 lo = lds_u4(row), hi = lds_u4(row + 4);
+        return make_uint4((lo.x >> 16) | (lo.y & 0xffff0000u), (lo.z >> 16) | (lo.w & 0xffff0000u),
+                          (hi.x >> 16) | (hi.y & 0xffff0000u), (hi.z >> 16) | (hi.w & 0xffff0000u));
+    };
     auto pack_lds = [&](uint4 (&r)[8], const LDS float* row) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const uint4 lo = lds_u4(row + c * 8), hi = lds_u4(row + c * 8 + 4);
-            r[c] = make_uint4((lo.x >> 16) | (lo.y & 0xffff0000u), (lo.z >> 16) | (lo.w & 0xffff0000u),
-                              (hi.x >> 16) | (hi.y & 0xffff0000u), (hi.z >> 16) | (hi.w & 0xffff0000u));
-        }
+        for (int c = 0; c < 8; ++c) r[c] = pack8(row + c * 8);
     };
-    // (with 64-dim heads V of that block too: its load then overlaps the wait
-    // instead of following the softmax; 128-dim heads lack the registers)
     if (sub * 64 < nkeys) {
-        load_half(kr, Kc, sub, 0);
-        if (NH == 1) load_half(vr, Vc, sub, 0);
+        if constexpr (NH == 1) {
+            load_blk(kr, Kc, sub);
+            load_blk(vr, Vc, sub);
+        } else {
+            load_half(kr, Kc, sub, 0);
+        }
     }
 
     // q of the group's heads (pre-scaled), then the new K and V rows, staged by the gather wave
@@ -1502,34 +1547,99 @@ __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& 
     float m = ninf, lsum = 0.f, o[NH];
 #pragma unroll
     for (int h = 0; h < NH; ++h) o[h] = 0.f;
-    for (int kb = sub; kb * 64 < nkeys; kb += wph) {
-        const int j = j0 + kb * 64 + cx.lane;
-        const bool valid = j < j1;
-        const bool is_new = valid && j == pos;  // the row this step appended: from LDS
-        float acc = 0.f;
+    // the output dim a lane's o[h] belongs to (less 64 h)
+    const int od = NH == 1 ? ch * 8 + grp : cx.lane;
+    if constexpr (NH == 1) {
+        const float4 qa = lds_f4(qh + ch * 8), qb = lds_f4(qh + ch * 8 + 4);
+        LDS float* eb = stt + NW * (D + 2) + cx.wave * 64;  // the wave's 64 softmax weights
+        for (int kb = sub; kb * 64 < nkeys; kb += wph) {
+            const int kbase = j0 + kb * 64;
+            const int rel = pos - kbase;
+            if (rel >= 0 && rel < 64 && pos < j1) {  // the row this step appended: from LDS
+                const uint4 pk = pack8(kn + ch * 8), pv = pack8(vn + ch * 8);
 #pragma unroll
-        for (int h = 0; h < NH; ++h) {
-            CBAR();  // keeps the two halves' loads apart (register budget)
-            if (kb != sub || h != 0) load_half(kr, Kc, kb, h);
-            if (is_new) pack_lds(kr, kn + h * 64);
+                for (int c = 0; c < 8; ++c)
+                    if (c * 8 + grp == rel) {
+                        kr[c] = pk;
+                        vr[c] = pv;
+                    }
+            }
+            float sp8[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) sp8[c] = dot8(kr[c], qa, qb);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sp8[i] = bfly<4>(sp8[i], sp8[i + 4], cx.lane);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) sp8[i] = bfly<2>(sp8[i], sp8[i + 2], cx.lane);
+            // (every lane takes part in the exchange: a lane left out would hand its partner a
+            // stale value)
+            const float sfull = bfly<1>(sp8[0], sp8[1], cx.lane);
+            const bool valid = kbase + od < j1;  // this lane's key is 8(L%8) + L/8, like its dim
+            const float sc = valid ? sfull : ninf;
+            const float mn = fmaxf(m, wave_max(sc));
+            const float e = valid ? __expf(sc - mn) : 0.f;
+            const float corr = m == ninf ? 0.f : __expf(m - mn);
+            lsum = lsum * corr + wave_sum(e);
+            m = mn;
+            eb[cx.lane] = e;
+            CBAR();  // a wave's LDS accesses complete in order: the reads below see all 64 writes
+            const float4 ea = lds_f4(eb + grp * 8), eb4 = lds_f4(eb + grp * 8 + 4);
+            const float e8[8] = {ea.x, ea.y, ea.z, ea.w, eb4.x, eb4.y, eb4.z, eb4.w};
+            float po[8];
+#pragma unroll
+            for (int d = 0; d < 8; ++d) po[d] = 0.f;
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
-                const float4 a = lds_f4(qh + h * 64 + c * 8), bq = lds_f4(qh + h * 64 + c * 8 + 4);
-                acc += dot8(kr[c], a, bq);
+                const uint4 v = vr[c];
+                po[0] = fmaf(e8[c], bf_lo(v.x), po[0]);
+                po[1] = fmaf(e8[c], bf_hi(v.x), po[1]);
+                po[2] = fmaf(e8[c], bf_lo(v.y), po[2]);
+                po[3] = fmaf(e8[c], bf_hi(v.y), po[3]);
+                po[4] = fmaf(e8[c], bf_lo(v.z), po[4]);
+                po[5] = fmaf(e8[c], bf_hi(v.z), po[5]);
+                po[6] = fmaf(e8[c], bf_lo(v.w), po[6]);
+                po[7] = fmaf(e8[c], bf_hi(v.w), po[7]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) po[i] = bfly<32>(po[i], po[i + 4], cx.lane);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) po[i] = bfly<16>(po[i], po[i + 2], cx.lane);
+            o[0] = o[0] * corr + bfly<8>(po[0], po[1], cx.lane);
+            if ((kb + wph) * 64 < nkeys) {
+                load_blk(kr, Kc, kb + wph);
+                load_blk(vr, Vc, kb + wph);
             }
         }
-        const float sc = valid ? acc : ninf;
-        const float mn = fmaxf(m, wave_max(sc));
-        const float e = valid ? __expf(sc - mn) : 0.f;
-        const float corr = m == ninf ? 0.f : __expf(m - mn);
-        lsum = lsum * corr + wave_sum(e);
-        m = mn;
+    } else {
+        for (int kb = sub; kb * 64 < nkeys; kb += wph) {
+            const int j = j0 + kb * 64 + cx.lane;
+            const bool valid = j < j1;
+            const bool is_new = valid && j == pos;  // the row this step appended: from LDS
+            float acc = 0.f;
 #pragma unroll
-        for (int h = 0; h < NH; ++h) {
-            CBAR();
-            if (NH != 1 || kb != sub) load_half(vr, Vc, kb, h);
-            if (is_new) pack_lds(vr, vn + h * 64);
-            o[h] = o[h] * corr + pv_reduce_scatter64(vr, e, cx.lane);
+            for (int h = 0; h < NH; ++h) {
+                CBAR();  // keeps the two halves' loads apart (register budget)
+                if (kb != sub || h != 0) load_half(kr, Kc, kb, h);
+                if (is_new) pack_lds(kr, kn + h * 64);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const float4 a = lds_f4(qh + h * 64 + c * 8), bq = lds_f4(qh + h * 64 + c * 8 + 4);
+                    acc += dot8(kr[c], a, bq);
+                }
+            }
+            const float sc = valid ? acc : ninf;
+            const float mn = fmaxf(m, wave_max(sc));
+            const float e = valid ? __expf(sc - mn) : 0.f;
+            const float corr = m == ninf ? 0.f : __expf(m - mn);
+            lsum = lsum * corr + wave_sum(e);
+            m = mn;
+#pragma unroll
+            for (int h = 0; h < NH; ++h) {
+                CBAR();
+                load_half(vr, Vc, kb, h);
+                if (is_new) pack_lds(vr, vn + h * 64);
+                o[h] = o[h] * corr + pv_reduce_scatter64(vr, e, cx.lane);
+            }
         }
     }
     mark_mid(cx);
@@ -1544,7 +1654,7 @@ __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& 
             st_tag(out + 1, lsum, cx.epoch);
         }
 #pragma unroll
-        for (int h = 0; h < NH; ++h) st_tag(out + 2 + h * 64 + cx.lane, o[h], cx.epoch);
+        for (int h = 0; h < NH; ++h) st_tag(out + 2 + h * 64 + od, o[h], cx.epoch);
         return;
     }
     // per-wave state -> LDS, merge the waves of each head
@@ -1554,7 +1664,7 @@ __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& 
         my[1] = lsum;
     }
 #pragma unroll
-    for (int h = 0; h < NH; ++h) my[2 + h * 64 + cx.lane] = o[h];
+    for (int h = 0; h < NH; ++h) my[2 + h * 64 + od] = o[h];
     cbar(cx, s, seq);
     if (sub != 0 || cx.aborted) return;
     float M = ninf;
