@@ -1391,16 +1391,6 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
 
 // ------------------------------------------------------- attention ops ------
 
-// element i (0..63) of a 64-dim row held as eight packed-bf16 uint4s
-__device__ __forceinline__ float bf_elem(const uint4 (&r)[8], int i) {
-    const uint4 c = r[i >> 3];
-    const uint32_t w = ((i >> 1) & 3) == 0 ? c.x : ((i >> 1) & 3) == 1 ? c.y : ((i >> 1) & 3) == 2 ? c.z : c.w;
-    return (i & 1) ? bf_hi(w) : bf_lo(w);
-}
-
-// Wave64 reduce-scatter of e * row[d] (d < 64) by recursive halving: afterwards
-// lane d holds the sum over lanes of e * row[d].  The first halving step is
-// fused with the products so at most 32 values are live; 63 lane exchanges.
 // One butterfly stage across lanes L and its partner L ^ stride: a lane whose stride bit is clear
 // keeps the lower-destined value a plus its partner's a, the other keeps b plus the partner's
 // b.  The exchanges are VALU lane permutations (gfx950's permlane swaps for strides 32 and 16,
@@ -1432,25 +1422,6 @@ __device__ __forceinline__ float bfly(float a, float b, int lane) {
     }
 }
 
-__device__ __forceinline__ float pv_reduce_scatter64(const uint4 (&row)[8], float e, int lane) {
-    float v[32];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int i = h * 16; i < h * 16 + 16; ++i) v[i] = bfly<32>(e * bf_elem(row, i), e * bf_elem(row, i + 32), lane);
-        CBAR();
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = bfly<16>(v[i], v[i + 16], lane);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = bfly<8>(v[i], v[i + 8], lane);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = bfly<4>(v[i], v[i + 4], lane);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) v[i] = bfly<2>(v[i], v[i + 2], lane);
-    return bfly<1>(v[0], v[1], lane);
-}
-
 // Split-KV partial attention of query heads g*G .. g*G+G-1 of batch row b over
 // keys [j0, j1) of split s: writes (m, l, o[D]) with m the max score, l the
 // sum of exp(score - m) and o the exp-weighted sum of V rows (unnormalised).
@@ -1478,35 +1449,41 @@ __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& 
     // K and V rows written by earlier steps do not depend on this step: the first block's are
     // loaded before the wait for q.
     //
-    // 64-dim heads (NH == 1) use a coalesced layout: in a block of 64 keys, load c (0..7) has
-    // lane L read dims 8(L%8) .. 8(L%8)+7 of key 8c + L/8, so one load instruction covers 1 KiB
-    // of consecutive cache rows.  A lane then holds eight partial scores (one per key it
-    // touched, over its eight dims); a reduce-scatter over the eight lanes of its group leaves
-    // it with the whole score of key 8(L%8) + L/8.  After the softmax the group's eight
-    // weights are shared through LDS, the lane accumulates its eight keys into its eight dims,
-    // and a reduce-scatter over the eight groups leaves it with output dim 8(L%8) + L/8.  A
-    // block's K and V are loaded together (the next block's at the end of the current one).
+    // Lane layout in a block of 64 keys: load c (0..7) of a 64-dim half h has lane L read dims
+    // 64h + 8(L%8) .. +7 of key 8c + L/8, so one load instruction covers eight whole 128-byte
+    // lines.  A lane first holds eight partial scores (one per key it touched, over its dims);
+    // a reduce-scatter over the eight lanes of its group leaves it with the whole score of key
+    // 8(L%8) + L/8.  After the softmax the group's eight weights are shared through LDS, the
+    // lane accumulates its eight keys into its dims, and a reduce-scatter over the eight
+    // groups leaves it with output dims 64h + 8(L%8) + L/8.
     //
-    // 128-dim heads keep one key per lane (eight 16-byte loads of a 64-dim half of its row,
-    // halves loaded on demand for the register budget) and reduce-scatter the PV product over
-    // the whole wave.
+    // Registers hold two 64-key x 64-dim tiles.  64-dim heads keep a block's K and V in them
+    // (one memory round trip per block: the next block's K is loaded once the scores are
+    // taken, its V once the PV product is); 128-dim heads keep the two K halves, then the two
+    // V halves (two round trips per block).
+    //
+    // The tiles are read with buffer loads whose range is the split's rows already in the cache,
+    // [j0, min(j1, pos)): the hardware range check on the vector offset returns zeros for keys
+    // past it (the row at pos, which comes from LDS, and the tail of the last block), so every
+    // load of a tile shares one offset register.
     uint4 kr[8], vr[8];
     const int ch = cx.lane & 7, grp = cx.lane >> 3;
-    auto load_blk = [&](uint4 (&r)[8], const uint16_t* base, int kb) {
-        const int jb = j0 + kb * 64 + grp;
+    const int ncached = min(j1, pos) - j0;  // keys of the split already in the cache
+    const uint32_t nbytes = (uint32_t)ncached * (uint32_t)(D * 2);
+    const __amdgpu_buffer_rsrc_t kres =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Kc + (size_t)j0 * D), (short)0, nbytes, RSRC_WORD3);
+    const __amdgpu_buffer_rsrc_t vres =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Vc + (size_t)j0 * D), (short)0, nbytes, RSRC_WORD3);
+    auto load_blk = [&](uint4 (&r)[8], __amdgpu_buffer_rsrc_t rs, int kb, int h) {
+        const uint32_t vo = (uint32_t)(((kb * 64 + grp) * D + h * 64 + ch * 8) * 2);
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            const int j = jb + c * 8;
-            const bool old = j < j1 && j < pos;
-            r[c] = old ? gld_u4(base + (size_t)(old ? j : 0) * 64 + ch * 8) : make_uint4(0, 0, 0, 0);
+            // (a load whose eight keys are all past the range is not issued: the returns of a
+            // wave's loads are in order, so it would only delay the ones after it)
+            u32x4 w = {0, 0, 0, 0};
+            if (kb * 64 + c * 8 < ncached) w = __builtin_amdgcn_raw_buffer_load_b128(rs, vo + (uint32_t)(c * 8 * D * 2), 0, 0);
+            r[c] = make_uint4(w.x, w.y, w.z, w.w);
         }
-    };
-    auto load_half = [&](uint4 (&r)[8], const uint16_t* base, int kb, int h) {
-        const int j = j0 + kb * 64 + cx.lane;
-        const bool old = j < j1 && j < pos;
-        const uint4* src = (const uint4*)(base + (size_t)(old ? j : 0) * D + h * 64);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) r[c] = old ? gld_u4(src + c) : make_uint4(0, 0, 0, 0);
     };
     // the new row's values are bf16 numbers held as fp32: their upper halves are the bf16 bits
     auto pack8 = [&](const LDS float* row) {
@@ -1514,17 +1491,17 @@ __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& 
         return make_uint4((lo.x >> 16) | (lo.y & 0xffff0000u), (lo.z >> 16) | (lo.w & 0xffff0000u),
                           (hi.x >> 16) | (hi.y & 0xffff0000u), (hi.z >> 16) | (hi.w & 0xffff0000u));
     };
-    auto pack_lds = [&](uint4 (&r)[8], const LDS float* row) {
+    // the row this step appended is not in the cache yet: its chunks come from LDS
+    auto put_new = [&](uint4 (&r)[8], const LDS float* row, int rel) {
+        const uint4 pk = pack8(row + ch * 8);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) r[c] = pack8(row + c * 8);
+        for (int c = 0; c < 8; ++c)
+            if (c * 8 + grp == rel) r[c] = pk;
     };
     if (sub * 64 < nkeys) {
-        if constexpr (NH == 1) {
-            load_blk(kr, Kc, sub);
-            load_blk(vr, Vc, sub);
-        } else {
-            load_half(kr, Kc, sub, 0);
-        }
+        load_blk(kr, kres, sub, 0);
+        if constexpr (NH == 1) load_blk(vr, vres, sub, 0);
+        else load_blk(vr, kres, sub, 1);
     }
 
     // q of the group's heads (pre-scaled), then the new K and V rows, staged by the gather wave
@@ -1547,98 +1524,93 @@ __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& 
     float m = ninf, lsum = 0.f, o[NH];
 #pragma unroll
     for (int h = 0; h < NH; ++h) o[h] = 0.f;
-    // the output dim a lane's o[h] belongs to (less 64 h)
-    const int od = NH == 1 ? ch * 8 + grp : cx.lane;
-    if constexpr (NH == 1) {
-        const float4 qa = lds_f4(qh + ch * 8), qb = lds_f4(qh + ch * 8 + 4);
-        LDS float* eb = stt + NW * (D + 2) + cx.wave * 64;  // the wave's 64 softmax weights
-        for (int kb = sub; kb * 64 < nkeys; kb += wph) {
-            const int kbase = j0 + kb * 64;
-            const int rel = pos - kbase;
-            if (rel >= 0 && rel < 64 && pos < j1) {  // the row this step appended: from LDS
-                const uint4 pk = pack8(kn + ch * 8), pv = pack8(vn + ch * 8);
+    const int od = ch * 8 + grp;  // the output dim (less 64 h) a lane's o[h] belongs to
+    float4 qa[NH], qb[NH];  // the lane's q dims
 #pragma unroll
-                for (int c = 0; c < 8; ++c)
-                    if (c * 8 + grp == rel) {
-                        kr[c] = pk;
-                        vr[c] = pv;
-                    }
-            }
-            float sp8[8];
+    for (int h = 0; h < NH; ++h) {
+        qa[h] = lds_f4(qh + h * 64 + ch * 8);
+        qb[h] = lds_f4(qh + h * 64 + ch * 8 + 4);
+    }
+    LDS float* eb = stt + NW * (D + 2) + cx.wave * 64;  // the wave's 64 softmax weights
+    // PV of one 64-dim half: the lane's eight keys into its eight dims, then the reduce-scatter
+    auto pv_half = [&](const uint4 (&r)[8], const float (&e8)[8]) {
+        float po[8];
 #pragma unroll
-            for (int c = 0; c < 8; ++c) sp8[c] = dot8(kr[c], qa, qb);
+        for (int d = 0; d < 8; ++d) po[d] = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sp8[i] = bfly<4>(sp8[i], sp8[i + 4], cx.lane);
-#pragma unroll
-            for (int i = 0; i < 2; ++i) sp8[i] = bfly<2>(sp8[i], sp8[i + 2], cx.lane);
-            // (every lane takes part in the exchange: a lane left out would hand its partner a
-            // stale value)
-            const float sfull = bfly<1>(sp8[0], sp8[1], cx.lane);
-            const bool valid = kbase + od < j1;  // this lane's key is 8(L%8) + L/8, like its dim
-            const float sc = valid ? sfull : ninf;
-            const float mn = fmaxf(m, wave_max(sc));
-            const float e = valid ? __expf(sc - mn) : 0.f;
-            const float corr = m == ninf ? 0.f : __expf(m - mn);
-            lsum = lsum * corr + wave_sum(e);
-            m = mn;
-            eb[cx.lane] = e;
-            CBAR();  // a wave's LDS accesses complete in order: the reads below see all 64 writes
-            const float4 ea = lds_f4(eb + grp * 8), eb4 = lds_f4(eb + grp * 8 + 4);
-            const float e8[8] = {ea.x, ea.y, ea.z, ea.w, eb4.x, eb4.y, eb4.z, eb4.w};
-            float po[8];
-#pragma unroll
-            for (int d = 0; d < 8; ++d) po[d] = 0.f;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const uint4 v = vr[c];
-                po[0] = fmaf(e8[c], bf_lo(v.x), po[0]);
-                po[1] = fmaf(e8[c], bf_hi(v.x), po[1]);
-                po[2] = fmaf(e8[c], bf_lo(v.y), po[2]);
-                po[3] = fmaf(e8[c], bf_hi(v.y), po[3]);
-                po[4] = fmaf(e8[c], bf_lo(v.z), po[4]);
-                po[5] = fmaf(e8[c], bf_hi(v.z), po[5]);
-                po[6] = fmaf(e8[c], bf_lo(v.w), po[6]);
-                po[7] = fmaf(e8[c], bf_hi(v.w), po[7]);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) po[i] = bfly<32>(po[i], po[i + 4], cx.lane);
-#pragma unroll
-            for (int i = 0; i < 2; ++i) po[i] = bfly<16>(po[i], po[i + 2], cx.lane);
-            o[0] = o[0] * corr + bfly<8>(po[0], po[1], cx.lane);
-            if ((kb + wph) * 64 < nkeys) {
-                load_blk(kr, Kc, kb + wph);
-                load_blk(vr, Vc, kb + wph);
-            }
+        for (int c = 0; c < 8; ++c) {
+            const uint4 v = r[c];
+            po[0] = fmaf(e8[c], bf_lo(v.x), po[0]);
+            po[1] = fmaf(e8[c], bf_hi(v.x), po[1]);
+            po[2] = fmaf(e8[c], bf_lo(v.y), po[2]);
+            po[3] = fmaf(e8[c], bf_hi(v.y), po[3]);
+            po[4] = fmaf(e8[c], bf_lo(v.z), po[4]);
+            po[5] = fmaf(e8[c], bf_hi(v.z), po[5]);
+            po[6] = fmaf(e8[c], bf_lo(v.w), po[6]);
+            po[7] = fmaf(e8[c], bf_hi(v.w), po[7]);
         }
-    } else {
-        for (int kb = sub; kb * 64 < nkeys; kb += wph) {
-            const int j = j0 + kb * 64 + cx.lane;
-            const bool valid = j < j1;
-            const bool is_new = valid && j == pos;  // the row this step appended: from LDS
-            float acc = 0.f;
 #pragma unroll
-            for (int h = 0; h < NH; ++h) {
-                CBAR();  // keeps the two halves' loads apart (register budget)
-                if (kb != sub || h != 0) load_half(kr, Kc, kb, h);
-                if (is_new) pack_lds(kr, kn + h * 64);
+        for (int i = 0; i < 4; ++i) po[i] = bfly<32>(po[i], po[i + 4], cx.lane);
 #pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    const float4 a = lds_f4(qh + h * 64 + c * 8), bq = lds_f4(qh + h * 64 + c * 8 + 4);
-                    acc += dot8(kr[c], a, bq);
-                }
+        for (int i = 0; i < 2; ++i) po[i] = bfly<16>(po[i], po[i + 2], cx.lane);
+        return bfly<8>(po[0], po[1], cx.lane);
+    };
+    for (int kb = sub; kb * 64 < nkeys; kb += wph) {
+        const int kbase = j0 + kb * 64;
+        const int rel = pos - kbase;
+        const bool has_new = rel >= 0 && rel < 64 && pos < j1;  // uniform
+        const bool has_next = (kb + wph) * 64 < nkeys;
+        if (has_new) {
+            put_new(kr, kn, rel);
+            if constexpr (NH == 1) put_new(vr, vn, rel);
+            else put_new(vr, kn + 64, rel);
+        }
+        float sp8[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            sp8[c] = dot8(kr[c], qa[0], qb[0]);
+            if constexpr (NH == 2) sp8[c] += dot8(vr[c], qa[1], qb[1]);
+        }
+        CBAR();  // the K tiles are consumed: their registers take the next loads
+        if constexpr (NH == 1) {
+            if (has_next) load_blk(kr, kres, kb + wph, 0);
+        } else {
+            load_blk(kr, vres, kb, 0);
+            load_blk(vr, vres, kb, 1);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sp8[i] = bfly<4>(sp8[i], sp8[i + 4], cx.lane);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) sp8[i] = bfly<2>(sp8[i], sp8[i + 2], cx.lane);
+        // (every lane takes part in the exchange: a lane left out would hand its partner a
+        // stale value)
+        const float sfull = bfly<1>(sp8[0], sp8[1], cx.lane);
+        const bool valid = kbase + od < j1;  // this lane's key is 8(L%8) + L/8, like its dim
+        const float sc = valid ? sfull : ninf;
+        const float mn = fmaxf(m, wave_max(sc));
+        const float e = valid ? __expf(sc - mn) : 0.f;
+        const float corr = m == ninf ? 0.f : __expf(m - mn);
+        lsum = lsum * corr + wave_sum(e);
+        m = mn;
+        eb[cx.lane] = e;
+        CBAR();  // a wave's LDS accesses complete in order: the reads below see all 64 writes
+        const float4 ea = lds_f4(eb + grp * 8), ec = lds_f4(eb + grp * 8 + 4);
+        const float e8[8] = {ea.x, ea.y, ea.z, ea.w, ec.x, ec.y, ec.z, ec.w};
+        if constexpr (NH == 1) {
+            o[0] = o[0] * corr + pv_half(vr, e8);
+            CBAR();
+            if (has_next) load_blk(vr, vres, kb + wph, 0);
+        } else {
+            if (has_new) {
+                put_new(kr, vn, rel);
+                put_new(vr, vn + 64, rel);
             }
-            const float sc = valid ? acc : ninf;
-            const float mn = fmaxf(m, wave_max(sc));
-            const float e = valid ? __expf(sc - mn) : 0.f;
-            const float corr = m == ninf ? 0.f : __expf(m - mn);
-            lsum = lsum * corr + wave_sum(e);
-            m = mn;
-#pragma unroll
-            for (int h = 0; h < NH; ++h) {
-                CBAR();
-                load_half(vr, Vc, kb, h);
-                if (is_new) pack_lds(vr, vn + h * 64);
-                o[h] = o[h] * corr + pv_reduce_scatter64(vr, e, cx.lane);
+            o[0] = o[0] * corr + pv_half(kr, e8);
+            o[1] = o[1] * corr + pv_half(vr, e8);
+            CBAR();
+            if (has_next) {
+                load_blk(kr, kres, kb + wph, 0);
+                load_blk(vr, kres, kb + wph, 1);
             }
         }
     }
@@ -1705,17 +1677,38 @@ __device__ __forceinline__ void op_reduce(Ctx& cx, const Lds& s, uint32_t r, con
         return;
     }
     const float ninf = -__builtin_inff();
+    // the splits' (m, l) across lanes: M = max over splits, each split's weight
+    // f_s = e^(m_s - M) (0 for a split without keys) replaces its m in LDS, Ls = sum of l_s f_s
     float M = ninf;
-    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, xb[sp * W]);
-    const int nh = D / 64;  // lane owns dims lane (and lane + 64)
-    float Ls = 0.f, O0 = 0.f, O1 = 0.f;
-    for (int sp = 0; sp < ns; ++sp) {
+    for (int sp = cx.lane; sp < ns; sp += 64) M = fmaxf(M, xb[sp * W]);
+    M = wave_max(M);
+    float Ls = 0.f;
+    for (int sp = cx.lane; sp < ns; sp += 64) {
         const float ms = xb[sp * W];
-        if (ms == ninf) continue;
-        const float f = __expf(ms - M);
+        const float f = ms == ninf ? 0.f : __expf(ms - M);
         Ls = fmaf(xb[sp * W + 1], f, Ls);
-        O0 = fmaf(xb[sp * W + 2 + cx.lane], f, O0);
-        if (nh == 2) O1 = fmaf(xb[sp * W + 2 + 64 + cx.lane], f, O1);
+        xb[sp * W] = f;
+    }
+    Ls = wave_sum(Ls);
+    CBAR();  // a wave's LDS accesses complete in order: the reads below see every weight
+    // lane d owns dims d (and d + 64); the loop is unrolled so the LDS reads overlap
+    const int nh = D / 64;
+    float O0 = 0.f, O1 = 0.f;
+    int sp = 0;
+    for (; sp + 8 <= ns; sp += 8) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const LDS float* ps = xb + (sp + i) * W;
+            const float f = ps[0];
+            O0 = fmaf(ps[2 + cx.lane], f, O0);
+            if (nh == 2) O1 = fmaf(ps[2 + 64 + cx.lane], f, O1);
+        }
+    }
+    for (; sp < ns; ++sp) {
+        const LDS float* ps = xb + sp * W;
+        const float f = ps[0];
+        O0 = fmaf(ps[2 + cx.lane], f, O0);
+        if (nh == 2) O1 = fmaf(ps[2 + 64 + cx.lane], f, O1);
     }
     const float inv = 1.0f / Ls;
     uint64_t* out = p.attn + ((size_t)l * B + b) * p.Hq * D + (size_t)head * D;
