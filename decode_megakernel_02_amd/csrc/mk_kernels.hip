@@ -1533,12 +1533,13 @@ __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& 
     }
     LDS float* eb = stt + NW * (D + 2) + cx.wave * 64;  // the wave's 64 softmax weights
     // PV of one 64-dim half: the lane's eight keys into its eight dims, then the reduce-scatter
-    auto pv_half = [&](const uint4 (&r)[8], const float (&e8)[8]) {
+    auto pv_half = [&](const uint4 (&r)[8], const float (&e8)[8], int nvalid) {
         float po[8];
 #pragma unroll
         for (int d = 0; d < 8; ++d) po[d] = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
+            if (c * 8 >= nvalid) break;  // key group c lies past the split's keys
             const uint4 v = r[c];
             po[0] = fmaf(e8[c], bf_lo(v.x), po[0]);
             po[1] = fmaf(e8[c], bf_hi(v.x), po[1]);
@@ -1560,6 +1561,10 @@ __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& 
         const int rel = pos - kbase;
         const bool has_new = rel >= 0 && rel < 64 && pos < j1;  // uniform
         const bool has_next = (kb + wph) * 64 < nkeys;
+        // keys of the block inside the split: with 128-dim heads the products of key groups c
+        // with 8c >= nvalid (which hold none) are skipped, half the block at 32 keys per split;
+        // with 64-dim heads the branches cost more than they save
+        const int nvalid = NH == 2 ? min(64, nkeys - kb * 64) : 64;
         if (has_new) {
             put_new(kr, kn, rel);
             if constexpr (NH == 1) put_new(vr, vn, rel);
@@ -1568,8 +1573,11 @@ __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& 
         float sp8[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            sp8[c] = dot8(kr[c], qa[0], qb[0]);
-            if constexpr (NH == 2) sp8[c] += dot8(vr[c], qa[1], qb[1]);
+            sp8[c] = 0.f;
+            if (c * 8 < nvalid) {
+                sp8[c] = dot8(kr[c], qa[0], qb[0]);
+                if constexpr (NH == 2) sp8[c] += dot8(vr[c], qa[1], qb[1]);
+            }
         }
         CBAR();  // the K tiles are consumed: their registers take the next loads
         if constexpr (NH == 1) {
@@ -1597,7 +1605,7 @@ __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& 
         const float4 ea = lds_f4(eb + grp * 8), ec = lds_f4(eb + grp * 8 + 4);
         const float e8[8] = {ea.x, ea.y, ea.z, ea.w, ec.x, ec.y, ec.z, ec.w};
         if constexpr (NH == 1) {
-            o[0] = o[0] * corr + pv_half(vr, e8);
+            o[0] = o[0] * corr + pv_half(vr, e8, nvalid);
             CBAR();
             if (has_next) load_blk(vr, vres, kb + wph, 0);
         } else {
@@ -1605,8 +1613,8 @@ __device__ __forceinline__ void op_attention_t(Ctx& cx, const Lds& s, uint32_t& 
                 put_new(kr, vn, rel);
                 put_new(vr, vn + 64, rel);
             }
-            o[0] = o[0] * corr + pv_half(kr, e8);
-            o[1] = o[1] * corr + pv_half(vr, e8);
+            o[0] = o[0] * corr + pv_half(kr, e8, nvalid);
+            o[1] = o[1] * corr + pv_half(vr, e8, nvalid);
             CBAR();
             if (has_next) {
                 load_blk(kr, kres, kb + wph, 0);
