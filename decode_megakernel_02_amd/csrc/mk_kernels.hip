@@ -853,30 +853,30 @@ __device__ __forceinline__ void gather_region(Ctx& cx, const uint64_t* base, int
 
 constexpr int GATHER_NB = 16;      // 16-byte loads per lane per polling round (2048 words)
 constexpr int GATHER_NB_ATTN = 6;  // (G + 2) * D <= 768 words
+#ifndef GATHER_NB_COMPUTE
+#define GATHER_NB_COMPUTE 8          // compute waves staging their own x row (1024 words a round)
+#endif
 
-// x[b][k] = raw[b][k] * gain[k] in the x-buffer layout, plus zero padding up
-// to kpad; ss[b] = sum_k raw[b][k]^2 when ss_out is given.
-template <bool GAIN, class Row>
-__device__ __forceinline__ void gather_x(Ctx& cx, int B, int K, int kpad, Row&& row, const uint16_t* gain,
-                                         LDS float* xb, LDS float* ss_out) {
+// x[b][k] = raw[k] * gain[k] for one batch row b in the x-buffer layout, plus zero padding up
+// to kpad; ss_out[b] = sum_k raw[k]^2 when ss_out is given.
+template <int NB, bool GAIN>
+__device__ __forceinline__ void gather_x_row(Ctx& cx, int b, int K, int kpad, const uint64_t* raw,
+                                             const uint16_t* gain, LDS float* xb, LDS float* ss_out) {
     const int xs = (int)uni((uint32_t)cx.p->xstride);
-    for (int b = 0; b < B; ++b) {
-        float ss = 0.f;
-        // lane l stores pairs k = k0 + 2l (k0 a multiple of 128): one base address per lane
-        LDS float* xl = xb + xidx(xs, b, 2 * cx.lane);
-        gather_region<GATHER_NB, GAIN>(cx, row(b), K, gain,
-                                      [&](int kb, float v0, float v1, uint32_t gp) {
-                                          ss = fmaf(v0, v0, ss);
-                                          ss = fmaf(v1, v1, ss);
-                                          LDS float* x = xl + (kb >> 1);  // k, k+1 adjacent
-                                          x[0] = v0 * bf_lo(gp);
-                                          x[1] = v1 * bf_hi(gp);
-                                      });
-        for (int k = K + cx.lane; k < kpad; k += 64) xb[xidx(xs, b, k)] = 0.f;
-        if (ss_out) {
-            ss = wave_sum(ss);
-            if (cx.lane == 0) ss_out[b] = ss;
-        }
+    float ss = 0.f;
+    // lane l stores pairs k = k0 + 2l (k0 a multiple of 128): one base address per lane
+    LDS float* xl = xb + xidx(xs, b, 2 * cx.lane);
+    gather_region<NB, GAIN>(cx, raw, K, gain, [&](int kb, float v0, float v1, uint32_t gp) {
+        ss = fmaf(v0, v0, ss);
+        ss = fmaf(v1, v1, ss);
+        LDS float* x = xl + (kb >> 1);  // k, k+1 adjacent
+        x[0] = v0 * bf_lo(gp);
+        x[1] = v1 * bf_hi(gp);
+    });
+    for (int k = K + cx.lane; k < kpad; k += 64) xb[xidx(xs, b, k)] = 0.f;
+    if (ss_out) {
+        ss = wave_sum(ss);
+        if (cx.lane == 0) ss_out[b] = ss;
     }
 }
 
@@ -972,8 +972,27 @@ __device__ __forceinline__ void gather_side(Ctx& cx, const Step& sp, const Inst&
 
 // Stages the inputs of one instruction in xb (see the op bodies for layouts).
 // (FP8 weights: units of 1024 elements, so the zero padding of x covers those)
+// With several batch rows the compute waves stage the x rows of the GEMV inputs themselves, wave
+// w row w, so the rows' polls run at once instead of one after another on the gather wave (one
+// round trip per instruction instead of B); the gather wave still frees the buffer set, stages
+// the side inputs and raises the ready flag.  The first layer's QKV input (embedding rows, no
+// tags) stays with the gather wave.
+__device__ __forceinline__ bool rows_by_compute(CParams& p, const Inst& in) {
+    if (p.B == 1) return false;
+    switch (in.op) {
+    case OP_RMS_QKV_ROPE: return in.layer > 0;
+    case OP_RMS_LM_HEAD:
+    case OP_RMS_UP_GATE:
+    case OP_O_PROJ_RES:
+    case OP_DOWN_RES: return true;
+    default: return false;
+    }
+}
+
 template <bool FP8>
 __device__ __forceinline__ void gather_inst(Ctx& cx, const Step& sp, const Inst& in, LDS float* xb, LDS float* ss) {
+    constexpr int NB = GATHER_NB;
+    const int b0 = 0, bstep = 1;
     constexpr int EPU = FP8 ? FP8_UNIT_ELEMS : UNIT_ELEMS;
     CParams& p = *cx.p;
     const int B = p.B, H = p.H, l = in.layer;
@@ -987,28 +1006,28 @@ __device__ __forceinline__ void gather_inst(Ctx& cx, const Step& sp, const Inst&
             gather_embed(cx, sp, kpad, gain, xb, ss);
         } else {
             const uint64_t* src = p.hout + (size_t)(src_layer - 1) * B * H;
-            gather_x<true>(cx, B, H, kpad, [&](int b) { return src + (size_t)b * H; }, gain, xb, ss);
+            for (int b = b0; b < B; b += bstep) gather_x_row<NB, true>(cx, b, H, kpad, src + (size_t)b * H, gain, xb, ss);
         }
         break;
     }
     case OP_RMS_UP_GATE: {
         const uint64_t* src = p.hmid + (size_t)l * B * H;
-        gather_x<true>(cx, B, H, p.ku_h * EPU, [&](int b) { return src + (size_t)b * H; },
-                       p.gain_mlp + (size_t)l * H, xb, ss);
+        for (int b = b0; b < B; b += bstep)
+            gather_x_row<NB, true>(cx, b, H, p.ku_h * EPU, src + (size_t)b * H, p.gain_mlp + (size_t)l * H, xb, ss);
         break;
     }
     case OP_O_PROJ_RES: {
         const int K = p.Hq * p.D;
         const uint64_t* src = p.attn + (size_t)l * B * K;
-        gather_x<false>(cx, B, K, p.ku_q * EPU, [&](int b) { return src + (size_t)b * K; }, nullptr, xb,
-                        nullptr);
+        for (int b = b0; b < B; b += bstep)
+            gather_x_row<NB, false>(cx, b, K, p.ku_q * EPU, src + (size_t)b * K, nullptr, xb, nullptr);
         break;
     }
     case OP_DOWN_RES: {
         const int c0 = p.chunk_begin[in.a], K = p.chunk_begin[in.a + 1] - c0;
         const uint64_t* src = p.act + (size_t)l * B * p.F + c0;
-        gather_x<false>(cx, B, K, p.ku_f * EPU, [&](int b) { return src + (size_t)b * p.F; }, nullptr, xb,
-                        nullptr);
+        for (int b = b0; b < B; b += bstep)
+            gather_x_row<NB, false>(cx, b, K, p.ku_f * EPU, src + (size_t)b * p.F, nullptr, xb, nullptr);
         break;
     }
     case OP_ATTENTION: {
@@ -1034,6 +1053,36 @@ __device__ __forceinline__ void gather_inst(Ctx& cx, const Step& sp, const Inst&
                                        });
         break;
     }
+    }
+}
+
+// Compute wave side of rows_by_compute: this wave stages x row b = cx.wave (if b < B) of a GEMV
+// instruction's input (only the GEMV cases, with fewer loads per round than the gather wave).
+template <bool FP8>
+__device__ __forceinline__ void gather_own_row(Ctx& cx, const Inst& in, LDS float* xb, LDS float* ss) {
+    constexpr int EPU = FP8 ? FP8_UNIT_ELEMS : UNIT_ELEMS;
+    constexpr int NB = GATHER_NB_COMPUTE;
+    CParams& p = *cx.p;
+    const int B = p.B, H = p.H, l = in.layer, b = cx.wave;
+    if (b >= B) return;
+    const uint64_t* raw;
+    const uint16_t* gain = nullptr;
+    int K, kpad;
+    if (in.op == OP_RMS_QKV_ROPE || in.op == OP_RMS_LM_HEAD || in.op == OP_RMS_UP_GATE) {
+        const bool up = in.op == OP_RMS_UP_GATE;
+        const int src_layer = in.op == OP_RMS_LM_HEAD ? p.L : l;  // (> 0: the embedding rows stay with the gather wave)
+        raw = up ? p.hmid + ((size_t)l * B + b) * H : p.hout + ((size_t)(src_layer - 1) * B + b) * H;
+        gain = up ? p.gain_mlp + (size_t)l * H : in.op == OP_RMS_LM_HEAD ? p.gain_final : p.gain_attn + (size_t)l * H;
+        K = H;
+        kpad = p.ku_h * EPU;
+        gather_x_row<NB, true>(cx, b, K, kpad, raw, gain, xb, ss);
+    } else if (in.op == OP_O_PROJ_RES) {
+        K = p.Hq * p.D;
+        gather_x_row<NB, false>(cx, b, K, p.ku_q * EPU, p.attn + ((size_t)l * B + b) * K, nullptr, xb, nullptr);
+    } else {  // OP_DOWN_RES
+        const int c0 = p.chunk_begin[in.a];
+        K = p.chunk_begin[in.a + 1] - c0;
+        gather_x_row<NB, false>(cx, b, K, p.ku_f * EPU, p.act + ((size_t)l * B + b) * p.F + c0, nullptr, xb, nullptr);
     }
 }
 
@@ -1106,13 +1155,17 @@ __device__ __forceinline__ void gatherer(Ctx& cx, const Lds& s, const Step& sp, 
         // side inputs first: each was complete before the main input's producers
         // began, so their round trip never waits behind the main poll
         if (p.side_floats) gather_side(cx, sp, in, sslot(s, p, slot));
-        const uint32_t key = input_key(in);
-        if (NGATHER == 1 && key != 0 && key == prev_key)  // its buffer set still holds it: the
-            // wave refills a set only nslot instructions later, after this copy
+        const bool by_compute = rows_by_compute(p, in);
+        const uint32_t key = by_compute ? 0u : input_key(in);
+        if (by_compute) {
+            // the compute waves stage the x rows
+        } else if (NGATHER == 1 && key != 0 && key == prev_key) {  // its buffer set still holds it:
+            // the wave refills a set only nslot instructions later, after this copy
             copy_staged(cx, xslot(s, p, prev_slot), xslot(s, p, slot), p.B * (int)uni((uint32_t)p.xstride),
                         s.ss + prev_slot * MAX_BATCH, s.ss + slot * MAX_BATCH, p.B);
-        else
+        } else {
             gather_inst<FP8>(cx, sp, in, xslot(s, p, slot), s.ss + slot * MAX_BATCH);
+        }
         prev_key = key;
         prev_slot = slot;
         if (uni(cx.aborted)) break;
@@ -1166,7 +1219,7 @@ __device__ __forceinline__ uint32_t ug_share(CParams& p, uint32_t t, int c, uint
 // KU == 0: general path.
 template <int KU, bool FP8, bool GREEDY, bool ABLATE>
 __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint32_t r, uint32_t slot, const Inst& in,
-                                        LDS float* xb, const Step& sp, DownAcc& da) {
+                                        LDS float* xb, const Step& sp, DownAcc& da, uint32_t& seq) {
     CParams& p = *cx.p;
     const int B = p.B, H = p.H, l = in.layer;
     const int ku = in.op == OP_O_PROJ_RES ? p.ku_q : in.op == OP_DOWN_RES ? p.ku_f : p.ku_h;
@@ -1197,9 +1250,16 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
         rgs = p.rgscale + 2 * (base + (in.op == OP_RMS_UP_GATE ? 0u : in.rg0));
         load_rsc(0);
     }
-    // x = raw input * gain, staged by the gather wave; lane b: RMSNorm scale of batch row b
+    // x = raw input * gain, staged by the gather wave (with several batch rows: by the compute
+    // waves, one row each, once the gather wave has handed over the buffer set); lane b: RMSNorm
+    // scale of batch row b
     wait_inputs(cx, s, r);
     if (cx.aborted) return;
+    if (rows_by_compute(p, in)) {
+        gather_own_row<FP8>(cx, in, xb, s.ss + slot * MAX_BATCH);
+        cbar(cx, s, seq);
+        if (cx.aborted) return;
+    }
     float scale = 1.f;
     if ((in.op == OP_RMS_QKV_ROPE || in.op == OP_RMS_LM_HEAD || in.op == OP_RMS_UP_GATE) && cx.lane < B)
         scale = rsqrtf(s.ss[slot * MAX_BATCH + cx.lane] * (1.0f / (float)H) + p.eps);
@@ -1926,9 +1986,9 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
         case OP_ATTN_REDUCE: op_reduce<ABLATE>(cx, s, r, in, xb); break;
         default: {
             const int ku = in.op == OP_O_PROJ_RES ? p.ku_q : in.op == OP_DOWN_RES ? p.ku_f : p.ku_h;
-            if (!batch1_path(p.B, ku, FP8)) op_gemv<0, FP8, GREEDY, ABLATE>(cx, s, st, r, slot, in, xb, sp, da);
-            else if (!FP8 && ku == 4) op_gemv<FP8 ? 2 : 4, FP8, GREEDY, ABLATE>(cx, s, st, r, slot, in, xb, sp, da);
-            else op_gemv<2, FP8, GREEDY, ABLATE>(cx, s, st, r, slot, in, xb, sp, da);
+            if (!batch1_path(p.B, ku, FP8)) op_gemv<0, FP8, GREEDY, ABLATE>(cx, s, st, r, slot, in, xb, sp, da, seq);
+            else if (!FP8 && ku == 4) op_gemv<FP8 ? 2 : 4, FP8, GREEDY, ABLATE>(cx, s, st, r, slot, in, xb, sp, da, seq);
+            else op_gemv<2, FP8, GREEDY, ABLATE>(cx, s, st, r, slot, in, xb, sp, da, seq);
             break;
         }
         }
