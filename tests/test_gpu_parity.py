@@ -108,6 +108,17 @@ def test_tiny_batch4_rows_independent():
     H.compare(run, ref, "tiny b4")
 
 
+@pytest.mark.parametrize("batch", [3, 5, 7])
+@pytest.mark.parametrize("multikernel", [False, True], ids=["megakernel", "multikernel"])
+def test_tiny_odd_batch(batch, multikernel):
+    """Odd batch sizes: with several rows each compute wave stages its own x row of every GEMV
+    input (waves past the last row only join the barrier), and the RMSNorm scales come from
+    those waves' sums of squares."""
+    weights, run, _, max_seq = tiny_prefill_run(multikernel, batch=batch, gain_std=0.3)
+    ref = H.oracle_replay(synth.TINY, weights, batch, max_seq, run)
+    H.compare(run, ref, f"tiny b{batch}" + (" per-op" if multikernel else ""))
+
+
 def test_invalid_token_reports_device_error_and_writes_nothing():
     import torch
     from decode_megakernel_02_amd import mk
