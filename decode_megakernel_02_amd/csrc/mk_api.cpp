@@ -267,6 +267,7 @@ int mk_create(const mk_config* cfg, mk_handle** out) {
         for (int i = 0; i <= p.n_chunk; ++i) hp.chunk_begin[i] = p.chunk_begin[i];
         hp.n_stages = p.n_stages;
         hp.fp8 = p.fp8 ? 1 : 0;
+        hp.lm_pairs = p.lm_pairs ? 1 : 0;
         if (p.fp8) {
             const size_t nrows = p.mat_row_off[(size_t)p.n_mats()];
             hp.rgscale = dalloc<float>(h, ((size_t)p.rgs_stride * p.L + p.V) * 2);

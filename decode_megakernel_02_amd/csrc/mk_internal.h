@@ -130,6 +130,7 @@ struct Params {
     uint32_t rgs_off[4];
     uint32_t rgs_stride;
     int32_t fp8;          // weights packed as FP8 codes (units of 1024 elements)
+    int32_t lm_pairs;     // LM-head row-groups are row pairs (2 rg, 2 rg + 1)
 
     // fused greedy decoding (mk_decode_step_greedy): arrival counter of the CUs (0 between
     // steps) and each CU's (max logit, lowest index) per batch row as two tagged words

@@ -1421,18 +1421,23 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
             }
             break;
         }
-        default: {  // OP_RMS_LM_HEAD
-            dot1(o);
+        default: {  // OP_RMS_LM_HEAD (row-group rg: row rg, or rows 2 rg and 2 rg + 1 with lm_pairs)
+            const int nr = KU == 0 && p.lm_pairs ? 2 : 1;
+            if (nr == 2) dot2(o);
+            else dot1(o);
             if constexpr (FP8) fp8_scale(o);
             if (lane_row) {
-                const float v = o.mine[0] * scale;
-                gst(sp.logits + (size_t)b * p.V + rg, v);
-                // running (max, lowest index) of the rows: NaN never compares greater or equal
-                if constexpr (GREEDY)
-                    if (v > cx.gv || (v == cx.gv && rg < cx.gi)) {
-                        cx.gv = v;
-                        cx.gi = rg;
-                    }
+                for (int k = 0; k < nr; ++k) {
+                    const uint32_t row = nr == 2 ? 2 * rg + (uint32_t)k : rg;
+                    const float v = o.mine[k] * scale;
+                    gst(sp.logits + (size_t)b * p.V + row, v);
+                    // running (max, lowest index) of the rows: NaN never compares greater or equal
+                    if constexpr (GREEDY)
+                        if (v > cx.gv || (v == cx.gv && row < cx.gi)) {
+                            cx.gv = v;
+                            cx.gi = row;
+                        }
+                }
             }
             break;
         }

@@ -102,6 +102,11 @@ struct Builder {
             return 1;
         }
         case OP_RMS_LM_HEAD:
+            if (p.lm_pairs) {
+                out[0] = {(uint32_t)p.lm_mat(), 2 * rg, 0, (uint32_t)p.H, (uint32_t)p.H};
+                out[1] = {(uint32_t)p.lm_mat(), 2 * rg + 1, 0, (uint32_t)p.H, (uint32_t)p.H};
+                return 2;
+            }
             out[0] = {(uint32_t)p.lm_mat(), rg, 0, (uint32_t)p.H, (uint32_t)p.H};
             return 1;
         default:
@@ -168,6 +173,7 @@ int build_plan(const mk_config& c, int ncu, Plan& p, std::string& err) {
         if (i) maxc = std::max(maxc, p.chunk_begin[i] - p.chunk_begin[i - 1]);
     }
     p.ku_f = ceil_div(maxc, p.epu);
+    p.lm_pairs = p.V % 2 == 0 && p.B > 1 && !batch1_path(p.B, p.ku_h, p.fp8);
     p.n_stages = p.L * STAGES_PER_LAYER + 1;
     // global row indices (per-row FP8 scales) and the row-group scale table layout
     {
@@ -245,7 +251,7 @@ int build_plan(const mk_config& c, int ncu, Plan& p, std::string& err) {
         }
     }
     mark(p.L * STAGES_PER_LAYER);
-    b.tiles(OP_RMS_LM_HEAD, p.L, p.V);  // layer field unused for the head
+    b.tiles(OP_RMS_LM_HEAD, p.L, p.lm_pairs ? p.V / 2 : p.V);  // layer field unused for the head
     for (auto& qq : b.q)
         for (auto& in : qq)
             if (in.op == OP_RMS_LM_HEAD) in.layer = 0;
@@ -369,7 +375,7 @@ void build_rg_scales(const Plan& p, const std::vector<float>& row_scale, std::ve
             }
             fill(Inst{ops[o], (uint16_t)l, 0, 0, 0, 0}, (size_t)l * p.rgs_stride + p.rgs_off[o], counts[o]);
         }
-    fill(Inst{OP_RMS_LM_HEAD, 0, 0, 0, 0, 0}, (size_t)p.L * p.rgs_stride, (uint32_t)p.V);
+    fill(Inst{OP_RMS_LM_HEAD, 0, 0, 0, 0, 0}, (size_t)p.L * p.rgs_stride, (uint32_t)(p.lm_pairs ? p.V / 2 : p.V));
 }
 
 // ---------------------------------------------------------------- checking --
@@ -412,7 +418,18 @@ bool check_plan(const Plan& p, std::string& err, bool check_order) {
                 for (uint32_t r = 0; r < in.nrg; ++r) dn[((size_t)in.layer * p.n_chunk + in.a) * p.H + in.rg0 + r]++;
                 break;
             case OP_RMS_LM_HEAD: stage = L * STAGES_PER_LAYER;
-                for (uint32_t r = 0; r < in.nrg; ++r) lm[in.rg0 + r]++;
+                for (uint32_t r = 0; r < in.nrg; ++r) {
+                    if (p.lm_pairs) {
+                        if (2 * (size_t)(in.rg0 + r) + 1 >= lm.size()) {
+                            err = "LM-head row pair beyond the vocabulary";
+                            return false;
+                        }
+                        lm[2 * (size_t)(in.rg0 + r)]++;
+                        lm[2 * (size_t)(in.rg0 + r) + 1]++;
+                    } else {
+                        lm[in.rg0 + r]++;
+                    }
+                }
                 break;
             default:
                 snprintf(buf, sizeof buf, "CU %d: unknown opcode %d", cu, in.op);

@@ -36,6 +36,9 @@ struct Plan {
     // schedule parameters
     int ncu = 0, n_split = 0, n_chunk = 0;
     bool fp8 = false;
+    // LM-head row-groups of two rows (2 rg, 2 rg + 1) with several batch rows (x read from LDS
+    // per unit for every batch row): one x read then serves two rows
+    bool lm_pairs = false;
     int epu = UNIT_ELEMS;                // weight elements per unit (1024 with FP8 codes)
     int ku_h = 0, ku_q = 0, ku_f = 0;
     int chunk_begin[17] = {0};
