@@ -30,13 +30,17 @@ def _run(cmd, verbose):
 def build(verbose: bool = False) -> str:
     from concurrent.futures import ThreadPoolExecutor
     os.makedirs(BUILD, exist_ok=True)
-    units = [("mk_kernels.hip", []), ("mk_prefill.hip", []), ("mk_api.cpp", ["-x", "hip"]),
-             ("mk_plan.cpp", ["-x", "hip"])]
-    objs = [os.path.join(BUILD, src + ".o") for src, _ in units]
+    # (source, extra flags, object): the step kernels are built twice, for batch-1 handles and
+    # for handles with several batch rows
+    units = [("mk_kernels.hip", [], "mk_kernels.hip.o"),
+             ("mk_kernels.hip", ["-DMK_BATCHED_TU=1"], "mk_kernels_batched.hip.o"),
+             ("mk_prefill.hip", [], "mk_prefill.hip.o"), ("mk_api.cpp", ["-x", "hip"], "mk_api.cpp.o"),
+             ("mk_plan.cpp", ["-x", "hip"], "mk_plan.cpp.o")]
+    objs = [os.path.join(BUILD, obj) for _, _, obj in units]
     # the translation units are independent: compile them side by side
     with ThreadPoolExecutor(len(units)) as ex:
-        for f in [ex.submit(_run, ["hipcc"] + HIP_FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj], verbose)
-                  for (src, lang), obj in zip(units, objs)]:
+        for f in [ex.submit(_run, ["hipcc"] + HIP_FLAGS + extra + ["-c", os.path.join(CSRC, src), "-o", obj], verbose)
+                  for (src, extra, _), obj in zip(units, objs)]:
             f.result()
     tmp = LIB + ".tmp"
     _run(["hipcc", "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs, verbose)

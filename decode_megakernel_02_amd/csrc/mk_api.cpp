@@ -453,7 +453,7 @@ static int step_args_ok(mk_handle* h, const int32_t* tokens, const int32_t* posi
 // handles created with profiling or tracing run the instrumented kernel build, FP8 handles the FP8 one
 static uint32_t instr_flag(const mk_handle* h) {
     return ((h->hp.prof || h->hp.trace) ? KF_INSTRUMENTED : 0u) | (h->hp.fp8 ? KF_FP8 : 0u) |
-           ((h->cfg.flags & MK_FLAG_DEBUG_NAN) ? KF_POISON : 0u);
+           ((h->cfg.flags & MK_FLAG_DEBUG_NAN) ? KF_POISON : 0u) | (h->hp.B > 1 ? KF_BATCHED : 0u);
 }
 
 // MK_FLAG_DEBUG_NAN: NaN into the step's scratch before its first launch

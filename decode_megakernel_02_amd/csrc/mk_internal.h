@@ -145,6 +145,7 @@ constexpr uint32_t KF_FP8 = 4u;           // run the kernel build for FP8 weight
 constexpr uint32_t KF_GREEDY = 8u;        // single launch only: the build that also takes the argmax
 constexpr uint32_t KF_ABLATE = 16u;       // single launch only: the build that can skip one opcode's math
 constexpr uint32_t KF_POISON = 32u;       // debugging: fill the workgroup's LDS with NaN at launch
+constexpr uint32_t KF_BATCHED = 64u;      // handle with several batch rows: the batched build of the step
 constexpr int PROF_SLOTS = 8;          // counters per wave
 // Timeline record per instruction (100 MHz real-time clock): [0] op | layer << 8 |
 // a << 16 | b << 32 | cu << 48, then per compute wave w at [1 + 6w]: start,

@@ -27,6 +27,16 @@
 
 namespace mk {
 
+// This file is compiled twice: the step kernels for batch-1 handles (MK_BATCHED_TU 0, which also
+// holds every other kernel and the host entry points) and for handles with several batch rows
+// (MK_BATCHED_TU 1).  Each build then carries only the code its batch size takes: the batch-1
+// step keeps none of the 2..8-row dot products, the compute waves' own-row gather or the paired
+// LM-head rows, and stays within its register budget.
+#ifndef MK_BATCHED_TU
+#define MK_BATCHED_TU 0
+#endif
+constexpr bool TU_BATCHED = MK_BATCHED_TU != 0;
+
 // Explicit address spaces: the compiler otherwise emits flat instructions for
 // pointers it cannot trace, and a flat access to LDS is routed through the
 // vector-memory path, where it queues behind the loader's DMA.
@@ -756,6 +766,11 @@ __device__ __forceinline__ void rowgroup_dot(Ctx& cx, const Lds& s, Stream& st, 
 template <int NROWS, bool FP8>
 __device__ __forceinline__ void rowgroup_dot_batch(Ctx& cx, const Lds& s, Stream& st, const LDS float* xb, int ku,
                                                    RowOut& out) {
+    if constexpr (!TU_BATCHED) {  // the batch-1 build: one batch row (heads whose rows are not
+        // 2 or 4 units long take this general path at batch 1)
+        rowgroup_dot<NROWS, 1, FP8>(cx, s, st, xb, ku, out);
+        return;
+    }
     if constexpr (FP8) {  // FP8 handles take at most four batch rows (register budget)
         switch (cx.p->B) {
         case 1: rowgroup_dot<NROWS, 1, true>(cx, s, st, xb, ku, out); break;
@@ -978,7 +993,7 @@ __device__ __forceinline__ void gather_side(Ctx& cx, const Step& sp, const Inst&
 // the side inputs and raises the ready flag.  The first layer's QKV input (embedding rows, no
 // tags) stays with the gather wave.
 __device__ __forceinline__ bool rows_by_compute(CParams& p, const Inst& in) {
-    if (p.B == 1) return false;
+    if (!TU_BATCHED || p.B == 1) return false;
     switch (in.op) {
     case OP_RMS_QKV_ROPE: return in.layer > 0;
     case OP_RMS_LM_HEAD:
@@ -1422,7 +1437,7 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
             break;
         }
         default: {  // OP_RMS_LM_HEAD (row-group rg: row rg, or rows 2 rg and 2 rg + 1 with lm_pairs)
-            const int nr = KU == 0 && p.lm_pairs ? 2 : 1;
+            const int nr = TU_BATCHED && KU == 0 && p.lm_pairs ? 2 : 1;
             if (nr == 2) dot2(o);
             else dot1(o);
             if constexpr (FP8) fp8_scale(o);
@@ -2022,7 +2037,9 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
 // The whole step in one launch (every workgroup runs its full queue); GREEDY: the build that
 // also writes the argmax tokens and advances the positions; ABLATE: the build that can skip
 // the arithmetic of one opcode (Params::ablate_op) while keeping its data flow.
-template <int HEAD_DIM, bool INSTR, bool FP8 = false, bool GREEDY = false, bool ABLATE = false>
+// (BATCHED names the build in the kernel's symbol: the two builds of this file never share one)
+template <int HEAD_DIM, bool INSTR, bool FP8 = false, bool GREEDY = false, bool ABLATE = false,
+          bool BATCHED = TU_BATCHED>
 __global__ void __launch_bounds__(WG_THREADS, 1)
 mk_decode_kernel(const Params* __restrict__ pp, const int32_t* tokens, const int32_t* positions, uint16_t* kv,
                  float* logits, int stage, uint32_t flags) {
@@ -2030,13 +2047,14 @@ mk_decode_kernel(const Params* __restrict__ pp, const int32_t* tokens, const int
 }
 
 // One stage of the step (one op of one layer) per launch.
-template <int HEAD_DIM, bool INSTR, bool FP8 = false>
+template <int HEAD_DIM, bool INSTR, bool FP8 = false, bool BATCHED = TU_BATCHED>
 __global__ void __launch_bounds__(WG_THREADS, 1)
 mk_stage_kernel(const Params* __restrict__ pp, const int32_t* tokens, const int32_t* positions, uint16_t* kv,
                 float* logits, int stage, uint32_t flags) {
     step_body<HEAD_DIM, INSTR, FP8, false, false>(pp, tokens, positions, kv, logits, stage, flags);
 }
 
+#if !MK_BATCHED_TU
 // ----------------------------------------------------------- debug fill --
 
 // The NaN fill of MK_FLAG_DEBUG_NAN before a step: the value half of every tagged word (its tag,
@@ -2348,12 +2366,29 @@ hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int 
 
 // ------------------------------------------------------------ host launch --
 
+#endif  // !MK_BATCHED_TU
+
+#if MK_BATCHED_TU
+#define MK_LAUNCH_STEP launch_step_batched
+#define MK_SET_STEP_LDS set_step_kernel_lds_batched
+#else
+#define MK_LAUNCH_STEP launch_step_single
+#define MK_SET_STEP_LDS set_step_kernel_lds_single
+#endif
+hipError_t launch_step_batched(const Params*, int, int, size_t, const int32_t*, const int32_t*, void*, float*, int,
+                               uint32_t, hipStream_t);
+hipError_t launch_step_single(const Params*, int, int, size_t, const int32_t*, const int32_t*, void*, float*, int,
+                              uint32_t, hipStream_t);
+hipError_t set_step_kernel_lds_batched(size_t);
+hipError_t set_step_kernel_lds_single(size_t);
+
 // The whole-step launch waits across workgroups, so it needs every workgroup
 // resident at once: a cooperative launch guarantees that (or fails).  Per-op
 // launches only read results of earlier launches and use an ordinary launch.
-hipError_t launch_step(const Params* dev_params, int head_dim, int ncu, size_t lds_bytes, const int32_t* tokens,
-                       const int32_t* positions, void* kv, float* logits, int stage, uint32_t flags,
-                       hipStream_t stream) {
+// (this build's step kernels: batch-1 or batched)
+hipError_t MK_LAUNCH_STEP(const Params* dev_params, int head_dim, int ncu, size_t lds_bytes, const int32_t* tokens,
+                          const int32_t* positions, void* kv, float* logits, int stage, uint32_t flags,
+                          hipStream_t stream) {
     uint16_t* kv16 = (uint16_t*)kv;
     void* args[] = {(void*)&dev_params, (void*)&tokens, (void*)&positions, (void*)&kv16, (void*)&logits,
                     (void*)&stage, (void*)&flags};
@@ -2387,7 +2422,7 @@ hipError_t launch_step(const Params* dev_params, int head_dim, int ncu, size_t l
     return hipLaunchKernel(fn, dim3(ncu), dim3(WG_THREADS), args, lds_bytes, stream);
 }
 
-hipError_t set_step_kernel_lds(size_t lds_bytes) {
+hipError_t MK_SET_STEP_LDS(size_t lds_bytes) {
     const void* fns[] = {(const void*)mk_decode_kernel<64, false>, (const void*)mk_decode_kernel<128, false>,
                          (const void*)mk_stage_kernel<64, false>,  (const void*)mk_stage_kernel<128, false>,
                          (const void*)mk_decode_kernel<64, true>,  (const void*)mk_decode_kernel<128, true>,
@@ -2403,6 +2438,19 @@ hipError_t set_step_kernel_lds(size_t lds_bytes) {
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+#if !MK_BATCHED_TU
+// handles with several batch rows run the batched build (KF_BATCHED), batch-1 handles the other
+hipError_t launch_step(const Params* dev_params, int head_dim, int ncu, size_t lds_bytes, const int32_t* tokens,
+                       const int32_t* positions, void* kv, float* logits, int stage, uint32_t flags,
+                       hipStream_t stream) {
+    return (flags & KF_BATCHED ? launch_step_batched : launch_step_single)(
+        dev_params, head_dim, ncu, lds_bytes, tokens, positions, kv, logits, stage, flags, stream);
+}
+hipError_t set_step_kernel_lds(size_t lds_bytes) {
+    const hipError_t e = set_step_kernel_lds_single(lds_bytes);
+    return e != hipSuccess ? e : set_step_kernel_lds_batched(lds_bytes);
 }
 
 hipError_t launch_pack(const void* rows, uint32_t n, const uint16_t* const* mats, uint8_t* dst, int fp8,
@@ -2421,5 +2469,7 @@ hipError_t launch_row_amax(const uint16_t* w, uint32_t rows, uint32_t cols, uint
                        out);
     return hipGetLastError();
 }
+
+#endif  // !MK_BATCHED_TU
 
 }  // namespace mk
