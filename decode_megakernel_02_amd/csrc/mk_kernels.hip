@@ -210,10 +210,28 @@ struct Ctx {
     uint64_t t_mid;    // real time at which the main loop ended
     uint64_t t_ring;   // real-time ticks spent waiting for weight units in the current instruction
     uint64_t cnt[8];   // see mk_get_profile
-    float gv;          // fused greedy: largest logit of this wave's LM-head rows for batch row `lane`
-    uint32_t gi;       // and its lowest index (GREEDY_NONE: no row, or only NaN)
 };
 constexpr uint32_t GREEDY_NONE = 0xffffffffu;
+// Fused greedy: a (value, row) candidate as one 64-bit key whose unsigned order is the selection
+// order: the float's bits mapped to an order-preserving unsigned integer (-0 taken as +0, so that
+// equal values tie) above the row's complement (the lower row wins a tie).  0 is below every
+// key: no candidate.
+__device__ __forceinline__ uint64_t greedy_key(float v, uint32_t row) {
+    uint32_t u = __float_as_uint(v == 0.f ? 0.f : v);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint64_t)(0xffffffffu - row);
+}
+__device__ __forceinline__ void greedy_unkey(uint64_t k, float& v, uint32_t& row) {
+    if (k == 0) {
+        v = -__builtin_inff();
+        row = GREEDY_NONE;
+        return;
+    }
+    uint32_t u = (uint32_t)(k >> 32);
+    u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
+    v = __uint_as_float(u);
+    row = 0xffffffffu - (uint32_t)k;
+}
 
 __device__ __forceinline__ uint64_t cycles() { return __builtin_readcyclecounter(); }
 // constant-rate (100 MHz) clock shared by all CUs
@@ -277,8 +295,10 @@ __device__ __forceinline__ bool keep_waiting(Ctx& cx, uint32_t& spins, uint32_t 
 
 // ---------------------------------------------------------------- LDS map --
 
-constexpr int SYNC_WORDS = 3 * NW + 4 + MAX_SLOTS * MAX_BATCH;  // counters + ss, zeroed at launch
-static_assert(SYNC_WORDS <= 64, "sync words precede the prefetch dump");  // dump: words 64..127 of 512 B
+// counters, ss, the greedy keys and the last-CU flag, zeroed at launch
+constexpr int SYNC_WORDS = 3 * NW + 4 + MAX_SLOTS * MAX_BATCH + 2 * MAX_BATCH + 1;
+static_assert(SYNC_WORDS * 4 <= 512, "the sync words fit the 512-byte sync area");
+static_assert((3 * NW + 4 + MAX_SLOTS * MAX_BATCH) % 2 == 0, "the greedy keys are 8-byte aligned");
 
 struct Lds {
     LDS uint8_t* ring;      // [NW][ring_units][1024]
@@ -289,6 +309,8 @@ struct Lds {
     LDS uint32_t* ready;    // [MAX_SLOTS] r + 1 once instruction r's inputs are staged in buffer set r % nslot
     LDS uint32_t* done;     // [NW] instructions each compute wave has finished
     LDS float* ss;          // [MAX_SLOTS][MAX_BATCH] sum of squares of each x buffer's raw input rows
+    LDS uint64_t* gkey;     // [MAX_BATCH] fused greedy: the CU's best LM-head row per batch row (greedy_key)
+    LDS uint32_t* glast;    // fused greedy: 1 in the CU that merges every CU's rows
     LDS float* side0;       // nslot side buffers (side_floats each): epilogue inputs staged with x buffer i
     LDS float* rope;        // [B][D] (cos, sin) pairs of the step's positions, loaded once per launch
     LDS float* res;         // [B][res_stride] the CU's residual rows (O and down-projection tile)
@@ -305,6 +327,8 @@ __device__ __forceinline__ Lds lds_map(LDS uint8_t* smem, CParams& p) {
     m.ready = sync + 2 * NW + 1;
     m.done = sync + 2 * NW + 4;
     m.ss = (LDS float*)(sync + 3 * NW + 4);
+    m.gkey = (LDS uint64_t*)(sync + 3 * NW + 4 + MAX_SLOTS * MAX_BATCH);
+    m.glast = sync + 3 * NW + 4 + MAX_SLOTS * MAX_BATCH + 2 * MAX_BATCH;
     m.side0 = (LDS float*)(smem + off + (size_t)p.nslot * p.xbuf_bytes + 512);
     m.rope = m.side0 + (size_t)p.nslot * p.side_floats;
     m.res = m.rope + (size_t)p.B * p.D;
@@ -1446,12 +1470,11 @@ __device__ __forceinline__ void op_gemv(Ctx& cx, const Lds& s, Stream& st, uint3
                     const uint32_t row = nr == 2 ? 2 * rg + (uint32_t)k : rg;
                     const float v = o.mine[k] * scale;
                     gst(sp.logits + (size_t)b * p.V + row, v);
-                    // running (max, lowest index) of the rows: NaN never compares greater or equal
+                    // the CU's best row so far (largest value, then lowest index); NaN is never selected
                     if constexpr (GREEDY)
-                        if (v > cx.gv || (v == cx.gv && row < cx.gi)) {
-                            cx.gv = v;
-                            cx.gi = row;
-                        }
+                        if (v == v)
+                            __hip_atomic_fetch_max(s.gkey + b, greedy_key(v, row), __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_WORKGROUP);
                 }
             }
             break;
@@ -1813,64 +1836,77 @@ __device__ __forceinline__ void argmax_pair(float& v, uint32_t& i, float ov, uin
     }
 }
 
-// Greedy decoding inside the step (the single-launch GREEDY build): after its queue, every
-// CU merges its compute waves' (max, lowest index) pairs and publishes them as tagged words;
-// the last CU to count itself in (every other CU has then finished its queue, so none reads
-// the tokens or positions any more) merges all pairs, writes next token = argmax of each
+// Greedy decoding inside the step (the single-launch GREEDY build): the LM-head epilogue keeps
+// each CU's best row per batch row as an LDS key (greedy_key, LDS atomic max); after its queue,
+// every CU publishes its (max, lowest index) pairs as tagged words; the last CU to count itself
+// in (every other CU has then finished its queue, so none reads the tokens or positions any
+// more) merges all pairs, one compute wave per batch row, writes next token = argmax of each
 // logits row (lowest index among equal maxima, NaN never wins, 0 for a row without a number)
 // and advances the positions, then resets the counter for the next launch.
 __device__ __forceinline__ void greedy_finish(Ctx& cx, const Lds& s, const Step& sp, uint32_t& seq) {
     CParams& p = *cx.p;
     const int B = p.B;
     if (cx.aborted) return;
-    cbar(cx, s, seq);  // every wave is past its last instruction: buffer set 0 is free
-    LDS uint32_t* gs = (LDS uint32_t*)xslot(s, p, 0);  // [NW][MAX_BATCH] (value, index)
-    if (cx.lane < B) {
-        gs[(cx.wave * MAX_BATCH + cx.lane) * 2] = __float_as_uint(cx.gv);
-        gs[(cx.wave * MAX_BATCH + cx.lane) * 2 + 1] = cx.gi;
+    cbar(cx, s, seq);  // every wave is past its last instruction (its key updates are applied)
+    if (cx.aborted) return;
+    if (cx.wave == 0) {
+        if (cx.lane < B) {
+            float v;
+            uint32_t i;
+            greedy_unkey(s.gkey[cx.lane], v, i);
+            uint64_t* q = p.greedy_pair + ((size_t)cx.cu * MAX_BATCH + cx.lane) * 2;
+            st_tag(q, v, cx.epoch);
+            st_tag(q + 1, __uint_as_float(i), cx.epoch);
+        }
+        uint32_t old = 0;
+        if (cx.lane == 0) old = __hip_atomic_fetch_add(p.greedy_cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = uni(old) == (uint32_t)p.ncu - 1;
+        if (cx.lane == 0) {
+            if (last) __hip_atomic_store(p.greedy_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *s.glast = last ? 1u : 0u;
+        }
     }
     cbar(cx, s, seq);
-    if (cx.wave != 0 || cx.aborted) return;
-    const float ninf = -__builtin_inff();
-    float v = ninf;
-    uint32_t i = GREEDY_NONE;
-    if (cx.lane < B)
-        for (int w = 0; w < NW; ++w)
-            argmax_pair(v, i, __uint_as_float(gs[(w * MAX_BATCH + cx.lane) * 2]), gs[(w * MAX_BATCH + cx.lane) * 2 + 1]);
-    if (cx.lane < B) {
-        uint64_t* q = p.greedy_pair + ((size_t)cx.cu * MAX_BATCH + cx.lane) * 2;
-        st_tag(q, v, cx.epoch);
-        st_tag(q + 1, __uint_as_float(i), cx.epoch);
-    }
-    uint32_t old = 0;
-    if (cx.lane == 0) old = __hip_atomic_fetch_add(p.greedy_cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (uni(old) != (uint32_t)p.ncu - 1) return;
-    if (cx.lane == 0) __hip_atomic_store(p.greedy_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int ncu = p.ncu;
-    for (int bb = 0; bb < B; ++bb) {
-        float bv = ninf;
-        uint32_t bi = GREEDY_NONE;
-        for (int c0 = 0; c0 < ncu; c0 += 64) {
-            const int c = c0 + cx.lane;
-            const uint64_t* q = p.greedy_pair + ((size_t)(c < ncu ? c : 0) * MAX_BATCH + bb) * 2;
-            uint64_t wv = ld_tag(q), wi = ld_tag(q + 1);
-            uint32_t spins = 0;
-            while (any_lane(c < ncu && (tag_of(wv) != cx.epoch || tag_of(wi) != cx.epoch))) {
-                if (!keep_waiting(cx, spins, 0x60000000u | (uint32_t)c0)) return;
-                if (tag_of(wv) != cx.epoch) wv = ld_tag(q);
-                if (tag_of(wi) != cx.epoch) wi = ld_tag(q + 1);
+    if (cx.aborted || uni(lds_ld(s.glast)) == 0u || cx.wave >= B) return;
+    // the last CU: compute wave bb merges batch row bb over every CU's pair, each lane polling four
+    // CUs' pairs (value word and index word in one 16-byte load) at once
+    const int bb = cx.wave, ncu = p.ncu;
+    const uint32_t ep = cx.epoch;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p.greedy_pair, (short)0, ncu * MAX_BATCH * 16, RSRC_WORD3);
+    float bv = -__builtin_inff();
+    uint32_t bi = GREEDY_NONE;
+    for (int c0 = 0; c0 < ncu; c0 += 256) {
+        u32x4 w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            w[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, ((c0 + 64 * j + cx.lane) * MAX_BATCH + bb) * 16, 0, CPOL_SC1);
+        uint32_t spins = 0;
+        while (true) {
+            bool stale = false;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) stale |= c0 + 64 * j + cx.lane < ncu && (w[j].y != ep || w[j].w != ep);
+            if (!any_lane(stale)) break;
+            if (!keep_waiting(cx, spins, 0x60000000u | (uint32_t)c0)) return;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c = c0 + 64 * j + cx.lane;
+                if (c < ncu && (w[j].y != ep || w[j].w != ep))
+                    w[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (c * MAX_BATCH + bb) * 16, 0, CPOL_SC1);
             }
-            if (c < ncu) argmax_pair(bv, bi, val_of(wv), __float_as_uint(val_of(wi)));
         }
-        for (int d = 32; d >= 1; d >>= 1) {
-            const float ov = __shfl_xor(bv, d);
-            const uint32_t oi = (uint32_t)__shfl_xor((int)bi, d);
-            argmax_pair(bv, bi, ov, oi);
-        }
-        if (cx.lane == 0) {
-            gst((int32_t*)sp.tokens + bb, bi == GREEDY_NONE ? 0 : (int32_t)bi);
-            gst((int32_t*)sp.positions + bb, __builtin_amdgcn_readlane(sp.pos, bb) + 1);
-        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (c0 + 64 * j + cx.lane < ncu) argmax_pair(bv, bi, __uint_as_float(w[j].x), w[j].z);
+    }
+    for (int d = 32; d >= 1; d >>= 1) {
+        const float ov = __shfl_xor(bv, d);
+        const uint32_t oi = (uint32_t)__shfl_xor((int)bi, d);
+        argmax_pair(bv, bi, ov, oi);
+    }
+    if (cx.lane == 0) {
+        gst((int32_t*)sp.tokens + bb, bi == GREEDY_NONE ? 0 : (int32_t)bi);
+        gst((int32_t*)sp.positions + bb, __builtin_amdgcn_readlane(sp.pos, bb) + 1);
     }
 }
 
@@ -1901,8 +1937,6 @@ __device__ __forceinline__ void step_body(const Params* __restrict__ pp, const i
     cx.trace = INSTR && p.trace != nullptr;
     cx.t_in = cx.t_acq = cx.t_mid = cx.t_ring = 0;
     for (int k = 0; k < 8; ++k) cx.cnt[k] = 0;
-    cx.gv = -__builtin_inff();
-    cx.gi = GREEDY_NONE;
     const uint64_t t_kernel = cx.prof ? cycles() : 0;
     auto flush_prof = [&](int wave_slot) {
         if (cx.prof && cx.lane == 0) {
