@@ -4,7 +4,8 @@ Against the two-launch path (mk_decode_step + mk_greedy_advance) from the same s
 logits of every step are bit-identical (the same op bodies), and so are the tokens and
 positions; every token is the lowest-index argmax of its step's logits; the logits follow the
 teacher-forced oracle to the usual bar (tokens where the oracle's top two are clearly apart).
-Also captured in a graph (MK_GRAPH_FUSED_GREEDY), replays separated by eager work."""
+Also captured in a graph (MK_GRAPH_FUSED_GREEDY), replays separated by eager work; and heads
+built so that the largest logit is tied across rows, waves and CUs (the lowest index wins)."""
 import dataclasses
 
 import numpy as np
@@ -18,7 +19,7 @@ pytestmark = pytest.mark.gpu
 FP8 = 4  # MK_FLAG_FP8_WEIGHTS
 
 
-def run_both(shape, weights, batch, prompt_lens, steps, flags=0, kv_fill=True):
+def run_both(shape, weights, batch, prompt_lens, steps, flags=0, kv_fill=True, return_run=False):
     import torch
     from decode_megakernel_02_amd import mk
     P = np.asarray(prompt_lens, dtype=np.int32)
@@ -61,13 +62,61 @@ def run_both(shape, weights, batch, prompt_lens, steps, flags=0, kv_fill=True):
     oracle_run = H.Run(b.tokens[:steps], b.positions[:steps], b.logits)
     ref = H.oracle_replay(shape, weights, batch, max_seq, oracle_run, kv_init=kv, nthreads=16,
                           fp8="row" if flags & FP8 else False)
-    return H.compare(oracle_run, ref, f"fused greedy {shape.name} b{batch}")
+    stats = H.compare(oracle_run, ref, f"fused greedy {shape.name} b{batch}")
+    return (stats, b) if return_run else stats
 
 
 @pytest.mark.parametrize("batch", [1, 2, 4])
 def test_tiny(batch):
     shape = synth.TINY
     print(run_both(shape, synth.make_weights(shape), batch, [20 + 3 * b for b in range(batch)], 6))
+
+
+def _head_with_every_row_four_times(shape):
+    """The seeded weights with an LM head (the tied embedding) in which every row occurs four
+    times: row 2k + 1 is a copy of row 2k, and the second half of the vocabulary a copy of the
+    first.  Whatever the hidden state, the largest logit is then a four-way tie at rows 2k,
+    2k + 1, 2k + V/2 and 2k + V/2 + 1: within one row pair (batched LM head), across the
+    waves of one CU (batch 1) and across CUs."""
+    w = dict(synth.make_weights(shape))
+    key = "embed" if w["lm_head"] is None else "lm_head"
+    head = np.ascontiguousarray(w[key]).copy()
+    V = shape.vocab
+    head[1::2] = head[0::2]
+    head[V // 2:] = head[:V // 2]
+    w[key] = head
+    return w
+
+
+@pytest.mark.parametrize("batch", [1, 3])
+def test_tied_maximum_takes_the_lowest_index(batch):
+    """Equal largest logits on several rows, waves and CUs: the fused token is the lowest of them
+    (the order np.argmax and the oracle's selection use)."""
+    shape = synth.TINY
+    V = shape.vocab
+    stats, run = run_both(shape, _head_with_every_row_four_times(shape), batch, [20 + 3 * b for b in range(batch)],
+                          4, return_run=True)
+    print(stats)
+    for i, lg in enumerate(run.logits):
+        for b in range(batch):
+            top = np.flatnonzero(lg[b] == lg[b].max())
+            t = top[0]
+            assert t % 2 == 0 and t < V // 2 and {t, t + 1, t + V // 2, t + V // 2 + 1} <= set(top.tolist()), (i, b, top)
+            assert run.tokens[i + 1][b] == t, (i, b, run.tokens[i + 1][b], top)
+
+
+@pytest.mark.parametrize("batch", [1, 3])
+def test_zero_head_ties_every_row(batch):
+    """An all-zero LM head (the tied embedding): every logit of every row is 0, a tie across all
+    rows, waves and CUs, so every fused token is 0."""
+    shape = synth.TINY
+    w = dict(synth.make_weights(shape))
+    w["embed"] = np.zeros_like(w["embed"])
+    stats, run = run_both(shape, w, batch, [20 + 3 * b for b in range(batch)], 3, return_run=True)
+    print(stats)
+    for i, lg in enumerate(run.logits):
+        assert not lg.any(), i
+        np.testing.assert_array_equal(run.tokens[i + 1], np.zeros(batch, dtype=np.int32))
 
 
 def test_llama1b_full(llama1b):
