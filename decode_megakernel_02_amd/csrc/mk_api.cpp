@@ -41,7 +41,9 @@ struct mk_handle {
     mk_config cfg{};
     Plan plan;
     Params hp{};
-    Params* dparams = nullptr;
+    Params* dparams = nullptr;        // the single-launch step's parameter block
+    Params* dparams_stage = nullptr;  // the per-op launches' block (its own LDS layout)
+    size_t lds_bytes_stage = 0;
     std::vector<void*> allocs;  // everything hipMalloc'ed, freed in mk_destroy
     size_t lds_bytes = 0;
     bool loaded = false;
@@ -242,15 +244,24 @@ int mk_create(const mk_config* cfg, mk_handle** out) {
             const long budget = (long)LDS_BYTES - nslot * (long)(xb + side_bytes) - (long)sync_bytes - (long)keep_bytes;
             return (int)std::min<long>(32, budget / (NW * UNIT_BYTES));
         };
-        // three buffer sets when the rings keep at least 12 slots, else two; one when two
-        // would leave the rings under 4 slots (large batch x hidden)
-        int nslot = rings_for(3) >= std::max(ring_need, 12) ? 3 : rings_for(2) >= 4 ? 2 : 1;
+        // one buffer set: the gather wave stages an instruction's inputs once every compute wave is
+        // done with the previous instruction.  Staging one or two instructions ahead (the kernel
+        // takes up to MAX_SLOTS sets) measured slower on every workload: the early polls of inputs
+        // that are not produced yet slow the step, and the sets' LDS serves the weight rings instead.
+        const int nslot = 1;
         const int ring_units = rings_for(nslot);
         if (ring_units < ring_need) {
             delete h;
             return fail(nullptr, MK_ERR_UNSUPPORTED_SHAPE, "batch x hidden too large for the LDS budget");
         }
         h->lds_bytes = (size_t)NW * ring_units * UNIT_BYTES + nslot * (xb + side_bytes) + sync_bytes + keep_bytes;
+        // the per-op launches run one stage per launch, where staging ahead still pays: three buffer
+        // sets when the rings keep at least 12 slots, else two when they keep 4 (and what the batch-1
+        // path needs), else one
+        int nslot_stage = rings_for(3) >= std::max(ring_need, 12) ? 3 : rings_for(2) >= std::max(ring_need, 4) ? 2 : 1;
+        const int ring_units_stage = rings_for(nslot_stage);
+        h->lds_bytes_stage =
+            (size_t)NW * ring_units_stage * UNIT_BYTES + nslot_stage * (xb + side_bytes) + sync_bytes + keep_bytes;
         h->hp.lds_bytes = (uint32_t)h->lds_bytes;
 
         Params& hp = h->hp;
@@ -345,7 +356,13 @@ int mk_create(const mk_config* cfg, mk_handle** out) {
         HIPCHK(hipMemset(h->greedy_cnt, 0, (size_t)B * 4));
         h->dparams = dalloc<Params>(h, 1);
         HIPCHK(hipMemcpy(h->dparams, &hp, sizeof hp, hipMemcpyHostToDevice));
-        HIPCHK(set_step_kernel_lds(h->lds_bytes));
+        Params hs = hp;
+        hs.nslot = nslot_stage;
+        hs.ring_units = ring_units_stage;
+        hs.lds_bytes = (uint32_t)h->lds_bytes_stage;
+        h->dparams_stage = dalloc<Params>(h, 1);
+        HIPCHK(hipMemcpy(h->dparams_stage, &hs, sizeof hs, hipMemcpyHostToDevice));
+        HIPCHK(set_step_kernel_lds(std::max(h->lds_bytes, h->lds_bytes_stage)));
         HIPCHK(hipDeviceSynchronize());
     } catch (const HipError& e) {
         int code = hip_fail(nullptr, e);
@@ -498,8 +515,8 @@ int mk_decode_step_multikernel(mk_handle* h, const int32_t* tokens, const int32_
     hipError_t e0 = poison_before_step(h, logits, (hipStream_t)stream);
     if (e0 != hipSuccess) return hip_fail(h, HipError{e0, "mk_poison_kernel launch"});
     for (int st = 0; st < ns; ++st) {
-        hipError_t e = launch_step(h->dparams, h->hp.D, h->hp.ncu, h->lds_bytes, tokens, positions, kv_cache, logits, st,
-                                   (st == ns - 1 ? KF_BUMP_EPOCH : 0u) | instr_flag(h), (hipStream_t)stream);
+        hipError_t e = launch_step(h->dparams_stage, h->hp.D, h->hp.ncu, h->lds_bytes_stage, tokens, positions, kv_cache,
+                                   logits, st, (st == ns - 1 ? KF_BUMP_EPOCH : 0u) | instr_flag(h), (hipStream_t)stream);
         if (e != hipSuccess) return hip_fail(h, HipError{e, "mk_step_kernel stage launch"});
     }
     return MK_OK;
@@ -530,6 +547,7 @@ int mk_set_spin_limit(mk_handle* h, uint32_t spins) {
         HIPCHK(hipSetDevice(h->cfg.device));
         HIPCHK(hipDeviceSynchronize());  // no step may be reading the parameter block
         HIPCHK(hipMemcpy(&h->dparams->spin_limit, &h->hp.spin_limit, sizeof(uint32_t), hipMemcpyHostToDevice));
+        HIPCHK(hipMemcpy(&h->dparams_stage->spin_limit, &h->hp.spin_limit, sizeof(uint32_t), hipMemcpyHostToDevice));
     } catch (const HipError& e) {
         return hip_fail(h, e);
     }
@@ -542,8 +560,8 @@ int mk_debug_stage(mk_handle* h, int32_t stage, const int32_t* tokens, const int
     if (rc != MK_OK) return rc;
     if (stage < 0 || stage >= h->hp.n_stages) return fail(h, MK_ERR_INVALID_ARG, "stage outside [0, n_stages)");
     // the epoch advances, so nothing this launch writes is ever taken for a later step's data
-    hipError_t e = launch_step(h->dparams, h->hp.D, h->hp.ncu, h->lds_bytes, tokens, positions, kv_cache, logits,
-                               stage, KF_BUMP_EPOCH | instr_flag(h), (hipStream_t)stream);
+    hipError_t e = launch_step(h->dparams_stage, h->hp.D, h->hp.ncu, h->lds_bytes_stage, tokens, positions, kv_cache,
+                               logits, stage, KF_BUMP_EPOCH | instr_flag(h), (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(h, HipError{e, "mk_step_kernel stage launch"});
     return MK_OK;
 }
@@ -651,8 +669,8 @@ int mk_graph_create(mk_handle* h, int32_t* tokens, int32_t* positions, void* kv_
             }
             if (flags & MK_GRAPH_MULTIKERNEL) {
                 for (int st = 0; st < ns && first.e == hipSuccess; ++st)
-                    first = HipError{launch_step(h->dparams, h->hp.D, h->hp.ncu, h->lds_bytes, tokens, positions,
-                                                 kv_cache, logits, st,
+                    first = HipError{launch_step(h->dparams_stage, h->hp.D, h->hp.ncu, h->lds_bytes_stage, tokens,
+                                                 positions, kv_cache, logits, st,
                                                  (st == ns - 1 ? KF_BUMP_EPOCH : 0u) | instr_flag(h), cs),
                                      "mk_step_kernel stage launch"};
             } else if (flags & MK_GRAPH_FUSED_GREEDY) {

@@ -79,7 +79,8 @@ struct Params {
     int32_t xbuf_bytes;     // bytes of one of the two LDS x buffers
     int32_t side_floats;    // floats of each LDS side buffer (epilogue inputs staged by the gather
                             // wave); 0: epilogue inputs are read from global memory instead
-    int32_t nslot;          // x / side buffer sets (2 or 3): the gather wave runs nslot - 1 instructions ahead
+    int32_t nslot;          // x / side buffer sets (1 to MAX_SLOTS; the host takes 1): the gather wave runs
+                            // nslot - 1 instructions ahead
     int32_t res_stride;     // floats per batch row of the LDS residual rows (the CU's rows of the O and
                             // down projections, which are the same tile); 0: no resident rows
     int32_t ncu;            // workgroups in the grid

@@ -1199,9 +1199,11 @@ __device__ __forceinline__ void gatherer(Ctx& cx, const Lds& s, const Step& sp, 
         if (by_compute) {
             // the compute waves stage the x rows
         } else if (NGATHER == 1 && key != 0 && key == prev_key) {  // its buffer set still holds it:
-            // the wave refills a set only nslot instructions later, after this copy
-            copy_staged(cx, xslot(s, p, prev_slot), xslot(s, p, slot), p.B * (int)uni((uint32_t)p.xstride),
-                        s.ss + prev_slot * MAX_BATCH, s.ss + slot * MAX_BATCH, p.B);
+            // the wave refills a set only nslot instructions later, after this copy (with one set,
+            // the data is already in place)
+            if (slot != prev_slot)
+                copy_staged(cx, xslot(s, p, prev_slot), xslot(s, p, slot), p.B * (int)uni((uint32_t)p.xstride),
+                            s.ss + prev_slot * MAX_BATCH, s.ss + slot * MAX_BATCH, p.B);
         } else {
             gather_inst<FP8>(cx, sp, in, xslot(s, p, slot), s.ss + slot * MAX_BATCH);
         }

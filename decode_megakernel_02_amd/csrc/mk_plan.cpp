@@ -145,7 +145,11 @@ int build_plan(const mk_config& c, int ncu, Plan& p, std::string& err) {
     p.F = c.ffn; p.V = c.vocab; p.B = c.batch; p.max_seq = c.max_seq; p.G = p.Hq / p.Hkv;
     p.tied = c.tied_embeddings != 0; p.eps = c.rms_eps; p.theta = c.rope_theta;
     p.ncu = ncu;
-    p.n_chunk = c.n_chunks ? c.n_chunks : 4;
+    // down-projection K-chunks: 2 for 2 to 4 batch rows with F <= 8192 (every GEMV takes the batched
+    // path there, and fewer chunk instructions mean fewer instruction boundaries on the critical
+    // path), else 4 (at batch 1 a chunk of at most four units keeps the batch-1 GEMV path; with
+    // more rows or a wider F, two chunks would take the LDS the weight rings need)
+    p.n_chunk = c.n_chunks ? c.n_chunks : (p.B >= 2 && p.B <= 4 && p.F <= 8192 ? 2 : 4);
     if (p.n_chunk > p.F / 8) p.n_chunk = std::max(1, p.F / 8);
     if (c.n_splits) {
         p.n_split = c.n_splits;

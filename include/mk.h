@@ -62,7 +62,8 @@ typedef struct {
     int32_t device;          /* HIP device ordinal */
     int32_t n_cus;           /* 0 = every CU of the device; else a smaller grid */
     int32_t n_splits;        /* split-KV partitions per (row, KV group); 0 = auto */
-    int32_t n_chunks;        /* K-chunks of the down projection; 0 = auto (4) */
+    int32_t n_chunks;        /* K-chunks of the down projection; 0 = auto (2 for 2..4 batch rows
+                                with ffn <= 8192, else 4) */
     uint32_t flags;          /* MK_FLAG_* */
 } mk_config;
 

@@ -60,7 +60,7 @@ def test_schedule_is_valid(shape_name, batch, max_seq, ncus):
     seg = pad(-(-F // info.n_chunks // 8) * 8) * info.n_chunks
     padded = 2 * (shape.n_layers * (rows_h * pad(H) + H * pad(shape.n_q_heads * D) + H * seg) + V * pad(H))
     assert dense <= info.packed_weight_bytes <= padded
-    if H % 512 == 0 and F % (512 * info.n_chunks) == 0:
+    if H % 512 == 0 and (shape.n_q_heads * D) % 512 == 0 and F % (512 * info.n_chunks) == 0:
         assert info.packed_weight_bytes == dense
     assert info.min_stream_bytes_per_wave >= 0
     assert info.max_stream_bytes_per_wave * 8 * ncus >= info.packed_weight_bytes
