@@ -394,7 +394,7 @@ __device__ __forceinline__ void cbar(Ctx& cx, const Lds& s, uint32_t& seq) {
 #define MK_LD_ROWS 7
 #endif
 #ifndef MK_LD_KEEP
-#define MK_LD_KEEP 3
+#define MK_LD_KEEP 2
 #endif
 constexpr uint32_t LD_ROWS = MK_LD_ROWS;  // unit-rows in flight (NW DMAs each; vmcnt counts at most 63)
 constexpr uint32_t LD_KEEP = MK_LD_KEEP;  // unit-rows left in flight when retiring
