@@ -245,9 +245,9 @@ int mk_create(const mk_config* cfg, mk_handle** out) {
             return (int)std::min<long>(32, budget / (NW * UNIT_BYTES));
         };
         // one buffer set: the gather wave stages an instruction's inputs once every compute wave is
-        // done with the previous instruction.  Staging one or two instructions ahead (the kernel
-        // takes up to MAX_SLOTS sets) measured slower on every workload: the early polls of inputs
-        // that are not produced yet slow the step, and the sets' LDS serves the weight rings instead.
+        // done with the previous instruction, and the LDS of further sets goes to the weight rings.
+        // Staging one or two instructions ahead (the kernel takes up to MAX_SLOTS sets) measured
+        // slower on every workload.
         const int nslot = 1;
         const int ring_units = rings_for(nslot);
         if (ring_units < ring_need) {
