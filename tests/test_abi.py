@@ -66,6 +66,18 @@ def test_schedule_is_valid(shape_name, batch, max_seq, ncus):
     assert info.max_stream_bytes_per_wave * 8 * ncus >= info.packed_weight_bytes
 
 
+@pytest.mark.parametrize("shape_name,batch,chunks", [
+    ("LLAMA_1B", 1, 4), ("LLAMA_1B", 2, 2), ("LLAMA_1B", 4, 2), ("LLAMA_1B", 5, 4), ("LLAMA_1B", 8, 4),
+    ("LLAMA_8B", 1, 4), ("LLAMA_8B", 4, 4), ("TINY", 3, 2), ("LLAMA_1B_TP8_SHARD", 1, 4),
+])
+def test_default_down_chunks(shape_name, batch, chunks):
+    """n_chunks = 0 picks 2 down-projection chunks for 2 to 4 batch rows with ffn <= 8192, else 4;
+    an explicit count is kept."""
+    shape = getattr(synth, shape_name)
+    assert mk.mk_schedule_inspect(mk.make_config(shape, batch, 1040), 256).n_chunks == chunks
+    assert mk.mk_schedule_inspect(mk.make_config(shape, batch, 1040, n_chunks=3), 256).n_chunks == 3
+
+
 @pytest.mark.parametrize("shape_name,bound", [("LLAMA_1B", 1.1), ("LLAMA_8B", 1.12)])
 def test_schedule_balances_weight_streams(shape_name, bound):
     """The eight compute waves of a CU get nearly equal weight streams at the
